@@ -1,0 +1,258 @@
+/*
+ * kda_tree.h -- C-ABI of the tree-packed chunkwise KDA library (libkda_tree.so)
+ *
+ * What the library computes follows the HARTS pages (arXiv 2608.28158):
+ *   - devfeed.tech abstract: prefix sharing over rollout trees; differentiable
+ *     boundary-state handoff and bounded replay keep each trajectory's
+ *     chunkwise numerical path; a linear-time planner reaches the minimum
+ *     number of sequential linear-attention calls under the packed
+ *     chunkwise-call model; log-probs are recovered per original position.
+ *   - thelatestinai.com Figure 1 (compact layout, call example), Figure 2
+ *     (continuations, replay-started side branches, rounds = packed calls),
+ *     Figure C.1(b) (replay inside the core writes no outputs) and C.1(d)
+ *     (mapped log-probs without expanded logits).
+ *   - zot.news summary: the interfaces keep gradient flow and RL objectives.
+ *
+ * The KDA recurrence (the pages name it but do not print it) is the gated
+ * delta rule, per head, with state S (dk x dv, fp32):
+ *     Sbar = diag(exp(g_t)) S;  u = beta_t (v_t - Sbar^T k_t);
+ *     S = Sbar + k_t u^T;       o_t = scale * S^T q_t.
+ *
+ * Conventions for every call:
+ *   - All device memory is owned by the caller.  Tensors are contiguous,
+ *     row-major, with the row (token) dimension first: q,k [rows,H,dk];
+ *     v [rows,H,dv]; g [rows,H,dk] fp32; beta [rows,H] fp32; o [rows,H,dv]
+ *     fp32; states [*,H,dk,dv] fp32.
+ *   - The library never allocates device memory and never synchronises the
+ *     device.  Work is enqueued on `stream` (a hipStream_t; NULL = default
+ *     stream) in stream order.
+ *   - Results are deterministic: bitwise identical from run to run (no
+ *     floating-point atomics; every reduction has a fixed order).
+ *   - Status codes: KDA_OK (0) or a negative KDA_ERR_*; on error nothing is
+ *     enqueued and kda_last_error() holds a message (thread-local).
+ */
+#ifndef KDA_TREE_H
+#define KDA_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KDA_OK = 0,
+  KDA_ERR_TREE = -1,      /* malformed tree: bad parent, cycle, zero length, overlapping rows */
+  KDA_ERR_SHAPE = -2,     /* unsupported head dims / chunk size / dtype */
+  KDA_ERR_WORKSPACE = -3, /* a workspace or buffer is smaller than required */
+  KDA_ERR_ARG = -4,       /* null pointer or inconsistent argument */
+  KDA_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed */
+};
+
+enum { KDA_MODE_MINCALL = 0, KDA_MODE_EXPANDED = 1 };
+enum { KDA_DTYPE_FP32 = 0, KDA_DTYPE_BF16 = 1 };
+
+typedef struct kda_plan kda_plan;
+
+typedef struct {
+  int32_t n_seg, n_rounds, n_seq, n_chunks, n_buf, n_leaf, n_root, chunk, mode;
+  int32_t max_seq_per_round;
+  int64_t n_rows;      /* compact (unique) rows N */
+  int64_t n_packed;    /* packed rows over all rounds (N + R in MINCALL mode) */
+  int64_t n_out_rows;  /* rows of o / dO / input gradients (N, or n_packed in EXPANDED) */
+  int64_t R;           /* total replay rows */
+  int64_t n_pos;       /* trajectory positions with a next-token target */
+  int64_t n_expanded;  /* sum of trajectory lengths */
+  size_t device_bytes; /* size of the device copy made by kda_plan_upload */
+} kda_plan_info_t;
+
+/*
+ * kda_tree_plan -- validate a rollout tree and build its min-call plan (host only).
+ *
+ * Follows the Figure 2 call model (thelatestinai.com) and the abstract's
+ * linear-time planner: every fork-free segment runs once; each internal
+ * segment continues one child directly (same sequence, same round); every
+ * other child is side-started from the boundary state at b = B*floor(p/B)
+ * (p = the fork position) and replays r = p - b < B parent rows without
+ * writing outputs.  It starts in the round of its parent's sequence when b is
+ * where that sequence started, otherwise in the next round.  A two-mode
+ * dynamic program picks the continuations that minimise the number of rounds
+ * (ties: larger side cost, larger subtree token count, smaller segment id).
+ * Sequences of a round are ordered by head segment id.
+ *
+ *   n_seg    number of segments (> 0)
+ *   parent   [n_seg] parent segment id, -1 for a root (a forest is allowed;
+ *            roots are indexed by ascending id for h0 / dh0)
+ *   seg_len  [n_seg] tokens per segment (> 0)
+ *   seg_row  [n_seg] first compact row of each segment, or NULL for segments
+ *            packed in id order; the ranges must tile [0, N) exactly
+ *   chunk    chunk size B (>= 1; the kernels accept 16 and 64)
+ *   mode     KDA_MODE_MINCALL, or KDA_MODE_EXPANDED: one sequence per
+ *            trajectory (leaf ascending), all in one round, no sharing; rows
+ *            of o / dO / gradients are then the packed (expanded) rows.
+ *   out      receives the plan (immutable; free with kda_plan_destroy)
+ * Host pointers.  Errors: KDA_ERR_TREE, KDA_ERR_ARG.
+ */
+int kda_tree_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
+                  const int64_t* seg_row, int32_t chunk, int32_t mode, kda_plan** out);
+
+void kda_plan_destroy(kda_plan* plan);
+
+/* Sizes and counts of a plan.  Host pointers. */
+int kda_plan_info(const kda_plan* plan, kda_plan_info_t* info);
+
+/*
+ * kda_plan_export -- copy one canonical plan array to host memory as int64.
+ * Returns the array length (>= 0) when dst is NULL or n >= length, else a
+ * KDA_ERR_*.  Arrays:
+ *   SEG_*      per segment: round, sequence, 1 if a direct continuation,
+ *              start b of a side/root sequence (-1 for continuations), replay r
+ *   ROUND_SEQ_PTR  [n_rounds+1] sequences of each round (sequence order)
+ *   SEQ_*      per sequence: round, head segment, leaf index, start position
+ *              b_head, replay rows, packed-row and chunk ranges ([n_seq+1]),
+ *              init kind (0 root h0, 1 handoff buffer) and index
+ *   CHUNK_*    per chunk: sequence, first packed row, rows (<= B), handoff
+ *              buffer saved at its end (-1 none)
+ *   ROW_INDEX  per packed row: compact row read;  OUT_ROW: row written (-1 replay)
+ *   BUF_*      per handoff buffer: producer sequence, trajectory position,
+ *              chunk whose end it is, consumer sequences (CSR)
+ *   POS_ROW, POS_NEXT_ROW  gather map (trajectories by leaf id, positions
+ *              0..L-2): row of the position and row of its next token;
+ *   ROW_POS_PTR/IDX  positions of every compact row (CSR, ascending)
+ *   LEAF_SEG, ROOT_SEG  leaf and root segment ids, ascending
+ */
+enum {
+  KDA_F_SEG_ROUND = 0, KDA_F_SEG_SEQ, KDA_F_SEG_IS_CONT, KDA_F_SEG_B, KDA_F_SEG_REPLAY,
+  KDA_F_ROUND_SEQ_PTR, KDA_F_SEQ_ROUND, KDA_F_SEQ_HEAD, KDA_F_SEQ_LEAF, KDA_F_SEQ_B_HEAD,
+  KDA_F_SEQ_REPLAY, KDA_F_SEQ_ROW_PTR, KDA_F_SEQ_CHUNK_PTR, KDA_F_SEQ_INIT_KIND,
+  KDA_F_SEQ_INIT_IDX, KDA_F_CHUNK_SEQ, KDA_F_CHUNK_ROW0, KDA_F_CHUNK_LEN, KDA_F_CHUNK_SAVE,
+  KDA_F_ROW_INDEX, KDA_F_OUT_ROW, KDA_F_BUF_SEQ, KDA_F_BUF_POS, KDA_F_BUF_CHUNK,
+  KDA_F_BUF_CONS_PTR, KDA_F_BUF_CONS, KDA_F_POS_ROW, KDA_F_POS_NEXT_ROW, KDA_F_ROW_POS_PTR,
+  KDA_F_ROW_POS_IDX, KDA_F_LEAF_SEG, KDA_F_ROOT_SEG,
+  KDA_F_COUNT
+};
+int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64_t n);
+
+/*
+ * kda_plan_upload -- copy the plan's int32 device tables into a caller-owned
+ * device buffer of at least info.device_bytes bytes (256-byte aligned), with
+ * an asynchronous host-to-device copy on `stream`.  The host staging memory
+ * stays owned by the plan, so the plan must outlive the copy.  This is the
+ * only host-to-device transfer of the library.
+ */
+int kda_plan_upload(const kda_plan* plan, void* dev, size_t bytes, void* stream);
+
+/* Byte offset of an int32 table (KDA_F_POS_ROW, KDA_F_POS_NEXT_ROW,
+ * KDA_F_ROW_POS_PTR, KDA_F_ROW_POS_IDX, KDA_F_ROW_INDEX, KDA_F_OUT_ROW) inside
+ * the uploaded device copy, or a negative KDA_ERR_*. */
+int64_t kda_plan_device_offset(const kda_plan* plan, int32_t field);
+
+/*
+ * Buffer sizes for kda_tree_fwd / kda_tree_bwd at head count H and head dims
+ * dk, dv.  `saved` is written by the forward and read by the backward (the
+ * start state of every chunk and every handoff state, fp32); `ws` is scratch
+ * (any content on entry).  Both are in bytes; 0 for an unsupported shape.
+ */
+size_t kda_saved_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv);
+size_t kda_fwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv);
+size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv);
+
+/*
+ * kda_tree_fwd -- forward pass of tree-packed chunkwise KDA.
+ *
+ * Runs every packed round (one launch group per round, in stream order): each
+ * sequence starts from its root's h0 or from a handoff state saved by an
+ * earlier round, replays its leading rows without writing outputs, and
+ * emits per-token outputs and its leaf's final state (Figure 1(b): linear
+ * attention consumes a state and produces a branch-specific next state).
+ *
+ *   plan, dev_plan  the plan and its uploaded device copy
+ *   H, dk, dv       heads and head dims; supported: dk = dv in {64, 128}
+ *   in_dtype        dtype of q, k, v: KDA_DTYPE_BF16 or KDA_DTYPE_FP32
+ *   scale           output scale (usually 1/sqrt(dk))
+ *   q, k, v         [N,H,dk], [N,H,dk], [N,H,dv] compact rows (device)
+ *   g               [N,H,dk] fp32 log-decay per channel (<= 0 expected)
+ *   beta            [N,H] fp32 write strength
+ *   h0              [n_root,H,dk,dv] fp32 initial states, or NULL for zeros
+ *   o               [n_out_rows,H,dv] fp32 outputs (replay rows write nothing)
+ *   h_leaf          [n_leaf,H,dk,dv] fp32 final state per leaf (leaves ascending)
+ *   saved           kda_saved_bytes(...) bytes, kept for kda_tree_bwd
+ *   ws, ws_bytes    scratch of kda_fwd_workspace_bytes(...) bytes
+ * Supported gate range: the chunk math factors per-pair decays through the
+ * first row of each 16-row block; sum(|g|) over any 15 consecutive rows of a
+ * chunk must stay below 80 per channel (fp32 exponent range).
+ * Errors: KDA_ERR_SHAPE, KDA_ERR_WORKSPACE, KDA_ERR_ARG, KDA_ERR_HIP.
+ */
+int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
+                 int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
+                 const float* g, const float* beta, const float* h0, float* o, float* h_leaf,
+                 void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kda_tree_bwd -- reverse mode of kda_tree_fwd (rounds in reverse order).
+ *
+ * Gradients flow back through every handoff (abstract: differentiable
+ * boundary-state handoff): a handoff state's gradient is the sum of its own
+ * sequence's continuation gradient and the start gradients of every
+ * sequence that started from it, added in a fixed order.  Gradients of
+ * replayed rows are added into the compact rows they were read from, in a
+ * fixed order.
+ *
+ *   q..h0      the forward's inputs (same pointers or equal contents)
+ *   saved      as written by kda_tree_fwd with the same inputs
+ *   dO         [n_out_rows,H,dv] output gradients, dtype in_dtype
+ *   dh_leaf    [n_leaf,H,dk,dv] fp32 gradient of each leaf state, or NULL for zeros
+ *   dq, dk     [n_out_rows,H,dk] fp32;  dv [n_out_rows,H,dv] fp32
+ *   dg         [n_out_rows,H,dk] fp32;  dbeta [n_out_rows,H] fp32
+ *   dh0        [n_root,H,dk,dv] fp32 gradient of each root state
+ *   dh_boundary [n_buf,H,dk,dv] fp32 total gradient of each handoff state, or NULL
+ *   ws, ws_bytes scratch of kda_bwd_workspace_bytes(...) bytes
+ * Errors: as kda_tree_fwd.
+ */
+int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
+                 int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
+                 const float* g, const float* beta, const float* h0, const void* saved,
+                 const void* dO, const float* dh_leaf, float* dq, float* dk_, float* dv_,
+                 float* dg, float* dbeta, float* dh0, float* dh_boundary, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
+ * gather_logprobs -- per-original-position log-probs from compact logit rows
+ * (abstract: recovering log-probabilities for each original trajectory
+ * position; Figure 1: one logit row serves several trajectories' targets;
+ * Figure C.1(d): no expanded vocabulary-sized logits).
+ *
+ *   logits      [n_rows, vocab] (dtype KDA_DTYPE_BF16 or KDA_DTYPE_FP32), device
+ *   pos_row     [n_pos] int32 compact row of each position (device)
+ *   pos_target  [n_pos] int32 target token id of each position, in [0, vocab)
+ *   logp        [n_pos] fp32 out: logits[row, tgt] - logsumexp(logits[row, :])
+ *   lse         [n_rows] fp32 out: logsumexp of every row
+ * Errors: KDA_ERR_ARG, KDA_ERR_SHAPE, KDA_ERR_HIP.
+ */
+int gather_logprobs(const void* logits, int32_t dtype, int64_t n_rows, int32_t vocab,
+                    const int32_t* pos_row, const int32_t* pos_target, int64_t n_pos,
+                    float* logp, float* lse, void* stream);
+
+/*
+ * gather_logprobs_bwd -- gradient of the logits for gather_logprobs:
+ *   dlogits[r, :] = sum over positions p of row r, in CSR order, of
+ *                   dlogp[p] * (onehot(pos_target[p]) - softmax(logits[r, :])).
+ *   row_pos_ptr [n_rows+1], row_pos_idx [n_pos] int32: positions of each row
+ *   (the plan exports them in ascending position order).
+ *   lse         [n_rows] from gather_logprobs;  dlogp [n_pos] fp32
+ *   dlogits     [n_rows, vocab], same dtype as logits; every element is written.
+ */
+int gather_logprobs_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32_t vocab,
+                        const float* lse, const int32_t* row_pos_ptr,
+                        const int32_t* row_pos_idx, const int32_t* pos_target,
+                        const float* dlogp, void* dlogits, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_TREE_H */

@@ -1,0 +1,121 @@
+"""GPU parity of the HIP path (through the C-ABI) against the float64 oracle.
+
+Bar: relative L2 <= 2e-3 per output tensor (outputs, leaf states, every
+gradient, handoff-state gradients); plans and indices bit-exact (checked on
+the CPU in test_planner_lib.py)."""
+import numpy as np
+import pytest
+
+from gpu_cases import TOL, compare, gpu_run, make_case, oracle_tree, rel_l2
+from oracle import kda as okda
+from oracle.tree import Tree
+from tree_packed_chunkwise_amd import binding as B
+from tree_packed_chunkwise_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+FWD = ("o", "h_leaf")
+ALL = ("o", "h_leaf", "dq", "dk", "dv", "dg", "dbeta", "dh0", "dh_boundary")
+
+
+def _check(t, inp, plan, dO, dhl, tol=TOL, names=ALL):
+    print(f"case rows={t.n_rows} H={inp.q.shape[1]} D={inp.q.shape[2]} B={plan.info['chunk']} "
+          f"bf16={inp.bf16} rounds={plan.info['n_rounds']} R={plan.info['R']}", flush=True)
+    got = gpu_run(plan, inp, dO, dhl)
+    ref = oracle_tree(t, inp, dO, dhl, plan)
+    errs, bad = compare(got, ref, names, tol)
+    print("  rel L2:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert not bad, bad
+    return got, ref
+
+
+def test_tiny_workload_fwd_bwd():
+    """Figure 1 tree, H=2, d=64, chunk 16, fp32 inputs, default gates."""
+    w = synth.workload(0)
+    t, inp, plan, dO, dhl = make_case(w.tree, 2, 64, False, 0, chunk=16)
+    _check(t, inp, plan, dO, dhl)
+
+
+@pytest.mark.parametrize("h0_mode,dhl", [("randn", "randn"), ("zero", "zero")])
+def test_tiny_weak_gates_handoff(h0_mode, dhl):
+    """Slow decay keeps boundary states visible at every row."""
+    t, inp, plan, dO, dh = make_case(synth.tree_fig1(), 2, 64, False, 1, gate="weak",
+                                     h0_mode=h0_mode, dh_leaf=dhl, chunk=16)
+    _check(t, inp, plan, dO, dh)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("D,chunk,bf16", [(64, 16, False), (128, 64, True), (64, 64, True),
+                                          (128, 16, False)])
+def test_random_forests(seed, D, chunk, bf16):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    spec = synth.tree_random(rng, 9, 1, 3 * chunk, n_roots=1 + seed % 2)
+    if seed % 2:
+        spec = synth.shuffled_rows(spec, rng)
+    gate = ("weak", "default", "zero")[seed]
+    t, inp, plan, dO, dhl = make_case(spec, 2, D, bf16, 10 + seed, gate=gate, h0_mode="randn",
+                                      chunk=chunk)
+    _check(t, inp, plan, dO, dhl)
+
+
+@pytest.mark.parametrize("beta_mode", ["zero", "one"])
+def test_degenerate_beta(beta_mode):
+    rng = np.random.Generator(np.random.PCG64(7))
+    spec = synth.tree_random(rng, 6, 5, 80)
+    t = Tree(spec.parent, spec.seg_len)
+    inp = synth.make_kda_inputs(rng, t.n_rows, 2, 64, 64, bf16=False, gate="weak",
+                                beta_mode=beta_mode, h0_mode="randn")
+    plan = B.KDAPlan(spec.parent, spec.seg_len, None, 16)
+    dO, dhl = synth.make_upstream(rng, t.n_rows, len(t.leaves), 2, 64, 64, bf16=False)
+    _check(t, inp, plan, dO, dhl)
+
+
+def test_single_token_and_path():
+    for lens in ([1], [64], [65, 1, 63]):
+        spec = synth.tree_path(lens)
+        t, inp, plan, dO, dhl = make_case(spec, 2, 64, False, 3, gate="weak", h0_mode="randn",
+                                          chunk=16)
+        _check(t, inp, plan, dO, dhl)
+
+
+def test_expanded_mode_matches_expansion():
+    rng = np.random.Generator(np.random.PCG64(21))
+    spec = synth.tree_random(rng, 8, 10, 150, n_roots=2)
+    t, inp, plan, dO, dhl = make_case(spec, 2, 128, True, 22, gate="weak", h0_mode="randn",
+                                      chunk=64, mode=B.EXPANDED)
+    got = gpu_run(plan, inp, dO, dhl)
+    outs, finals = okda.expanded_fwd(t, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale)
+    assert rel_l2(got["o"], np.concatenate(outs)) <= TOL
+    assert rel_l2(got["h_leaf"], finals) <= TOL
+    offs = np.cumsum([0] + [len(o) for o in outs])
+    dO_traj = [dO[offs[i]:offs[i + 1]] for i in range(len(outs))]
+    exp = okda.expanded_bwd(t, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale, dO_traj,
+                            dhl)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert rel_l2(got[n], np.concatenate([e[n] for e in exp])) <= TOL, n
+
+
+def test_tree_equals_expanded_bitwise_on_gpu():
+    """Replay keeps every trajectory's chunk grid: the packed tree run and the
+    trajectory-expanded run compute the same chunks from the same states, so
+    outputs and leaf states agree bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    spec = synth.tree_random(rng, 10, 20, 200, n_roots=1)
+    t, inp, plan, dO, dhl = make_case(spec, 2, 128, True, 32, chunk=64, h0_mode="randn",
+                                      gate="weak")
+    tree = gpu_run(plan, inp)
+    eplan = B.KDAPlan(spec.parent, spec.seg_len, spec.seg_row, 64, B.EXPANDED)
+    exp = gpu_run(eplan, inp)
+    row_index = eplan.export("ROW_INDEX")
+    assert np.array_equal(exp["o"], tree["o"][row_index])
+    assert np.array_equal(exp["h_leaf"], tree["h_leaf"])
+
+
+def test_deterministic():
+    rng = np.random.Generator(np.random.PCG64(41))
+    spec = synth.tree_random(rng, 8, 30, 300)
+    t, inp, plan, dO, dhl = make_case(spec, 2, 128, True, 42, chunk=64)
+    a = gpu_run(plan, inp, dO, dhl)
+    b = gpu_run(plan, inp, dO, dhl)
+    for n in ("o", "h_leaf", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert np.array_equal(a[n], b[n]), n

@@ -1,0 +1,297 @@
+"""Thin ctypes binding over libkda_tree.so (the C-ABI of include/kda_tree.h).
+
+Argument marshalling only: tensors are passed as raw device pointers with the
+current torch stream; every step of the computation runs in the library's
+HIP kernels.  torch is used for device memory and streams.  There is no CPU
+fallback: if the shared library is missing, or no GPU is present when a
+compute call is made, the call raises.
+
+Names follow the C-ABI: kda_tree_plan, kda_tree_fwd, kda_tree_bwd,
+gather_logprobs, gather_logprobs_bwd.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+
+LIB_PATH = Path(__file__).resolve().with_name("libkda_tree.so")
+
+MINCALL, EXPANDED = 0, 1
+DT_FP32, DT_BF16 = 0, 1
+
+FIELDS = [
+    "SEG_ROUND", "SEG_SEQ", "SEG_IS_CONT", "SEG_B", "SEG_REPLAY", "ROUND_SEQ_PTR", "SEQ_ROUND",
+    "SEQ_HEAD", "SEQ_LEAF", "SEQ_B_HEAD", "SEQ_REPLAY", "SEQ_ROW_PTR", "SEQ_CHUNK_PTR",
+    "SEQ_INIT_KIND", "SEQ_INIT_IDX", "CHUNK_SEQ", "CHUNK_ROW0", "CHUNK_LEN", "CHUNK_SAVE",
+    "ROW_INDEX", "OUT_ROW", "BUF_SEQ", "BUF_POS", "BUF_CHUNK", "BUF_CONS_PTR", "BUF_CONS",
+    "POS_ROW", "POS_NEXT_ROW", "ROW_POS_PTR", "ROW_POS_IDX", "LEAF_SEG", "ROOT_SEG",
+]
+FIELD_ID = {n: i for i, n in enumerate(FIELDS)}
+
+# every symbol include/kda_tree.h declares
+EXPORTS = [
+    "kda_tree_plan", "kda_plan_destroy", "kda_plan_info", "kda_plan_export", "kda_plan_upload",
+    "kda_plan_device_offset", "kda_saved_bytes", "kda_fwd_workspace_bytes",
+    "kda_bwd_workspace_bytes", "kda_tree_fwd", "kda_tree_bwd", "gather_logprobs",
+    "gather_logprobs_bwd", "kda_last_error",
+]
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_seg", "n_rounds", "n_seq", "n_chunks", "n_buf", "n_leaf", "n_root", "chunk", "mode",
+        "max_seq_per_round")] + [(n, ctypes.c_int64) for n in (
+            "n_rows", "n_packed", "n_out_rows", "R", "n_pos", "n_expanded")] + [
+        ("device_bytes", ctypes.c_size_t)]
+
+
+_LIB = None
+
+
+def load_library(path: Path | str | None = None):
+    """Loads libkda_tree.so once; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise KDAError(f"{p} not found: build it with `python -m tree_packed_chunkwise_amd.build`")
+    L = ctypes.CDLL(str(p))
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    f32 = ctypes.c_float
+    L.kda_tree_plan.argtypes = [i32, vp, vp, vp, i32, i32, ctypes.POINTER(vp)]
+    L.kda_tree_plan.restype = ctypes.c_int
+    L.kda_plan_destroy.argtypes = [vp]
+    L.kda_plan_destroy.restype = None
+    L.kda_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    L.kda_plan_info.restype = ctypes.c_int
+    L.kda_plan_export.argtypes = [vp, i32, vp, i64]
+    L.kda_plan_export.restype = i64
+    L.kda_plan_upload.argtypes = [vp, vp, sz, vp]
+    L.kda_plan_upload.restype = ctypes.c_int
+    L.kda_plan_device_offset.argtypes = [vp, i32]
+    L.kda_plan_device_offset.restype = i64
+    for n in ("kda_saved_bytes", "kda_fwd_workspace_bytes", "kda_bwd_workspace_bytes"):
+        getattr(L, n).argtypes = [vp, i32, i32, i32]
+        getattr(L, n).restype = sz
+    L.kda_tree_fwd.argtypes = [vp, vp, i32, i32, i32, i32, f32] + [vp] * 10 + [sz, vp]
+    L.kda_tree_fwd.restype = ctypes.c_int
+    L.kda_tree_bwd.argtypes = [vp, vp, i32, i32, i32, i32, f32] + [vp] * 17 + [sz, vp]
+    L.kda_tree_bwd.restype = ctypes.c_int
+    L.gather_logprobs.argtypes = [vp, i32, i64, i32, vp, vp, i64, vp, vp, vp]
+    L.gather_logprobs.restype = ctypes.c_int
+    L.gather_logprobs_bwd.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.gather_logprobs_bwd.restype = ctypes.c_int
+    L.kda_last_error.argtypes = []
+    L.kda_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _LIB = L
+    return L
+
+
+def _check(rc):
+    if rc < 0:
+        msg = load_library().kda_last_error().decode()
+        raise KDAError(f"status {rc}: {msg}")
+    return rc
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class KDAPlan:
+    """Host plan (kda_tree_plan) plus its uploaded device copy per device."""
+
+    def __init__(self, parent, seg_len, seg_row=None, chunk: int = 64, mode: int = MINCALL):
+        L = load_library()
+        self._parent = np.ascontiguousarray(parent, dtype=np.int32)
+        self._len = np.ascontiguousarray(seg_len, dtype=np.int32)
+        self._row = None if seg_row is None else np.ascontiguousarray(seg_row, dtype=np.int64)
+        h = ctypes.c_void_p()
+        _check(L.kda_tree_plan(len(self._parent), _np_ptr(self._parent), _np_ptr(self._len),
+                               _np_ptr(self._row) if self._row is not None else None,
+                               chunk, mode, ctypes.byref(h)))
+        self._h = h
+        pi = PlanInfo()
+        _check(L.kda_plan_info(h, ctypes.byref(pi)))
+        self.info = {n: getattr(pi, n) for n, _ in PlanInfo._fields_}
+        self._dev = {}
+
+    @property
+    def handle(self):
+        return self._h
+
+    def export(self, field: str) -> np.ndarray:
+        L = load_library()
+        n = _check(L.kda_plan_export(self._h, FIELD_ID[field], None, 0))
+        out = np.zeros(max(n, 1), dtype=np.int64)
+        _check(L.kda_plan_export(self._h, FIELD_ID[field], _np_ptr(out), n))
+        return out[:n]
+
+    def export_all(self) -> dict:
+        return {f: self.export(f) for f in FIELDS}
+
+    def device(self, device=None):
+        """int32 device copy of the plan tables (uploaded once per device)."""
+        import torch
+        dev = torch.device(device if device is not None else "cuda")
+        key = str(dev)
+        if key not in self._dev:
+            nb = int(self.info["device_bytes"])
+            buf = torch.empty(nb // 4, dtype=torch.int32, device=dev)
+            s = torch.cuda.current_stream(dev).cuda_stream
+            _check(load_library().kda_plan_upload(self._h, ctypes.c_void_p(buf.data_ptr()), nb,
+                                                  ctypes.c_void_p(s)))
+            torch.cuda.current_stream(dev).synchronize()
+            self._dev[key] = buf
+        return self._dev[key]
+
+    def device_table(self, field: str, device=None):
+        """View of one int32 table of the uploaded copy (gather map and CSR)."""
+        buf = self.device(device)
+        off = _check(load_library().kda_plan_device_offset(self._h, FIELD_ID[field])) // 4
+        n = len(self.export(field))
+        return buf[off:off + n]
+
+    def saved_bytes(self, H, D):
+        return load_library().kda_saved_bytes(self._h, H, D, D)
+
+    def fwd_ws_bytes(self, H, D):
+        return load_library().kda_fwd_workspace_bytes(self._h, H, D, D)
+
+    def bwd_ws_bytes(self, H, D):
+        return load_library().kda_bwd_workspace_bytes(self._h, H, D, D)
+
+    def __del__(self):
+        try:
+            if getattr(self, "_h", None):
+                load_library().kda_plan_destroy(self._h)
+                self._h = None
+        except Exception:
+            pass
+
+
+def kda_tree_plan(parent, seg_len, seg_row=None, chunk: int = 64, mode: int = MINCALL) -> KDAPlan:
+    return KDAPlan(parent, seg_len, seg_row, chunk, mode)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_FP32
+    raise KDAError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise KDAError("kda kernels need device tensors (no CPU path)")
+        if t is not None and not t.is_contiguous():
+            raise KDAError("tensors must be contiguous")
+
+
+def alloc_fwd(plan: KDAPlan, H: int, D: int, device):
+    """Output and scratch buffers of kda_tree_fwd (torch allocations)."""
+    import torch
+    i = plan.info
+    return dict(
+        o=torch.empty((i["n_out_rows"], H, D), dtype=torch.float32, device=device),
+        h_leaf=torch.empty((i["n_leaf"], H, D, D), dtype=torch.float32, device=device),
+        saved=torch.empty(plan.saved_bytes(H, D), dtype=torch.uint8, device=device),
+        ws=torch.empty(plan.fwd_ws_bytes(H, D), dtype=torch.uint8, device=device),
+    )
+
+
+def kda_tree_fwd(plan: KDAPlan, q, k, v, g, beta, h0=None, scale=None, out=None):
+    """Forward pass; returns dict(o, h_leaf, saved[, ws])."""
+    _need_cuda(q, k, v, g, beta, h0)
+    N, H, D = q.shape
+    if out is None:
+        out = alloc_fwd(plan, H, D, q.device)
+    sc = float(scale) if scale is not None else 1.0 / float(np.sqrt(D))
+    _check(load_library().kda_tree_fwd(
+        plan.handle, _p(plan.device(q.device)), H, D, v.shape[2], _dtype_code(q), sc,
+        _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), _p(out["o"]), _p(out["h_leaf"]),
+        _p(out["saved"]), _p(out["ws"]), out["ws"].numel(), _stream(q)))
+    return out
+
+
+def alloc_bwd(plan: KDAPlan, H: int, D: int, device, boundary=True):
+    import torch
+    i = plan.info
+    n = i["n_out_rows"]
+    f = dict(dtype=torch.float32, device=device)
+    return dict(
+        dq=torch.empty((n, H, D), **f), dk=torch.empty((n, H, D), **f),
+        dv=torch.empty((n, H, D), **f), dg=torch.empty((n, H, D), **f),
+        dbeta=torch.empty((n, H), **f), dh0=torch.empty((i["n_root"], H, D, D), **f),
+        dh_boundary=(torch.empty((i["n_buf"], H, D, D), **f) if boundary else None),
+        ws=torch.empty(plan.bwd_ws_bytes(H, D), dtype=torch.uint8, device=device),
+    )
+
+
+def kda_tree_bwd(plan: KDAPlan, q, k, v, g, beta, saved, dO, dh_leaf=None, h0=None, scale=None,
+                 out=None, boundary=True):
+    """Reverse mode; returns dict(dq, dk, dv, dg, dbeta, dh0, dh_boundary[, ws])."""
+    _need_cuda(q, k, v, g, beta, saved, dO, dh_leaf, h0)
+    N, H, D = q.shape
+    if dO.dtype != q.dtype:
+        raise KDAError("dO must have the dtype of q/k/v")
+    if out is None:
+        out = alloc_bwd(plan, H, D, q.device, boundary)
+    sc = float(scale) if scale is not None else 1.0 / float(np.sqrt(D))
+    _check(load_library().kda_tree_bwd(
+        plan.handle, _p(plan.device(q.device)), H, D, v.shape[2], _dtype_code(q), sc,
+        _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), _p(saved), _p(dO), _p(dh_leaf),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dg"]), _p(out["dbeta"]),
+        _p(out["dh0"]), _p(out.get("dh_boundary")), _p(out["ws"]), out["ws"].numel(),
+        _stream(q)))
+    return out
+
+
+def gather_logprobs(logits, pos_row, pos_target, out=None):
+    """logp[p] = logits[pos_row[p], pos_target[p]] - logsumexp(logits[pos_row[p]]).
+    Returns (logp, lse)."""
+    import torch
+    _need_cuda(logits, pos_row, pos_target)
+    n_rows, vocab = logits.shape
+    n_pos = pos_row.shape[0]
+    if out is None:
+        out = (torch.empty(n_pos, dtype=torch.float32, device=logits.device),
+               torch.empty(n_rows, dtype=torch.float32, device=logits.device))
+    logp, lse = out
+    _check(load_library().gather_logprobs(_p(logits), _dtype_code(logits), n_rows, vocab,
+                                          _p(pos_row), _p(pos_target), n_pos, _p(logp), _p(lse),
+                                          _stream(logits)))
+    return logp, lse
+
+
+def gather_logprobs_bwd(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp, out=None):
+    import torch
+    _need_cuda(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp)
+    n_rows, vocab = logits.shape
+    if out is None:
+        out = torch.empty_like(logits)
+    _check(load_library().gather_logprobs_bwd(_p(logits), _dtype_code(logits), n_rows, vocab,
+                                              _p(lse), _p(row_pos_ptr), _p(row_pos_idx),
+                                              _p(pos_target), _p(dlogp), _p(out),
+                                              _stream(logits)))
+    return out

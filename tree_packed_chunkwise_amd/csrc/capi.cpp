@@ -1,0 +1,425 @@
+// capi.cpp -- extern "C" entry points of libkda_tree.so (declared in include/kda_tree.h).
+//
+// Argument checking, buffer carving and launch sequencing only; every step of
+// the computation runs in the HIP kernels of kda_fwd.hip, kda_bwd.hip and
+// gather.hip, enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+
+#include "../../include/kda_tree.h"
+#include "common.h"
+#include "plan.h"
+
+namespace kda {
+hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+                      const int* round_ptr_host, int n_rounds, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs& a, const FwdArgs& pa, bool bf16, int BC, int D,
+                      int n_chunks, const int* round_ptr_host, int n_rounds, int n_rep_rows,
+                      int n_root, hipStream_t st);
+hipError_t launch_gather_fwd(const void* logits, bool bf16, int64_t n_rows, int vocab,
+                             const int* pos_row, const int* pos_tgt, int64_t n_pos, float* logp,
+                             float* lse, hipStream_t st);
+hipError_t launch_gather_bwd(const void* logits, bool bf16, int64_t n_rows, int vocab,
+                             const float* lse, const int* row_pos_ptr, const int* row_pos_idx,
+                             const int* pos_tgt, const float* dlogp, void* dlogits,
+                             hipStream_t st);
+}  // namespace kda
+
+struct kda_plan {
+  kda::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(KDA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves consecutive 256-byte-aligned float regions out of a byte buffer.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  float* take(size_t nfloats) {
+    float* p = base ? (float*)(base + off) : nullptr;
+    off += al(nfloats * sizeof(float));
+    return p;
+  }
+};
+
+bool shape_ok(int32_t B, int32_t H, int32_t dk, int32_t dv) {
+  return H > 0 && dk == dv && (dk == 64 || dk == 128) && (B == 16 || B == 64);
+}
+
+kda::DevPlan make_dev_plan(const kda::Plan& p, const void* dev) {
+  const int32_t* b = (const int32_t*)dev;
+  const kda::DevLayout& d = p.dev;
+  kda::DevPlan v;
+  v.round_seq_ptr = b + d.round_seq_ptr;
+  v.seq_chunk_ptr = b + d.seq_chunk_ptr;
+  v.seq_row_ptr = b + d.seq_row_ptr;
+  v.seq_init_kind = b + d.seq_init_kind;
+  v.seq_init_idx = b + d.seq_init_idx;
+  v.seq_leaf = b + d.seq_leaf;
+  v.chunk_seq = b + d.chunk_seq;
+  v.chunk_row0 = b + d.chunk_row0;
+  v.chunk_len = b + d.chunk_len;
+  v.chunk_save = b + d.chunk_save;
+  v.chunk_nrep = b + d.chunk_nrep;
+  v.chunk_rep0 = b + d.chunk_rep0;
+  v.row_index = b + d.row_index;
+  v.out_row = b + d.out_row;
+  v.buf_cons_ptr = b + d.buf_cons_ptr;
+  v.buf_cons = b + d.buf_cons;
+  v.buf_chunk = b + d.buf_chunk;
+  v.rep_row = b + d.rep_row;
+  v.rep_ptr = b + d.rep_ptr;
+  v.rep_slot = b + d.rep_slot;
+  v.root_seq_ptr = b + d.root_seq_ptr;
+  v.root_seq = b + d.root_seq;
+  return v;
+}
+
+// saved = [chunk start states | handoff states]
+struct SavedView {
+  float* chunk_h;
+  float* bufs;
+};
+SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* total) {
+  Carver c(base);
+  SavedView s;
+  const size_t st = (size_t)H * D * D;
+  s.chunk_h = c.take((size_t)p.n_chunks() * st);
+  s.bufs = c.take((size_t)p.n_buf() * st);
+  if (total) *total = c.off;
+  return s;
+}
+
+kda::ChunkWS carve_chunk_ws(Carver& c, const kda::Plan& p, int H, int D) {
+  const size_t nb = (size_t)p.n_chunks() * H;
+  const size_t BC = p.B;
+  kda::ChunkWS w;
+  w.W = c.take(nb * BC * D);
+  w.U = c.take(nb * BC * D);
+  w.Gam = c.take(nb * BC * D);
+  w.P = c.take(nb * BC * BC);
+  w.T = c.take(nb * BC * BC);
+  w.A = c.take(nb * BC * BC);
+  return w;
+}
+
+struct BwdWS {
+  kda::ChunkWS cw;
+  kda::GradWS gw;
+  float *dy, *dhc, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
+};
+BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) {
+  Carver c(base);
+  BwdWS w;
+  w.cw = carve_chunk_ws(c, p, H, D);
+  const size_t nb = (size_t)p.n_chunks() * H;
+  const size_t BC = p.B;
+  w.gw.dQt = c.take(nb * BC * D);
+  w.gw.dKt = c.take(nb * BC * D);
+  w.gw.X = c.take(nb * BC * D);
+  w.gw.dKh = c.take(nb * BC * D);
+  w.gw.dP = c.take(nb * BC * BC);
+  w.gw.dA = c.take(nb * BC * BC);
+  w.gw.deGC = c.take(nb * D);
+  w.dy = c.take((size_t)p.n_packed * H * D);
+  w.dhc = c.take(nb * D * D);
+  w.slot = c.take((size_t)p.n_seq() * H * D * D);
+  const size_t nrep = (size_t)p.R;
+  w.rep_dq = c.take(nrep * H * D);
+  w.rep_dk = c.take(nrep * H * D);
+  w.rep_dg = c.take(nrep * H * D);
+  w.rep_dv = c.take(nrep * H * D);
+  w.rep_db = c.take(nrep * H);
+  if (total) *total = c.off;
+  return w;
+}
+
+int check_dev_plan(const kda_plan* plan, const void* dev_plan) {
+  if (!plan) return fail(KDA_ERR_ARG, "plan is null");
+  if (!dev_plan) return fail(KDA_ERR_ARG, "dev_plan is null");
+  if (((uintptr_t)dev_plan) % 4) return fail(KDA_ERR_ARG, "dev_plan misaligned");
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_err.c_str(); }
+
+int kda_tree_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
+                  const int64_t* seg_row, int32_t chunk, int32_t mode, kda_plan** out) {
+  if (!out) return fail(KDA_ERR_ARG, "out is null");
+  *out = nullptr;
+  kda_plan* p = new kda_plan();
+  std::string err;
+  int rc = kda::build_plan(n_seg, parent, seg_len, seg_row, chunk, mode, p->p, err);
+  if (rc != 0) {
+    delete p;
+    return fail(rc, err);
+  }
+  *out = p;
+  g_err.clear();
+  return KDA_OK;
+}
+
+void kda_plan_destroy(kda_plan* plan) { delete plan; }
+
+int kda_plan_info(const kda_plan* plan, kda_plan_info_t* info) {
+  if (!plan || !info) return fail(KDA_ERR_ARG, "null argument");
+  const kda::Plan& p = plan->p;
+  std::memset(info, 0, sizeof(*info));
+  info->n_seg = p.n_seg;
+  info->n_rounds = p.n_rounds;
+  info->n_seq = p.n_seq();
+  info->n_chunks = p.n_chunks();
+  info->n_buf = p.n_buf();
+  info->n_leaf = p.n_leaf;
+  info->n_root = p.n_root;
+  info->chunk = p.B;
+  info->mode = p.mode;
+  info->max_seq_per_round = p.max_seq_per_round;
+  info->n_rows = p.n_rows;
+  info->n_packed = p.n_packed;
+  info->n_out_rows = p.n_out_rows;
+  info->R = p.R;
+  info->n_pos = (int64_t)p.pos_row.size();
+  info->n_expanded = p.n_expanded;
+  info->device_bytes = (size_t)p.dev.total * sizeof(int32_t);
+  return KDA_OK;
+}
+
+int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64_t n) {
+  if (!plan) return fail(KDA_ERR_ARG, "plan is null");
+  const kda::Plan& p = plan->p;
+  auto put32 = [&](const std::vector<int32_t>& v) -> int64_t {
+    const int64_t len = (int64_t)v.size();
+    if (dst) {
+      if (n < len) return fail(KDA_ERR_ARG, "export buffer too small");
+      for (int64_t i = 0; i < len; ++i) dst[i] = v[i];
+    }
+    return len;
+  };
+  auto put64 = [&](const std::vector<int64_t>& v) -> int64_t {
+    const int64_t len = (int64_t)v.size();
+    if (dst) {
+      if (n < len) return fail(KDA_ERR_ARG, "export buffer too small");
+      for (int64_t i = 0; i < len; ++i) dst[i] = v[i];
+    }
+    return len;
+  };
+  switch (field) {
+    case KDA_F_SEG_ROUND: return put32(p.seg_round);
+    case KDA_F_SEG_SEQ: return put32(p.seg_seq);
+    case KDA_F_SEG_IS_CONT: return put32(p.seg_is_cont);
+    case KDA_F_SEG_B: return put32(p.seg_b);
+    case KDA_F_SEG_REPLAY: return put32(p.seg_replay);
+    case KDA_F_ROUND_SEQ_PTR: return put32(p.round_seq_ptr);
+    case KDA_F_SEQ_ROUND: return put32(p.seq_round);
+    case KDA_F_SEQ_HEAD: return put32(p.seq_head);
+    case KDA_F_SEQ_LEAF: return put32(p.seq_leaf);
+    case KDA_F_SEQ_B_HEAD: return put32(p.seq_b_head);
+    case KDA_F_SEQ_REPLAY: return put32(p.seq_replay);
+    case KDA_F_SEQ_ROW_PTR: return put32(p.seq_row_ptr);
+    case KDA_F_SEQ_CHUNK_PTR: return put32(p.seq_chunk_ptr);
+    case KDA_F_SEQ_INIT_KIND: return put32(p.seq_init_kind);
+    case KDA_F_SEQ_INIT_IDX: return put32(p.seq_init_idx);
+    case KDA_F_CHUNK_SEQ: return put32(p.chunk_seq);
+    case KDA_F_CHUNK_ROW0: return put32(p.chunk_row0);
+    case KDA_F_CHUNK_LEN: return put32(p.chunk_len);
+    case KDA_F_CHUNK_SAVE: return put32(p.chunk_save);
+    case KDA_F_ROW_INDEX: return put32(p.row_index);
+    case KDA_F_OUT_ROW: return put32(p.out_row);
+    case KDA_F_BUF_SEQ: return put32(p.buf_seq);
+    case KDA_F_BUF_POS: return put64(p.buf_pos);
+    case KDA_F_BUF_CHUNK: return put32(p.buf_chunk);
+    case KDA_F_BUF_CONS_PTR: return put32(p.buf_cons_ptr);
+    case KDA_F_BUF_CONS: return put32(p.buf_cons);
+    case KDA_F_POS_ROW: return put32(p.pos_row);
+    case KDA_F_POS_NEXT_ROW: return put32(p.pos_next_row);
+    case KDA_F_ROW_POS_PTR: return put32(p.row_pos_ptr);
+    case KDA_F_ROW_POS_IDX: return put32(p.row_pos_idx);
+    case KDA_F_LEAF_SEG: return put32(p.leaf_seg);
+    case KDA_F_ROOT_SEG: return put32(p.root_seg);
+    default: return fail(KDA_ERR_ARG, "unknown export field");
+  }
+}
+
+int kda_plan_upload(const kda_plan* plan, void* dev, size_t bytes, void* stream) {
+  if (!plan || !dev) return fail(KDA_ERR_ARG, "null argument");
+  const kda::Plan& p = plan->p;
+  const size_t need = (size_t)p.dev.total * sizeof(int32_t);
+  if (bytes < need) return fail(KDA_ERR_WORKSPACE, "device plan buffer too small");
+  if (((uintptr_t)dev) % 256) return fail(KDA_ERR_ARG, "device plan buffer must be 256-byte aligned");
+  hipError_t e = hipMemcpyAsync(dev, p.dev_blob.data(), need, hipMemcpyHostToDevice,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_plan_upload");
+  return KDA_OK;
+}
+
+int64_t kda_plan_device_offset(const kda_plan* plan, int32_t field) {
+  if (!plan) return fail(KDA_ERR_ARG, "plan is null");
+  const kda::DevLayout& d = plan->p.dev;
+  switch (field) {
+    case KDA_F_POS_ROW: return d.pos_row * 4;
+    case KDA_F_POS_NEXT_ROW: return d.pos_next_row * 4;
+    case KDA_F_ROW_POS_PTR: return d.row_pos_ptr * 4;
+    case KDA_F_ROW_POS_IDX: return d.row_pos_idx * 4;
+    case KDA_F_ROW_INDEX: return d.row_index * 4;
+    case KDA_F_OUT_ROW: return d.out_row * 4;
+    default: return fail(KDA_ERR_ARG, "field has no device table");
+  }
+}
+
+size_t kda_saved_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv) {
+  if (!plan || !shape_ok(plan->p.B, H, dk, dv)) return 0;
+  size_t total = 0;
+  carve_saved(plan->p, H, dk, nullptr, &total);
+  return total;
+}
+
+size_t kda_fwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv) {
+  if (!plan || !shape_ok(plan->p.B, H, dk, dv)) return 0;
+  Carver c(nullptr);
+  carve_chunk_ws(c, plan->p, H, dk);
+  return c.off;
+}
+
+size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv) {
+  if (!plan || !shape_ok(plan->p.B, H, dk, dv)) return 0;
+  size_t total = 0;
+  carve_bwd_ws(plan->p, H, dk, nullptr, &total);
+  return total;
+}
+
+int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
+                 int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
+                 const float* g, const float* beta, const float* h0, float* o, float* h_leaf,
+                 void* saved, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dev_plan(plan, dev_plan);
+  if (rc) return rc;
+  const kda::Plan& p = plan->p;
+  if (!shape_ok(p.B, H, dk, dv))
+    return fail(KDA_ERR_SHAPE, "supported: dk == dv in {64,128}, chunk in {16,64}, H > 0");
+  if (in_dtype != KDA_DTYPE_BF16 && in_dtype != KDA_DTYPE_FP32)
+    return fail(KDA_ERR_SHAPE, "in_dtype must be KDA_DTYPE_BF16 or KDA_DTYPE_FP32");
+  if (!q || !k || !v || !g || !beta || !o || !h_leaf || !saved || !ws)
+    return fail(KDA_ERR_ARG, "null tensor argument");
+  if (ws_bytes < kda_fwd_workspace_bytes(plan, H, dk, dv))
+    return fail(KDA_ERR_WORKSPACE, "forward workspace too small");
+  kda::FwdArgs a;
+  a.plan = make_dev_plan(p, dev_plan);
+  a.H = H;
+  a.scale = scale;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0;
+  a.o = o;
+  a.h_leaf = h_leaf;
+  SavedView sv = carve_saved(p, H, dk, saved, nullptr);
+  a.chunk_h = sv.chunk_h;
+  a.bufs = sv.bufs;
+  Carver c(ws);
+  a.ws = carve_chunk_ws(c, p, H, dk);
+  hipError_t e = kda::launch_fwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
+                                 p.round_seq_ptr.data(), p.n_rounds, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_tree_fwd launch");
+  return KDA_OK;
+}
+
+int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
+                 int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
+                 const float* g, const float* beta, const float* h0, const void* saved,
+                 const void* dO, const float* dh_leaf, float* dq, float* dk_, float* dv_,
+                 float* dg, float* dbeta, float* dh0, float* dh_boundary, void* ws,
+                 size_t ws_bytes, void* stream) {
+  (void)h0;  // the start states of all chunks are in `saved`
+  int rc = check_dev_plan(plan, dev_plan);
+  if (rc) return rc;
+  const kda::Plan& p = plan->p;
+  if (!shape_ok(p.B, H, dk, dv))
+    return fail(KDA_ERR_SHAPE, "supported: dk == dv in {64,128}, chunk in {16,64}, H > 0");
+  if (in_dtype != KDA_DTYPE_BF16 && in_dtype != KDA_DTYPE_FP32)
+    return fail(KDA_ERR_SHAPE, "in_dtype must be KDA_DTYPE_BF16 or KDA_DTYPE_FP32");
+  if (!q || !k || !v || !g || !beta || !saved || !dO || !dq || !dk_ || !dv_ || !dg || !dbeta ||
+      !dh0 || !ws)
+    return fail(KDA_ERR_ARG, "null tensor argument");
+  if (ws_bytes < kda_bwd_workspace_bytes(plan, H, dk, dv))
+    return fail(KDA_ERR_WORKSPACE, "backward workspace too small");
+  SavedView sv = carve_saved(p, H, dk, (void*)saved, nullptr);
+  BwdWS w = carve_bwd_ws(p, H, dk, ws, nullptr);
+  kda::BwdArgs a;
+  a.plan = make_dev_plan(p, dev_plan);
+  a.H = H;
+  a.scale = scale;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.chunk_h = sv.chunk_h;
+  a.dO = dO;
+  a.dh_leaf = dh_leaf;
+  a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  a.dh_boundary = dh_boundary;
+  a.ws = w.cw;
+  a.gw = w.gw;
+  a.dy = w.dy;
+  a.dhc = w.dhc;
+  a.slot = w.slot;
+  a.rep_dq = w.rep_dq; a.rep_dk = w.rep_dk; a.rep_dg = w.rep_dg; a.rep_dv = w.rep_dv;
+  a.rep_db = w.rep_db;
+  kda::FwdArgs pa;  // chunk-local recompute uses the forward's prep kernel
+  std::memset(&pa, 0, sizeof(pa));
+  pa.plan = a.plan;
+  pa.H = H;
+  pa.scale = scale;
+  pa.q = q; pa.k = k; pa.v = v; pa.g = g; pa.beta = beta;
+  pa.ws = w.cw;
+  hipError_t e = kda::launch_bwd(a, pa, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
+                                 p.round_seq_ptr.data(), p.n_rounds, (int)p.rep_row.size(),
+                                 p.n_root, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_tree_bwd launch");
+  return KDA_OK;
+}
+
+int gather_logprobs(const void* logits, int32_t dtype, int64_t n_rows, int32_t vocab,
+                    const int32_t* pos_row, const int32_t* pos_target, int64_t n_pos, float* logp,
+                    float* lse, void* stream) {
+  if (!logits || !lse || (n_pos > 0 && (!pos_row || !pos_target || !logp)))
+    return fail(KDA_ERR_ARG, "null argument");
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32) return fail(KDA_ERR_SHAPE, "dtype");
+  if (vocab <= 0 || n_rows < 0 || n_pos < 0 || n_rows >= (int64_t)INT32_MAX)
+    return fail(KDA_ERR_ARG, "bad sizes");
+  hipError_t e = kda::launch_gather_fwd(logits, dtype == KDA_DTYPE_BF16, n_rows, vocab, pos_row,
+                                        pos_target, n_pos, logp, lse, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gather_logprobs launch");
+  return KDA_OK;
+}
+
+int gather_logprobs_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32_t vocab,
+                        const float* lse, const int32_t* row_pos_ptr, const int32_t* row_pos_idx,
+                        const int32_t* pos_target, const float* dlogp, void* dlogits,
+                        void* stream) {
+  if (!logits || !lse || !row_pos_ptr || !dlogits) return fail(KDA_ERR_ARG, "null argument");
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32) return fail(KDA_ERR_SHAPE, "dtype");
+  if (vocab <= 0 || n_rows < 0 || n_rows >= (int64_t)INT32_MAX) return fail(KDA_ERR_ARG, "bad sizes");
+  hipError_t e = kda::launch_gather_bwd(logits, dtype == KDA_DTYPE_BF16, n_rows, vocab, lse,
+                                        row_pos_ptr, row_pos_idx, pos_target, dlogp, dlogits,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gather_logprobs_bwd launch");
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// common.h -- shared device-side declarations of the KDA tree kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Device views of the uploaded plan tables (int32).
+struct DevPlan {
+  const int* round_seq_ptr;
+  const int* seq_chunk_ptr;
+  const int* seq_row_ptr;
+  const int* seq_init_kind;
+  const int* seq_init_idx;
+  const int* seq_leaf;
+  const int* chunk_seq;
+  const int* chunk_row0;
+  const int* chunk_len;
+  const int* chunk_save;
+  const int* chunk_nrep;
+  const int* chunk_rep0;
+  const int* row_index;
+  const int* out_row;
+  const int* buf_cons_ptr;
+  const int* buf_cons;
+  const int* buf_chunk;
+  const int* rep_row;
+  const int* rep_ptr;
+  const int* rep_slot;
+  const int* root_seq_ptr;
+  const int* root_seq;
+};
+
+// Per-chunk products of the chunk-local pass, one block per (chunk, head),
+// row-major, fp32.  Layout of one block (BC = chunk size, D = head dim):
+//   W   [BC][D]   T diag(beta) (K * e^Gam)
+//   U   [BC][D]   T diag(beta) V
+//   Gam [BC][D]   inclusive cumulative log-decay within the chunk
+//   P   [BC][BC]  sum_c q_ic k_jc e^(Gam_ic - Gam_jc), j <= i
+//   T   [BC][BC]  (I + diag(beta) A)^-1
+//   A   [BC][BC]  sum_c k_ic k_jc e^(Gam_ic - Gam_jc), j < i
+struct ChunkWS {
+  float* W;
+  float* U;
+  float* Gam;
+  float* P;
+  float* T;
+  float* A;
+};
+
+inline __host__ __device__ size_t chunk_ws_floats(int BC, int D) {
+  return (size_t)BC * D * 3 + (size_t)BC * BC * 3;
+}
+
+struct FwdArgs {
+  DevPlan plan;
+  int H;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* h0;     // may be null
+  float* o;
+  float* h_leaf;
+  float* chunk_h;      // [n_chunks,H,D,D]
+  float* bufs;         // [n_buf,H,D,D]
+  ChunkWS ws;
+};
+
+// Per-chunk intermediates of the reverse chunk-local passes, one block per
+// (chunk, head): dQt = scale dO h^T, dKt = -diag(beta) dy h^T, X = (K e^Gam) h,
+// dKh = delta dh'^T (each [BC][D]); dP, dA ([BC][BC]); deGC ([D]).
+struct GradWS {
+  float* dQt;
+  float* dKt;
+  float* X;
+  float* dKh;
+  float* dP;
+  float* dA;
+  float* deGC;
+};
+
+inline __host__ __device__ size_t grad_ws_floats(int BC, int D) {
+  return (size_t)BC * D * 4 + (size_t)BC * BC * 2 + (size_t)D;
+}
+
+struct BwdArgs {
+  DevPlan plan;
+  int H;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* chunk_h;   // saved start state per chunk [n_chunks,H,D,D]
+  const void* dO;
+  const float* dh_leaf;   // may be null
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;
+  float* dh_boundary;     // may be null
+  ChunkWS ws;             // U is overwritten with delta
+  GradWS gw;
+  float* dy;              // [n_packed,H,D]
+  float* dhc;             // [n_chunks,H,D,D] gradient of each chunk's end state
+  float* slot;            // [n_seq,H,D,D] gradient of each sequence's start state
+  float* rep_dq;          // [n_replay,H,D] gradients of replayed rows
+  float* rep_dk;
+  float* rep_dg;
+  float* rep_dv;
+  float* rep_db;          // [n_replay,H]
+};
+
+inline __device__ float ld_in(const float* p, size_t i) { return p[i]; }
+inline __device__ float ld_in(const uint16_t* p, size_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+
+}  // namespace kda

@@ -1,0 +1,171 @@
+// gather.hip -- per-original-position log-probs from compact logit rows (gfx950).
+//
+// HARTS abstract: log-probabilities are recovered for each original
+// trajectory position; Figure 1: one logit row serves several trajectories'
+// distinct targets; Figure C.1(d): no expanded vocabulary-sized logits.
+//
+//   k_row_lse   one block per compact row: online max / sum-of-exp over the
+//               vocabulary in one pass (16-byte loads), fixed-order tree
+//               reduction -> lse[row]
+//   k_pos_logp  one thread per position: logits[row, tgt] - lse[row]
+//   k_row_grad  one block per compact row: w = sum of the row's dlogp (CSR
+//               order); every element -softmax * w, then the row's target
+//               columns get their exact value (-softmax*w + sum of dlogp of the
+//               positions targeting that column), written by one thread.
+// HBM-bound: each logit is read once per pass and each gradient written once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int GT = 256;
+
+__device__ inline float ld_logit(const float* p, size_t i) { return p[i]; }
+__device__ inline float ld_logit(const uint16_t* p, size_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+__device__ inline void st_logit(float* p, size_t i, float x) { p[i] = x; }
+__device__ inline void st_logit(uint16_t* p, size_t i, float x) {
+  p[i] = __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ inline void online_add(float& m, float& s, float x) {
+  if (x > m) {
+    s = s * __expf(m - x) + 1.f;
+    m = x;
+  } else {
+    s += __expf(x - m);
+  }
+}
+
+__device__ inline void online_merge(float& m, float& s, float m2, float s2) {
+  if (m2 > m) {
+    s = s * __expf(m - m2) + s2;
+    m = m2;
+  } else if (m2 > -INFINITY) {
+    s += s2 * __expf(m2 - m);
+  }
+}
+
+template <typename T>
+__device__ inline void row_stats(const T* z, int vocab, float& m, float& s, float* sm, float* ss) {
+  m = -INFINITY;
+  s = 0.f;
+  const int tid = threadIdx.x;
+  constexpr int VEC = 16 / sizeof(T);
+  const int nvec = vocab / VEC;
+  if ((((uintptr_t)z) % 16) == 0) {
+    typedef __attribute__((__vector_size__(16))) int v4i;
+    const v4i* zv = (const v4i*)z;
+    for (int i = tid; i < nvec; i += GT) {
+      v4i pk = zv[i];
+      const T* e = (const T*)&pk;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) online_add(m, s, ld_logit(e, j));
+    }
+    for (int i = nvec * VEC + tid; i < vocab; i += GT) online_add(m, s, ld_logit(z, i));
+  } else {
+    for (int i = tid; i < vocab; i += GT) online_add(m, s, ld_logit(z, i));
+  }
+  sm[tid] = m;
+  ss[tid] = s;
+  __syncthreads();
+  for (int w = GT / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      float a = sm[tid], b = ss[tid];
+      online_merge(a, b, sm[tid + w], ss[tid + w]);
+      sm[tid] = a;
+      ss[tid] = b;
+    }
+    __syncthreads();
+  }
+  m = sm[0];
+  s = ss[0];
+}
+
+template <typename T>
+__global__ __launch_bounds__(GT) void k_row_lse(const T* logits, int vocab, float* lse) {
+  __shared__ float sm[GT], ss[GT];
+  const size_t row = blockIdx.x;
+  float m, s;
+  row_stats(logits + row * vocab, vocab, m, s, sm, ss);
+  if (threadIdx.x == 0) lse[row] = m + __logf(s);
+}
+
+template <typename T>
+__global__ void k_pos_logp(const T* logits, int vocab, const int* pos_row, const int* pos_tgt,
+                           int64_t n_pos, const float* lse, float* logp) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= n_pos) return;
+  const int r = pos_row[p];
+  logp[p] = ld_logit(logits, (size_t)r * vocab + pos_tgt[p]) - lse[r];
+}
+
+template <typename T>
+__global__ __launch_bounds__(GT) void k_row_grad(const T* logits, int vocab, const float* lse,
+                                                 const int* row_pos_ptr, const int* row_pos_idx,
+                                                 const int* pos_tgt, const float* dlogp,
+                                                 T* dlogits) {
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int p0 = row_pos_ptr[row], p1 = row_pos_ptr[row + 1];
+  float w = 0.f;
+  for (int p = p0; p < p1; ++p) w += dlogp[row_pos_idx[p]];
+  const float l = lse[row];
+  const T* z = logits + row * vocab;
+  T* dz = dlogits + row * vocab;
+  for (int i = tid; i < vocab; i += GT) st_logit(dz, i, -__expf(ld_logit(z, i) - l) * w);
+  __syncthreads();
+  if (tid == 0) {
+    for (int p = p0; p < p1; ++p) {
+      const int t = pos_tgt[row_pos_idx[p]];
+      float acc = -__expf(ld_logit(z, t) - l) * w;
+      for (int p2 = p0; p2 < p1; ++p2)
+        if (pos_tgt[row_pos_idx[p2]] == t) acc += dlogp[row_pos_idx[p2]];
+      st_logit(dz, t, acc);
+    }
+  }
+}
+
+hipError_t launch_gather_fwd(const void* logits, bool bf16, int64_t n_rows, int vocab,
+                             const int* pos_row, const int* pos_tgt, int64_t n_pos, float* logp,
+                             float* lse, hipStream_t st) {
+  if (n_rows > 0) {
+    if (bf16)
+      hipLaunchKernelGGL(k_row_lse<uint16_t>, dim3(n_rows), dim3(GT), 0, st, (const uint16_t*)logits,
+                         vocab, lse);
+    else
+      hipLaunchKernelGGL(k_row_lse<float>, dim3(n_rows), dim3(GT), 0, st, (const float*)logits, vocab,
+                         lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n_pos > 0) {
+    const int nb = (int)((n_pos + 255) / 256);
+    if (bf16)
+      hipLaunchKernelGGL(k_pos_logp<uint16_t>, dim3(nb), dim3(256), 0, st, (const uint16_t*)logits,
+                         vocab, pos_row, pos_tgt, n_pos, lse, logp);
+    else
+      hipLaunchKernelGGL(k_pos_logp<float>, dim3(nb), dim3(256), 0, st, (const float*)logits, vocab,
+                         pos_row, pos_tgt, n_pos, lse, logp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gather_bwd(const void* logits, bool bf16, int64_t n_rows, int vocab,
+                             const float* lse, const int* row_pos_ptr, const int* row_pos_idx,
+                             const int* pos_tgt, const float* dlogp, void* dlogits,
+                             hipStream_t st) {
+  if (n_rows <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(k_row_grad<uint16_t>, dim3(n_rows), dim3(GT), 0, st, (const uint16_t*)logits,
+                       vocab, lse, row_pos_ptr, row_pos_idx, pos_tgt, dlogp, (uint16_t*)dlogits);
+  else
+    hipLaunchKernelGGL(k_row_grad<float>, dim3(n_rows), dim3(GT), 0, st, (const float*)logits, vocab,
+                       lse, row_pos_ptr, row_pos_idx, pos_tgt, dlogp, (float*)dlogits);
+  return hipGetLastError();
+}
+
+}  // namespace kda
