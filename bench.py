@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-packed chunkwise KDA hot path on one MI355X.
+
+One step = forward + backward of one KDA layer (16 heads, d = 128, chunk 64,
+bf16 q/k/v, fp32 gates and state) over the whole synthetic rollout tree of
+the workload (default: complete 4-ary tree of depth 3, segment lengths
+U{256..2048}), with the plan built and uploaded before the timed region (the
+plan belongs to the tree and is shared by every KDA layer of a model; its
+host time is reported separately as plan_ms).
+
+Prints one JSON line: unique tokens/s, roofline of the dominant kernel
+(per-kernel launch durations measured live with hipEvents on the launch
+stream through the library's timing hook), the float64 CPU oracle timed on a
+bounded sample of the same workload, and the speedup over trajectory-expanded
+execution of the same tree with the same kernels.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--expanded-steps 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "unique tokens/s, tree-packed KDA fwd+bwd @16 heads d=128; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--expanded-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timing", action="store_true",
+                    help="do not record per-kernel launch events in the timed region")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (per unique token at H heads, head dim D; bf16 inputs)
+# ---------------------------------------------------------------------------
+
+def path_bytes_per_token(H, D, in_bytes=2):
+    """Minimum HBM traffic of the whole layer per unique token: forward reads
+    q,k,v (bf16), g (fp32 per channel), beta, writes o (fp32); backward
+    re-reads the inputs, reads dO (bf16), writes dq, dk, dv, dg (fp32), dbeta."""
+    fwd = H * (3 * D * in_bytes + D * 4 + 4 + D * 4)
+    bwd = H * (3 * D * in_bytes + D * 4 + 4 + D * in_bytes + 4 * D * 4 + 4)
+    return fwd, bwd
+
+
+def kernel_bytes(name, info, H, D, in_bytes=2):
+    """Algorithmic bytes of all launches of one kernel class in one step: the
+    tensors its role requires it to read and write once (documented per
+    kernel in the design doc).  Units: packed rows x heads (row kernels), chunks x
+    heads (chunk kernels)."""
+    P = info["n_packed"]
+    Nrow = info["n_rows"]
+    C = info["n_chunks"]
+    B = info["chunk"]
+    f = 4
+    st = D * D * f  # one state, one head
+    rowin = H * (3 * D * in_bytes + D * f + f)  # q, k, v, g, beta of one row
+    if name == "kda_chunk_prep":
+        # read q,k,v,g,beta of every packed row; write W,U,Gam (D each) and P,T,A (B each)
+        return P * rowin + C * H * B * (3 * D + 3 * B) * f
+    if name == "kda_fwd_state":
+        # read W,U,Gam,P per chunk row, q,k; write o, start state per chunk, handoff/leaf states
+        return (P * H * ((3 * D + B) * f + 2 * D * in_bytes) + Nrow * H * D * f
+                + C * H * st + (info["n_buf"] + info["n_leaf"]) * H * st)
+    if name == "kda_bwd_state":
+        return (P * H * ((D + 2 * B) * f + 2 * D * in_bytes + D * in_bytes + D * f)
+                + 2 * C * H * st + info["n_seq"] * H * st)
+    if name == "kda_bwd_delta":
+        return C * H * (st + 3 * B * D * f)
+    if name == "kda_bwd_hprod":
+        return C * H * (st + B * D * (3 * f + 2 * in_bytes)) + C * H * B * 3 * D * f
+    if name == "kda_bwd_dhprod":
+        return C * H * (2 * st + B * D * f + B * D * f + D * f)
+    if name == "kda_bwd_small":
+        return C * H * B * (D * (2 * f + 2 * in_bytes + f) + B * f * 3) + P * H * (D + 1) * f
+    if name == "kda_bwd_final":
+        return C * H * B * (2 * D * in_bytes + 4 * D * f + 2 * B * f) + P * H * 3 * D * f
+    return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def _oracle_head(args):
+    sub_parent, sub_len, q, k, v, g, beta, dO, dhl, scale = args
+    from oracle import kda as okda
+    from oracle.tree import Tree
+    t = Tree(sub_parent, sub_len)
+    h0 = np.zeros((1, 1, q.shape[2], v.shape[2]))
+    okda.tree_fwd(t, q, k, v, g, beta, h0, scale)
+    okda.tree_bwd(t, q, k, v, g, beta, h0, scale, dO, dhl)
+    return True
+
+
+def cpu_baseline(spec, inp, dO, dhl_full, H, leaves):
+    """Oracle forward + backward, all heads (one process per head), on the
+    subtree root -> first child -> first grandchild -> its leaves."""
+    import multiprocessing as mp
+    from oracle.tree import Tree
+    t = Tree(spec.parent, spec.seg_len, spec.seg_row)
+    keep = [t.roots[0]]
+    c1 = t.children[keep[0]][0]
+    c2 = t.children[c1][0]
+    keep += [c1, c2]
+    stack = list(t.children[c2])
+    while stack:
+        v = stack.pop()
+        keep.append(v)
+        stack.extend(t.children[v])
+    keep = sorted(keep)
+    idx = {v: i for i, v in enumerate(keep)}
+    sub_parent = np.array([-1 if t.parent[v] < 0 else idx[int(t.parent[v])] for v in keep])
+    sub_len = np.array([int(t.seg_len[v]) for v in keep])
+    rows = np.concatenate([t.seg_rows(v) for v in keep])
+    sub_leaves = [v for v in keep if not t.children[v]]
+    li = [leaves.index(v) for v in sub_leaves]
+    n_sub = len(rows)
+    cores = min(16, os.cpu_count() or 1)
+    tasks = []
+    for h in range(H):
+        sl = lambda a: np.ascontiguousarray(a[rows][:, h:h + 1], dtype=np.float64)
+        tasks.append((sub_parent, sub_len, sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.g),
+                      np.ascontiguousarray(inp.beta[rows][:, h:h + 1], dtype=np.float64),
+                      sl(dO), np.ascontiguousarray(dhl_full[li][:, h:h + 1], dtype=np.float64),
+                      inp.scale))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_head, tasks)
+    wall = time.perf_counter() - t0
+    return {"value": n_sub / wall, "unit": "unique tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 numpy oracle forward+backward of all {H} heads (one process "
+                       f"per head, {cores} workers) on a {n_sub}-row subtree of the workload "
+                       f"tree (root, its first child and first grandchild, and that "
+                       f"grandchild's {len(sub_leaves)} leaves); {wall:.1f} s wall")}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+
+    w = synth.workload(a.workload)
+    H, D = w.H, w.dk
+    rng = synth.workload_rng(w)
+    t0 = time.perf_counter()
+    plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk)
+    plan_host_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info
+    N = info["n_rows"]
+    inp = synth.make_kda_inputs(rng, N, H, D, D, bf16=w.bf16)
+    dO_np, dhl_np = synth.make_upstream(rng, N, info["n_leaf"], H, D, D, bf16=w.bf16)
+    # the CPU baseline runs first, in forked workers, before anything touches the GPU
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(w.tree, inp, dO_np, dhl_np, H, list(plan.export("LEAF_SEG")))
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    f = lambda x, d: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev).to(d)
+    q, k, v = f(inp.q, dt), f(inp.k, dt), f(inp.v, dt)
+    g, beta = f(inp.g, torch.float32), f(inp.beta, torch.float32)
+    dO, dhl = f(dO_np, dt), f(dhl_np, torch.float32)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    plan.device(dev)
+    torch.cuda.synchronize()
+    upload_ms = (time.perf_counter() - t0) * 1e3
+
+    fo = B.alloc_fwd(plan, H, D, dev)
+    bo = B.alloc_bwd(plan, H, D, dev)
+
+    def step():
+        B.kda_tree_fwd(plan, q, k, v, g, beta, None, inp.scale, out=fo)
+        B.kda_tree_bwd(plan, q, k, v, g, beta, fo["saved"], dO, dhl, None, inp.scale, out=bo)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not a.no_timing:
+        B.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(a.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    kt = {}
+    if not a.no_timing:
+        kt = B.timing_read()
+        B.timing_enable(False)
+
+    # fwd / bwd split (one extra step each, untimed for the headline)
+    ef = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ef[0].record()
+    B.kda_tree_fwd(plan, q, k, v, g, beta, None, inp.scale, out=fo)
+    ef[1].record()
+    B.kda_tree_bwd(plan, q, k, v, g, beta, fo["saved"], dO, dhl, None, inp.scale, out=bo)
+    ef[2].record()
+    torch.cuda.synchronize()
+    fwd_ms, bwd_ms = ef[0].elapsed_time(ef[1]), ef[1].elapsed_time(ef[2])
+    ok = bool(torch.isfinite(fo["o"]).all() and torch.isfinite(bo["dq"]).all())
+
+    value = N / (ms * 1e-3)
+    fwd_b, bwd_b = path_bytes_per_token(H, D, 2 if w.bf16 else 4)
+    st = H * D * D * 4
+    extra = (info["n_buf"] * 2 * st + info["n_leaf"] * 2 * st)  # handoff and leaf states + grads
+    step_bytes = N * (fwd_b + bwd_b) + extra
+    path_frac = (step_bytes / (ms * 1e-3)) / (HBM_PEAK_GBS * 1e9)
+
+    roof = None
+    kernels = {}
+    if kt:
+        for name, (cnt, tot) in kt.items():
+            per_step = cnt / a.steps
+            kernels[name] = {"launches_per_step": per_step, "ms_per_step": tot / a.steps,
+                             "avg_launch_ms": tot / max(cnt, 1)}
+        dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+        kb = kernel_bytes(dom, info, H, D, 2 if w.bf16 else 4)
+        if kb is not None:
+            lps = kernels[dom]["launches_per_step"]
+            per_launch = kb / lps
+            achieved = per_launch / (kernels[dom]["avg_launch_ms"] * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                    "traffic": None, "bytes_per_launch": int(per_launch),
+                    "avg_launch_ms": round(kernels[dom]["avg_launch_ms"], 4)}
+
+    # trajectory-expanded execution of the same tree, same kernels
+    expanded = None
+    if a.expanded_steps > 0:
+        eplan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk, B.EXPANDED)
+        ei = eplan.info
+        eg = torch.Generator(device=dev)
+        eg.manual_seed(7)
+        dOe = torch.randn((ei["n_out_rows"], H, D), device=dev, generator=eg).to(dt)
+        efo = B.alloc_fwd(eplan, H, D, dev)
+        ebo = B.alloc_bwd(eplan, H, D, dev)
+
+        def estep():
+            B.kda_tree_fwd(eplan, q, k, v, g, beta, None, inp.scale, out=efo)
+            B.kda_tree_bwd(eplan, q, k, v, g, beta, efo["saved"], dOe, dhl, None, inp.scale,
+                           out=ebo)
+        estep()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(a.expanded_steps):
+            estep()
+        e1.record()
+        torch.cuda.synchronize()
+        ems = e0.elapsed_time(e1) / a.expanded_steps
+        expanded = {"ms_per_step": round(ems, 3), "speedup": round(ems / ms, 3),
+                    "expanded_rows": int(ei["n_packed"])}
+        del efo, ebo, dOe
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "unique tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tree": w.tree.name, "heads": H, "d": D,
+                   "chunk": w.chunk, "unique_rows": N, "expanded_rows": int(info["n_expanded"]),
+                   "rounds": info["n_rounds"], "replay_rows": int(info["R"]),
+                   "seq_per_round": [int(x) for x in np.diff(plan.export("ROUND_SEQ_PTR"))],
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "path_roofline": {"bound": "hbm", "bytes_per_step": int(step_bytes),
+                          "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_frac, 5)},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "plan_host_ms": round(plan_host_ms, 3), "plan_upload_ms": round(upload_ms, 3),
+        "expanded": expanded, "kernels": kernels, "finite": ok,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

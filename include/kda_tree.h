@@ -248,6 +248,20 @@ int gather_logprobs_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32
                         const int32_t* row_pos_idx, const int32_t* pos_target,
                         const float* dlogp, void* dlogits, void* stream);
 
+/*
+ * Launch timing for benchmarks and profilers (not needed for computing).
+ * kda_timing_enable(1) clears the counters and makes every later kernel launch
+ * of the library record a pair of hipEvents around it on its launch stream
+ * (the events are created by the library and reused); kda_timing_enable(0)
+ * stops recording.  kda_timing_read(idx, ...) synchronises the recorded events
+ * and returns, for kernel class idx, its name, the number of timed launches
+ * and their summed duration in milliseconds; it returns the number of kernel
+ * classes (call with idx < 0 to get the count only), or KDA_ERR_ARG.
+ */
+int kda_timing_enable(int32_t on);
+int kda_timing_read(int32_t idx, char* name, int32_t name_len, int64_t* launches,
+                    double* total_ms);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* kda_last_error(void);
 

@@ -35,7 +35,7 @@ EXPORTS = [
     "kda_tree_plan", "kda_plan_destroy", "kda_plan_info", "kda_plan_export", "kda_plan_upload",
     "kda_plan_device_offset", "kda_saved_bytes", "kda_fwd_workspace_bytes",
     "kda_bwd_workspace_bytes", "kda_tree_fwd", "kda_tree_bwd", "gather_logprobs",
-    "gather_logprobs_bwd", "kda_last_error",
+    "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
 ]
 
 
@@ -88,6 +88,11 @@ def load_library(path: Path | str | None = None):
     L.gather_logprobs.restype = ctypes.c_int
     L.gather_logprobs_bwd.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
     L.gather_logprobs_bwd.restype = ctypes.c_int
+    L.kda_timing_enable.argtypes = [i32]
+    L.kda_timing_enable.restype = ctypes.c_int
+    L.kda_timing_read.argtypes = [i32, ctypes.c_char_p, i32, ctypes.POINTER(i64),
+                                  ctypes.POINTER(ctypes.c_double)]
+    L.kda_timing_read.restype = ctypes.c_int
     L.kda_last_error.argtypes = []
     L.kda_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -294,4 +299,23 @@ def gather_logprobs_bwd(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp
                                               _p(lse), _p(row_pos_ptr), _p(row_pos_idx),
                                               _p(pos_target), _p(dlogp), _p(out),
                                               _stream(logits)))
+    return out
+
+
+def timing_enable(on: bool = True):
+    """Start (clearing the counters) or stop per-kernel launch timing."""
+    _check(load_library().kda_timing_enable(1 if on else 0))
+
+
+def timing_read() -> dict:
+    """{kernel name: (launches, total ms)} since the last timing_enable."""
+    L = load_library()
+    n = _check(L.kda_timing_read(-1, None, 0, None, None))
+    out = {}
+    for i in range(n):
+        buf = ctypes.create_string_buffer(128)
+        cnt = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(L.kda_timing_read(i, buf, 128, ctypes.byref(cnt), ctypes.byref(ms)))
+        out[buf.value.decode()] = (int(cnt.value), float(ms.value))
     return out

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "timing.h"
+
 namespace kda {
 
 constexpr int GT = 256;
@@ -132,10 +134,10 @@ hipError_t launch_gather_fwd(const void* logits, bool bf16, int64_t n_rows, int 
                              float* lse, hipStream_t st) {
   if (n_rows > 0) {
     if (bf16)
-      hipLaunchKernelGGL(k_row_lse<uint16_t>, dim3(n_rows), dim3(GT), 0, st, (const uint16_t*)logits,
+      KDA_LAUNCH("gather_row_lse", k_row_lse<uint16_t>, dim3(n_rows), dim3(GT), st, (const uint16_t*)logits,
                          vocab, lse);
     else
-      hipLaunchKernelGGL(k_row_lse<float>, dim3(n_rows), dim3(GT), 0, st, (const float*)logits, vocab,
+      KDA_LAUNCH("gather_row_lse", k_row_lse<float>, dim3(n_rows), dim3(GT), st, (const float*)logits, vocab,
                          lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -143,10 +145,10 @@ hipError_t launch_gather_fwd(const void* logits, bool bf16, int64_t n_rows, int 
   if (n_pos > 0) {
     const int nb = (int)((n_pos + 255) / 256);
     if (bf16)
-      hipLaunchKernelGGL(k_pos_logp<uint16_t>, dim3(nb), dim3(256), 0, st, (const uint16_t*)logits,
+      KDA_LAUNCH("gather_pos_logp", k_pos_logp<uint16_t>, dim3(nb), dim3(256), st, (const uint16_t*)logits,
                          vocab, pos_row, pos_tgt, n_pos, lse, logp);
     else
-      hipLaunchKernelGGL(k_pos_logp<float>, dim3(nb), dim3(256), 0, st, (const float*)logits, vocab,
+      KDA_LAUNCH("gather_pos_logp", k_pos_logp<float>, dim3(nb), dim3(256), st, (const float*)logits, vocab,
                          pos_row, pos_tgt, n_pos, lse, logp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -160,10 +162,10 @@ hipError_t launch_gather_bwd(const void* logits, bool bf16, int64_t n_rows, int 
                              hipStream_t st) {
   if (n_rows <= 0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(k_row_grad<uint16_t>, dim3(n_rows), dim3(GT), 0, st, (const uint16_t*)logits,
+    KDA_LAUNCH("gather_row_grad", k_row_grad<uint16_t>, dim3(n_rows), dim3(GT), st, (const uint16_t*)logits,
                        vocab, lse, row_pos_ptr, row_pos_idx, pos_tgt, dlogp, (uint16_t*)dlogits);
   else
-    hipLaunchKernelGGL(k_row_grad<float>, dim3(n_rows), dim3(GT), 0, st, (const float*)logits, vocab,
+    KDA_LAUNCH("gather_row_grad", k_row_grad<float>, dim3(n_rows), dim3(GT), st, (const float*)logits, vocab,
                        lse, row_pos_ptr, row_pos_idx, pos_tgt, dlogp, (float*)dlogits);
   return hipGetLastError();
 }

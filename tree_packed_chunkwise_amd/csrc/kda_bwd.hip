@@ -27,6 +27,7 @@
 // Every sum has a fixed order: results are bitwise reproducible.
 #include "common.h"
 #include "gemm.h"
+#include "timing.h"
 
 namespace kda {
 
@@ -628,34 +629,34 @@ hipError_t launch_bwd_t(const BwdArgs& a, const FwdArgs& pa, int n_chunks,
   if (e != hipSuccess) return e;
   const dim3 cg(n_chunks, a.H);
   if (n_chunks > 0) {
-    hipLaunchKernelGGL((k_prep<TIn, BC, D>), cg, dim3(BT), 0, st, pa);
+    KDA_LAUNCH("kda_chunk_prep", (k_prep<TIn, BC, D>), cg, dim3(BT), st, pa);
     KDA_CHECK();
   }
   for (int r = n_rounds - 1; r >= 0; --r) {
     const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
     if (nseq == 0) continue;
-    hipLaunchKernelGGL((k_bstate<TIn, BC, D, DVS>), dim3(nseq, a.H, D / DVS), dim3(BT), 0, st, a,
-                       round_ptr_host[r]);
+    KDA_LAUNCH("kda_bwd_state", (k_bstate<TIn, BC, D, DVS>), dim3(nseq, a.H, D / DVS), dim3(BT),
+               st, a, round_ptr_host[r]);
     KDA_CHECK();
   }
   if (n_chunks > 0) {
-    hipLaunchKernelGGL((k_gdelta<BC, D>), cg, dim3(BT), 0, st, a);
+    KDA_LAUNCH("kda_bwd_delta", (k_gdelta<BC, D>), cg, dim3(BT), st, a);
     KDA_CHECK();
-    hipLaunchKernelGGL((k_ghprod<TIn, BC, D>), cg, dim3(BT), 0, st, a);
+    KDA_LAUNCH("kda_bwd_hprod", (k_ghprod<TIn, BC, D>), cg, dim3(BT), st, a);
     KDA_CHECK();
-    hipLaunchKernelGGL((k_gdhprod<BC, D>), cg, dim3(BT), 0, st, a);
+    KDA_LAUNCH("kda_bwd_dhprod", (k_gdhprod<BC, D>), cg, dim3(BT), st, a);
     KDA_CHECK();
-    hipLaunchKernelGGL((k_gsmall<TIn, BC, D>), cg, dim3(BT), 0, st, a);
+    KDA_LAUNCH("kda_bwd_small", (k_gsmall<TIn, BC, D>), cg, dim3(BT), st, a);
     KDA_CHECK();
-    hipLaunchKernelGGL((k_gfinal<TIn, BC, D>), cg, dim3(BT), 0, st, a);
+    KDA_LAUNCH("kda_bwd_final", (k_gfinal<TIn, BC, D>), cg, dim3(BT), st, a);
     KDA_CHECK();
   }
   if (n_rep_rows > 0) {
-    hipLaunchKernelGGL((k_reduce_rep<D>), dim3(n_rep_rows, a.H), dim3(BT), 0, st, a);
+    KDA_LAUNCH("kda_bwd_reduce_replay", (k_reduce_rep<D>), dim3(n_rep_rows, a.H), dim3(BT), st, a);
     KDA_CHECK();
   }
   if (n_root > 0) {
-    hipLaunchKernelGGL((k_reduce_dh0<D>), dim3(n_root, a.H), dim3(BT), 0, st, a);
+    KDA_LAUNCH("kda_bwd_reduce_dh0", (k_reduce_dh0<D>), dim3(n_root, a.H), dim3(BT), st, a);
     KDA_CHECK();
   }
 #undef KDA_CHECK

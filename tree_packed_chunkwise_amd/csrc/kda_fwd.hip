@@ -33,6 +33,7 @@
 // each trajectory's chunkwise numerical path).
 #include "common.h"
 #include "gemm.h"
+#include "timing.h"
 
 namespace kda {
 
@@ -337,15 +338,15 @@ hipError_t launch_fwd_t(const FwdArgs& a, int n_chunks, const int* round_ptr_hos
                         hipStream_t st) {
   constexpr int DVS = (D == 128) ? 32 : 16;
   if (n_chunks > 0) {
-    hipLaunchKernelGGL((k_prep<TIn, BC, D>), dim3(n_chunks, a.H), dim3(NTHREADS), 0, st, a);
+    KDA_LAUNCH("kda_chunk_prep", (k_prep<TIn, BC, D>), dim3(n_chunks, a.H), dim3(NTHREADS), st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   for (int r = 0; r < n_rounds; ++r) {
     const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
     if (nseq == 0) continue;
-    hipLaunchKernelGGL((k_state<TIn, BC, D, DVS>), dim3(nseq, a.H, D / DVS), dim3(NTHREADS), 0,
-                       st, a, round_ptr_host[r]);
+    KDA_LAUNCH("kda_fwd_state", (k_state<TIn, BC, D, DVS>), dim3(nseq, a.H, D / DVS),
+               dim3(NTHREADS), st, a, round_ptr_host[r]);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -145,13 +145,14 @@ def shuffled_rows(spec: TreeSpec, rng: np.random.Generator) -> TreeSpec:
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32/float64 values to the nearest bfloat16 (ties to even),
-    returned as float32 (exactly representable)."""
-    f = np.asarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    u = (u + 0x7FFF + lsb) & 0xFFFF0000
-    out = u.astype(np.uint32).view(np.float32)
-    return np.where(np.isnan(f), f, out)
+    returned as float32 (exactly representable).  Finite inputs only."""
+    f = np.array(x, dtype=np.float32, copy=True)
+    u = f.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return f
 
 
 def bf16_bits(x_f32_bf16exact: np.ndarray) -> np.ndarray:
@@ -174,11 +175,14 @@ class KDAInputs:
 
 
 def _l2n(x):
-    return x / np.sqrt((x * x).sum(-1, keepdims=True))
+    n = np.sqrt(np.einsum("...i,...i->...", x, x))[..., None]
+    x /= n
+    return x
 
 
 def softplus(x):
-    return np.logaddexp(0.0, x)
+    """log(1 + e^x), computed stably."""
+    return np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x)))
 
 
 def make_kda_inputs(rng: np.random.Generator, n_rows: int, H: int, dk: int, dv: int,
@@ -187,33 +191,34 @@ def make_kda_inputs(rng: np.random.Generator, n_rows: int, H: int, dk: int, dv: 
                     h0_mode: str = "zero") -> KDAInputs:
     """Per-row KDA inputs with the workload's value distributions:
     q,k ~ N(0,1) L2-normalised per head; v ~ N(0,1); beta = sigmoid(N(0,1));
-    per-channel log-gate g = -softplus(N(gate_mean,1)).  q,k,v are rounded to
-    bf16 (RNE) when bf16=True.  Draw order: q, k, v, beta-pre, g-pre, h0.
+    per-channel log-gate g = -softplus(N(gate_mean,1)).  Draws are float32;
+    q,k,v are rounded to bf16 (RNE) when bf16=True.  Draw order: q, k, v,
+    beta-pre, g-pre, h0.
 
     Test-only variants: gate="weak" draws g = -softplus(N(-4,1)) (slow decay,
     so boundary states stay visible), gate="zero" sets g = 0; beta_mode
     "zero"/"one" pin beta; h0_mode="randn" draws h0 ~ N(0,1)/sqrt(dk)."""
-    q = _l2n(rng.standard_normal((n_rows, H, dk)))
-    k = _l2n(rng.standard_normal((n_rows, H, dk)))
-    v = rng.standard_normal((n_rows, H, dv))
-    bpre = rng.standard_normal((n_rows, H))
-    gpre = rng.standard_normal((n_rows, H, dk))
+    f32 = np.float32
+    q = _l2n(rng.standard_normal((n_rows, H, dk), dtype=f32))
+    k = _l2n(rng.standard_normal((n_rows, H, dk), dtype=f32))
+    v = rng.standard_normal((n_rows, H, dv), dtype=f32)
+    bpre = rng.standard_normal((n_rows, H), dtype=f32)
+    gpre = rng.standard_normal((n_rows, H, dk), dtype=f32)
     if gate == "weak":
-        gpre = gpre - 4.0
-        g = -softplus(gpre)
+        g = -softplus(gpre - np.float32(4.0))
     elif gate == "zero":
         g = np.zeros_like(gpre)
     else:
-        g = -softplus(gpre + gate_mean)
+        g = -softplus(gpre + np.float32(gate_mean))
     beta = 1.0 / (1.0 + np.exp(-bpre))
     if beta_mode == "zero":
         beta = np.zeros_like(beta)
     elif beta_mode == "one":
         beta = np.ones_like(beta)
     if h0_mode == "randn":
-        h0 = rng.standard_normal((n_root, H, dk, dv)) / np.sqrt(dk)
+        h0 = rng.standard_normal((n_root, H, dk, dv), dtype=f32) / np.sqrt(dk)
     else:
-        h0 = np.zeros((n_root, H, dk, dv))
+        h0 = np.zeros((n_root, H, dk, dv), dtype=f32)
     cast = round_bf16 if bf16 else (lambda a: np.asarray(a, dtype=np.float32))
     return KDAInputs(q=cast(q), k=cast(k), v=cast(v),
                      g=np.asarray(g, dtype=np.float32),
@@ -226,12 +231,12 @@ def make_upstream(rng: np.random.Generator, n_out_rows: int, n_leaf: int, H: int
                   dv: int, bf16: bool = True, dh_leaf: str = "randn"):
     """Upstream gradients: dO ~ N(0,1) per output row (bf16-rounded when
     bf16=True), dh_leaf ~ N(0,1) fp32 (or zeros when dh_leaf='zero')."""
-    dO = rng.standard_normal((n_out_rows, H, dv))
-    dO = round_bf16(dO) if bf16 else dO.astype(np.float32)
+    dO = rng.standard_normal((n_out_rows, H, dv), dtype=np.float32)
+    dO = round_bf16(dO) if bf16 else dO
     if dh_leaf == "zero":
         dhl = np.zeros((n_leaf, H, dk, dv), dtype=np.float32)
     else:
-        dhl = rng.standard_normal((n_leaf, H, dk, dv)).astype(np.float32)
+        dhl = rng.standard_normal((n_leaf, H, dk, dv), dtype=np.float32)
     return dO, dhl
 
 
