@@ -92,10 +92,11 @@ kda::DevPlan make_dev_plan(const kda::Plan& p, const void* dev) {
   return v;
 }
 
-// saved = [chunk start states | handoff states]
+// saved = [chunk start states | handoff states | chunk decay products (fp16)]
 struct SavedView {
   float* chunk_h;
   float* bufs;
+  _Float16* prep;
 };
 SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
@@ -103,6 +104,7 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
   const size_t st = (size_t)H * D * D;
   s.chunk_h = c.take((size_t)p.n_chunks() * st);
   s.bufs = c.take((size_t)p.n_buf() * st);
+  s.prep = (_Float16*)c.take(((size_t)p.n_chunks() * H * kda::prep_halves(p.B) + 1) / 2);
   if (total) *total = c.off;
   return s;
 }
@@ -297,9 +299,7 @@ size_t kda_saved_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv) 
 
 size_t kda_fwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv) {
   if (!plan || !shape_ok(plan->p.B, H, dk, dv)) return 0;
-  Carver c(nullptr);
-  carve_chunk_ws(c, plan->p, H, dk);
-  return c.off;
+  return kAlign;  // the forward keeps everything it needs in `saved`
 }
 
 size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv) {
@@ -334,8 +334,8 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   SavedView sv = carve_saved(p, H, dk, saved, nullptr);
   a.chunk_h = sv.chunk_h;
   a.bufs = sv.bufs;
-  Carver c(ws);
-  a.ws = carve_chunk_ws(c, p, H, dk);
+  a.prep = sv.prep;
+  std::memset(&a.ws, 0, sizeof(a.ws));
   hipError_t e = kda::launch_fwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
                                  p.round_seq_ptr.data(), p.n_rounds, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_fwd launch");
@@ -369,6 +369,7 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.scale = scale;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.chunk_h = sv.chunk_h;
+  a.prep = sv.prep;
   a.dO = dO;
   a.dh_leaf = dh_leaf;
   a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;

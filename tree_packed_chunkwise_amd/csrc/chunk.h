@@ -1,0 +1,406 @@
+// chunk.h -- chunk-local building blocks shared by the fused forward and the
+// reverse kernels (gfx950, 512 threads = 8 waves per block).
+//
+// Matrix-core formats used:
+//   * v_mfma_f32_16x16x32_bf16 on hi/lo-split operands (hi = bf16(x),
+//     lo = bf16(x - hi); product hi*hi + hi*lo + lo*hi) for the decay-factored
+//     products A and P, whose factors span a wide exponent range.
+//   * v_mfma_f32_16x16x4_f32 for the small triangular solve.
+//   * v_mfma_f32_16x16x32_f16, one pass, for every other product (operand
+//     magnitudes are bounded, and fp16 keeps 11 mantissa bits).
+//
+// Register-resident operands.  A 16x16 fp32 accumulator tile gives lane l the
+// rows 4(l/16)..4(l/16)+3 of column l%16.  Two vertically adjacent tiles,
+// converted to fp16, are therefore a valid 32-deep B fragment when the k
+// index of lane group g = l/16 runs over {4g..4g+3, 16+4g..16+4g+3}; the A
+// fragment (read from LDS) uses the same k order.  This keeps the recurrent
+// state and the per-chunk delta in registers across every product of a chunk.
+//
+// Decay factors: e^(Gam_i - Gam_j) (j <= i) is split around a reference m per
+// 16-row block pair (I, J) as e^(Gam_i - m) e^(m - Gam_j), m = Gam at the
+// first row of block J.  The left factor is <= 1; the right one is bounded by
+// the decay of at most 15 consecutive rows.  The reference never lies after
+// either row of the pair, so an output row depends only on the rows up to it:
+// a chunk shared by two trajectories up to a fork gives the same bits before
+// the fork in both.
+#pragma once
+
+#include "common.h"
+#include "gemm.h"
+
+namespace kda {
+
+constexpr int NT = 512;  // threads per block
+constexpr int NW = 8;    // waves per block
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfmab(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// B fragment from two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k step)
+__device__ inline f16x8 acc_pair(const f32x4& t0, const f32x4& t1) {
+  f16x8 r;
+  r[0] = (_Float16)t0[0]; r[1] = (_Float16)t0[1]; r[2] = (_Float16)t0[2]; r[3] = (_Float16)t0[3];
+  r[4] = (_Float16)t1[0]; r[5] = (_Float16)t1[1]; r[6] = (_Float16)t1[2]; r[7] = (_Float16)t1[3];
+  return r;
+}
+__device__ inline f16x8 acc_half(const f32x4& t0) {
+  f16x8 r;
+  r[0] = (_Float16)t0[0]; r[1] = (_Float16)t0[1]; r[2] = (_Float16)t0[2]; r[3] = (_Float16)t0[3];
+  r[4] = r[5] = r[6] = r[7] = (_Float16)0.f;
+  return r;
+}
+
+// A fragment in register k order: row `row` of an fp16 [*][pitch] array,
+// k = kb + {4g..4g+3, 16+4g..16+4g+3}; `half_only` zeroes the second half
+// (a k step wider than the contraction).
+__device__ inline f16x8 lds_a_perm(const _Float16* base, int pitch, int row, int kb, int g,
+                                   bool half_only = false) {
+  const _Float16* p = base + row * pitch + kb + 4 * g;
+  const f16x4 lo = *(const f16x4*)p;
+  f16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  if (half_only) {
+    r[4] = r[5] = r[6] = r[7] = (_Float16)0.f;
+  } else {
+    const f16x4 hi = *(const f16x4*)(p + 16);
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  }
+  return r;
+}
+
+template <int BC, int D>
+struct Geom {
+  static constexpr int NB = BC / 16;               // 16-row blocks of a chunk
+  static constexpr int NPAIR = NB * (NB + 1) / 2;  // lower block pairs
+  static constexpr int NOFF = NB * (NB - 1) / 2;   // strictly lower block pairs
+  static constexpr int NCB = D / 16;               // 16-column blocks of a head dim
+  static constexpr int DH = 64;                    // channels per pass of the A/P phase
+  static constexpr int NHALF = D / DH;             // passes
+  static constexpr int NRG = NT / DH;              // row groups of the element mapping
+  static constexpr int RPT = BC / NRG;             // rows per thread in the element mapping
+  static constexpr int PH = DH + 8;                // pitch (halves) of [row][DH] hi/lo arrays
+  static constexpr int PD = D + 8;                 // pitch (halves) of [row][D] fp16 arrays
+  static constexpr int PB = BC + 8;                // pitch (halves) of [*][BC] fp16 arrays
+  static constexpr int PF = BC + 1;                // pitch (floats) of [BC][BC] fp32 arrays
+  static_assert(RPT >= 1 && BC % 16 == 0 && D % DH == 0, "geometry");
+};
+
+// pair index p (0..NPAIR-1) -> block pair (I, J), J <= I, row-major over I
+__device__ inline void pair_of(int p, int& I, int& J) {
+  I = 0;
+  while (p > I) { p -= I + 1; ++I; }
+  J = p;
+}
+// strictly lower pair index of (I, J), J < I
+__device__ inline int off_index(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// Shared tables of a chunk: decay references and per-row metadata.
+template <int BC, int D>
+struct ChunkTables {
+  float gref[BC / 16][D];                    // Gam at the first row of each block
+  float eref[BC / 16][D];                    // e^gref
+  float ecg[BC / 16][D];                     // e^(Gam_C - gref)
+  float gc[D];                               // e^Gam_C
+  float part[Geom<BC, D>::NRG][D];           // per-row-group sums of g
+  float dfac[(Geom<BC, D>::NOFF > 0 ? Geom<BC, D>::NOFF : 1)][D];  // e^(gref_I - gref_J)
+  float beta[BC];
+  int row[BC];
+  int orow[BC];
+};
+
+// hi/lo operands of the decay-factored products for one 64-channel pass:
+//   Lk = K e^(Gam - gref_blk), Lq = Q e^(Gam - gref_blk), Rk = K e^(gref_blk - Gam)
+template <int BC, int D>
+struct APOps {
+  __bf16 kh[BC][Geom<BC, D>::PH], kl[BC][Geom<BC, D>::PH];
+  __bf16 qh[BC][Geom<BC, D>::PH], ql[BC][Geom<BC, D>::PH];
+  __bf16 rh[BC][Geom<BC, D>::PH], rl[BC][Geom<BC, D>::PH];
+};
+
+// Element mapping of the chunk-local pass: thread t owns channels
+// t%64 + 64*half (half = 0..NHALF-1) and rows [rg*RPT, (rg+1)*RPT), rg = t/64.
+template <int BC, int D>
+struct ElemRegs {
+  static constexpr int N = Geom<BC, D>::RPT * Geom<BC, D>::NHALF;
+  float k[N], q[N], gam[N];   // raw inputs, then Gam
+  float lk[N], lq[N], rk[N];  // factored operands
+};
+
+// Issues the loads of k, q, g for the thread's elements (rows via tb.row;
+// zero past the chunk).  No synchronisation.
+template <typename TIn, int BC, int D>
+__device__ inline void elems_load(const TIn* q, const TIn* k, const float* g, int H, int h,
+                                  const ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) {
+  using G = Geom<BC, D>;
+  const int tid = threadIdx.x;
+  const int c0 = tid % G::DH;
+  const int r0 = (tid / G::DH) * G::RPT;
+  int rows[G::RPT];
+#pragma unroll
+  for (int t = 0; t < G::RPT; ++t) rows[t] = tb.row[r0 + t];
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf)
+#pragma unroll
+    for (int t = 0; t < G::RPT; ++t) {
+      const int n = hf * G::RPT + t;
+      const int r = rows[t];
+      const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf;
+      const float kk = ld_in(k, off), qq = ld_in(q, off), gg = g[off];
+      er.k[n] = r >= 0 ? kk : 0.f;
+      er.q[n] = r >= 0 ? qq : 0.f;
+      er.gam[n] = r >= 0 ? gg : 0.f;
+    }
+}
+
+// Gam (cumulative log-decay over the chunk), the block tables and the
+// factored operands in registers.  Ends synchronised.
+template <int BC, int D>
+__device__ inline void elems_gamma(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) {
+  using G = Geom<BC, D>;
+  const int tid = threadIdx.x;
+  const int c0 = tid % G::DH;
+  const int rg = tid / G::DH;
+  const int r0 = rg * G::RPT;
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf) {
+    float run = 0.f;
+#pragma unroll
+    for (int t = 0; t < G::RPT; ++t) {
+      run += er.gam[hf * G::RPT + t];
+      er.gam[hf * G::RPT + t] = run;
+    }
+    tb.part[rg][c0 + G::DH * hf] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf) {
+    const int c = c0 + G::DH * hf;
+    float offs = 0.f;
+    for (int j = 0; j < rg; ++j) offs += tb.part[j][c];
+#pragma unroll
+    for (int t = 0; t < G::RPT; ++t) {
+      const int n = hf * G::RPT + t;
+      er.gam[n] += offs;
+      const int i = r0 + t;
+      if ((i & 15) == 0) tb.gref[i >> 4][c] = er.gam[n];
+      if (i == BC - 1) tb.gc[c] = __expf(er.gam[n]);
+    }
+  }
+  __syncthreads();
+  if (rg == G::NRG - 1) {
+#pragma unroll
+    for (int hf = 0; hf < G::NHALF; ++hf) {
+      const int c = c0 + G::DH * hf;
+      const float gcl = er.gam[hf * G::RPT + G::RPT - 1];  // Gam_C (rows past the chunk add zero)
+      for (int b = 0; b < G::NB; ++b) {
+        tb.eref[b][c] = __expf(tb.gref[b][c]);
+        tb.ecg[b][c] = __expf(gcl - tb.gref[b][c]);
+      }
+    }
+  }
+  if (G::NOFF > 0 && tid < D) {
+    for (int I = 1; I < G::NB; ++I)
+      for (int J = 0; J < I; ++J)
+        tb.dfac[off_index(I, J)][tid] = __expf(tb.gref[I][tid] - tb.gref[J][tid]);
+  }
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf) {
+    const int c = c0 + G::DH * hf;
+#pragma unroll
+    for (int t = 0; t < G::RPT; ++t) {
+      const int n = hf * G::RPT + t;
+      const float ref = tb.gref[(r0 + t) >> 4][c];
+      const float f = __expf(er.gam[n] - ref);
+      const float fi = __expf(ref - er.gam[n]);
+      er.lk[n] = er.k[n] * f;
+      er.lq[n] = er.q[n] * f;
+      er.rk[n] = er.k[n] * fi;
+    }
+  }
+  __syncthreads();
+}
+
+// Writes the hi/lo operands of pass `hf` to LDS.  No synchronisation.
+template <int BC, int D>
+__device__ inline void elems_store(int hf, const ElemRegs<BC, D>& er, APOps<BC, D>& ap) {
+  using G = Geom<BC, D>;
+  const int tid = threadIdx.x;
+  const int c0 = tid % G::DH;
+  const int r0 = (tid / G::DH) * G::RPT;
+#pragma unroll
+  for (int t = 0; t < G::RPT; ++t) {
+    const int n = hf * G::RPT + t, i = r0 + t;
+    __bf16 hh, ll;
+    split_bf16(er.lk[n], hh, ll);
+    ap.kh[i][c0] = hh; ap.kl[i][c0] = ll;
+    split_bf16(er.lq[n], hh, ll);
+    ap.qh[i][c0] = hh; ap.ql[i][c0] = ll;
+    split_bf16(er.rk[n], hh, ll);
+    ap.rh[i][c0] = hh; ap.rl[i][c0] = ll;
+  }
+}
+
+__device__ inline bf16x8 ld_bf8(const __bf16* p) { return *(const bf16x8*)p; }
+
+// Accumulates one 64-channel pass of A_IJ and P_IJ (block pair (I, J),
+// J <= I) on the calling wave; factors taken around gref_J:
+//   A_IJ += (Lk_I e^(gref_I - gref_J)) Rk_J^T,  P_IJ += (Lq_I e^(...)) Rk_J^T
+template <int BC, int D>
+__device__ inline void pair_pass(const APOps<BC, D>& ap, const ChunkTables<BC, D>& tb, int hf,
+                                 int I, int J, f32x4& accA, f32x4& accP) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int g8 = (lane >> 4) * 8;
+  const int ri = 16 * I + l16, rj = 16 * J + l16;
+  const bool off = I != J;
+  const float* df = off ? tb.dfac[off_index(I, J)] + Geom<BC, D>::DH * hf : nullptr;
+#pragma unroll
+  for (int kb = 0; kb < Geom<BC, D>::DH; kb += 32) {
+    const int c0 = kb + g8;
+    bf16x8 kh = ld_bf8(&ap.kh[ri][c0]), kl = ld_bf8(&ap.kl[ri][c0]);
+    bf16x8 qh = ld_bf8(&ap.qh[ri][c0]), ql = ld_bf8(&ap.ql[ri][c0]);
+    const bf16x8 rh = ld_bf8(&ap.rh[rj][c0]), rl = ld_bf8(&ap.rl[rj][c0]);
+    if (off) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = df[c0 + e];
+        __bf16 h2, l2;
+        split_bf16(((float)kh[e] + (float)kl[e]) * f, h2, l2);
+        kh[e] = h2; kl[e] = l2;
+        split_bf16(((float)qh[e] + (float)ql[e]) * f, h2, l2);
+        qh[e] = h2; ql[e] = l2;
+      }
+    }
+    accA = mfmab(kh, rh, accA);
+    accA = mfmab(kh, rl, accA);
+    accA = mfmab(kl, rh, accA);
+    accP = mfmab(qh, rh, accP);
+    accP = mfmab(qh, rl, accP);
+    accP = mfmab(ql, rh, accP);
+  }
+}
+
+// Full chunk-local A/P phase: loads issued by the caller (elems_load), then
+// Gam, the factored operands, and A (strict lower) / P (lower) in fp16 LDS
+// arrays [BC][pitch]; blocks above the diagonal are zeroed.  Ends synchronised.
+template <int BC, int D>
+__device__ inline void chunk_AP(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er, APOps<BC, D>& ap,
+                                _Float16* Aout, int pa, _Float16* Pout, int pp) {
+  using G = Geom<BC, D>;
+  constexpr int MAXP = (G::NPAIR + NW - 1) / NW;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  elems_gamma<BC, D>(tb, er);
+  f32x4 accA[MAXP], accP[MAXP];
+#pragma unroll
+  for (int m = 0; m < MAXP; ++m) accA[m] = accP[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf) {
+    if (hf > 0) __syncthreads();
+    elems_store<BC, D>(hf, er, ap);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      const int p = wave + NW * m;
+      if (p < G::NPAIR) {
+        int I, J;
+        pair_of(p, I, J);
+        pair_pass<BC, D>(ap, tb, hf, I, J, accA[m], accP[m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MAXP; ++m) {
+    const int p = wave + NW * m;
+    if (p < G::NPAIR) {
+      int I, J;
+      pair_of(p, I, J);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + (lane >> 4) * 4 + r;
+        const int j = 16 * J + (lane & 15);
+        Aout[i * pa + j] = (_Float16)((j < i) ? accA[m][r] : 0.f);
+        Pout[i * pp + j] = (_Float16)((j <= i) ? accP[m][r] : 0.f);
+      }
+    }
+  }
+  for (int e = threadIdx.x; e < BC * BC; e += NT) {
+    const int i = e / BC, j = e % BC;
+    if ((j >> 4) > (i >> 4)) {
+      Aout[i * pa + j] = (_Float16)0.f;
+      Pout[i * pp + j] = (_Float16)0.f;
+    }
+  }
+  __syncthreads();
+}
+
+// T = (I + diag(beta) A)^-1 (unit lower triangular, fp32, [BC][PF]):
+// 16x16 diagonal blocks by forward substitution in registers (one lane per
+// block column), then the off-diagonal blocks by distance d on fp32 matrix
+// cores, one wave per block:  S = sum_{K=J}^{I-1} L_IK T_KJ,  T_IJ = -T_II S,
+// with L = diag(beta) A.  S is scratch of NB-1 16x17 blocks.  Ends synchronised.
+template <int BC, int D>
+__device__ inline void chunk_T(const _Float16* A, int pa, const float* beta, float* T, float* S) {
+  using G = Geom<BC, D>;
+  constexpr int PF = G::PF;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+  for (int e = tid; e < BC * BC; e += NT) {
+    const int i = e / BC, j = e % BC;
+    if ((j >> 4) != (i >> 4)) T[i * PF + j] = 0.f;
+  }
+  if (tid < 16 * G::NB) {
+    const int I = tid >> 4, j = tid & 15;
+    const int b0 = 16 * I;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const f16x8 a0 = *(const f16x8*)(A + (b0 + i) * pa + b0);
+      const f16x8 a1 = *(const f16x8*)(A + (b0 + i) * pa + b0 + 8);
+      const float bi = beta[b0 + i];
+      float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc -= bi * (float)(m < 8 ? a0[m] : a1[m - 8]) * x[m];
+      x[i] = (i >= j) ? acc : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) T[(b0 + i) * PF + b0 + j] = x[i];
+  }
+  __syncthreads();
+  for (int d = 1; d < G::NB; ++d) {
+    const int nblk = G::NB - d;  // blocks (I, I-d), I = d..NB-1
+    if (wave < nblk) {
+      const int I = d + wave, J = I - d;
+      const int row = 16 * I + l16;
+      const float b = beta[row];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int m = 16 * J; m < 16 * I; m += 4)
+        acc = mfma32(b * (float)A[row * pa + m + q4], T[(m + q4) * PF + 16 * J + l16], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[(wave * 16 + 4 * q4 + r) * 17 + l16] = acc[r];
+    }
+    __syncthreads();
+    if (wave < nblk) {
+      const int I = d + wave, J = I - d;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 16; m += 4)
+        acc = mfma32(T[(16 * I + l16) * PF + 16 * I + m + q4], S[(wave * 16 + m + q4) * 17 + l16], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) T[(16 * I + 4 * q4 + r) * PF + 16 * J + l16] = -acc[r];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace kda

@@ -49,6 +49,13 @@ struct ChunkWS {
   float* A;
 };
 
+// Chunk-local decay products kept from the forward for the reverse pass, one
+// block per (chunk, head), fp16: A [BC][BC], P [BC][BC], and the inverses of
+// the 16x16 diagonal blocks of I + diag(beta) A, [BC/16][16][16].
+constexpr __host__ __device__ size_t prep_halves(int BC) {
+  return (size_t)2 * BC * BC + (size_t)16 * BC;
+}
+
 inline __host__ __device__ size_t chunk_ws_floats(int BC, int D) {
   return (size_t)BC * D * 3 + (size_t)BC * BC * 3;
 }
@@ -67,6 +74,7 @@ struct FwdArgs {
   float* h_leaf;
   float* chunk_h;      // [n_chunks,H,D,D]
   float* bufs;         // [n_buf,H,D,D]
+  _Float16* prep;      // [n_chunks,H,prep_halves(BC)]
   ChunkWS ws;
 };
 
@@ -97,6 +105,7 @@ struct BwdArgs {
   const float* g;
   const float* beta;
   const float* chunk_h;   // saved start state per chunk [n_chunks,H,D,D]
+  const _Float16* prep;   // saved chunk decay products [n_chunks,H,prep_halves(BC)]
   const void* dO;
   const float* dh_leaf;   // may be null
   float* dq;

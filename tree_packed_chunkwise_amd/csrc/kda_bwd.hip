@@ -36,6 +36,8 @@ constexpr int BW = 4;    // waves per block
 
 template <typename TIn, int BC, int D>
 __global__ void k_prep(FwdArgs a);  // kda_fwd.hip
+hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
+                             int n_rounds, hipStream_t st);  // kda_bwd2.hip
 
 // ---------------------------------------------------------------------------
 // state-gradient recurrence
@@ -622,7 +624,6 @@ template <typename TIn, int BC, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, const FwdArgs& pa, int n_chunks,
                         const int* round_ptr_host, int n_rounds, int n_rep_rows, int n_root,
                         hipStream_t st) {
-  constexpr int DVS = (D == 128) ? 32 : 16;
   hipError_t e;
 #define KDA_CHECK()                      \
   e = hipGetLastError();                 \
@@ -632,13 +633,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const FwdArgs& pa, int n_chunks,
     KDA_LAUNCH("kda_chunk_prep", (k_prep<TIn, BC, D>), cg, dim3(BT), st, pa);
     KDA_CHECK();
   }
-  for (int r = n_rounds - 1; r >= 0; --r) {
-    const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
-    if (nseq == 0) continue;
-    KDA_LAUNCH("kda_bwd_state", (k_bstate<TIn, BC, D, DVS>), dim3(nseq, a.H, D / DVS), dim3(BT),
-               st, a, round_ptr_host[r]);
-    KDA_CHECK();
-  }
+  e = launch_bwd_rounds(a, sizeof(TIn) == 2, BC, D, round_ptr_host, n_rounds, st);
+  if (e != hipSuccess) return e;
   if (n_chunks > 0) {
     KDA_LAUNCH("kda_bwd_delta", (k_gdelta<BC, D>), cg, dim3(BT), st, a);
     KDA_CHECK();

@@ -12,15 +12,10 @@
 //   O     = scale (Q e^Gam h + P delta)
 //   h'    = diag(e^Gam_C) h + (K e^(Gam_C - Gam))^T delta
 //
-// Two launches shapes (HARTS Figure 2(c): all sequences of a round form one
-// packed call; a later round starts only from states of earlier rounds):
-//   k_prep   one block per (chunk, head) over every chunk of every round:
-//            everything that does not depend on the state (Gam, A, P, T, W, U).
-//   k_state  one block per (sequence, head, dv slice) of one round: walks the
-//            sequence's chunks in order carrying its slice of the state; writes
-//            outputs of non-replay rows (Figure C.1(b): replayed rows write no
-//            semantic outputs), the start state of every chunk (for the
-//            backward), handoff states at chunk ends, and the leaf state.
+// k_prep: one block per (chunk, head) over every chunk of every round, used by
+// the reverse pass to recompute everything of a chunk that does not depend on
+// the state (Gam, A, P, T, W, U).  The forward itself runs fused per round
+// (kda_fwd2.hip).
 //
 // Decay factors: e^(Gam_i - Gam_j) (j <= i) is split around a reference m
 // per 16-row block pair as e^(Gam_i - m) * e^(m - Gam_j), with m = Gam at the
@@ -201,176 +196,14 @@ __global__ __launch_bounds__(NTHREADS) void k_prep(FwdArgs a) {
   }
 }
 
-template <int BC, int D, int DVS>
-struct StateSmem {
-  float H[D][DVS + 1];
-  float Del[BC][DVS + 1];
-  float M[BC][D + 1];
-  float P[BC][BC + 1];
-  float GC[D];
-};
-
-template <typename TIn, int BC, int D, int DVS>
-__global__ __launch_bounds__(NTHREADS) void k_state(FwdArgs a, int seq_begin) {
-  __shared__ StateSmem<BC, D, DVS> s;
-  const int seq = seq_begin + blockIdx.x;
-  const int h = blockIdx.y;
-  const int v0 = blockIdx.z * DVS;
-  const int tid = threadIdx.x;
-  const int H = a.H;
-  const TIn* q = (const TIn*)a.q;
-  const TIn* k = (const TIn*)a.k;
-  const size_t DD = (size_t)D * D;
-
-  // initial state slice
-  {
-    const float* src = nullptr;
-    if (a.plan.seq_init_kind[seq] == 0) {
-      if (a.h0) src = a.h0 + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
-    } else {
-      src = a.bufs + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
-    }
-    for (int e = tid; e < D * DVS; e += NTHREADS) {
-      const int r = e / DVS, cc = e % DVS;
-      s.H[r][cc] = src ? src[(size_t)r * D + v0 + cc] : 0.f;
-    }
-  }
-  const int cbeg = a.plan.seq_chunk_ptr[seq];
-  const int cend = a.plan.seq_chunk_ptr[seq + 1];
-  for (int c = cbeg; c < cend; ++c) {
-    const int row0 = a.plan.chunk_row0[c];
-    const int len = a.plan.chunk_len[c];
-    const int nrep = a.plan.chunk_nrep[c];
-    const size_t blk = (size_t)c * H + h;
-    const float* Wg = a.ws.W + blk * BC * D;
-    const float* Ug = a.ws.U + blk * BC * D;
-    const float* Gg = a.ws.Gam + blk * BC * D;
-    const float* Pg = a.ws.P + blk * BC * BC;
-    __syncthreads();
-    {
-      float* dst = a.chunk_h + blk * DD;
-      for (int e = tid; e < D * DVS; e += NTHREADS) {
-        const int r = e / DVS, cc = e % DVS;
-        dst[(size_t)r * D + v0 + cc] = s.H[r][cc];
-      }
-    }
-    for (int e = tid; e < BC * D; e += NTHREADS) s.M[e / D][e % D] = Wg[e];
-    for (int e = tid; e < BC * DVS; e += NTHREADS) {
-      const int i = e / DVS, cc = e % DVS;
-      s.Del[i][cc] = Ug[i * D + v0 + cc];
-    }
-    __syncthreads();
-    // delta = U - W h
-    gemm3<BC, DVS, D, NWAVES>(
-        [&](int i, int ch) { return s.M[i][ch]; },
-        [&](int ch, int cc) { return s.H[ch][cc]; },
-        [&](int i, int cc, float x) { s.Del[i][cc] -= x; });
-    __syncthreads();
-    // Q e^Gam, and P
-    for (int e = tid; e < BC * D; e += NTHREADS) {
-      const int i = e / D, ch = e % D;
-      float qv = 0.f;
-      if (i < len) {
-        const int r = a.plan.row_index[row0 + i];
-        qv = ld_in(q, ((size_t)r * H + h) * D + ch) * __expf(Gg[e]);
-      }
-      s.M[i][ch] = qv;
-    }
-    for (int e = tid; e < BC * BC; e += NTHREADS) s.P[e / BC][e % BC] = Pg[e];
-    __syncthreads();
-    // O = scale (Q e^Gam h + P delta): one product over the concatenated inner dim
-    {
-      const float sc = a.scale;
-      gemm3<BC, DVS, D + BC, NWAVES>(
-          [&](int i, int kk) { return kk < D ? s.M[i][kk] : s.P[i][kk - D]; },
-          [&](int kk, int cc) { return kk < D ? s.H[kk][cc] : s.Del[kk - D][cc]; },
-          [&](int i, int cc, float x) {
-            if (i >= nrep && i < len) {
-              const int orow = a.plan.out_row[row0 + i];
-              a.o[((size_t)orow * H + h) * D + v0 + cc] = sc * x;
-            }
-          });
-    }
-    __syncthreads();
-    // K e^(Gam_C - Gam) and e^Gam_C
-    for (int e = tid; e < BC * D; e += NTHREADS) {
-      const int i = e / D, ch = e % D;
-      float kv = 0.f;
-      if (i < len) {
-        const int r = a.plan.row_index[row0 + i];
-        kv = ld_in(k, ((size_t)r * H + h) * D + ch) * __expf(Gg[(BC - 1) * D + ch] - Gg[e]);
-      }
-      s.M[i][ch] = kv;
-    }
-    for (int ch = tid; ch < D; ch += NTHREADS) s.GC[ch] = __expf(Gg[(BC - 1) * D + ch]);
-    __syncthreads();
-    // h' = diag(e^Gam_C) h + (K e^(Gam_C-Gam))^T delta
-    gemm3<D, DVS, BC, NWAVES>(
-        [&](int ch, int j) { return s.M[j][ch]; },
-        [&](int j, int cc) { return s.Del[j][cc]; },
-        [&](int ch, int cc, float x) { s.H[ch][cc] = s.GC[ch] * s.H[ch][cc] + x; });
-    __syncthreads();
-    const int save = a.plan.chunk_save[c];
-    if (save >= 0) {
-      float* dst = a.bufs + ((size_t)save * H + h) * DD;
-      for (int e = tid; e < D * DVS; e += NTHREADS) {
-        const int r = e / DVS, cc = e % DVS;
-        dst[(size_t)r * D + v0 + cc] = s.H[r][cc];
-      }
-    }
-  }
-  __syncthreads();
-  {
-    float* dst = a.h_leaf + ((size_t)a.plan.seq_leaf[seq] * H + h) * DD;
-    for (int e = tid; e < D * DVS; e += NTHREADS) {
-      const int r = e / DVS, cc = e % DVS;
-      dst[(size_t)r * D + v0 + cc] = s.H[r][cc];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// host launchers
-// ---------------------------------------------------------------------------
-
-template <typename TIn, int BC, int D>
-hipError_t launch_fwd_t(const FwdArgs& a, int n_chunks, const int* round_ptr_host, int n_rounds,
-                        hipStream_t st) {
-  constexpr int DVS = (D == 128) ? 32 : 16;
-  if (n_chunks > 0) {
-    KDA_LAUNCH("kda_chunk_prep", (k_prep<TIn, BC, D>), dim3(n_chunks, a.H), dim3(NTHREADS), st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  for (int r = 0; r < n_rounds; ++r) {
-    const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
-    if (nseq == 0) continue;
-    KDA_LAUNCH("kda_fwd_state", (k_state<TIn, BC, D, DVS>), dim3(nseq, a.H, D / DVS),
-               dim3(NTHREADS), st, a, round_ptr_host[r]);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
-                      const int* round_ptr_host, int n_rounds, hipStream_t st) {
-#define KDA_FWD_CASE(T, BCv, Dv)                                                         \
-  if (BC == BCv && D == Dv) return launch_fwd_t<T, BCv, Dv>(a, n_chunks, round_ptr_host, \
-                                                           n_rounds, st);
-  if (bf16) {
-    KDA_FWD_CASE(uint16_t, 64, 128)
-    KDA_FWD_CASE(uint16_t, 64, 64)
-    KDA_FWD_CASE(uint16_t, 16, 128)
-    KDA_FWD_CASE(uint16_t, 16, 64)
-  } else {
-    KDA_FWD_CASE(float, 64, 128)
-    KDA_FWD_CASE(float, 64, 64)
-    KDA_FWD_CASE(float, 16, 128)
-    KDA_FWD_CASE(float, 16, 64)
-  }
-#undef KDA_FWD_CASE
-  return hipErrorInvalidValue;
-}
+// instantiations launched by the reverse pass (kda_bwd.hip)
+template __global__ void k_prep<uint16_t, 64, 128>(FwdArgs);
+template __global__ void k_prep<uint16_t, 64, 64>(FwdArgs);
+template __global__ void k_prep<uint16_t, 16, 128>(FwdArgs);
+template __global__ void k_prep<uint16_t, 16, 64>(FwdArgs);
+template __global__ void k_prep<float, 64, 128>(FwdArgs);
+template __global__ void k_prep<float, 64, 64>(FwdArgs);
+template __global__ void k_prep<float, 16, 128>(FwdArgs);
+template __global__ void k_prep<float, 16, 64>(FwdArgs);
 
 }  // namespace kda

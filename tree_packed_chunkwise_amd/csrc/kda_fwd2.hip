@@ -1,0 +1,333 @@
+// kda_fwd2.hip -- fused forward of one packed round (gfx950).
+//
+// One block per (sequence, head, dv slice) of the round (HARTS Figure 2(c):
+// all sequences of a round form one packed call).  The block walks its
+// sequence's chunks in order; per chunk (C rows, state h of dk x dv), with
+// A, P and the diagonal-block inverses Td from the chunk-parallel pass
+// (kda_prep.hip):
+//   Gam   = cumulative log-decay of the chunk rows (per key channel)
+//   Z     = V - (K e^Gam) h                 (value minus the decayed state's prediction)
+//   delta : (I + diag(beta) A) delta = diag(beta) Z   (the delta-rule writes of
+//                                            the chunk's rows; block substitution)
+//   O     = scale ((Q e^Gam) h + P delta)   (written for non-replay rows only, Figure C.1(b))
+//   h'    = diag(e^Gam_C) h + (K e^(Gam_C - Gam))^T delta
+// The state h and the chunk's Z / delta never leave registers: they are MFMA
+// accumulators reused as B operands (chunk.h).  The start state of every
+// chunk is saved for the reverse pass; handoff states are saved at chunk
+// ends; the leaf state is written at the end of the sequence.
+//
+// dv slicing: a block owns NV 16-wide column blocks of the state (one per
+// wave); a round with few sequences is cut into D/(16 NV) slices so that more
+// compute units work on it (the chunk-local part is then recomputed per slice).
+#include "chunk.h"
+#include "timing.h"
+
+namespace kda {
+
+__device__ inline f32x4 mfma16k16(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ inline f16x4 acc4(const f32x4& t) {
+  f16x4 r;
+  r[0] = (_Float16)t[0]; r[1] = (_Float16)t[1]; r[2] = (_Float16)t[2]; r[3] = (_Float16)t[3];
+  return r;
+}
+
+template <int BC, int D>
+struct Fwd2Smem {
+  using G = Geom<BC, D>;
+  static constexpr int PT = 24;  // pitch (halves) of the 16-wide diagonal inverses
+  _Float16 Qt[BC][G::PD];        // Q e^Gam                [i][c]
+  _Float16 Kn[BC][G::PD];        // -(K e^Gam)             [j][c]
+  _Float16 KhT[D][G::PB];        // (K e^(Gam_C - Gam))^T  [c][j]
+  _Float16 L[BC][G::PB];         // A                      [i][j]
+  _Float16 P[BC][G::PB];         //                        [i][j]
+  _Float16 Td[BC][PT];           // (I + L_II)^-1, block I at rows 16I..16I+15
+  float part[G::NRG][D];
+  float gc[D];                   // e^Gam_C
+  float beta[BC];
+  int row[BC];
+  int orow[BC];
+};
+
+template <typename TIn, int BC, int D, int NV>
+__global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
+  using G = Geom<BC, D>;
+  using SM = Fwd2Smem<BC, D>;
+  static_assert(NV <= NW, "one column block per wave");
+  constexpr int KD = D / 32;                 // 32-deep k steps over the head dim
+  constexpr int KB = (BC + 31) / 32;         // 32-deep k steps over the chunk rows
+  constexpr bool HALF = (BC == 16);          // chunk rows cover half a k step
+  constexpr int NE = G::RPT * G::NHALF;      // elements per thread of the element mapping
+  __shared__ SM s;
+  const int seq = seq_begin + blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const bool sw = wave < NV;                 // this wave carries a column block of the state
+  const int col = 16 * (blockIdx.z * NV + wave) + l16;
+  const int H = a.H;
+  const TIn* q = (const TIn*)a.q;
+  const TIn* k = (const TIn*)a.k;
+  const TIn* v = (const TIn*)a.v;
+  const size_t DD = (size_t)D * D;
+  const int c0 = tid % G::DH, rg = tid / G::DH, r0 = rg * G::RPT;
+
+  f32x4 hs[G::NCB];
+  {
+    const float* src = nullptr;
+    if (a.plan.seq_init_kind[seq] == 0) {
+      if (a.h0) src = a.h0 + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
+    } else {
+      src = a.bufs + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
+    }
+#pragma unroll
+    for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        hs[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
+  }
+
+  const int cbeg = a.plan.seq_chunk_ptr[seq];
+  const int cend = a.plan.seq_chunk_ptr[seq + 1];
+  for (int c = cbeg; c < cend; ++c) {
+    const int row0 = a.plan.chunk_row0[c];
+    const int len = a.plan.chunk_len[c];
+    const int nrep = a.plan.chunk_nrep[c];
+    const size_t blk = (size_t)c * H + h;
+    __syncthreads();
+    if (tid < BC) {
+      const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
+      s.row[tid] = r;
+      s.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
+      s.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
+    }
+    // decay products of the chunk (chunk-parallel pass)
+    {
+      const _Float16* src = a.prep + blk * prep_halves(BC);
+      constexpr int NV8 = (int)(prep_halves(BC) / 8);
+      for (int e = tid; e < NV8; e += NT) {
+        const f16x8 x = *(const f16x8*)(src + 8 * e);
+        const int hoff = 8 * e;
+        if (hoff < BC * BC) {
+          *(f16x8*)&s.L[hoff / BC][hoff % BC] = x;
+        } else if (hoff < 2 * BC * BC) {
+          const int o = hoff - BC * BC;
+          *(f16x8*)&s.P[o / BC][o % BC] = x;
+        } else {
+          const int o = hoff - 2 * BC * BC;  // [I][i][m], 16 wide
+          *(f16x8*)&s.Td[o / 16][o % 16] = x;
+        }
+      }
+    }
+    __syncthreads();
+    // k, q, g of the element mapping; v of the state's column block
+    float kk[NE], qq[NE], gm[NE];
+    {
+      int rows[G::RPT];
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) rows[t] = s.row[r0 + t];
+#pragma unroll
+      for (int hf = 0; hf < G::NHALF; ++hf)
+#pragma unroll
+        for (int t = 0; t < G::RPT; ++t) {
+          const int n = hf * G::RPT + t, r = rows[t];
+          const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf;
+          const float x1 = ld_in(k, off), x2 = ld_in(q, off), x3 = a.g[off];
+          kk[n] = r >= 0 ? x1 : 0.f;
+          qq[n] = r >= 0 ? x2 : 0.f;
+          gm[n] = r >= 0 ? x3 : 0.f;
+        }
+    }
+    float vz[G::NB][4];
+#pragma unroll
+    for (int J = 0; J < G::NB; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = s.row[16 * J + 4 * g + r];
+        const float x = ld_in(v, ((size_t)(rr < 0 ? 0 : rr) * H + h) * D + (sw ? col : 0));
+        vz[J][r] = rr >= 0 ? x : 0.f;
+      }
+    // Gam: cumulative sum over the chunk rows (row groups, then their prefix)
+#pragma unroll
+    for (int hf = 0; hf < G::NHALF; ++hf) {
+      float run = 0.f;
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) {
+        run += gm[hf * G::RPT + t];
+        gm[hf * G::RPT + t] = run;
+      }
+      s.part[rg][c0 + G::DH * hf] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hf = 0; hf < G::NHALF; ++hf) {
+      const int cc = c0 + G::DH * hf;
+      float offs = 0.f, tot = 0.f;
+#pragma unroll
+      for (int j = 0; j < G::NRG; ++j) {
+        const float pj = s.part[j][cc];
+        offs += (j < rg) ? pj : 0.f;
+        tot += pj;
+      }
+      if (rg == 0) s.gc[cc] = __expf(tot);
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) {
+        const int n = hf * G::RPT + t, i = r0 + t;
+        const float gam = gm[n] + offs;
+        const float e1 = __expf(gam);
+        const float e2 = __expf(tot - gam);
+        s.Qt[i][cc] = (_Float16)(qq[n] * e1);
+        s.Kn[i][cc] = (_Float16)(-kk[n] * e1);
+        s.KhT[cc][i] = (_Float16)(kk[n] * e2);
+      }
+    }
+    __syncthreads();
+
+    // ---- state phase: wave w < NV owns column block w of the slice ----
+    if (sw) {
+      const float sc = a.scale;
+      {  // start state of the chunk, kept for the reverse pass
+        float* dst = a.chunk_h + blk * DD;
+#pragma unroll
+        for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = hs[C][r];
+      }
+      f16x8 hb[KD];
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hs[2 * ks], hs[2 * ks + 1]);
+      // Z = V - (K e^Gam) h
+      f32x4 z[G::NB];
+#pragma unroll
+      for (int J = 0; J < G::NB; ++J) {
+        z[J] = (f32x4){vz[J][0], vz[J][1], vz[J][2], vz[J][3]};
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks)
+          z[J] = mfma16(lds_a_perm(&s.Kn[0][0], G::PD, 16 * J + l16, 32 * ks, g), hb[ks], z[J]);
+      }
+      // (I + diag(beta) A) delta = diag(beta) Z, block forward substitution with
+      // the diagonal inverses: delta_I = Td_I diag(beta_I) (Z_I - sum_{J<I} A_IJ delta_J)
+      f32x4 d[G::NB];
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I) {
+        f32x4 rr = z[I];
+#pragma unroll
+        for (int J = 0; J < I; ++J) {
+          f16x4 la = *(const f16x4*)&s.L[16 * I + l16][16 * J + 4 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) la[e] = -la[e];
+          rr = mfma16k16(la, acc4(d[J]), rr);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rr[r] *= s.beta[16 * I + 4 * g + r];
+        d[I] = mfma16k16(*(const f16x4*)&s.Td[16 * I + l16][4 * g], acc4(rr),
+                         (f32x4){0.f, 0.f, 0.f, 0.f});
+      }
+      f16x8 db[KB];
+#pragma unroll
+      for (int ks = 0; ks < KB; ++ks) db[ks] = HALF ? acc_half(d[0]) : acc_pair(d[2 * ks], d[2 * ks + 1]);
+      // O = scale (Q e^Gam h + P delta)
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks)
+          o = mfma16(lds_a_perm(&s.Qt[0][0], G::PD, 16 * I + l16, 32 * ks, g), hb[ks], o);
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks)
+          if (32 * ks <= 16 * I + 15)
+            o = mfma16(lds_a_perm(&s.P[0][0], G::PB, 16 * I + l16, 32 * ks, g, HALF), db[ks], o);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int orow = s.orow[16 * I + 4 * g + r];
+          if (orow >= 0) a.o[((size_t)orow * H + h) * D + col] = sc * o[r];
+        }
+      }
+      // h' = diag(e^Gam_C) h + (K e^(Gam_C-Gam))^T delta
+#pragma unroll
+      for (int C = 0; C < G::NCB; ++C) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[C][r] *= s.gc[16 * C + 4 * g + r];
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks)
+          hs[C] = mfma16(lds_a_perm(&s.KhT[0][0], G::PB, 16 * C + l16, 32 * ks, g, HALF), db[ks],
+                         hs[C]);
+      }
+      const int save = a.plan.chunk_save[c];
+      if (save >= 0) {
+        float* dst = a.bufs + ((size_t)save * H + h) * DD;
+#pragma unroll
+        for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = hs[C][r];
+      }
+    }
+  }
+  if (sw) {
+    float* dst = a.h_leaf + ((size_t)a.plan.seq_leaf[seq] * H + h) * DD;
+#pragma unroll
+    for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = hs[C][r];
+  }
+}
+
+// Slices of a round: as many as keep every block on its own compute unit
+// (256 CUs) without exceeding D/16 column blocks.
+int round_slices(int nseq, int H, int D) {
+  const int maxs = D / 16;
+  int sl = 1;
+  while (sl * 2 <= maxs && (long)nseq * H * sl * 2 <= 256) sl *= 2;
+  return sl;
+}
+
+template <typename TIn, int BC, int D, int NV>
+hipError_t launch_round(const FwdArgs& a, int nseq, int seq0, int slices, hipStream_t st) {
+  KDA_LAUNCH("kda_fwd_round", (k_fwd_round<TIn, BC, D, NV>), dim3(nseq, a.H, slices), dim3(NT),
+             st, a, seq0);
+  return hipGetLastError();
+}
+
+template <typename TIn, int BC, int D>
+hipError_t launch_fwd2_t(const FwdArgs& a, const int* round_ptr_host, int n_rounds,
+                         hipStream_t st) {
+  constexpr int NCB = D / 16;
+  for (int r = 0; r < n_rounds; ++r) {
+    const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
+    if (nseq == 0) continue;
+    const int sl = round_slices(nseq, a.H, D);
+    const int nv = NCB / sl;
+    hipError_t e = hipErrorInvalidValue;
+    if (nv == NCB) e = launch_round<TIn, BC, D, NCB>(a, nseq, round_ptr_host[r], sl, st);
+    else if (nv == 4) e = launch_round<TIn, BC, D, 4>(a, nseq, round_ptr_host[r], sl, st);
+    else if (nv == 2) e = launch_round<TIn, BC, D, 2>(a, nseq, round_ptr_host[r], sl, st);
+    else if (nv == 1) e = launch_round<TIn, BC, D, 1>(a, nseq, round_ptr_host[r], sl, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st);
+
+hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+                      const int* round_ptr_host, int n_rounds, hipStream_t st) {
+  hipError_t e = launch_prep(a, bf16, BC, D, n_chunks, st);
+  if (e != hipSuccess) return e;
+#define KDA_FWD_CASE(T, BCv, Dv) \
+  if (BC == BCv && D == Dv) return launch_fwd2_t<T, BCv, Dv>(a, round_ptr_host, n_rounds, st);
+  if (bf16) {
+    KDA_FWD_CASE(uint16_t, 64, 128)
+    KDA_FWD_CASE(uint16_t, 64, 64)
+    KDA_FWD_CASE(uint16_t, 16, 128)
+    KDA_FWD_CASE(uint16_t, 16, 64)
+  } else {
+    KDA_FWD_CASE(float, 64, 128)
+    KDA_FWD_CASE(float, 64, 64)
+    KDA_FWD_CASE(float, 16, 128)
+    KDA_FWD_CASE(float, 16, 64)
+  }
+#undef KDA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda
