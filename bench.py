@@ -63,35 +63,33 @@ def path_bytes_per_token(H, D, in_bytes=2):
 def kernel_bytes(name, info, H, D, in_bytes=2):
     """Algorithmic bytes of all launches of one kernel class in one step: the
     tensors its role requires it to read and write once (documented per
-    kernel in the design doc).  Units: packed rows x heads (row kernels), chunks x
-    heads (chunk kernels)."""
+    kernel in the design doc).  P = packed rows (unique rows + replayed rows),
+    C = chunks, per head; states are D x D fp32."""
     P = info["n_packed"]
     Nrow = info["n_rows"]
     C = info["n_chunks"]
     B = info["chunk"]
     f = 4
-    st = D * D * f  # one state, one head
-    rowin = H * (3 * D * in_bytes + D * f + f)  # q, k, v, g, beta of one row
-    if name == "kda_chunk_prep":
-        # read q,k,v,g,beta of every packed row; write W,U,Gam (D each) and P,T,A (B each)
-        return P * rowin + C * H * B * (3 * D + 3 * B) * f
-    if name == "kda_fwd_state":
-        # read W,U,Gam,P per chunk row, q,k; write o, start state per chunk, handoff/leaf states
-        return (P * H * ((3 * D + B) * f + 2 * D * in_bytes) + Nrow * H * D * f
+    st = D * D * f                        # one state of one head
+    prep = (2 * B * B + 16 * B) * 2       # A, P, Td of one chunk-head (fp16)
+    if name == "kda_chunk_decay":
+        # reads q, k, g, beta; writes A, P, Td
+        return P * H * (2 * D * in_bytes + D * f + f) + C * H * prep
+    if name == "kda_fwd_round":
+        # reads q, k, v, g, beta, A/P/Td; writes o (unique rows), the start
+        # state of every chunk, handoff and leaf states
+        return (P * H * (3 * D * in_bytes + D * f + f) + C * H * prep + Nrow * H * D * f
                 + C * H * st + (info["n_buf"] + info["n_leaf"]) * H * st)
-    if name == "kda_bwd_state":
-        return (P * H * ((D + 2 * B) * f + 2 * D * in_bytes + D * in_bytes + D * f)
-                + 2 * C * H * st + info["n_seq"] * H * st)
-    if name == "kda_bwd_delta":
-        return C * H * (st + 3 * B * D * f)
-    if name == "kda_bwd_hprod":
-        return C * H * (st + B * D * (3 * f + 2 * in_bytes)) + C * H * B * 3 * D * f
-    if name == "kda_bwd_dhprod":
-        return C * H * (2 * st + B * D * f + B * D * f + D * f)
-    if name == "kda_bwd_small":
-        return C * H * B * (D * (2 * f + 2 * in_bytes + f) + B * f * 3) + P * H * (D + 1) * f
-    if name == "kda_bwd_final":
-        return C * H * B * (2 * D * in_bytes + 4 * D * f + 2 * B * f) + P * H * 3 * D * f
+    if name == "kda_bwd_round":
+        # reads q, k, g, beta, dO, A/P/Td, leaf-state gradients; writes dy,
+        # the end-state gradient of every chunk, sequence start gradients
+        return (P * H * (3 * D * in_bytes + D * f + f + D * f) + C * H * (prep + st)
+                + (info["n_seq"] + info["n_leaf"]) * H * st)
+    if name == "kda_bwd_chunk_grad":
+        # reads q, k, v, dO, g, beta, dy, A/Td, start state and end-state
+        # gradient of every chunk; writes dq, dk, dv, dg, dbeta
+        return (P * H * (4 * D * in_bytes + 2 * D * f + f + 4 * D * f + f)
+                + C * H * ((B * B + 16 * B) * 2 + 2 * st))
     return None
 
 

@@ -15,7 +15,7 @@
 namespace kda {
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
                       const int* round_ptr_host, int n_rounds, hipStream_t st);
-hipError_t launch_bwd(const BwdArgs& a, const FwdArgs& pa, bool bf16, int BC, int D,
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D,
                       int n_chunks, const int* round_ptr_host, int n_rounds, int n_rep_rows,
                       int n_root, hipStream_t st);
 hipError_t launch_gather_fwd(const void* logits, bool bf16, int64_t n_rows, int vocab,
@@ -109,37 +109,13 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
   return s;
 }
 
-kda::ChunkWS carve_chunk_ws(Carver& c, const kda::Plan& p, int H, int D) {
-  const size_t nb = (size_t)p.n_chunks() * H;
-  const size_t BC = p.B;
-  kda::ChunkWS w;
-  w.W = c.take(nb * BC * D);
-  w.U = c.take(nb * BC * D);
-  w.Gam = c.take(nb * BC * D);
-  w.P = c.take(nb * BC * BC);
-  w.T = c.take(nb * BC * BC);
-  w.A = c.take(nb * BC * BC);
-  return w;
-}
-
 struct BwdWS {
-  kda::ChunkWS cw;
-  kda::GradWS gw;
   float *dy, *dhc, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
 };
 BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
   BwdWS w;
-  w.cw = carve_chunk_ws(c, p, H, D);
   const size_t nb = (size_t)p.n_chunks() * H;
-  const size_t BC = p.B;
-  w.gw.dQt = c.take(nb * BC * D);
-  w.gw.dKt = c.take(nb * BC * D);
-  w.gw.X = c.take(nb * BC * D);
-  w.gw.dKh = c.take(nb * BC * D);
-  w.gw.dP = c.take(nb * BC * BC);
-  w.gw.dA = c.take(nb * BC * BC);
-  w.gw.deGC = c.take(nb * D);
   w.dy = c.take((size_t)p.n_packed * H * D);
   w.dhc = c.take(nb * D * D);
   w.slot = c.take((size_t)p.n_seq() * H * D * D);
@@ -335,7 +311,6 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.chunk_h = sv.chunk_h;
   a.bufs = sv.bufs;
   a.prep = sv.prep;
-  std::memset(&a.ws, 0, sizeof(a.ws));
   hipError_t e = kda::launch_fwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
                                  p.round_seq_ptr.data(), p.n_rounds, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_fwd launch");
@@ -374,21 +349,12 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.dh_leaf = dh_leaf;
   a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
   a.dh_boundary = dh_boundary;
-  a.ws = w.cw;
-  a.gw = w.gw;
   a.dy = w.dy;
   a.dhc = w.dhc;
   a.slot = w.slot;
   a.rep_dq = w.rep_dq; a.rep_dk = w.rep_dk; a.rep_dg = w.rep_dg; a.rep_dv = w.rep_dv;
   a.rep_db = w.rep_db;
-  kda::FwdArgs pa;  // chunk-local recompute uses the forward's prep kernel
-  std::memset(&pa, 0, sizeof(pa));
-  pa.plan = a.plan;
-  pa.H = H;
-  pa.scale = scale;
-  pa.q = q; pa.k = k; pa.v = v; pa.g = g; pa.beta = beta;
-  pa.ws = w.cw;
-  hipError_t e = kda::launch_bwd(a, pa, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
+  hipError_t e = kda::launch_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
                                  p.round_seq_ptr.data(), p.n_rounds, (int)p.rep_row.size(),
                                  p.n_root, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_bwd launch");

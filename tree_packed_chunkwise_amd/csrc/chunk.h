@@ -5,9 +5,11 @@
 //   * v_mfma_f32_16x16x32_bf16 on hi/lo-split operands (hi = bf16(x),
 //     lo = bf16(x - hi); product hi*hi + hi*lo + lo*hi) for the decay-factored
 //     products A and P, whose factors span a wide exponent range.
-//   * v_mfma_f32_16x16x4_f32 for the small triangular solve.
-//   * v_mfma_f32_16x16x32_f16, one pass, for every other product (operand
-//     magnitudes are bounded, and fp16 keeps 11 mantissa bits).
+//   * v_mfma_f32_16x16x32_f16, one pass, for the state products, and
+//     v_mfma_f32_16x16x16_f16 for the 16x16 blocks of the triangular solves
+//     (operand magnitudes are bounded, and fp16 keeps 11 mantissa bits).
+//   Each hi/lo product keeps about 16 mantissa bits; a single bf16 rounding
+//   per operand would cost about 1.6e-3 relative error by itself.
 //
 // Register-resident operands.  A 16x16 fp32 accumulator tile gives lane l the
 // rows 4(l/16)..4(l/16)+3 of column l%16.  Two vertically adjacent tiles,
@@ -26,15 +28,22 @@
 #pragma once
 
 #include "common.h"
-#include "gemm.h"
 
 namespace kda {
 
 constexpr int NT = 512;  // threads per block
 constexpr int NW = 8;    // waves per block
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// hi = bf16(x), lo = bf16(x - hi)
+__device__ inline void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
 
 __device__ inline f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -42,8 +51,13 @@ __device__ inline f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
 __device__ inline f32x4 mfmab(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ inline f32x4 mfma32(float a, float b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+__device__ inline f32x4 mfma16k16(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ inline f16x4 acc4(const f32x4& t) {
+  f16x4 r;
+  r[0] = (_Float16)t[0]; r[1] = (_Float16)t[1]; r[2] = (_Float16)t[2]; r[3] = (_Float16)t[3];
+  return r;
 }
 
 // B fragment from two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k step)
@@ -342,65 +356,6 @@ __device__ inline void chunk_AP(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er, APO
     }
   }
   __syncthreads();
-}
-
-// T = (I + diag(beta) A)^-1 (unit lower triangular, fp32, [BC][PF]):
-// 16x16 diagonal blocks by forward substitution in registers (one lane per
-// block column), then the off-diagonal blocks by distance d on fp32 matrix
-// cores, one wave per block:  S = sum_{K=J}^{I-1} L_IK T_KJ,  T_IJ = -T_II S,
-// with L = diag(beta) A.  S is scratch of NB-1 16x17 blocks.  Ends synchronised.
-template <int BC, int D>
-__device__ inline void chunk_T(const _Float16* A, int pa, const float* beta, float* T, float* S) {
-  using G = Geom<BC, D>;
-  constexpr int PF = G::PF;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
-  for (int e = tid; e < BC * BC; e += NT) {
-    const int i = e / BC, j = e % BC;
-    if ((j >> 4) != (i >> 4)) T[i * PF + j] = 0.f;
-  }
-  if (tid < 16 * G::NB) {
-    const int I = tid >> 4, j = tid & 15;
-    const int b0 = 16 * I;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const f16x8 a0 = *(const f16x8*)(A + (b0 + i) * pa + b0);
-      const f16x8 a1 = *(const f16x8*)(A + (b0 + i) * pa + b0 + 8);
-      const float bi = beta[b0 + i];
-      float acc = (i == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) acc -= bi * (float)(m < 8 ? a0[m] : a1[m - 8]) * x[m];
-      x[i] = (i >= j) ? acc : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) T[(b0 + i) * PF + b0 + j] = x[i];
-  }
-  __syncthreads();
-  for (int d = 1; d < G::NB; ++d) {
-    const int nblk = G::NB - d;  // blocks (I, I-d), I = d..NB-1
-    if (wave < nblk) {
-      const int I = d + wave, J = I - d;
-      const int row = 16 * I + l16;
-      const float b = beta[row];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int m = 16 * J; m < 16 * I; m += 4)
-        acc = mfma32(b * (float)A[row * pa + m + q4], T[(m + q4) * PF + 16 * J + l16], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[(wave * 16 + 4 * q4 + r) * 17 + l16] = acc[r];
-    }
-    __syncthreads();
-    if (wave < nblk) {
-      const int I = d + wave, J = I - d;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 16; m += 4)
-        acc = mfma32(T[(16 * I + l16) * PF + 16 * I + m + q4], S[(wave * 16 + m + q4) * 17 + l16], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) T[(16 * I + 4 * q4 + r) * PF + 16 * J + l16] = -acc[r];
-    }
-    __syncthreads();
-  }
 }
 
 }  // namespace kda

@@ -32,32 +32,11 @@ struct DevPlan {
   const int* root_seq;
 };
 
-// Per-chunk products of the chunk-local pass, one block per (chunk, head),
-// row-major, fp32.  Layout of one block (BC = chunk size, D = head dim):
-//   W   [BC][D]   T diag(beta) (K * e^Gam)
-//   U   [BC][D]   T diag(beta) V
-//   Gam [BC][D]   inclusive cumulative log-decay within the chunk
-//   P   [BC][BC]  sum_c q_ic k_jc e^(Gam_ic - Gam_jc), j <= i
-//   T   [BC][BC]  (I + diag(beta) A)^-1
-//   A   [BC][BC]  sum_c k_ic k_jc e^(Gam_ic - Gam_jc), j < i
-struct ChunkWS {
-  float* W;
-  float* U;
-  float* Gam;
-  float* P;
-  float* T;
-  float* A;
-};
-
 // Chunk-local decay products kept from the forward for the reverse pass, one
 // block per (chunk, head), fp16: A [BC][BC], P [BC][BC], and the inverses of
 // the 16x16 diagonal blocks of I + diag(beta) A, [BC/16][16][16].
 constexpr __host__ __device__ size_t prep_halves(int BC) {
   return (size_t)2 * BC * BC + (size_t)16 * BC;
-}
-
-inline __host__ __device__ size_t chunk_ws_floats(int BC, int D) {
-  return (size_t)BC * D * 3 + (size_t)BC * BC * 3;
 }
 
 struct FwdArgs {
@@ -75,25 +54,7 @@ struct FwdArgs {
   float* chunk_h;      // [n_chunks,H,D,D]
   float* bufs;         // [n_buf,H,D,D]
   _Float16* prep;      // [n_chunks,H,prep_halves(BC)]
-  ChunkWS ws;
 };
-
-// Per-chunk intermediates of the reverse chunk-local passes, one block per
-// (chunk, head): dQt = scale dO h^T, dKt = -diag(beta) dy h^T, X = (K e^Gam) h,
-// dKh = delta dh'^T (each [BC][D]); dP, dA ([BC][BC]); deGC ([D]).
-struct GradWS {
-  float* dQt;
-  float* dKt;
-  float* X;
-  float* dKh;
-  float* dP;
-  float* dA;
-  float* deGC;
-};
-
-inline __host__ __device__ size_t grad_ws_floats(int BC, int D) {
-  return (size_t)BC * D * 4 + (size_t)BC * BC * 2 + (size_t)D;
-}
 
 struct BwdArgs {
   DevPlan plan;
@@ -115,8 +76,6 @@ struct BwdArgs {
   float* dbeta;
   float* dh0;
   float* dh_boundary;     // may be null
-  ChunkWS ws;             // U is overwritten with delta
-  GradWS gw;
   float* dy;              // [n_packed,H,D]
   float* dhc;             // [n_chunks,H,D,D] gradient of each chunk's end state
   float* slot;            // [n_seq,H,D,D] gradient of each sequence's start state

@@ -1,209 +1,324 @@
-// kda_fwd.hip -- forward kernels of tree-packed chunkwise KDA (gfx950).
+// kda_fwd.hip -- fused forward of one packed round (gfx950).
 //
-// Chunk algebra (gated delta rule, per head; the recurrence itself is the
-// reading fixed for the KDA layers that the HARTS pages name in Table 1 and
-// Figure 1(b)).  For a chunk of C rows with start state h (dk x dv):
-//   Gam_i = sum_{s<=i} g_s                       per key channel
-//   A_ij  = sum_c k_ic k_jc e^(Gam_ic-Gam_jc)    j <  i
-//   P_ij  = sum_c q_ic k_jc e^(Gam_ic-Gam_jc)    j <= i
-//   T     = (I + diag(beta) A)^-1
-//   W     = T diag(beta) (K e^Gam),  U = T diag(beta) V
-//   delta = U - W h                              (the delta-rule writes)
-//   O     = scale (Q e^Gam h + P delta)
+// One block per (sequence, head, dv slice) of the round (HARTS Figure 2(c):
+// all sequences of a round form one packed call).  The block walks its
+// sequence's chunks in order; per chunk (C rows, state h of dk x dv), with
+// A, P and the diagonal-block inverses Td from the chunk-parallel pass
+// (kda_prep.hip):
+//   Gam   = cumulative log-decay of the chunk rows (per key channel)
+//   Z     = V - (K e^Gam) h                 (value minus the decayed state's prediction)
+//   delta : (I + diag(beta) A) delta = diag(beta) Z   (the delta-rule writes of
+//                                            the chunk's rows; block substitution)
+//   O     = scale ((Q e^Gam) h + P delta)   (written for non-replay rows only, Figure C.1(b))
 //   h'    = diag(e^Gam_C) h + (K e^(Gam_C - Gam))^T delta
+// The state h and the chunk's Z / delta never leave registers: they are MFMA
+// accumulators reused as B operands (chunk.h).  The start state of every
+// chunk is saved for the reverse pass; handoff states are saved at chunk
+// ends; the leaf state is written at the end of the sequence.
 //
-// k_prep: one block per (chunk, head) over every chunk of every round, used by
-// the reverse pass to recompute everything of a chunk that does not depend on
-// the state (Gam, A, P, T, W, U).  The forward itself runs fused per round
-// (kda_fwd2.hip).
-//
-// Decay factors: e^(Gam_i - Gam_j) (j <= i) is split around a reference m
-// per 16-row block pair as e^(Gam_i - m) * e^(m - Gam_j), with m = Gam at the
-// first row of the column block.  The left factor is <= 1; the right one is
-// bounded by the decay of at most 15 consecutive rows.  The reference never
-// lies after either row of the pair, so every output row depends only on the
-// rows up to it: a chunk shared by two trajectories up to a fork gives the
-// same bits before the fork in both, which is what lets the packed tree run
-// reproduce the trajectory-expanded run exactly (HARTS abstract: replay keeps
-// each trajectory's chunkwise numerical path).
-#include "common.h"
-#include "gemm.h"
+// dv slicing: a block owns NV 16-wide column blocks of the state (one per
+// wave); a round with few sequences is cut into D/(16 NV) slices so that more
+// compute units work on it (the chunk-local part is then recomputed per slice).
+#include "chunk.h"
 #include "timing.h"
 
 namespace kda {
 
-constexpr int NTHREADS = 256;
-constexpr int NWAVES = 4;
-
 template <int BC, int D>
-struct PrepSmem {
-  float K[BC][D + 1];
-  float Q[BC][D + 1];   // q, later K e^Gam, later V
-  float G[BC][D + 1];   // Gam
-  float A[BC][BC + 1];
-  float T[BC][BC + 1];
+struct FwdRoundSmem {
+  using G = Geom<BC, D>;
+  static constexpr int PT = 24;  // pitch (halves) of the 16-wide diagonal inverses
+  _Float16 Qt[BC][G::PD];        // Q e^Gam                [i][c]
+  _Float16 Kn[BC][G::PD];        // -(K e^Gam)             [j][c]
+  _Float16 KhT[D][G::PB];        // (K e^(Gam_C - Gam))^T  [c][j]
+  _Float16 L[BC][G::PB];         // A                      [i][j]
+  _Float16 P[BC][G::PB];         //                        [i][j]
+  _Float16 Td[BC][PT];           // (I + L_II)^-1, block I at rows 16I..16I+15
+  float part[G::NRG][D];
+  float gc[D];                   // e^Gam_C
   float beta[BC];
   int row[BC];
+  int orow[BC];
 };
 
-// Computes A and P for one 16x16 block pair (I, J), J <= I, on the calling wave.
-template <int BC, int D>
-__device__ inline void pair_AP(PrepSmem<BC, D>& s, int I, int J, float* Pout) {
-  const int lane = threadIdx.x & 63;
-  const int l16 = lane & 15;
-  const int kq = (lane >> 4) * 8;
-  const int mrow = 16 * J;
-  f32x4 accA = {0.f, 0.f, 0.f, 0.f};
-  f32x4 accP = {0.f, 0.f, 0.f, 0.f};
-  const int ri = 16 * I + l16;  // row of the A / P operand
-  const int rj = 16 * J + l16;  // row of the key operand
-  for (int kb = 0; kb < D; kb += 32) {
-    bf16x8 kh, kl, qh, ql, rh, rl;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = kb + kq + e;
-      const float m = s.G[mrow][c];
-      const float li = __expf(s.G[ri][c] - m);
-      const float lj = __expf(m - s.G[rj][c]);
-      __bf16 h, l;
-      split_bf16(s.K[ri][c] * li, h, l);
-      kh[e] = h; kl[e] = l;
-      split_bf16(s.Q[ri][c] * li, h, l);
-      qh[e] = h; ql[e] = l;
-      split_bf16(s.K[rj][c] * lj, h, l);
-      rh[e] = h; rl[e] = l;
-    }
-    accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, rh, accA, 0, 0, 0);
-    accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, rl, accA, 0, 0, 0);
-    accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, rh, accA, 0, 0, 0);
-    accP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, rh, accP, 0, 0, 0);
-    accP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, rl, accP, 0, 0, 0);
-    accP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, rh, accP, 0, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 16 * I + (lane >> 4) * 4 + r;
-    const int j = 16 * J + l16;
-    s.A[i][j] = (j < i) ? accA[r] : 0.f;
-    Pout[i * BC + j] = (j <= i) ? accP[r] : 0.f;
-  }
-}
-
-template <typename TIn, int BC, int D>
-__global__ __launch_bounds__(NTHREADS) void k_prep(FwdArgs a) {
-  __shared__ PrepSmem<BC, D> s;
-  const int c = blockIdx.x;
+template <typename TIn, int BC, int D, int NV>
+__global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
+  using G = Geom<BC, D>;
+  using SM = FwdRoundSmem<BC, D>;
+  static_assert(NV <= NW, "one column block per wave");
+  constexpr int KD = D / 32;                 // 32-deep k steps over the head dim
+  constexpr int KB = (BC + 31) / 32;         // 32-deep k steps over the chunk rows
+  constexpr bool HALF = (BC == 16);          // chunk rows cover half a k step
+  constexpr int NE = G::RPT * G::NHALF;      // elements per thread of the element mapping
+  __shared__ SM s;
+  const int seq = seq_begin + blockIdx.x;
   const int h = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const bool sw = wave < NV;                 // this wave carries a column block of the state
+  const int col = 16 * (blockIdx.z * NV + wave) + l16;
   const int H = a.H;
-  const int row0 = a.plan.chunk_row0[c];
-  const int len = a.plan.chunk_len[c];
   const TIn* q = (const TIn*)a.q;
   const TIn* k = (const TIn*)a.k;
   const TIn* v = (const TIn*)a.v;
-  const size_t blk = ((size_t)c * H + h);
-  float* Wg = a.ws.W + blk * BC * D;
-  float* Ug = a.ws.U + blk * BC * D;
-  float* Gg = a.ws.Gam + blk * BC * D;
-  float* Pg = a.ws.P + blk * BC * BC;
-  float* Tg = a.ws.T + blk * BC * BC;
-  float* Ag = a.ws.A + blk * BC * BC;
+  const size_t DD = (size_t)D * D;
+  const int c0 = tid % G::DH, rg = tid / G::DH, r0 = rg * G::RPT;
 
-  if (tid < BC) {
-    const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
-    s.row[tid] = r;
-    s.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
-  }
-  __syncthreads();
-  for (int e = tid; e < BC * D; e += NTHREADS) {
-    const int i = e / D, ch = e % D;
-    const int r = s.row[i];
-    float kv = 0.f, qv = 0.f, gv = 0.f;
-    if (r >= 0) {
-      const size_t off = ((size_t)r * H + h) * D + ch;
-      kv = ld_in(k, off);
-      qv = ld_in(q, off);
-      gv = a.g[off];
-    }
-    s.K[i][ch] = kv;
-    s.Q[i][ch] = qv;
-    s.G[i][ch] = gv;
-  }
-  __syncthreads();
-  // inclusive cumulative sum of the log-decay over the chunk's rows
-  for (int ch = tid; ch < D; ch += NTHREADS) {
-    float acc = 0.f;
-    for (int i = 0; i < BC; ++i) {
-      acc += s.G[i][ch];
-      s.G[i][ch] = acc;
-    }
-  }
-  __syncthreads();
-  // A (strict lower) and P (lower) by 16x16 block pairs
+  f32x4 hs[G::NCB];
   {
-    constexpr int NB = BC / 16;
-    constexpr int NPAIR = NB * (NB + 1) / 2;
-    const int wave = tid >> 6;
-    for (int p = wave; p < NPAIR; p += NWAVES) {
-      int I = 0, rem = p;
-      while (rem > I) { rem -= I + 1; ++I; }
-      pair_AP<BC, D>(s, I, rem, Pg);
+    const float* src = nullptr;
+    if (a.plan.seq_init_kind[seq] == 0) {
+      if (a.h0) src = a.h0 + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
+    } else {
+      src = a.bufs + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
     }
+#pragma unroll
+    for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        hs[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
-  __syncthreads();
-  // T = (I + diag(beta) A)^-1, one column per thread (forward substitution)
-  for (int j = tid; j < BC; j += NTHREADS) {
-    for (int i = 0; i < BC; ++i) {
-      float acc = (i == j) ? 1.f : 0.f;
-      if (i > j) {
-        const float bi = s.beta[i];
-        for (int m = j; m < i; ++m) acc -= bi * s.A[i][m] * s.T[m][j];
+
+  const int cbeg = a.plan.seq_chunk_ptr[seq];
+  const int cend = a.plan.seq_chunk_ptr[seq + 1];
+  for (int c = cbeg; c < cend; ++c) {
+    const int row0 = a.plan.chunk_row0[c];
+    const int len = a.plan.chunk_len[c];
+    const int nrep = a.plan.chunk_nrep[c];
+    const size_t blk = (size_t)c * H + h;
+    __syncthreads();
+    if (tid < BC) {
+      const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
+      s.row[tid] = r;
+      s.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
+      s.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
+    }
+    // decay products of the chunk (chunk-parallel pass)
+    {
+      const _Float16* src = a.prep + blk * prep_halves(BC);
+      constexpr int NV8 = (int)(prep_halves(BC) / 8);
+      for (int e = tid; e < NV8; e += NT) {
+        const f16x8 x = *(const f16x8*)(src + 8 * e);
+        const int hoff = 8 * e;
+        if (hoff < BC * BC) {
+          *(f16x8*)&s.L[hoff / BC][hoff % BC] = x;
+        } else if (hoff < 2 * BC * BC) {
+          const int o = hoff - BC * BC;
+          *(f16x8*)&s.P[o / BC][o % BC] = x;
+        } else {
+          const int o = hoff - 2 * BC * BC;  // [I][i][m], 16 wide
+          *(f16x8*)&s.Td[o / 16][o % 16] = x;
+        }
       }
-      s.T[i][j] = (i >= j) ? acc : 0.f;
+    }
+    __syncthreads();
+    // k, q, g of the element mapping; v of the state's column block
+    float kk[NE], qq[NE], gm[NE];
+    {
+      int rows[G::RPT];
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) rows[t] = s.row[r0 + t];
+#pragma unroll
+      for (int hf = 0; hf < G::NHALF; ++hf)
+#pragma unroll
+        for (int t = 0; t < G::RPT; ++t) {
+          const int n = hf * G::RPT + t, r = rows[t];
+          const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf;
+          const float x1 = ld_in(k, off), x2 = ld_in(q, off), x3 = a.g[off];
+          kk[n] = r >= 0 ? x1 : 0.f;
+          qq[n] = r >= 0 ? x2 : 0.f;
+          gm[n] = r >= 0 ? x3 : 0.f;
+        }
+    }
+    float vz[G::NB][4];
+#pragma unroll
+    for (int J = 0; J < G::NB; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = s.row[16 * J + 4 * g + r];
+        const float x = ld_in(v, ((size_t)(rr < 0 ? 0 : rr) * H + h) * D + (sw ? col : 0));
+        vz[J][r] = rr >= 0 ? x : 0.f;
+      }
+    // Gam: cumulative sum over the chunk rows (row groups, then their prefix)
+#pragma unroll
+    for (int hf = 0; hf < G::NHALF; ++hf) {
+      float run = 0.f;
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) {
+        run += gm[hf * G::RPT + t];
+        gm[hf * G::RPT + t] = run;
+      }
+      s.part[rg][c0 + G::DH * hf] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hf = 0; hf < G::NHALF; ++hf) {
+      const int cc = c0 + G::DH * hf;
+      float offs = 0.f, tot = 0.f;
+#pragma unroll
+      for (int j = 0; j < G::NRG; ++j) {
+        const float pj = s.part[j][cc];
+        offs += (j < rg) ? pj : 0.f;
+        tot += pj;
+      }
+      if (rg == 0) s.gc[cc] = __expf(tot);
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) {
+        const int n = hf * G::RPT + t, i = r0 + t;
+        const float gam = gm[n] + offs;
+        const float e1 = __expf(gam);
+        const float e2 = __expf(tot - gam);
+        s.Qt[i][cc] = (_Float16)(qq[n] * e1);
+        s.Kn[i][cc] = (_Float16)(-kk[n] * e1);
+        s.KhT[cc][i] = (_Float16)(kk[n] * e2);
+      }
+    }
+    __syncthreads();
+
+    // ---- state phase: wave w < NV owns column block w of the slice ----
+    if (sw) {
+      const float sc = a.scale;
+      {  // start state of the chunk, kept for the reverse pass
+        float* dst = a.chunk_h + blk * DD;
+#pragma unroll
+        for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = hs[C][r];
+      }
+      f16x8 hb[KD];
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hs[2 * ks], hs[2 * ks + 1]);
+      // Z = V - (K e^Gam) h
+      f32x4 z[G::NB];
+#pragma unroll
+      for (int J = 0; J < G::NB; ++J) {
+        z[J] = (f32x4){vz[J][0], vz[J][1], vz[J][2], vz[J][3]};
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks)
+          z[J] = mfma16(lds_a_perm(&s.Kn[0][0], G::PD, 16 * J + l16, 32 * ks, g), hb[ks], z[J]);
+      }
+      // (I + diag(beta) A) delta = diag(beta) Z, block forward substitution with
+      // the diagonal inverses: delta_I = Td_I diag(beta_I) (Z_I - sum_{J<I} A_IJ delta_J)
+      f32x4 d[G::NB];
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I) {
+        f32x4 rr = z[I];
+#pragma unroll
+        for (int J = 0; J < I; ++J) {
+          f16x4 la = *(const f16x4*)&s.L[16 * I + l16][16 * J + 4 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) la[e] = -la[e];
+          rr = mfma16k16(la, acc4(d[J]), rr);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rr[r] *= s.beta[16 * I + 4 * g + r];
+        d[I] = mfma16k16(*(const f16x4*)&s.Td[16 * I + l16][4 * g], acc4(rr),
+                         (f32x4){0.f, 0.f, 0.f, 0.f});
+      }
+      f16x8 db[KB];
+#pragma unroll
+      for (int ks = 0; ks < KB; ++ks) db[ks] = HALF ? acc_half(d[0]) : acc_pair(d[2 * ks], d[2 * ks + 1]);
+      // O = scale (Q e^Gam h + P delta)
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks)
+          o = mfma16(lds_a_perm(&s.Qt[0][0], G::PD, 16 * I + l16, 32 * ks, g), hb[ks], o);
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks)
+          if (32 * ks <= 16 * I + 15)
+            o = mfma16(lds_a_perm(&s.P[0][0], G::PB, 16 * I + l16, 32 * ks, g, HALF), db[ks], o);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int orow = s.orow[16 * I + 4 * g + r];
+          if (orow >= 0) a.o[((size_t)orow * H + h) * D + col] = sc * o[r];
+        }
+      }
+      // h' = diag(e^Gam_C) h + (K e^(Gam_C-Gam))^T delta
+#pragma unroll
+      for (int C = 0; C < G::NCB; ++C) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[C][r] *= s.gc[16 * C + 4 * g + r];
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks)
+          hs[C] = mfma16(lds_a_perm(&s.KhT[0][0], G::PB, 16 * C + l16, 32 * ks, g, HALF), db[ks],
+                         hs[C]);
+      }
+      const int save = a.plan.chunk_save[c];
+      if (save >= 0) {
+        float* dst = a.bufs + ((size_t)save * H + h) * DD;
+#pragma unroll
+        for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = hs[C][r];
+      }
     }
   }
-  // K e^Gam replaces q
-  for (int e = tid; e < BC * D; e += NTHREADS) {
-    const int i = e / D, ch = e % D;
-    s.Q[i][ch] = s.K[i][ch] * __expf(s.G[i][ch]);
-  }
-  __syncthreads();
-  auto tri_skip = [](int i0, int, int kb) { return kb > i0 + 15; };
-  // W = T diag(beta) (K e^Gam)
-  gemm3<BC, D, BC, NWAVES>(
-      [&](int i, int j) { return s.T[i][j] * s.beta[j]; },
-      [&](int j, int ch) { return s.Q[j][ch]; },
-      [&](int i, int ch, float x) { Wg[i * D + ch] = x; }, tri_skip);
-  __syncthreads();
-  // V replaces K e^Gam
-  for (int e = tid; e < BC * D; e += NTHREADS) {
-    const int i = e / D, ch = e % D;
-    const int r = s.row[i];
-    s.Q[i][ch] = r >= 0 ? ld_in(v, ((size_t)r * H + h) * D + ch) : 0.f;
-  }
-  __syncthreads();
-  gemm3<BC, D, BC, NWAVES>(
-      [&](int i, int j) { return s.T[i][j] * s.beta[j]; },
-      [&](int j, int ch) { return s.Q[j][ch]; },
-      [&](int i, int ch, float x) { Ug[i * D + ch] = x; }, tri_skip);
-  for (int e = tid; e < BC * D; e += NTHREADS) Gg[e] = s.G[e / D][e % D];
-  for (int e = tid; e < BC * BC; e += NTHREADS) {
-    const int i = e / BC, j = e % BC;
-    const bool low = j < i;
-    Tg[e] = s.T[i][j];
-    Ag[e] = low ? s.A[i][j] : 0.f;
-    if ((j >> 4) > (i >> 4)) Pg[e] = 0.f;  // blocks above the diagonal
+  if (sw) {
+    float* dst = a.h_leaf + ((size_t)a.plan.seq_leaf[seq] * H + h) * DD;
+#pragma unroll
+    for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = hs[C][r];
   }
 }
 
-// instantiations launched by the reverse pass (kda_bwd.hip)
-template __global__ void k_prep<uint16_t, 64, 128>(FwdArgs);
-template __global__ void k_prep<uint16_t, 64, 64>(FwdArgs);
-template __global__ void k_prep<uint16_t, 16, 128>(FwdArgs);
-template __global__ void k_prep<uint16_t, 16, 64>(FwdArgs);
-template __global__ void k_prep<float, 64, 128>(FwdArgs);
-template __global__ void k_prep<float, 64, 64>(FwdArgs);
-template __global__ void k_prep<float, 16, 128>(FwdArgs);
-template __global__ void k_prep<float, 16, 64>(FwdArgs);
+// Slices of a round: as many as keep every block on its own compute unit
+// (256 CUs) without exceeding D/16 column blocks.
+int round_slices(int nseq, int H, int D) {
+  const int maxs = D / 16;
+  int sl = 1;
+  while (sl * 2 <= maxs && (long)nseq * H * sl * 2 <= 256) sl *= 2;
+  return sl;
+}
+
+template <typename TIn, int BC, int D, int NV>
+hipError_t launch_round(const FwdArgs& a, int nseq, int seq0, int slices, hipStream_t st) {
+  KDA_LAUNCH("kda_fwd_round", (k_fwd_round<TIn, BC, D, NV>), dim3(nseq, a.H, slices), dim3(NT),
+             st, a, seq0);
+  return hipGetLastError();
+}
+
+template <typename TIn, int BC, int D>
+hipError_t launch_fwd2_t(const FwdArgs& a, const int* round_ptr_host, int n_rounds,
+                         hipStream_t st) {
+  constexpr int NCB = D / 16;
+  for (int r = 0; r < n_rounds; ++r) {
+    const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
+    if (nseq == 0) continue;
+    const int sl = round_slices(nseq, a.H, D);
+    const int nv = NCB / sl;
+    hipError_t e = hipErrorInvalidValue;
+    if (nv == NCB) e = launch_round<TIn, BC, D, NCB>(a, nseq, round_ptr_host[r], sl, st);
+    else if (nv == 4) e = launch_round<TIn, BC, D, 4>(a, nseq, round_ptr_host[r], sl, st);
+    else if (nv == 2) e = launch_round<TIn, BC, D, 2>(a, nseq, round_ptr_host[r], sl, st);
+    else if (nv == 1) e = launch_round<TIn, BC, D, 1>(a, nseq, round_ptr_host[r], sl, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st);
+
+hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+                      const int* round_ptr_host, int n_rounds, hipStream_t st) {
+  hipError_t e = launch_prep(a, bf16, BC, D, n_chunks, st);
+  if (e != hipSuccess) return e;
+#define KDA_FWD_CASE(T, BCv, Dv) \
+  if (BC == BCv && D == Dv) return launch_fwd2_t<T, BCv, Dv>(a, round_ptr_host, n_rounds, st);
+  if (bf16) {
+    KDA_FWD_CASE(uint16_t, 64, 128)
+    KDA_FWD_CASE(uint16_t, 64, 64)
+    KDA_FWD_CASE(uint16_t, 16, 128)
+    KDA_FWD_CASE(uint16_t, 16, 64)
+  } else {
+    KDA_FWD_CASE(float, 64, 128)
+    KDA_FWD_CASE(float, 64, 64)
+    KDA_FWD_CASE(float, 16, 128)
+    KDA_FWD_CASE(float, 16, 64)
+  }
+#undef KDA_FWD_CASE
+  return hipErrorInvalidValue;
+}
 
 }  // namespace kda

@@ -1,0 +1,95 @@
+// kda_reduce.hip -- the reverse pass in full, and its two fixed-order reductions
+// (gfx950).
+//
+// Order of the reverse pass of a plan:
+//   1. the state-gradient rounds, last round first (kda_bwd.hip);
+//   2. the chunk-local gradients of every chunk, fully parallel (kda_grad.hip);
+//   3. gradients of replayed rows (rows a side sequence recomputes from the
+//      start of its chunk, HARTS Figure 2(c)) added into their compact rows;
+//   4. dh0 of every root: the sum of the start-state gradients of the
+//      sequences that start from it.
+// Both reductions add in a fixed order, so results do not depend on timing.
+#include "common.h"
+#include "timing.h"
+
+namespace kda {
+
+constexpr int BT = 256;  // threads per block of the reductions
+
+hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
+                             int n_rounds, hipStream_t st);
+hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st);
+
+// replayed-row gradients added into their compact rows (fixed order)
+template <int D>
+__global__ __launch_bounds__(BT) void k_reduce_rep(BwdArgs a) {
+  const int e = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int H = a.H;
+  const int row = a.plan.rep_row[e];
+  const int p0 = a.plan.rep_ptr[e], p1 = a.plan.rep_ptr[e + 1];
+  for (int ch = tid; ch < D; ch += BT) {
+    const size_t o = ((size_t)row * H + h) * D + ch;
+    float sq = a.dq[o], sk = a.dk[o], sg = a.dg[o], sv = a.dv[o];
+    for (int p = p0; p < p1; ++p) {
+      const size_t r = ((size_t)a.plan.rep_slot[p] * H + h) * D + ch;
+      sq += a.rep_dq[r];
+      sk += a.rep_dk[r];
+      sg += a.rep_dg[r];
+      sv += a.rep_dv[r];
+    }
+    a.dq[o] = sq;
+    a.dk[o] = sk;
+    a.dg[o] = sg;
+    a.dv[o] = sv;
+  }
+  if (tid == 0) {
+    float sb = a.dbeta[(size_t)row * H + h];
+    for (int p = p0; p < p1; ++p) sb += a.rep_db[(size_t)a.plan.rep_slot[p] * H + h];
+    a.dbeta[(size_t)row * H + h] = sb;
+  }
+}
+
+// dh0 of every root: sum of the start gradients of its sequences (fixed order)
+template <int D>
+__global__ __launch_bounds__(BT) void k_reduce_dh0(BwdArgs a) {
+  const int rt = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int H = a.H;
+  const int p0 = a.plan.root_seq_ptr[rt], p1 = a.plan.root_seq_ptr[rt + 1];
+  const size_t DD = (size_t)D * D;
+  for (int e = tid; e < D * D; e += BT) {
+    float acc = 0.f;
+    for (int p = p0; p < p1; ++p) acc += a.slot[((size_t)a.plan.root_seq[p] * H + h) * DD + e];
+    a.dh0[((size_t)rt * H + h) * DD + e] = acc;
+  }
+}
+
+template <int D>
+hipError_t launch_reduce_t(const BwdArgs& a, int n_rep_rows, int n_root, hipStream_t st) {
+  if (n_rep_rows > 0) {
+    KDA_LAUNCH("kda_bwd_reduce_replay", (k_reduce_rep<D>), dim3(n_rep_rows, a.H), dim3(BT), st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n_root > 0) {
+    KDA_LAUNCH("kda_bwd_reduce_dh0", (k_reduce_dh0<D>), dim3(n_root, a.H), dim3(BT), st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+                      const int* round_ptr_host, int n_rounds, int n_rep_rows, int n_root,
+                      hipStream_t st) {
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  hipError_t e = launch_bwd_rounds(a, bf16, BC, D, round_ptr_host, n_rounds, st);
+  if (e != hipSuccess) return e;
+  if (n_chunks > 0) {
+    e = launch_grad(a, bf16, BC, D, n_chunks, st);
+    if (e != hipSuccess) return e;
+  }
+  return D == 128 ? launch_reduce_t<128>(a, n_rep_rows, n_root, st)
+                  : launch_reduce_t<64>(a, n_rep_rows, n_root, st);
+}
+
+}  // namespace kda
