@@ -44,7 +44,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel launch events in the timed region")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (1 GiB read + 1 GiB "
+                         "written per launch, 3 launches), to scale HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # floats: 1 GiB
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 4,
+                                           "bytes_written_per_launch": n * 4, "launches": 3}}))
 
 
 # ---------------------------------------------------------------------------
@@ -159,6 +175,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from tree_packed_chunkwise_amd import binding as B
     from tree_packed_chunkwise_amd import synth

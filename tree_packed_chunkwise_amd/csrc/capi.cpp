@@ -8,7 +8,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/kda_tree.h"
+#include "kda_tree.h"
 #include "common.h"
 #include "plan.h"
 

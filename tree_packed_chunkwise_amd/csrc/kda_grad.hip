@@ -18,29 +18,90 @@
 // Gradients of replayed rows go to replay slots (added into their compact rows
 // afterwards in a fixed order).
 //
-// Phases: (1) each wave owns a 16-column block of dv: Z, delta, the dbeta and
-// deGC partials in registers, dO / -dZ / delta / h staged in LDS as fp16;
-// (2) products contracting dv on fp16 matrix cores; (3) the decay-weighted
-// products on hi/lo bf16 matrix cores in 32-channel passes, decay split
-// around the first row of the column block as in the forward, with the
-// per-pair channel factor applied to output columns; (4) the combine and the
-// reverse cumulative sum.
+// Layout of the work.  Every global load of the block is issued first.  Phase 1:
+// wave w owns a 16-column block of dv (Z, delta, dbeta and deGC partials,
+// dv), with dO, -dZ, delta and h staged in LDS as fp16.  Phase 2: wave w owns
+// the 16-row block tI = w % NB of the chunk and, transposed ([channel][row]),
+// the output tiles (C, tI) with C = w / NB + (8 / NB) m; it forms dQt^T, dKt^T,
+// dKh^T for them, and the dP / dA blocks that its row block meets -- (tI, J),
+// J <= tI as [j][i] tiles and (I, tI), I >= tI as [i][j] tiles -- which stay in
+// registers as hi/lo bf16 B operands (an accumulator tile is a B fragment of
+// the 16x16x16 matrix-core op).  Phase 3, per 64-channel pass: the decay
+// factored q / k operands are staged transposed, the decay-weighted products
+// run on hi/lo bf16 matrix cores (each block pair around the first row of its
+// column block, the channel factor between the two references applied to the
+// output rows), the gradients are combined, and dg is formed by a parallel
+// reverse scan.
 #include "chunk.h"
 #include "timing.h"
 
 namespace kda {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfmab16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ inline short bf16_bits(__bf16 x) { return __builtin_bit_cast(short, x); }
+__device__ inline float bf16_val(__bf16 x) { return (float)x; }
+// accumulator tile -> hi/lo bf16 B fragment of the 16x16x16 op
+__device__ inline void split_tile(const f32x4& t, s16x4& hi, s16x4& lo) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    __bf16 h, l;
+    split_bf16(t[r], h, l);
+    hi[r] = bf16_bits(h);
+    lo[r] = bf16_bits(l);
+  }
+}
+// the hi/lo product  ah bh + ah bl + al bh
+__device__ inline f32x4 mma3(const s16x4& ah, const s16x4& al, const s16x4& bh, const s16x4& bl) {
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+  t = mfmab16(ah, bh, t);
+  t = mfmab16(ah, bl, t);
+  t = mfmab16(al, bh, t);
+  return t;
+}
+
+// eight consecutive input elements (bf16 bit patterns or fp32)
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 x;
+  __device__ void load(const uint16_t* p) { x = *(const uint4*)p; }
+  __device__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ float at(int e) const {
+    const uint32_t w = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <> struct Raw8<float> {
+  float4 x, y;
+  __device__ void load(const float* p) { x = *(const float4*)p; y = *(const float4*)(p + 4); }
+  __device__ void zero() { x = y = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ float at(int e) const {
+    const float4& v = e < 4 ? x : y;
+    const int k = e & 3;
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+};
+
 template <int BC, int D>
 struct GradGeom {
-  static constexpr int NB = BC / 16;
-  static constexpr int NCB = D / 16;
-  static constexpr int NQ = D / 32;              // 32-channel passes of the decay phase
+  static constexpr int NB = BC / 16;             // 16-row blocks of the chunk
+  static constexpr int NCB = D / 16;             // 16-channel blocks
+  static constexpr int KD = D / 32;              // 32-deep k steps over a head dim
+  static constexpr int NHF = D / 64;             // 64-channel passes of phase 3
+  static constexpr int NS = NB + 1;              // dP / dA blocks met by one row block
+  static constexpr int NG = NW / NB;             // waves per row block
+  static constexpr int NTW = (NCB / NG) > 0 ? NCB / NG : 1;  // output tiles per wave
   static constexpr int PD = D + 8;               // fp16 [*][D] pitch
-  static constexpr int PB = BC + 8;              // fp16 [*][BC] pitch
-  static constexpr int PF = BC + 1;              // fp32 [BC][BC] pitch
-  static constexpr int PG = D + 1;               // fp32 [BC][D] pitch
-  static constexpr int PQ = BC + 8;              // bf16 [32][BC] pitch of the decay operands
-  static constexpr int NLOW = NB * (NB + 1) / 2; // lower 16x16 blocks of dP / dA
+  static constexpr int PB = BC + 8;              // 16-bit [*][BC] pitch
+  static constexpr int PG = BC + 1;              // fp32 [64][BC] pitch
+  static constexpr int NLOW = NB * (NB + 1) / 2; // lower block pairs
+  static constexpr int DH = 64;
+  static constexpr int NRG = NT / DH;            // row groups of the element mapping
+  static constexpr int RPT = BC / NRG;           // rows per thread in the element mapping
+  static_assert(RPT >= 1 && NCB % 4 == 0, "geometry");
 };
 
 // lower block pair (I, J), J <= I -> I (I + 1) / 2 + J
@@ -50,53 +111,54 @@ template <int BC, int D>
 struct GradSmem {
   using G = GradGeom<BC, D>;
   union {
-    struct {
-      _Float16 A[BC][G::PB];     // A (strict lower)
-      _Float16 Td[BC][24];       // diagonal-block inverses
+    struct {                       // phases 1-2
+      _Float16 A[BC][G::PB];       // A (strict lower)
+      _Float16 Td[BC][24];         // diagonal-block inverses
       union {
-        _Float16 Kn[BC][G::PD];  // -(K e^Gam)          [i][c], until Z is formed
-        _Float16 dO[BC][G::PD];  // scale dO            [i][v]
+        _Float16 Kn[BC][G::PD];    // -(K e^Gam)        [i][c], until Z is formed
+        _Float16 dO[BC][G::PD];    // scale dO          [i][v]
       } x;
-      _Float16 nZ[BC][G::PD];    // -diag(beta) dy      [i][v]
-      _Float16 dl[BC][G::PD];    // delta               [j][v]
-      _Float16 Hs[D][G::PD];     // h, later dh'        [c][v]
+      _Float16 nZ[BC][G::PD];      // -diag(beta) dy    [i][v]
+      _Float16 dl[BC][G::PD];      // delta             [j][v]
+      _Float16 Hs[D][G::PD];       // h, later dh'      [c][v]
     } p;
-    struct {
-      __bf16 rh[32][G::PQ], rl[32][G::PQ];   // (K e^(gref - Gam))^T    [c][j]
-      __bf16 qh[32][G::PQ], ql[32][G::PQ];   // (Q e^(Gam - gref))^T    [c][i]
-      __bf16 kh[32][G::PQ], kl[32][G::PQ];   // (K e^(Gam - gref))^T    [c][i]
-      float Gam[BC][G::PG];                  // Gam, replaced by dGam tile by tile
+    struct {                       // phase 3, one 64-channel pass, transposed
+      __bf16 rh[64][G::PB], rl[64][G::PB];   // K e^(gref - Gam)   [c][j]
+      __bf16 qh[64][G::PB], ql[64][G::PB];   // Q e^(Gam - gref)   [c][i]
+      __bf16 kh[64][G::PB], kl[64][G::PB];   // K e^(Gam - gref)   [c][i]
+      float gam[64][G::PG];                  // Gam, replaced by dGam
     } d;
   } u;
-  float dP[BC][G::PF];
-  float dA[BC][G::PF];
-  float redb[NW][BC];        // dbeta partials per wave
-  float redg[NW][D];         // deGC partials per wave
-  float csum[G::NB][D];      // sum_j dKh_jc K_jc e^(Gam_C - Gam_jc) partials per row block
-  float gref[G::NB][D];      // Gam at the first row of each block
-  float dfac[G::NLOW][D];    // e^(gref_I - gref_J), J <= I
-  float part[8][D];
+  __attribute__((aligned(16))) float dfac[G::NLOW][D];   // e^(gref_I - gref_J), J <= I
+  __attribute__((aligned(16))) float gref[G::NB][D];     // Gam at the first row of each block
+  __attribute__((aligned(16))) float eref[G::NB][D];     // e^gref
+  __attribute__((aligned(16))) float ecg[G::NB][D];      // e^(Gam_C - gref)
+  float csum[G::NB][D];     // sum over a row block of dKh_jc K_jc e^(Gam_C - Gam_jc)
+  float redb[NW][BC];       // dbeta partials per wave
+  float redg[NW][D];        // deGC partials per wave
+  float part[G::NRG][D];    // row-group sums (Gam, then the reverse scan)
   float degc[D];
-  float gcl[D];              // Gam_C
   float beta[BC];
   int row[BC];
   int orow[BC];
 };
 
 // destination of a row gradient: the output row, or the replay slot
-__device__ inline float* grad_dst(const BwdArgs& a, float* base, float* rep, int c, int i,
-                                  int nrep, int row0, int h, int width) {
-  if (i < nrep) return rep + ((size_t)(a.plan.chunk_rep0[c] + i) * a.H + h) * width;
-  return base + ((size_t)a.plan.out_row[row0 + i] * a.H + h) * width;
+__device__ inline float* grad_dst(const BwdArgs& a, float* base, float* rep, int rep0, int orow,
+                                  int i, int nrep, int h, int width) {
+  if (i < nrep) return rep + ((size_t)(rep0 + i) * a.H + h) * width;
+  return base + ((size_t)orow * a.H + h) * width;
 }
 
 template <typename TIn, int BC, int D>
 __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
   using G = GradGeom<BC, D>;
-  constexpr int NB = G::NB, NCB = G::NCB;
-  constexpr int KD = D / 32;
+  constexpr int NB = G::NB, NCB = G::NCB, KD = G::KD, NHF = G::NHF, NS = G::NS;
+  constexpr int NG = G::NG, NTW = G::NTW, DH = G::DH, NRG = G::NRG, RPT = G::RPT;
+  constexpr int NE = RPT * NHF;
   constexpr int KB = (BC + 31) / 32;
   constexpr bool HALF = (BC == 16);
+  constexpr int NV8 = (BC * D / 8 + NT - 1) / NT;   // 8-element vectors of dO per thread
   __shared__ GradSmem<BC, D> s;
   const int c = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -104,6 +166,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
   const size_t blk = (size_t)c * H + h;
   const size_t DD = (size_t)D * D;
   const int row0 = a.plan.chunk_row0[c], len = a.plan.chunk_len[c], nrep = a.plan.chunk_nrep[c];
+  const int rep0 = a.plan.chunk_rep0[c];
   const TIn* q = (const TIn*)a.q;
   const TIn* k = (const TIn*)a.k;
   const TIn* v = (const TIn*)a.v;
@@ -127,57 +190,11 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
       *(f16x8*)&s.u.p.Td[o / 16][o % 16] = *(const f16x8*)(src + 2 * BC * BC + o);
     }
   }
-  __syncthreads();
-
-  // ---- Gam of the chunk; element mapping: channel c0 + 64 hf, rows r0 .. r0+RPT-1 ----
-  constexpr int DH = 64, NRG = NT / DH, RPT = BC / NRG, NHF = D / DH;
-  const int c0 = tid % DH, rg = tid / DH, r0 = rg * RPT;
-  float gm[RPT * NHF];
-  {
-    float kk[RPT * NHF];
-#pragma unroll
-    for (int hf = 0; hf < NHF; ++hf) {
-      float run = 0.f;
-#pragma unroll
-      for (int t = 0; t < RPT; ++t) {
-        const int r = s.row[r0 + t];
-        const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf;
-        const float x = a.g[off], y = ld_in(k, off);
-        run += r >= 0 ? x : 0.f;
-        gm[hf * RPT + t] = run;
-        kk[hf * RPT + t] = r >= 0 ? y : 0.f;
-      }
-      s.part[rg][c0 + DH * hf] = run;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hf = 0; hf < NHF; ++hf) {
-      const int cc = c0 + DH * hf;
-      float offs = 0.f, tot = 0.f;
-#pragma unroll
-      for (int j = 0; j < NRG; ++j) {
-        const float pj = s.part[j][cc];
-        offs += (j < rg) ? pj : 0.f;
-        tot += pj;
-      }
-      if (rg == 0) s.gcl[cc] = tot;
-#pragma unroll
-      for (int t = 0; t < RPT; ++t) {
-        const int n = hf * RPT + t, i = r0 + t;
-        gm[n] += offs;
-        if ((i & 15) == 0) s.gref[i >> 4][cc] = gm[n];
-        s.u.p.x.Kn[i][cc] = (_Float16)(-kk[n] * __expf(gm[n]));
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 1: wave w < NCB owns column block w of dv ----
+  // ---- loads that need no row table: states and dy (wave layout) ----
   const bool vw = wave < NCB;
   const int col = 16 * wave + l16;
-  f32x4 z[NB];
+  f32x4 hC[NCB], dhC[NCB], dyv[NB];
   if (vw) {
-    f32x4 hC[NCB];
     const float* hsrc = a.chunk_h + blk * DD;
     const float* dhsrc = a.dhc + blk * DD;
 #pragma unroll
@@ -186,34 +203,129 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const size_t o = (size_t)(16 * C + 4 * g + r) * D + col;
         hC[C][r] = hsrc[o];
-        float x = hC[C][r] * dhsrc[o];
-        s.u.p.Hs[16 * C + 4 * g + r][col] = (_Float16)hC[C][r];
-        // deGC partial over this wave's 16 columns (lanes of equal g)
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
-        if (l16 == 0) s.redg[wave][16 * C + 4 * g + r] = x;
+        dhC[C][r] = dhsrc[o];
       }
-    f16x8 hb[KD];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hC[2 * ks], hC[2 * ks + 1]);
-    // Z = V - (K e^Gam) h
+    for (int J = 0; J < NB; ++J)
 #pragma unroll
-    for (int J = 0; J < NB; ++J) {
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * J + 4 * g + r;
+        dyv[J][r] = i < len ? a.dy[((size_t)(row0 + i) * H + h) * D + col] : 0.f;
+      }
+  }
+  __syncthreads();
+  // ---- loads through the row table ----
+  const int c0 = tid % DH, rg = tid / DH, r0 = rg * RPT;
+  float gm[NE], kk[NE], qq[NE];   // element mapping: channel c0 + 64 hf, rows r0 .. r0 + RPT - 1
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int n = hf * RPT + t, r = s.row[r0 + t];
+      const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf;
+      const float x = a.g[off], y = ld_in(k, off), w = ld_in(q, off);
+      gm[n] = r >= 0 ? x : 0.f;
+      kk[n] = r >= 0 ? y : 0.f;
+      qq[n] = r >= 0 ? w : 0.f;
+    }
+  Raw8<TIn> dov[NV8];
+#pragma unroll
+  for (int n = 0; n < NV8; ++n) {
+    const int e = tid + NT * n;
+    dov[n].zero();
+    if (e < BC * D / 8) {
+      const int i = e / (D / 8), orow = s.orow[i];
+      if (orow >= 0) dov[n].load(dO + ((size_t)orow * H + h) * D + (e % (D / 8)) * 8);
+    }
+  }
+  f32x4 z[NB];
+  if (vw) {
+#pragma unroll
+    for (int J = 0; J < NB; ++J)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int rr = s.row[16 * J + 4 * g + r];
         const float x = ld_in(v, ((size_t)(rr < 0 ? 0 : rr) * H + h) * D + col);
         z[J][r] = rr >= 0 ? x : 0.f;
       }
+  }
+
+  // ---- Gam: running sums per row group, then their prefix ----
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf) {
+    float run = 0.f;
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      run += gm[hf * RPT + t];
+      gm[hf * RPT + t] = run;
+    }
+    s.part[rg][c0 + DH * hf] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf) {
+    const int cc = c0 + DH * hf;
+    float offs = 0.f, tot = 0.f;
+#pragma unroll
+    for (int j = 0; j < NRG; ++j) {
+      const float pj = s.part[j][cc];
+      offs += (j < rg) ? pj : 0.f;
+      tot += pj;
+    }
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int n = hf * RPT + t, i = r0 + t;
+      gm[n] += offs;
+      if ((i & 15) == 0) {
+        s.gref[i >> 4][cc] = gm[n];
+        s.eref[i >> 4][cc] = __expf(gm[n]);
+        s.ecg[i >> 4][cc] = __expf(tot - gm[n]);
+      }
+      s.u.p.x.Kn[i][cc] = (_Float16)(-kk[n] * __expf(gm[n]));
+    }
+    if (rg == 0) s.degc[cc] = __expf(tot);   // e^Gam_C until deGC is formed
+  }
+  __syncthreads();
+
+  // ---- phase 1: Z = V - (K e^Gam) h on column block `wave` ----
+  if (vw) {
+    f16x8 hb[KD];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hC[2 * ks], hC[2 * ks + 1]);
+#pragma unroll
+    for (int C = 0; C < NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s.u.p.Hs[16 * C + 4 * g + r][col] = (_Float16)hC[C][r];
+#pragma unroll
+    for (int J = 0; J < NB; ++J)
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks)
         z[J] = mfma16(lds_a_perm(&s.u.p.x.Kn[0][0], G::PD, 16 * J + l16, 32 * ks, g), hb[ks], z[J]);
-    }
   }
   __syncthreads();  // Kn is dead: dO takes its place
+#pragma unroll
+  for (int n = 0; n < NV8; ++n) {
+    const int e = tid + NT * n;
+    if (e < BC * D / 8) {
+      f16x8 x;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) x[t] = (_Float16)(sc * dov[n].at(t));
+      *(f16x8*)&s.u.p.x.dO[e / (D / 8)][(e % (D / 8)) * 8] = x;
+    }
+  }
   if (vw) {
+    // deGC partial over this wave's 16 columns (lanes of equal g)
+#pragma unroll
+    for (int C = 0; C < NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = hC[C][r] * dhC[C][r];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        if (l16 == 0) s.redg[wave][16 * C + 4 * g + r] = x;
+      }
     // delta by block forward substitution with the diagonal inverses
     f32x4 d[NB];
 #pragma unroll
@@ -229,7 +341,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) rr[r] *= s.beta[16 * I + 4 * g + r];
       d[I] = mfma16k16(*(const f16x4*)&s.u.p.Td[16 * I + l16][4 * g], acc4(rr),
-                      (f32x4){0.f, 0.f, 0.f, 0.f});
+                       (f32x4){0.f, 0.f, 0.f, 0.f});
     }
     f16x8 db[KB];
 #pragma unroll
@@ -249,20 +361,15 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
-        float dyv = 0.f, dov = 0.f;
-        if (i < len) dyv = a.dy[((size_t)(row0 + i) * H + h) * D + col];
-        const int orow = s.orow[i];
-        if (orow >= 0) dov = ld_in(dO, ((size_t)orow * H + h) * D + col);
-        const float b = s.beta[i];
-        float x = dyv * e[r];
+        const float dy = dyv[I][r], b = s.beta[i];
+        float x = dy * e[r];
         x += __shfl_xor(x, 1);
         x += __shfl_xor(x, 2);
         x += __shfl_xor(x, 4);
         x += __shfl_xor(x, 8);
         if (l16 == 0) s.redb[wave][i] = x;
-        if (i < len) grad_dst(a, a.dv, a.rep_dv, c, i, nrep, row0, h, D)[col] = b * dyv;
-        s.u.p.x.dO[i][col] = (_Float16)(sc * dov);
-        s.u.p.nZ[i][col] = (_Float16)(-b * dyv);
+        if (i < len) grad_dst(a, a.dv, a.rep_dv, rep0, s.orow[i], i, nrep, h, D)[col] = b * dy;
+        s.u.p.nZ[i][col] = (_Float16)(-b * dy);
         s.u.p.dl[i][col] = (_Float16)d[I][r];
       }
     }
@@ -271,236 +378,200 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
   if (tid < BC && tid < len) {
     float acc = 0.f;
     for (int w = 0; w < NCB; ++w) acc += s.redb[w][tid];
-    *grad_dst(a, a.dbeta, a.rep_db, c, tid, nrep, row0, h, 1) = acc;
+    *grad_dst(a, a.dbeta, a.rep_db, rep0, s.orow[tid], tid, nrep, h, 1) = acc;
   }
   if (tid < D) {
     float acc = 0.f;
     for (int w = 0; w < NCB; ++w) acc += s.redg[w][tid];
-    s.degc[tid] = acc;
-  }
-
-  // ---- phase 2: products contracting dv (fp16 matrix cores) ----
-  // [BC][D] tile (I, C) belongs to wave I + NB (C % 2); m = C / 2 indexes its registers
-  constexpr int NTW = NCB / 2;
-  const bool tw = wave < 2 * NB;
-  const int tI = wave % NB, tu = wave / NB;
-  f32x4 dQt[NTW], dKt[NTW], dKh[NTW];
-  if (tw) {
-#pragma unroll
-    for (int m = 0; m < NTW; ++m) {
-      const int C = 2 * m + tu;
-      f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KD; ++ks) {
-        const f16x8 bh = *(const f16x8*)&s.u.p.Hs[16 * C + l16][32 * ks + 8 * g];
-        x1 = mfma16(*(const f16x8*)&s.u.p.x.dO[16 * tI + l16][32 * ks + 8 * g], bh, x1);
-        x2 = mfma16(*(const f16x8*)&s.u.p.nZ[16 * tI + l16][32 * ks + 8 * g], bh, x2);
-      }
-      dQt[m] = x1;
-      dKt[m] = x2;
-    }
-  }
-  // dP (j <= i) and dA (j < i): lower 16x16 blocks dealt over the waves
-  for (int t = wave; t < 2 * G::NLOW; t += NW) {
-    const bool isA = t >= G::NLOW;
-    int I, J;
-    pair_of(isA ? t - G::NLOW : t, I, J);
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KD; ++ks) {
-      const f16x8 aa = isA ? *(const f16x8*)&s.u.p.nZ[16 * I + l16][32 * ks + 8 * g]
-                           : *(const f16x8*)&s.u.p.x.dO[16 * I + l16][32 * ks + 8 * g];
-      x = mfma16(aa, *(const f16x8*)&s.u.p.dl[16 * J + l16][32 * ks + 8 * g], x);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * I + 4 * g + r, j = 16 * J + l16;
-      if (isA) s.dA[i][j] = (j < i) ? x[r] : 0.f;
-      else s.dP[i][j] = (j <= i) ? x[r] : 0.f;
-    }
-  }
-  for (int e = tid; e < BC * BC; e += NT) {
-    const int i = e / BC, j = e % BC;
-    if ((j >> 4) > (i >> 4)) s.dP[i][j] = s.dA[i][j] = 0.f;
-  }
-  __syncthreads();
-  {  // dh' replaces h
-    const float* dhsrc = a.dhc + blk * DD;
-    for (int e = tid; e < D * D / 4; e += NT) {
-      const int r = (4 * e) / D, cc = (4 * e) % D;
-      const float4 x = *(const float4*)(dhsrc + (size_t)r * D + cc);
-      s.u.p.Hs[r][cc] = (_Float16)x.x;
-      s.u.p.Hs[r][cc + 1] = (_Float16)x.y;
-      s.u.p.Hs[r][cc + 2] = (_Float16)x.z;
-      s.u.p.Hs[r][cc + 3] = (_Float16)x.w;
-    }
-  }
-  __syncthreads();
-  if (tw) {
-#pragma unroll
-    for (int m = 0; m < NTW; ++m) {
-      const int C = 2 * m + tu;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KD; ++ks)
-        x = mfma16(*(const f16x8*)&s.u.p.dl[16 * tI + l16][32 * ks + 8 * g],
-                   *(const f16x8*)&s.u.p.Hs[16 * C + l16][32 * ks + 8 * g], x);
-      dKh[m] = x;
-    }
-  }
-  __syncthreads();  // the fp16 operands are dead: the decay phase takes their space
-
-  // ---- phase 3: decay-weighted products (hi/lo bf16), 32 channels per pass ----
-#pragma unroll
-  for (int hf = 0; hf < NHF; ++hf)
-#pragma unroll
-    for (int t = 0; t < RPT; ++t) s.u.d.Gam[r0 + t][c0 + DH * hf] = gm[hf * RPT + t];
-  if (tid < D)
+    s.degc[tid] *= acc;   // deGC e^Gam_C
     for (int I = 0; I < NB; ++I)
       for (int J = 0; J <= I; ++J)
         s.dfac[low_index(I, J)][tid] = __expf(s.gref[I][tid] - s.gref[J][tid]);
-  // staging of a pass: channel cq = tid % 32, rows rq0 .. rq0 + RPQ - 1
-  constexpr int RPQ = (BC * 32 + NT - 1) / NT;
-  const int cq = tid % 32, rq0 = (tid / 32) * RPQ;
-  float csum_acc[NTW];
+  }
+
+  // ---- phase 2: products contracting dv (fp16 matrix cores), transposed tiles ----
+  const int tI = wave % NB, tu = wave / NB;
+  f32x4 dQt[NTW], dKt[NTW], dKh[NTW];
 #pragma unroll
-  for (int m = 0; m < NTW; ++m) csum_acc[m] = 0.f;
+  for (int m = 0; m < NTW; ++m) {
+    const int C = tu + NG * m;
+    f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
+    if (C < NCB) {
 #pragma unroll
-  for (int qp = 0; qp < G::NQ; ++qp) {
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < RPQ; ++t) {
-      const int i = rq0 + t;
-      if (i < BC) {
-        const int cc = 32 * qp + cq;
-        const int r = s.row[i];
-        const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + cc;
-        const float kv = r >= 0 ? ld_in(k, off) : 0.f;
-        const float qv = r >= 0 ? ld_in(q, off) : 0.f;
-        const float gam = s.u.d.Gam[i][cc];
-        const float ref = s.gref[i >> 4][cc];
-        const float f = __expf(gam - ref), fi = __expf(ref - gam);
-        __bf16 hh, ll;
-        split_bf16(kv * fi, hh, ll);
-        s.u.d.rh[cq][i] = hh; s.u.d.rl[cq][i] = ll;
-        split_bf16(qv * f, hh, ll);
-        s.u.d.qh[cq][i] = hh; s.u.d.ql[cq][i] = ll;
-        split_bf16(kv * f, hh, ll);
-        s.u.d.kh[cq][i] = hh; s.u.d.kl[cq][i] = ll;
+      for (int ks = 0; ks < KD; ++ks) {
+        const f16x8 ah = *(const f16x8*)&s.u.p.Hs[16 * C + l16][32 * ks + 8 * g];
+        x1 = mfma16(ah, *(const f16x8*)&s.u.p.x.dO[16 * tI + l16][32 * ks + 8 * g], x1);
+        x2 = mfma16(ah, *(const f16x8*)&s.u.p.nZ[16 * tI + l16][32 * ks + 8 * g], x2);
       }
     }
-    __syncthreads();
-    if (tw) {
-      const int m = qp;               // tile (tI, C = 2 qp + tu)
-      const int cl = 16 * tu + l16;   // channel within the pass
-      const int ch = 32 * qp + cl;    // channel in the head
-      const int B0 = 16 * tI;
-      f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};   // row side: dqP, dkAr
-      f32x4 cp = {0.f, 0.f, 0.f, 0.f}, ca = {0.f, 0.f, 0.f, 0.f};   // column side: dkP, dkAc
-      // row side: pairs (tI, J), J <= tI, around gref_J; the channel factor
-      // e^(gref_tI - gref_J) scales the output column
-      for (int J = 0; J <= tI; ++J) {
-        bf16x8 ph, pl, ah, al, bh, bl;
+    dQt[m] = x1;
+    dKt[m] = x2;
+  }
+  // dP / dA blocks met by row block tI: slot sl <= tI is (tI, J = sl) as a [j][i]
+  // tile, slot sl > tI is (I = sl - 1, tI) as an [i][j] tile
+  s16x4 Ph[NS], Pl[NS], Ah[NS], Al[NS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = 8 * g + e;
-          float pv = 0.f, av = 0.f;
-          __bf16 h2 = (__bf16)0.f, l2 = (__bf16)0.f;
-          if (jj < 16) {
-            pv = s.dP[B0 + l16][16 * J + jj];
-            av = s.dA[B0 + l16][16 * J + jj];
-            h2 = s.u.d.rh[cl][16 * J + jj];
-            l2 = s.u.d.rl[cl][16 * J + jj];
-          }
-          __bf16 x, y;
-          split_bf16(pv, x, y); ph[e] = x; pl[e] = y;
-          split_bf16(av, x, y); ah[e] = x; al[e] = y;
-          bh[e] = h2; bl[e] = l2;
-        }
-        f32x4 tp = {0.f, 0.f, 0.f, 0.f}, ta = {0.f, 0.f, 0.f, 0.f};
-        tp = mfmab(ph, bh, tp); tp = mfmab(ph, bl, tp); tp = mfmab(pl, bh, tp);
-        ta = mfmab(ah, bh, ta); ta = mfmab(ah, bl, ta); ta = mfmab(al, bh, ta);
-        const float f = s.dfac[low_index(tI, J)][ch];
+  for (int sl = 0; sl < NS; ++sl) {
+    const bool rside = sl <= tI;
+    const _Float16* a1 = rside ? &s.u.p.dl[16 * sl][0] : &s.u.p.x.dO[16 * (sl - 1)][0];
+    const _Float16* a2 = rside ? &s.u.p.dl[16 * sl][0] : &s.u.p.nZ[16 * (sl - 1)][0];
+    const _Float16* b1 = rside ? &s.u.p.x.dO[16 * tI][0] : &s.u.p.dl[16 * tI][0];
+    const _Float16* b2 = rside ? &s.u.p.nZ[16 * tI][0] : &s.u.p.dl[16 * tI][0];
+    f32x4 tp = {0.f, 0.f, 0.f, 0.f}, ta = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          aq[r] += f * tp[r];
-          ak[r] += f * ta[r];
-        }
-      }
-      // column side: pairs (I, tI), I >= tI, around gref_tI; channel factor e^(gref_I - gref_tI)
-      for (int I = tI; I < NB; ++I) {
-        bf16x8 ph, pl, ah, al, qh, ql, kh, kl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ii = 8 * g + e;
-          float pv = 0.f, av = 0.f;
-          __bf16 q1 = (__bf16)0.f, q2 = (__bf16)0.f, k1 = (__bf16)0.f, k2 = (__bf16)0.f;
-          if (ii < 16) {
-            pv = s.dP[16 * I + ii][B0 + l16];
-            av = s.dA[16 * I + ii][B0 + l16];
-            q1 = s.u.d.qh[cl][16 * I + ii]; q2 = s.u.d.ql[cl][16 * I + ii];
-            k1 = s.u.d.kh[cl][16 * I + ii]; k2 = s.u.d.kl[cl][16 * I + ii];
-          }
-          __bf16 x, y;
-          split_bf16(pv, x, y); ph[e] = x; pl[e] = y;
-          split_bf16(av, x, y); ah[e] = x; al[e] = y;
-          qh[e] = q1; ql[e] = q2; kh[e] = k1; kl[e] = k2;
-        }
-        f32x4 tp = {0.f, 0.f, 0.f, 0.f}, ta = {0.f, 0.f, 0.f, 0.f};
-        tp = mfmab(ph, qh, tp); tp = mfmab(ph, ql, tp); tp = mfmab(pl, qh, tp);
-        ta = mfmab(ah, kh, ta); ta = mfmab(ah, kl, ta); ta = mfmab(al, kh, ta);
-        const float f = s.dfac[low_index(I, tI)][ch];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          cp[r] += f * tp[r];
-          ca[r] += f * ta[r];
-        }
-      }
-      // ---- phase 4 for this tile: dq, dk, dGam ----
-      const float gC = s.gcl[ch];
-      const float ref = s.gref[tI][ch];
+    for (int ks = 0; ks < KD; ++ks) {
+      const int o = l16 * G::PD + 32 * ks + 8 * g;
+      tp = mfma16(*(const f16x8*)(a1 + o), *(const f16x8*)(b1 + o), tp);
+      ta = mfma16(*(const f16x8*)(a2 + o), *(const f16x8*)(b2 + o), ta);
+    }
+    // diagonal blocks: keep j <= i (P) and j < i (A)
+    const bool diag = rside ? (sl == tI) : (sl == tI + 1);
+    if (diag) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = B0 + 4 * g + r;
-        const float gam = s.u.d.Gam[i][ch];
-        const float lf = __expf(gam - ref), rf = __expf(ref - gam);
-        const float e1 = __expf(gam), e2 = __expf(gC - gam);
-        const int rr = s.row[i];
-        const size_t off = ((size_t)(rr < 0 ? 0 : rr) * H + h) * D + ch;
-        const float kv = rr >= 0 ? ld_in(k, off) : 0.f;
-        const float qv = rr >= 0 ? ld_in(q, off) : 0.f;
-        const float vq = aq[r] * lf, vkr = ak[r] * lf, vkp = cp[r] * rf, vka = ca[r] * rf;
-        const float dq = dQt[m][r] * e1 + vq;
-        const float dk = dKt[m][r] * e1 + dKh[m][r] * e2 + vkr + vkp + vka;
-        const float kh2 = dKh[m][r] * kv * e2;
-        const float dG = dQt[m][r] * qv * e1 + dKt[m][r] * kv * e1 - kh2 + qv * vq +
-                         kv * (vkr - vkp - vka);
-        csum_acc[m] += kh2;
-        s.u.d.Gam[i][ch] = dG;   // (i, ch) belongs to this lane alone from here on
+        const int rw = 4 * g + r;            // tile row
+        const int jj = rside ? rw : l16;     // j within the block
+        const int ii = rside ? l16 : rw;     // i within the block
+        if (jj > ii) tp[r] = 0.f;
+        if (jj >= ii) ta[r] = 0.f;
+      }
+    }
+    split_tile(tp, Ph[sl], Pl[sl]);
+    split_tile(ta, Ah[sl], Al[sl]);
+  }
+  __syncthreads();  // h is dead: dh' takes its place
+  if (vw) {
+#pragma unroll
+    for (int C = 0; C < NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s.u.p.Hs[16 * C + 4 * g + r][col] = (_Float16)dhC[C][r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) {
+    const int C = tu + NG * m;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (C < NCB) {
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks)
+        x = mfma16(*(const f16x8*)&s.u.p.Hs[16 * C + l16][32 * ks + 8 * g],
+                   *(const f16x8*)&s.u.p.dl[16 * tI + l16][32 * ks + 8 * g], x);
+    }
+    dKh[m] = x;
+  }
+
+  // ---- phase 3: decay-weighted products and the combine, 64 channels per pass ----
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf) {
+    __syncthreads();  // the previous phase's LDS readers are done
+    {  // staging: channel c0 of the pass, rows r0 .. r0 + RPT - 1
+      const int ch = DH * hf + c0;
+#pragma unroll
+      for (int t = 0; t < RPT; ++t) {
+        const int n = hf * RPT + t, i = r0 + t;
+        const float ref = s.gref[i >> 4][ch];
+        const float f = __expf(gm[n] - ref), fi = __expf(ref - gm[n]);
+        __bf16 x, y;
+        split_bf16(kk[n] * fi, x, y);
+        s.u.d.rh[c0][i] = x; s.u.d.rl[c0][i] = y;
+        split_bf16(qq[n] * f, x, y);
+        s.u.d.qh[c0][i] = x; s.u.d.ql[c0][i] = y;
+        split_bf16(kk[n] * f, x, y);
+        s.u.d.kh[c0][i] = x; s.u.d.kl[c0][i] = y;
+        s.u.d.gam[c0][i] = gm[n];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+      const int C = tu + NG * m;
+      if (C < NCB && C / 4 == hf) {
+        const int cb = 16 * (C % 4);          // first channel of the tile within the pass
+        const int ca = cb + l16;              // A-operand row (channel) of this lane
+        const int cf = DH * hf + cb + 4 * g;  // first output channel of this lane
+        f32x4 rP = {0.f, 0.f, 0.f, 0.f}, rA = rP, cP = rP, cA = rP;
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+          if (sl <= tI) {  // row side, block pair (tI, J = sl), around gref_J
+            const int J = sl;
+            const s16x4 ah = *(const s16x4*)&s.u.d.rh[ca][16 * J + 4 * g];
+            const s16x4 al = *(const s16x4*)&s.u.d.rl[ca][16 * J + 4 * g];
+            const f32x4 tp = mma3(ah, al, Ph[sl], Pl[sl]);
+            const f32x4 ta = mma3(ah, al, Ah[sl], Al[sl]);
+            const float4 f = *(const float4*)&s.dfac[low_index(tI, J)][cf];
+            rP[0] += f.x * tp[0]; rP[1] += f.y * tp[1]; rP[2] += f.z * tp[2]; rP[3] += f.w * tp[3];
+            rA[0] += f.x * ta[0]; rA[1] += f.y * ta[1]; rA[2] += f.z * ta[2]; rA[3] += f.w * ta[3];
+          } else {         // column side, block pair (I = sl - 1, tI), around gref_tI
+            const int I = sl - 1;
+            const s16x4 qh = *(const s16x4*)&s.u.d.qh[ca][16 * I + 4 * g];
+            const s16x4 ql = *(const s16x4*)&s.u.d.ql[ca][16 * I + 4 * g];
+            const s16x4 kh = *(const s16x4*)&s.u.d.kh[ca][16 * I + 4 * g];
+            const s16x4 kl = *(const s16x4*)&s.u.d.kl[ca][16 * I + 4 * g];
+            const f32x4 tp = mma3(qh, ql, Ph[sl], Pl[sl]);
+            const f32x4 ta = mma3(kh, kl, Ah[sl], Al[sl]);
+            const float4 f = *(const float4*)&s.dfac[low_index(I, tI)][cf];
+            cP[0] += f.x * tp[0]; cP[1] += f.y * tp[1]; cP[2] += f.z * tp[2]; cP[3] += f.w * tp[3];
+            cA[0] += f.x * ta[0]; cA[1] += f.y * ta[1]; cA[2] += f.z * ta[2]; cA[3] += f.w * ta[3];
+          }
+        }
+        // combine: lane element (channel cf + r, row i)
+        const int i = 16 * tI + l16;
+        float4 vq, vk;
+        float cs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int cl = cb + 4 * g + r, ch = cf + r;
+          const float gam = s.u.d.gam[cl][i];
+          const float ref = s.gref[tI][ch], er = s.eref[tI][ch], eg = s.ecg[tI][ch];
+          const float lf = __expf(gam - ref), rf = __expf(ref - gam);
+          const float qd = bf16_val(s.u.d.qh[cl][i]) + bf16_val(s.u.d.ql[cl][i]);   // q e^(Gam-ref)
+          const float kd = bf16_val(s.u.d.kh[cl][i]) + bf16_val(s.u.d.kl[cl][i]);   // k e^(Gam-ref)
+          const float kr = bf16_val(s.u.d.rh[cl][i]) + bf16_val(s.u.d.rl[cl][i]);   // k e^(ref-Gam)
+          const float xq = dQt[m][r] * er + rP[r];
+          const float xk = dKt[m][r] * er + rA[r];
+          const float kh2 = dKh[m][r] * kr * eg;
+          cs[r] = kh2;
+          s.u.d.gam[cl][i] = xq * qd + xk * kd - kh2 - kr * (cP[r] + cA[r]);   // dGam, this lane's
+          (&vq.x)[r] = xq * lf;
+          (&vk.x)[r] = xk * lf + (dKh[m][r] * eg + cP[r] + cA[r]) * rf;
+        }
         if (i < len) {
-          grad_dst(a, a.dq, a.rep_dq, c, i, nrep, row0, h, D)[ch] = dq;
-          grad_dst(a, a.dk, a.rep_dk, c, i, nrep, row0, h, D)[ch] = dk;
+          const int orow = s.orow[i];
+          *(float4*)(grad_dst(a, a.dq, a.rep_dq, rep0, orow, i, nrep, h, D) + cf) = vq;
+          *(float4*)(grad_dst(a, a.dk, a.rep_dk, rep0, orow, i, nrep, h, D) + cf) = vk;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = cs[r];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          if (l16 == 0) s.csum[tI][cf + r] = x;
         }
       }
     }
-  }
-  if (tw) {
+    __syncthreads();
+    // dg = reverse cumulative sum of dGam, the Gam_C terms entering at the last row
+    const int ch = DH * hf + c0;
+    float loc[RPT];
+    float run = 0.f;
 #pragma unroll
-    for (int m = 0; m < NTW; ++m) {
-      float cs = csum_acc[m];
-      cs += __shfl_xor(cs, 16);
-      cs += __shfl_xor(cs, 32);
-      if (g == 0) s.csum[tI][32 * m + 16 * tu + l16] = cs;
+    for (int t = RPT - 1; t >= 0; --t) {
+      run += s.u.d.gam[c0][r0 + t];
+      loc[t] = run;
     }
-  }
-  __syncthreads();
-  // dg = reverse cumulative sum of dGam; the Gam_C terms enter at the last row
-  if (tid < D) {
-    float acc = s.degc[tid] * __expf(s.gcl[tid]);
-    for (int I = 0; I < NB; ++I) acc += s.csum[I][tid];
-    for (int i = BC - 1; i >= 0; --i) {
-      acc += s.u.d.Gam[i][tid];
-      if (i < len) grad_dst(a, a.dg, a.rep_dg, c, i, nrep, row0, h, D)[tid] = acc;
+    s.part[rg][ch] = run;
+    __syncthreads();
+    float tail = s.degc[ch];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) tail += s.csum[I][ch];
+#pragma unroll
+    for (int j = 0; j < NRG; ++j) tail += (j > rg) ? s.part[j][ch] : 0.f;
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int i = r0 + t;
+      if (i < len) grad_dst(a, a.dg, a.rep_dg, rep0, s.orow[i], i, nrep, h, D)[ch] = loc[t] + tail;
     }
   }
 }

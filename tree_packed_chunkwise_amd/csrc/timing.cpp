@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/kda_tree.h"
+#include "kda_tree.h"
 
 namespace kda {
 namespace {
