@@ -240,6 +240,29 @@ def make_upstream(rng: np.random.Generator, n_out_rows: int, n_leaf: int, H: int
     return dO, dhl
 
 
+def make_kda_inputs_device(seed: int, n_rows: int, H: int, dk: int, dv: int, device,
+                           bf16: bool = True):
+    """The make_kda_inputs distributions drawn on a device with a seeded torch
+    generator (for full-size workloads, whose host draws would take minutes):
+    q,k ~ N(0,1) L2-normalised per head, v ~ N(0,1) (bf16 when bf16=True),
+    beta = sigmoid(N(0,1)), g = -softplus(N(2,1)) fp32.  Returns a dict of
+    device tensors; draw order q, k, v, beta-pre, g-pre."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = torch.bfloat16 if bf16 else torch.float32
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    q = torch.nn.functional.normalize(randn(n_rows, H, dk), dim=-1).to(dt)
+    k = torch.nn.functional.normalize(randn(n_rows, H, dk), dim=-1).to(dt)
+    v = randn(n_rows, H, dv).to(dt)
+    beta = torch.sigmoid(randn(n_rows, H))
+    g = -torch.nn.functional.softplus(randn(n_rows, H, dk) + 2.0)
+    return dict(q=q, k=k, v=v, beta=beta, g=g, scale=1.0 / float(np.sqrt(dk)))
+
+
 # ---------------------------------------------------------------------------
 # The five workloads
 # ---------------------------------------------------------------------------
