@@ -100,6 +100,14 @@ def measured_traffic(kernel, workload):
     return m["bytes_per_launch"] if h.hexdigest()[:16] == m["sha256_16"] else None
 
 
+def image_bytes(B, D, in_bytes):
+    """(forward image as used, reverse image) bytes of one chunk-head: the
+    padded fp16 LDS images of a chunk step (layouts in csrc/common.h)."""
+    head = 2 * (2 * B * (D + 8) + D * (B + 8) + 2 * B * (B + 8) + B * 24) + 4 * D + 8 * B
+    bwd = 2 * (B * (D + 8) + 2 * D * (B + 8) + 2 * B * (B + 8) + B * 24) + 4 * D + 4 * B
+    return head + in_bytes * B * D, bwd
+
+
 def kernel_bytes(name, info, H, D, in_bytes=2):
     """Algorithmic bytes of all launches of one kernel class in one step: the
     tensors its role requires it to read and write once (documented per
@@ -111,25 +119,28 @@ def kernel_bytes(name, info, H, D, in_bytes=2):
     B = info["chunk"]
     f = 4
     st = D * D * f                        # one state of one head
-    prep = (2 * B * B + 16 * B) * 2       # A, P, Td of one chunk-head (fp16)
+    fimg, bimg = image_bytes(B, D, in_bytes)
     if name == "kda_chunk_decay":
-        # reads q, k, g, beta; writes A, P, Td
-        return P * H * (2 * D * in_bytes + D * f + f) + C * H * prep
+        # reads q, k, v, g, beta; writes both chunk images
+        return P * H * (3 * D * in_bytes + D * f + f) + C * H * (fimg + bimg)
     if name == "kda_fwd_round":
-        # reads q, k, v, g, beta, A/P/Td; writes o (unique rows), the start
-        # state of every chunk, handoff and leaf states
-        return (P * H * (3 * D * in_bytes + D * f + f) + C * H * prep + Nrow * H * D * f
-                + C * H * st + (info["n_buf"] + info["n_leaf"]) * H * st)
+        # reads the forward images; writes o (unique rows), the start state of
+        # every chunk, handoff and leaf states
+        return (C * H * fimg + Nrow * H * D * f + C * H * st
+                + (info["n_buf"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_round":
-        # reads q, k, g, beta, dO, A/P/Td, leaf-state gradients; writes dy,
+        # reads the reverse images, packed dO, leaf-state gradients; writes dy,
         # the end-state gradient of every chunk, sequence start gradients
-        return (P * H * (3 * D * in_bytes + D * f + f + D * f) + C * H * (prep + st)
+        return (C * H * bimg + P * H * D * (in_bytes + f) + C * H * st
                 + (info["n_seq"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_chunk_grad":
-        # reads q, k, v, dO, g, beta, dy, A/Td, start state and end-state
-        # gradient of every chunk; writes dq, dk, dv, dg, dbeta
-        return (P * H * (4 * D * in_bytes + 2 * D * f + f + 4 * D * f + f)
-                + C * H * ((B * B + 16 * B) * 2 + 2 * st))
+        # reads q, k, g, beta, dy, packed dO, A / Td / V of the forward image,
+        # the start state and end-state gradient of every chunk; writes dq, dk,
+        # dv, dg, dbeta
+        return (P * H * (2 * D * in_bytes + D * f + f + D * f + D * in_bytes + 4 * D * f + f)
+                + C * H * ((B * (B + 8) + B * 24) * 2 + B * D * in_bytes + 2 * st))
+    if name == "kda_bwd_gather_dO":
+        return Nrow * H * D * in_bytes + P * H * D * in_bytes
     return None
 
 

@@ -16,7 +16,7 @@ namespace kda {
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
                       const int* round_ptr_host, int n_rounds, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D,
-                      int n_chunks, const int* round_ptr_host, int n_rounds, int n_rep_rows,
+                      int n_chunks, int64_t n_packed, const int* round_ptr_host, int n_rounds, int n_rep_rows,
                       int n_root, hipStream_t st);
 hipError_t launch_gather_fwd(const void* logits, bool bf16, int64_t n_rows, int vocab,
                              const int* pos_row, const int* pos_tgt, int64_t n_pos, float* logp,
@@ -92,11 +92,14 @@ kda::DevPlan make_dev_plan(const kda::Plan& p, const void* dev) {
   return v;
 }
 
-// saved = [chunk start states | handoff states | chunk decay products (fp16)]
+// saved = [chunk start states | handoff states | forward chunk images |
+//          reverse chunk images]  (image layouts in common.h; the forward
+//          image reserves fp32 space for V whatever the input dtype)
 struct SavedView {
   float* chunk_h;
   float* bufs;
-  _Float16* prep;
+  unsigned char* fimg;
+  unsigned char* bimg;
 };
 SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
@@ -104,18 +107,23 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
   const size_t st = (size_t)H * D * D;
   s.chunk_h = c.take((size_t)p.n_chunks() * st);
   s.bufs = c.take((size_t)p.n_buf() * st);
-  s.prep = (_Float16*)c.take(((size_t)p.n_chunks() * H * kda::prep_halves(p.B) + 1) / 2);
+  const size_t nb = (size_t)p.n_chunks() * H;
+  s.fimg = (unsigned char*)c.take(nb * kda::fwd_image_bytes(p.B, D) / 4);
+  s.bimg = (unsigned char*)c.take(nb * kda::bwd_image_bytes(p.B, D) / 4);
   if (total) *total = c.off;
   return s;
 }
 
+// bwd workspace = [dO in packed order (sized for fp32) | dy | chunk end-state
+//                  gradients | sequence start gradients | replay-row gradients]
 struct BwdWS {
-  float *dy, *dhc, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
+  float *dOp, *dy, *dhc, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
 };
 BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
   BwdWS w;
   const size_t nb = (size_t)p.n_chunks() * H;
+  w.dOp = c.take((size_t)p.n_packed * H * D);
   w.dy = c.take((size_t)p.n_packed * H * D);
   w.dhc = c.take(nb * D * D);
   w.slot = c.take((size_t)p.n_seq() * H * D * D);
@@ -310,7 +318,8 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   SavedView sv = carve_saved(p, H, dk, saved, nullptr);
   a.chunk_h = sv.chunk_h;
   a.bufs = sv.bufs;
-  a.prep = sv.prep;
+  a.fimg = sv.fimg;
+  a.bimg = sv.bimg;
   hipError_t e = kda::launch_fwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
                                  p.round_seq_ptr.data(), p.n_rounds, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_fwd launch");
@@ -344,17 +353,19 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.scale = scale;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.chunk_h = sv.chunk_h;
-  a.prep = sv.prep;
+  a.fimg = sv.fimg;
+  a.bimg = sv.bimg;
   a.dO = dO;
   a.dh_leaf = dh_leaf;
   a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
   a.dh_boundary = dh_boundary;
+  a.dOp = w.dOp;
   a.dy = w.dy;
   a.dhc = w.dhc;
   a.slot = w.slot;
   a.rep_dq = w.rep_dq; a.rep_dk = w.rep_dk; a.rep_dg = w.rep_dg; a.rep_dv = w.rep_dv;
   a.rep_db = w.rep_db;
-  hipError_t e = kda::launch_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
+  hipError_t e = kda::launch_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(), p.n_packed,
                                  p.round_seq_ptr.data(), p.n_rounds, (int)p.rep_row.size(),
                                  p.n_root, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_bwd launch");

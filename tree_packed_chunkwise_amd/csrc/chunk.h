@@ -60,6 +60,23 @@ __device__ inline f16x4 acc4(const f32x4& t) {
   return r;
 }
 
+// Sum over the 16 lanes of a row (lanes 16r .. 16r+15) with DPP moves: quad
+// swaps (xor 1, xor 2), then the half-row and row mirrors.  Every lane of the
+// row ends with the same value (each step adds a commutative pair), in a
+// fixed order.  VALU only: no LDS round trips, unlike a lane shuffle.
+template <int CTRL>
+__device__ inline float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+__device__ inline float row_sum16(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
 // B fragment from two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k step)
 __device__ inline f16x8 acc_pair(const f32x4& t0, const f32x4& t1) {
   f16x8 r;
@@ -109,6 +126,58 @@ struct Geom {
   static_assert(RPT >= 1 && BC % 16 == 0 && D % DH == 0, "geometry");
 };
 
+// The chunk images (layouts and sizes in common.h).  VT is the element type
+// of V (uint16_t bf16 bits or float); the stored image always reserves fp32
+// space for V, and an image with VT = uint16_t is a prefix of it.
+template <int BC, int D>
+struct FwdHead {   // everything but V: what a forward chunk step keeps in LDS
+  _Float16 Qt[BC][D + 8];
+  _Float16 Kn[BC][D + 8];
+  _Float16 KhT[D][BC + 8];
+  _Float16 L[BC][BC + 8];
+  _Float16 P[BC][BC + 8];
+  _Float16 Td[BC][24];
+  float gc[D];
+  float beta[BC];
+  int orow[BC];
+};
+template <int BC, int D, typename VT>
+struct FwdImage : FwdHead<BC, D> {
+  VT V[BC][D];
+};
+template <int BC, int D>
+struct BwdImage {
+  _Float16 KhA[BC][D + 8];
+  _Float16 QtT[D][BC + 8];
+  _Float16 KnT[D][BC + 8];
+  _Float16 PT[BC][BC + 8];
+  _Float16 AT[BC][BC + 8];
+  _Float16 TdT[BC][24];
+  float gc[D];
+  float beta[BC];
+};
+static_assert(sizeof(FwdImage<64, 128, float>) == fwd_image_bytes(64, 128), "image layout");
+static_assert(sizeof(FwdImage<16, 64, uint16_t>) == fwd_image_used(16, 64, 2), "image layout");
+static_assert(sizeof(FwdHead<64, 128>) == fwd_image_head_bytes(64, 128), "image layout");
+static_assert(sizeof(BwdImage<64, 128>) == bwd_image_bytes(64, 128), "image layout");
+static_assert(sizeof(BwdImage<16, 64>) == bwd_image_bytes(16, 64), "image layout");
+
+// Asynchronous copy of `nvec` 16-byte vectors from global memory into LDS
+// (global_load_lds_dwordx4: the data goes straight to LDS, no registers).
+// Wave w moves the 1 KB pieces w, w + 8, ...; lane l of a piece moves its
+// 16 bytes to piece base + 16 l.  Completion is the caller's: s_waitcnt
+// vmcnt(0), then a barrier, before any wave reads the copy.
+__device__ inline void lds_copy_async(void* dst, const unsigned char* src, int nvec) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int p = wave; 64 * p < nvec; p += NW) {
+    const int e = 64 * p + lane;
+    if (e < nvec)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 16 * (size_t)e),
+                                       (__attribute__((address_space(3))) void*)((char*)dst + 1024 * p),
+                                       16, 0, 0);
+  }
+}
+
 // pair index p (0..NPAIR-1) -> block pair (I, J), J <= I, row-major over I
 __device__ inline void pair_of(int p, int& I, int& J) {
   I = 0;
@@ -125,6 +194,7 @@ struct ChunkTables {
   float eref[BC / 16][D];                    // e^gref
   float ecg[BC / 16][D];                     // e^(Gam_C - gref)
   float gc[D];                               // e^Gam_C
+  float gcl[D];                              // Gam_C
   float part[Geom<BC, D>::NRG][D];           // per-row-group sums of g
   float dfac[(Geom<BC, D>::NOFF > 0 ? Geom<BC, D>::NOFF : 1)][D];  // e^(gref_I - gref_J)
   float beta[BC];
@@ -207,7 +277,10 @@ __device__ inline void elems_gamma(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) 
       er.gam[n] += offs;
       const int i = r0 + t;
       if ((i & 15) == 0) tb.gref[i >> 4][c] = er.gam[n];
-      if (i == BC - 1) tb.gc[c] = __expf(er.gam[n]);
+      if (i == BC - 1) {
+        tb.gc[c] = __expf(er.gam[n]);
+        tb.gcl[c] = er.gam[n];
+      }
     }
   }
   __syncthreads();

@@ -32,11 +32,43 @@ struct DevPlan {
   const int* root_seq;
 };
 
-// Chunk-local decay products kept from the forward for the reverse pass, one
-// block per (chunk, head), fp16: A [BC][BC], P [BC][BC], and the inverses of
-// the 16x16 diagonal blocks of I + diag(beta) A, [BC/16][16][16].
-constexpr __host__ __device__ size_t prep_halves(int BC) {
-  return (size_t)2 * BC * BC + (size_t)16 * BC;
+// Chunk images.  The state-independent part of every chunk step is computed
+// once, fully parallel, by the chunk pass (kda_prep.hip) and stored per
+// (chunk, head) as the exact LDS image that a round kernel's state phase
+// reads: the round kernels copy it verbatim (16-byte vectors) and never touch
+// q, k, g or the exponentials on their sequential path.  fp16 arrays are
+// padded (pitch +8 halves) so that matrix-core fragment reads do not collide
+// in LDS banks; every array is a multiple of 16 bytes.
+//
+// Forward image (BC rows, head dim D):
+//   Qt  [BC][D+8]   q e^Gam                 Kn  [BC][D+8]  -k e^Gam
+//   KhT [D][BC+8]   (k e^(Gam_C - Gam))^T   L   [BC][BC+8] A (strict lower)
+//   P   [BC][BC+8]  P (lower)               Td  [BC][24]   (I + diag(beta) A_II)^-1 per 16-row block
+//   gc  [D] fp32    e^Gam_C                 beta [BC] fp32     orow [BC] int (-1: no output)
+//   V   [BC][D]     v in the input dtype (the region is sized for fp32)
+// Backward image:
+//   KhA [BC][D+8]   k e^(Gam_C - Gam)       QtT [D][BC+8]  scale (q e^Gam)^T
+//   KnT [D][BC+8]   -(k e^Gam)^T            PT  [BC][BC+8] scale P^T
+//   AT  [BC][BC+8]  A^T                     TdT [BC][24]   Td_I^T per block
+//   gc  [D] fp32, beta [BC] fp32
+// Rows past the chunk hold zeros (Gam, and so e^Gam, stays flat there).
+constexpr __host__ __device__ size_t fwd_image_head_bytes(int BC, int D) {
+  return (size_t)2 * (2 * (size_t)BC * (D + 8) + (size_t)D * (BC + 8) + 2 * (size_t)BC * (BC + 8) +
+                      (size_t)BC * 24) +
+         4 * (size_t)D + 8 * (size_t)BC;
+}
+// bytes of one forward image as stored (V sized for fp32) and as used for an
+// input element size of `elem` bytes
+constexpr __host__ __device__ size_t fwd_image_bytes(int BC, int D) {
+  return fwd_image_head_bytes(BC, D) + 4 * (size_t)BC * D;
+}
+constexpr __host__ __device__ size_t fwd_image_used(int BC, int D, int elem) {
+  return fwd_image_head_bytes(BC, D) + (size_t)elem * BC * D;
+}
+constexpr __host__ __device__ size_t bwd_image_bytes(int BC, int D) {
+  return (size_t)2 * ((size_t)BC * (D + 8) + 2 * (size_t)D * (BC + 8) + 2 * (size_t)BC * (BC + 8) +
+                      (size_t)BC * 24) +
+         4 * (size_t)D + 4 * (size_t)BC;
 }
 
 struct FwdArgs {
@@ -53,7 +85,8 @@ struct FwdArgs {
   float* h_leaf;
   float* chunk_h;      // [n_chunks,H,D,D]
   float* bufs;         // [n_buf,H,D,D]
-  _Float16* prep;      // [n_chunks,H,prep_halves(BC)]
+  unsigned char* fimg; // [n_chunks,H] forward images, stride fwd_image_bytes
+  unsigned char* bimg; // [n_chunks,H] backward images, stride bwd_image_bytes
 };
 
 struct BwdArgs {
@@ -66,7 +99,8 @@ struct BwdArgs {
   const float* g;
   const float* beta;
   const float* chunk_h;   // saved start state per chunk [n_chunks,H,D,D]
-  const _Float16* prep;   // saved chunk decay products [n_chunks,H,prep_halves(BC)]
+  const unsigned char* fimg;  // forward images (read: A, Td, V)
+  const unsigned char* bimg;  // backward images
   const void* dO;
   const float* dh_leaf;   // may be null
   float* dq;
@@ -76,6 +110,7 @@ struct BwdArgs {
   float* dbeta;
   float* dh0;
   float* dh_boundary;     // may be null
+  void* dOp;              // [n_packed,H,D] dO in packed row order, zero on replay rows
   float* dy;              // [n_packed,H,D]
   float* dhc;             // [n_chunks,H,D,D] gradient of each chunk's end state
   float* slot;            // [n_seq,H,D,D] gradient of each sequence's start state

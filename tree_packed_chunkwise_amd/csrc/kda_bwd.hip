@@ -4,8 +4,10 @@
 // One block per (sequence, head, dv slice) of the round, rounds in reverse
 // order; the block walks its sequence's chunks backwards carrying dh, the
 // gradient of the state at the current chunk end (it starts from the leaf
-// state's gradient).  Per chunk, with A, P and the diagonal-block inverses Td
-// saved by the forward (kda_prep.hip):
+// state's gradient).  Per chunk it copies the chunk's reverse image (written
+// by the chunk-parallel pass, kda_prep.hip: k e^(Gam_C - Gam),
+// scale (q e^Gam)^T, -(k e^Gam)^T, scale P^T, A^T, Td^T, e^Gam_C, beta) into
+// LDS and runs:
 //   at a handoff chunk end: dh += start gradients of every sequence that
 //        started from that state (later rounds, already final); the total is
 //        the handoff state's gradient (HARTS abstract: differentiable
@@ -15,50 +17,36 @@
 //   dh     <- diag(e^Gam_C) dh + scale (Q e^Gam)^T dO - (K e^Gam)^T diag(beta) dy
 // and writes dy and the chunk-end dh for the chunk-local gradient pass; the
 // sequence's start gradient goes to its slot.  dh, ddelta and dy stay in
-// registers (MFMA accumulators reused as B operands, see chunk.h).
+// registers (MFMA accumulators reused as B operands, see chunk.h).  The
+// previous chunk's image is copied asynchronously into a second LDS buffer
+// (and its dO rows into registers) while the current chunk's state phase
+// runs.
 #include "chunk.h"
 #include "timing.h"
 
 namespace kda {
 
-template <int BC, int D>
-struct BwdRoundSmem {
-  using G = Geom<BC, D>;
-  static constexpr int PTD = 24;
-  _Float16 KhA[BC][G::PD];   // K e^(Gam_C - Gam)     [j][c]
-  _Float16 QtT[D][G::PB];    // scale (Q e^Gam)^T     [c][i]
-  _Float16 KnT[D][G::PB];    // -(K e^Gam)^T          [c][j]
-  _Float16 PT[BC][G::PB];    // scale P^T             [j][i]
-  _Float16 AT[BC][G::PB];    // A^T                   [i][j]
-  _Float16 TdT[BC][PTD];     // Td_I^T at rows 16I..  [16I+i][m] = Td_I[m][i]
-  float part[G::NRG][D];
-  float gc[D];               // e^Gam_C
-  float beta[BC];
-  int row[BC];
-  int orow[BC];
-};
-
 template <typename TIn, int BC, int D, int NV>
 __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   using G = Geom<BC, D>;
+  using BI = BwdImage<BC, D>;
   static_assert(NV <= NW, "one column block per wave");
   constexpr int KD = D / 32;
   constexpr int KB = (BC + 31) / 32;
   constexpr bool HALF = (BC == 16);
-  constexpr int NE = G::RPT * G::NHALF;
-  __shared__ BwdRoundSmem<BC, D> s;
+  constexpr int NVEC = (int)(sizeof(BI) / 16);
+  __shared__ BI buf[2];   // this chunk's image and the next one's (chunks run backwards)
   const int seq = seq_begin + blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;
   const int col = 16 * (blockIdx.z * NV + wave) + l16;
   const int H = a.H;
-  const TIn* q = (const TIn*)a.q;
-  const TIn* k = (const TIn*)a.k;
-  const TIn* dO = (const TIn*)a.dO;
+  const TIn* dOp = (const TIn*)a.dOp;
   const size_t DD = (size_t)D * D;
-  const float sc = a.scale;
-  const int c0 = tid % G::DH, rg = tid / G::DH, r0 = rg * G::RPT;
+  const int cbeg = a.plan.seq_chunk_ptr[seq];
+  const int cend = a.plan.seq_chunk_ptr[seq + 1];
+  auto image = [&](int cc) { return a.bimg + ((size_t)cc * H + h) * bwd_image_bytes(BC, D); };
 
   f32x4 dh[G::NCB];
   {
@@ -69,109 +57,40 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       for (int r = 0; r < 4; ++r)
         dh[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
-  const int cbeg = a.plan.seq_chunk_ptr[seq];
-  const int cend = a.plan.seq_chunk_ptr[seq + 1];
-  for (int c = cend - 1; c >= cbeg; --c) {
-    const int row0 = a.plan.chunk_row0[c];
-    const int len = a.plan.chunk_len[c];
-    const int nrep = a.plan.chunk_nrep[c];
-    const size_t blk = (size_t)c * H + h;
-    __syncthreads();
-    if (tid < BC) {
-      const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
-      s.row[tid] = r;
-      s.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
-      s.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
-    }
-    {  // saved decay products, transposed into LDS
-      const _Float16* src = a.prep + blk * prep_halves(BC);
-      constexpr int NV8 = (int)(prep_halves(BC) / 8);
-      for (int e = tid; e < NV8; e += NT) {
-        const f16x8 x = *(const f16x8*)(src + 8 * e);
-        const int hoff = 8 * e;
-        if (hoff < BC * BC) {
-          const int i = hoff / BC, j0 = hoff % BC;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) s.AT[j0 + m][i] = x[m];
-        } else if (hoff < 2 * BC * BC) {
-          const int o = hoff - BC * BC, i = o / BC, j0 = o % BC;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) s.PT[j0 + m][i] = (_Float16)(sc * (float)x[m]);
-        } else {
-          const int o = hoff - 2 * BC * BC;
-          const int I = o / 256, mm = (o % 256) / 16, i0 = o % 16;
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) s.TdT[16 * I + i0 + e2][mm] = x[e2];
-        }
-      }
-    }
-    __syncthreads();
-    float kk[NE], qq[NE], gm[NE];
-    {
-      int rows[G::RPT];
-#pragma unroll
-      for (int t = 0; t < G::RPT; ++t) rows[t] = s.row[r0 + t];
-#pragma unroll
-      for (int hf = 0; hf < G::NHALF; ++hf)
-#pragma unroll
-        for (int t = 0; t < G::RPT; ++t) {
-          const int n = hf * G::RPT + t, r = rows[t];
-          const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf;
-          const float x1 = ld_in(k, off), x2 = ld_in(q, off), x3 = a.g[off];
-          kk[n] = r >= 0 ? x1 : 0.f;
-          qq[n] = r >= 0 ? x2 : 0.f;
-          gm[n] = r >= 0 ? x3 : 0.f;
-        }
-    }
-    // dO as B fragments over the chunk rows (register k order), zero on replay rows
-    f16x8 dob[KB];
+  // dO of the chunk in flight, raw, in register k order (see chunk.h); packed
+  // dO is zero on replay rows
+  TIn dor[KB][8];
+  auto load_do = [&](int cc) {
+    const int r0c = a.plan.chunk_row0[cc], lenc = a.plan.chunk_len[cc];
 #pragma unroll
     for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 32 * ks + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-        float x = 0.f;
-        if (i < BC) {
-          const int orow = s.orow[i];
-          const float y = ld_in(dO, ((size_t)(orow < 0 ? 0 : orow) * H + h) * D + (sw ? col : 0));
-          x = orow >= 0 ? y : 0.f;
-        }
-        dob[ks][e] = (_Float16)x;
+        dor[ks][e] = (TIn)0;
+        if (sw && i < BC && i < lenc) dor[ks][e] = dOp[((size_t)(r0c + i) * H + h) * D + col];
       }
+  };
+  if (cbeg < cend) {
+    lds_copy_async(&buf[0], image(cend - 1), NVEC);
+    load_do(cend - 1);
+  }
+  for (int c = cend - 1; c >= cbeg; --c) {
+    const int row0 = a.plan.chunk_row0[c];
+    const int len = a.plan.chunk_len[c];
+    const size_t blk = (size_t)c * H + h;
+    __builtin_amdgcn_s_waitcnt(0);  // this chunk's image (and dO) have landed ...
+    __syncthreads();                // ... for every wave; the other buffer is free
+    const BI& s = buf[(cend - 1 - c) & 1];
+    f16x8 dob[KB];
 #pragma unroll
-    for (int hf = 0; hf < G::NHALF; ++hf) {
-      float run = 0.f;
+    for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
-      for (int t = 0; t < G::RPT; ++t) {
-        run += gm[hf * G::RPT + t];
-        gm[hf * G::RPT + t] = run;
-      }
-      s.part[rg][c0 + G::DH * hf] = run;
+      for (int e = 0; e < 8; ++e) dob[ks][e] = (_Float16)ld_in(&dor[ks][0], e);
+    if (c > cbeg) {
+      lds_copy_async(&buf[(cend - c) & 1], image(c - 1), NVEC);
+      load_do(c - 1);
     }
-    __syncthreads();
-#pragma unroll
-    for (int hf = 0; hf < G::NHALF; ++hf) {
-      const int cc = c0 + G::DH * hf;
-      float offs = 0.f, tot = 0.f;
-#pragma unroll
-      for (int j = 0; j < G::NRG; ++j) {
-        const float pj = s.part[j][cc];
-        offs += (j < rg) ? pj : 0.f;
-        tot += pj;
-      }
-      if (rg == 0) s.gc[cc] = __expf(tot);
-#pragma unroll
-      for (int t = 0; t < G::RPT; ++t) {
-        const int n = hf * G::RPT + t, i = r0 + t;
-        const float gam = gm[n] + offs;
-        const float e1 = __expf(gam);
-        const float e2 = __expf(tot - gam);
-        s.KhA[i][cc] = (_Float16)(kk[n] * e2);
-        s.QtT[cc][i] = (_Float16)(sc * qq[n] * e1);
-        s.KnT[cc][i] = (_Float16)(-kk[n] * e1);
-      }
-    }
-    __syncthreads();
 
     if (sw) {
       const int save = a.plan.chunk_save[c];
@@ -260,6 +179,40 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = dh[C][r];
   }
+}
+
+// dO in packed row order: dOp[p] = dO[out_row[p]] for rows with an output,
+// zero on replay rows (16-byte vectors).
+template <typename TIn, int D>
+__global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, const int* out_row, int H,
+                                                   int64_t n_packed, TIn* dOp) {
+  constexpr int PER = 16 / sizeof(TIn);  // elements per vector
+  const int64_t nvec = n_packed * H * (D / PER);
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < nvec; e += (int64_t)gridDim.x * 256) {
+    const int64_t rowh = e / (D / PER);
+    const int64_t p = rowh / H;
+    const int h = (int)(rowh % H);
+    const int o = out_row[p];
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (o >= 0) x = ((const uint4*)(dO + ((size_t)o * H + h) * D))[e % (D / PER)];
+    ((uint4*)dOp)[e] = x;
+  }
+}
+
+hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int D, int64_t n_packed, hipStream_t st) {
+  if (n_packed <= 0) return hipSuccess;
+  const int64_t nvec = n_packed * a.H * (D / (bf16 ? 8 : 4));
+  const int nb = (int)((nvec + 255) / 256 < 65536 ? (nvec + 255) / 256 : 65536);
+#define KDA_GDO(T, Dv)                                                                       \
+  KDA_LAUNCH("kda_bwd_gather_dO", (k_gather_dO<T, Dv>), dim3(nb), dim3(256), st, (const T*)a.dO, \
+             a.plan.out_row, a.H, n_packed, (T*)a.dOp)
+  if (bf16) {
+    if (D == 128) KDA_GDO(uint16_t, 128); else KDA_GDO(uint16_t, 64);
+  } else {
+    if (D == 128) KDA_GDO(float, 128); else KDA_GDO(float, 64);
+  }
+#undef KDA_GDO
+  return hipGetLastError();
 }
 
 int round_slices(int nseq, int H, int D);

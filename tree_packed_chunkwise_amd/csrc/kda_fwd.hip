@@ -2,66 +2,52 @@
 //
 // One block per (sequence, head, dv slice) of the round (HARTS Figure 2(c):
 // all sequences of a round form one packed call).  The block walks its
-// sequence's chunks in order; per chunk (C rows, state h of dk x dv), with
-// A, P and the diagonal-block inverses Td from the chunk-parallel pass
-// (kda_prep.hip):
-//   Gam   = cumulative log-decay of the chunk rows (per key channel)
+// sequence's chunks in order; per chunk (C rows, state h of dk x dv) it
+// copies the chunk's forward image (written by the chunk-parallel pass,
+// kda_prep.hip: q e^Gam, -k e^Gam, (k e^(Gam_C - Gam))^T, A, P, the
+// diagonal-block inverses Td, e^Gam_C, beta, V) into LDS and runs:
 //   Z     = V - (K e^Gam) h                 (value minus the decayed state's prediction)
 //   delta : (I + diag(beta) A) delta = diag(beta) Z   (the delta-rule writes of
 //                                            the chunk's rows; block substitution)
 //   O     = scale ((Q e^Gam) h + P delta)   (written for non-replay rows only, Figure C.1(b))
 //   h'    = diag(e^Gam_C) h + (K e^(Gam_C - Gam))^T delta
 // The state h and the chunk's Z / delta never leave registers: they are MFMA
-// accumulators reused as B operands (chunk.h).  The start state of every
-// chunk is saved for the reverse pass; handoff states are saved at chunk
-// ends; the leaf state is written at the end of the sequence.
+// accumulators reused as B operands (chunk.h).  The next chunk's image is
+// copied asynchronously into a second LDS buffer (and its V into registers)
+// while the current chunk's state phase runs, so the sequential chain waits
+// on no global load.  The start state of every chunk
+// is saved for the reverse pass; handoff states are saved at chunk ends; the
+// leaf state is written at the end of the sequence.
 //
 // dv slicing: a block owns NV 16-wide column blocks of the state (one per
 // wave); a round with few sequences is cut into D/(16 NV) slices so that more
-// compute units work on it (the chunk-local part is then recomputed per slice).
+// compute units work on it.
 #include "chunk.h"
 #include "timing.h"
 
 namespace kda {
 
-template <int BC, int D>
-struct FwdRoundSmem {
-  using G = Geom<BC, D>;
-  static constexpr int PT = 24;  // pitch (halves) of the 16-wide diagonal inverses
-  _Float16 Qt[BC][G::PD];        // Q e^Gam                [i][c]
-  _Float16 Kn[BC][G::PD];        // -(K e^Gam)             [j][c]
-  _Float16 KhT[D][G::PB];        // (K e^(Gam_C - Gam))^T  [c][j]
-  _Float16 L[BC][G::PB];         // A                      [i][j]
-  _Float16 P[BC][G::PB];         //                        [i][j]
-  _Float16 Td[BC][PT];           // (I + L_II)^-1, block I at rows 16I..16I+15
-  float part[G::NRG][D];
-  float gc[D];                   // e^Gam_C
-  float beta[BC];
-  int row[BC];
-  int orow[BC];
-};
-
 template <typename TIn, int BC, int D, int NV>
 __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
   using G = Geom<BC, D>;
-  using SM = FwdRoundSmem<BC, D>;
+  using FH = FwdHead<BC, D>;
+  using FI = FwdImage<BC, D, TIn>;
   static_assert(NV <= NW, "one column block per wave");
   constexpr int KD = D / 32;                 // 32-deep k steps over the head dim
   constexpr int KB = (BC + 31) / 32;         // 32-deep k steps over the chunk rows
   constexpr bool HALF = (BC == 16);          // chunk rows cover half a k step
-  constexpr int NE = G::RPT * G::NHALF;      // elements per thread of the element mapping
-  __shared__ SM s;
+  constexpr int NVEC = (int)(sizeof(FH) / 16);
+  __shared__ FH buf[2];                      // this chunk's image and the next one's
   const int seq = seq_begin + blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;                 // this wave carries a column block of the state
   const int col = 16 * (blockIdx.z * NV + wave) + l16;
   const int H = a.H;
-  const TIn* q = (const TIn*)a.q;
-  const TIn* k = (const TIn*)a.k;
-  const TIn* v = (const TIn*)a.v;
   const size_t DD = (size_t)D * D;
-  const int c0 = tid % G::DH, rg = tid / G::DH, r0 = rg * G::RPT;
+  const int cbeg = a.plan.seq_chunk_ptr[seq];
+  const int cend = a.plan.seq_chunk_ptr[seq + 1];
+  auto image = [&](int cc) { return a.fimg + ((size_t)cc * H + h) * fwd_image_bytes(BC, D); };
 
   f32x4 hs[G::NCB];
   {
@@ -77,102 +63,33 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       for (int r = 0; r < 4; ++r)
         hs[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
-
-  const int cbeg = a.plan.seq_chunk_ptr[seq];
-  const int cend = a.plan.seq_chunk_ptr[seq + 1];
-  for (int c = cbeg; c < cend; ++c) {
-    const int row0 = a.plan.chunk_row0[c];
-    const int len = a.plan.chunk_len[c];
-    const int nrep = a.plan.chunk_nrep[c];
-    const size_t blk = (size_t)c * H + h;
-    __syncthreads();
-    if (tid < BC) {
-      const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
-      s.row[tid] = r;
-      s.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
-      s.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
-    }
-    // decay products of the chunk (chunk-parallel pass)
-    {
-      const _Float16* src = a.prep + blk * prep_halves(BC);
-      constexpr int NV8 = (int)(prep_halves(BC) / 8);
-      for (int e = tid; e < NV8; e += NT) {
-        const f16x8 x = *(const f16x8*)(src + 8 * e);
-        const int hoff = 8 * e;
-        if (hoff < BC * BC) {
-          *(f16x8*)&s.L[hoff / BC][hoff % BC] = x;
-        } else if (hoff < 2 * BC * BC) {
-          const int o = hoff - BC * BC;
-          *(f16x8*)&s.P[o / BC][o % BC] = x;
-        } else {
-          const int o = hoff - 2 * BC * BC;  // [I][i][m], 16 wide
-          *(f16x8*)&s.Td[o / 16][o % 16] = x;
-        }
-      }
-    }
-    __syncthreads();
-    // k, q, g of the element mapping; v of the state's column block
-    float kk[NE], qq[NE], gm[NE];
-    {
-      int rows[G::RPT];
-#pragma unroll
-      for (int t = 0; t < G::RPT; ++t) rows[t] = s.row[r0 + t];
-#pragma unroll
-      for (int hf = 0; hf < G::NHALF; ++hf)
-#pragma unroll
-        for (int t = 0; t < G::RPT; ++t) {
-          const int n = hf * G::RPT + t, r = rows[t];
-          const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf;
-          const float x1 = ld_in(k, off), x2 = ld_in(q, off), x3 = a.g[off];
-          kk[n] = r >= 0 ? x1 : 0.f;
-          qq[n] = r >= 0 ? x2 : 0.f;
-          gm[n] = r >= 0 ? x3 : 0.f;
-        }
-    }
-    float vz[G::NB][4];
+  // V of the chunk in flight, raw, for this lane's rows of column `col`
+  TIn vr[G::NB][4];
+  auto load_v = [&](int cc) {
+    const FI* F = (const FI*)image(cc);
 #pragma unroll
     for (int J = 0; J < G::NB; ++J)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = s.row[16 * J + 4 * g + r];
-        const float x = ld_in(v, ((size_t)(rr < 0 ? 0 : rr) * H + h) * D + (sw ? col : 0));
-        vz[J][r] = rr >= 0 ? x : 0.f;
-      }
-    // Gam: cumulative sum over the chunk rows (row groups, then their prefix)
+      for (int r = 0; r < 4; ++r) vr[J][r] = sw ? F->V[16 * J + 4 * g + r][col] : (TIn)0;
+  };
+  if (cbeg < cend) {
+    lds_copy_async(&buf[0], image(cbeg), NVEC);
+    load_v(cbeg);
+  }
+  for (int c = cbeg; c < cend; ++c) {
+    const size_t blk = (size_t)c * H + h;
+    __builtin_amdgcn_s_waitcnt(0);  // this chunk's image (and V) have landed ...
+    __syncthreads();                // ... for every wave; the other buffer is free
+    const FH& s = buf[(c - cbeg) & 1];
+    f32x4 z[G::NB];
 #pragma unroll
-    for (int hf = 0; hf < G::NHALF; ++hf) {
-      float run = 0.f;
+    for (int J = 0; J < G::NB; ++J)
 #pragma unroll
-      for (int t = 0; t < G::RPT; ++t) {
-        run += gm[hf * G::RPT + t];
-        gm[hf * G::RPT + t] = run;
-      }
-      s.part[rg][c0 + G::DH * hf] = run;
+      for (int r = 0; r < 4; ++r) z[J][r] = ld_in(&vr[J][0], r);
+    if (c + 1 < cend) {
+      lds_copy_async(&buf[(c - cbeg + 1) & 1], image(c + 1), NVEC);
+      load_v(c + 1);
     }
-    __syncthreads();
-#pragma unroll
-    for (int hf = 0; hf < G::NHALF; ++hf) {
-      const int cc = c0 + G::DH * hf;
-      float offs = 0.f, tot = 0.f;
-#pragma unroll
-      for (int j = 0; j < G::NRG; ++j) {
-        const float pj = s.part[j][cc];
-        offs += (j < rg) ? pj : 0.f;
-        tot += pj;
-      }
-      if (rg == 0) s.gc[cc] = __expf(tot);
-#pragma unroll
-      for (int t = 0; t < G::RPT; ++t) {
-        const int n = hf * G::RPT + t, i = r0 + t;
-        const float gam = gm[n] + offs;
-        const float e1 = __expf(gam);
-        const float e2 = __expf(tot - gam);
-        s.Qt[i][cc] = (_Float16)(qq[n] * e1);
-        s.Kn[i][cc] = (_Float16)(-kk[n] * e1);
-        s.KhT[cc][i] = (_Float16)(kk[n] * e2);
-      }
-    }
-    __syncthreads();
 
     // ---- state phase: wave w < NV owns column block w of the slice ----
     if (sw) {
@@ -188,10 +105,8 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hs[2 * ks], hs[2 * ks + 1]);
       // Z = V - (K e^Gam) h
-      f32x4 z[G::NB];
 #pragma unroll
       for (int J = 0; J < G::NB; ++J) {
-        z[J] = (f32x4){vz[J][0], vz[J][1], vz[J][2], vz[J][3]};
 #pragma unroll
         for (int ks = 0; ks < KD; ++ks)
           z[J] = mfma16(lds_a_perm(&s.Kn[0][0], G::PD, 16 * J + l16, 32 * ks, g), hb[ks], z[J]);

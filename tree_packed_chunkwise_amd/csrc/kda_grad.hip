@@ -2,7 +2,7 @@
 //
 // One block (8 waves) per (chunk, head), after the state-gradient rounds.  With
 // h the chunk's start state (saved by the forward), dh' its end-state gradient
-// and dy (kda_bwd.hip), and the saved decay products A and Td:
+// and dy (kda_bwd.hip), and A, Td and V from the chunk's forward image:
 //   Z      = V - (K e^Gam) h,   delta: (I + diag(beta) A) delta = diag(beta) Z
 //   dV     = diag(beta) dy = dZ
 //   dbeta  = rowsum(dy * (Z - A delta))
@@ -169,8 +169,9 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
   const int rep0 = a.plan.chunk_rep0[c];
   const TIn* q = (const TIn*)a.q;
   const TIn* k = (const TIn*)a.k;
-  const TIn* v = (const TIn*)a.v;
-  const TIn* dO = (const TIn*)a.dO;
+  const TIn* dOp = (const TIn*)a.dOp;
+  const FwdImage<BC, D, TIn>* F =
+      (const FwdImage<BC, D, TIn>*)(a.fimg + blk * fwd_image_bytes(BC, D));
   const float sc = a.scale;
 
   if (tid < BC) {
@@ -179,15 +180,14 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
     s.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
     s.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
   }
-  {  // saved A and Td
-    const _Float16* src = a.prep + blk * prep_halves(BC);
+  {  // A and Td of the forward image
     for (int e = tid; e < BC * BC / 8; e += NT) {
       const int i = e / (BC / 8), j0 = (e % (BC / 8)) * 8;
-      *(f16x8*)&s.u.p.A[i][j0] = *(const f16x8*)(src + i * BC + j0);
+      *(f16x8*)&s.u.p.A[i][j0] = *(const f16x8*)&F->L[i][j0];
     }
-    for (int e = tid; e < NB * 256 / 8; e += NT) {
-      const int o = 8 * e;
-      *(f16x8*)&s.u.p.Td[o / 16][o % 16] = *(const f16x8*)(src + 2 * BC * BC + o);
+    for (int e = tid; e < BC * 2; e += NT) {
+      const int i = e / 2, j0 = (e % 2) * 8;
+      *(f16x8*)&s.u.p.Td[i][j0] = *(const f16x8*)&F->Td[i][j0];
     }
   }
   // ---- loads that need no row table: states and dy (wave layout) ----
@@ -228,14 +228,14 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
       kk[n] = r >= 0 ? y : 0.f;
       qq[n] = r >= 0 ? w : 0.f;
     }
-  Raw8<TIn> dov[NV8];
+  Raw8<TIn> dov[NV8];   // packed dO is zero on replay rows
 #pragma unroll
   for (int n = 0; n < NV8; ++n) {
     const int e = tid + NT * n;
     dov[n].zero();
     if (e < BC * D / 8) {
-      const int i = e / (D / 8), orow = s.orow[i];
-      if (orow >= 0) dov[n].load(dO + ((size_t)orow * H + h) * D + (e % (D / 8)) * 8);
+      const int i = e / (D / 8);
+      if (i < len) dov[n].load(dOp + ((size_t)(row0 + i) * H + h) * D + (e % (D / 8)) * 8);
     }
   }
   f32x4 z[NB];
@@ -243,11 +243,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
 #pragma unroll
     for (int J = 0; J < NB; ++J)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = s.row[16 * J + 4 * g + r];
-        const float x = ld_in(v, ((size_t)(rr < 0 ? 0 : rr) * H + h) * D + col);
-        z[J][r] = rr >= 0 ? x : 0.f;
-      }
+      for (int r = 0; r < 4; ++r) z[J][r] = ld_in(&F->V[0][0], (size_t)(16 * J + 4 * g + r) * D + col);
   }
 
   // ---- Gam: running sums per row group, then their prefix ----
@@ -319,11 +315,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
     for (int C = 0; C < NCB; ++C)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = hC[C][r] * dhC[C][r];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
+        const float x = row_sum16(hC[C][r] * dhC[C][r]);
         if (l16 == 0) s.redg[wave][16 * C + 4 * g + r] = x;
       }
     // delta by block forward substitution with the diagonal inverses
@@ -362,11 +354,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
         const float dy = dyv[I][r], b = s.beta[i];
-        float x = dy * e[r];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
+        const float x = row_sum16(dy * e[r]);
         if (l16 == 0) s.redb[wave][i] = x;
         if (i < len) grad_dst(a, a.dv, a.rep_dv, rep0, s.orow[i], i, nrep, h, D)[col] = b * dy;
         s.u.p.nZ[i][col] = (_Float16)(-b * dy);
@@ -542,11 +530,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = cs[r];
-          x += __shfl_xor(x, 1);
-          x += __shfl_xor(x, 2);
-          x += __shfl_xor(x, 4);
-          x += __shfl_xor(x, 8);
+          const float x = row_sum16(cs[r]);
           if (l16 == 0) s.csum[tI][cf + r] = x;
         }
       }

@@ -1,17 +1,21 @@
-// kda_prep.hip -- chunk-local decay products of every chunk (gfx950).
+// kda_prep.hip -- the chunk-parallel pass: the state-independent part of every
+// chunk step, for all chunks of all rounds at once (gfx950).
 //
-// One block per (chunk, head) over all chunks of all rounds: this part of
-// the chunk algebra does not depend on the recurrent state, so it runs fully
-// parallel ahead of the per-round passes and is shared by the forward and the
-// reverse pass.  Per chunk (C rows):
+// One block per (chunk, head).  This part of the chunk algebra does not
+// depend on the recurrent state, so it runs fully parallel ahead of the
+// per-round passes and is shared by the forward and the reverse pass.  Per
+// chunk (C rows, HARTS Figure 2(c): a chunk of a packed sequence):
 //   Gam_i = sum_{s<=i} g_s                                     per key channel
 //   A_ij  = sum_c k_ic k_jc e^(Gam_ic - Gam_jc)   (j < i)
 //   P_ij  = sum_c q_ic k_jc e^(Gam_ic - Gam_jc)   (j <= i)
 //   Td_I  = (I + diag(beta_I) A_II)^-1 for every 16-row diagonal block I
-// Stored per (chunk, head), fp16: A [C][C] (blocks above the diagonal zero),
-// P [C][C], Td [C/16][16][16].  The state-dependent passes solve
-// (I + diag(beta) A) delta = diag(beta) Z (and its transpose) block by block
-// with Td, so the full inverse is never formed.
+// and the decayed operands q e^Gam, k e^Gam, k e^(Gam_C - Gam).  Everything
+// is written as the two chunk images (layouts in common.h): the LDS image of
+// a forward chunk step and that of a reverse chunk step, so that the round
+// kernels' sequential chain only copies an image and runs the state phase.
+// The state-dependent passes solve (I + diag(beta) A) delta = diag(beta) Z
+// (and its transpose) block by block with Td; the full inverse is never
+// formed.
 #include "chunk.h"
 #include "timing.h"
 
@@ -26,32 +30,113 @@ struct PrepSmem {
   ChunkTables<BC, D> tb;
 };
 
+template <typename TIn>
+__device__ inline TIn to_in(float x);
+template <>
+__device__ inline float to_in<float>(float x) { return x; }
+template <>
+__device__ inline uint16_t to_in<uint16_t>(float x) {  // exact: x holds a bf16 value
+  return (uint16_t)(__float_as_uint(x) >> 16);
+}
+
 template <typename TIn, int BC, int D>
 __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
   using G = Geom<BC, D>;
+  using FI = FwdImage<BC, D, TIn>;
+  using BI = BwdImage<BC, D>;
+  constexpr int NE = G::RPT * G::NHALF;
   __shared__ PrepSmem<BC, D> s;
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int H = a.H;
+  const size_t blk = (size_t)c * H + h;
   const int row0 = a.plan.chunk_row0[c];
   const int len = a.plan.chunk_len[c];
+  const int nrep = a.plan.chunk_nrep[c];
+  const float sc = a.scale;
   if (tid < BC) {
     const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
     s.tb.row[tid] = r;
+    s.tb.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
     s.tb.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
   }
   __syncthreads();
   ElemRegs<BC, D> er;
   elems_load<TIn, BC, D>((const TIn*)a.q, (const TIn*)a.k, a.g, H, h, s.tb, er);
+  const int c0 = tid % G::DH, r0 = (tid / G::DH) * G::RPT;
+  float vv[NE];
+  {
+    const TIn* v = (const TIn*)a.v;
+#pragma unroll
+    for (int hf = 0; hf < G::NHALF; ++hf)
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) {
+        const int r = s.tb.row[r0 + t];
+        const float x = ld_in(v, ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf);
+        vv[hf * G::RPT + t] = r >= 0 ? x : 0.f;
+      }
+  }
   chunk_AP<BC, D>(s.tb, er, s.ap, &s.A[0][0], G::PB, &s.P[0][0], G::PB);
-  _Float16* out = a.prep + ((size_t)c * H + h) * prep_halves(BC);
-  _Float16* Lg = out;
-  _Float16* Pg = out + BC * BC;
-  _Float16* Tg = out + 2 * BC * BC;
-  // A and P, 8 halves per thread per pass
+  FI* F = (FI*)(a.fimg + blk * fwd_image_bytes(BC, D));
+  BI* Bm = (BI*)(a.bimg + blk * bwd_image_bytes(BC, D));
+
+  // decayed operands from the element mapping (channel c0 + 64 hf, rows r0..)
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf) {
+    const int cc = c0 + G::DH * hf;
+    const float gcl = s.tb.gcl[cc];
+    _Float16 kht[G::RPT], qtt[G::RPT], knt[G::RPT];
+#pragma unroll
+    for (int t = 0; t < G::RPT; ++t) {
+      const int n = hf * G::RPT + t, i = r0 + t;
+      const float e1 = __expf(er.gam[n]);
+      const float e2 = __expf(gcl - er.gam[n]);
+      F->Qt[i][cc] = (_Float16)(er.q[n] * e1);
+      F->Kn[i][cc] = (_Float16)(-er.k[n] * e1);
+      F->V[i][cc] = to_in<TIn>(vv[n]);
+      Bm->KhA[i][cc] = (_Float16)(er.k[n] * e2);
+      kht[t] = (_Float16)(er.k[n] * e2);
+      qtt[t] = (_Float16)(sc * er.q[n] * e1);
+      knt[t] = (_Float16)(-er.k[n] * e1);
+    }
+    if constexpr (G::RPT == 8) {
+      f16x8 x, y, z;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) { x[t] = kht[t]; y[t] = qtt[t]; z[t] = knt[t]; }
+      *(f16x8*)&F->KhT[cc][r0] = x;
+      *(f16x8*)&Bm->QtT[cc][r0] = y;
+      *(f16x8*)&Bm->KnT[cc][r0] = z;
+    } else {
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) {
+        F->KhT[cc][r0 + t] = kht[t];
+        Bm->QtT[cc][r0 + t] = qtt[t];
+        Bm->KnT[cc][r0 + t] = knt[t];
+      }
+    }
+  }
+  if (tid < D) {
+    F->gc[tid] = s.tb.gc[tid];
+    Bm->gc[tid] = s.tb.gc[tid];
+  }
+  if (tid < BC) {
+    F->beta[tid] = s.tb.beta[tid];
+    Bm->beta[tid] = s.tb.beta[tid];
+    F->orow[tid] = s.tb.orow[tid];
+  }
+  // A and P as they are (same pitch), and transposed for the reverse pass
   for (int e = tid; e < BC * BC / 8; e += NT) {
     const int i = e / (BC / 8), j0 = (e % (BC / 8)) * 8;
-    *(f16x8*)(Lg + i * BC + j0) = *(const f16x8*)&s.A[i][j0];
-    *(f16x8*)(Pg + i * BC + j0) = *(const f16x8*)&s.P[i][j0];
+    *(f16x8*)&F->L[i][j0] = *(const f16x8*)&s.A[i][j0];
+    *(f16x8*)&F->P[i][j0] = *(const f16x8*)&s.P[i][j0];
+    // row j = i of the transposes, columns j0 .. j0+7
+    f16x8 at, pt;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      at[m] = s.A[j0 + m][i];
+      pt[m] = (_Float16)(sc * (float)s.P[j0 + m][i]);
+    }
+    *(f16x8*)&Bm->AT[i][j0] = at;
+    *(f16x8*)&Bm->PT[i][j0] = pt;
   }
   // diagonal inverses: one lane per (block, column), forward substitution
   if (tid < 16 * G::NB) {
@@ -67,8 +152,15 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
       for (int m = 0; m < i; ++m) acc -= bi * (float)(m < 8 ? a0[m] : a1[m - 8]) * x[m];
       x[i] = (i >= j) ? acc : 0.f;
     }
+    f16x8 lo, hi;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Tg[(I * 16 + i) * 16 + j] = (_Float16)x[i];
+    for (int i = 0; i < 16; ++i) {
+      const _Float16 v16 = (_Float16)x[i];
+      F->Td[b0 + i][j] = v16;
+      if (i < 8) lo[i] = v16; else hi[i - 8] = v16;
+    }
+    *(f16x8*)&Bm->TdT[b0 + j][0] = lo;
+    *(f16x8*)&Bm->TdT[b0 + j][8] = hi;
   }
 }
 

@@ -2,6 +2,7 @@
 // (gfx950).
 //
 // Order of the reverse pass of a plan:
+//   0. dO gathered into packed row order (zero on replay rows);
 //   1. the state-gradient rounds, last round first (kda_bwd.hip);
 //   2. the chunk-local gradients of every chunk, fully parallel (kda_grad.hip);
 //   3. gradients of replayed rows (rows a side sequence recomputes from the
@@ -19,6 +20,7 @@ constexpr int BT = 256;  // threads per block of the reductions
 hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
                              int n_rounds, hipStream_t st);
 hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st);
+hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int D, int64_t n_packed, hipStream_t st);
 
 // replayed-row gradients added into their compact rows (fixed order)
 template <int D>
@@ -78,11 +80,13 @@ hipError_t launch_reduce_t(const BwdArgs& a, int n_rep_rows, int n_root, hipStre
   return hipSuccess;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks, int64_t n_packed,
                       const int* round_ptr_host, int n_rounds, int n_rep_rows, int n_root,
                       hipStream_t st) {
   if (D != 64 && D != 128) return hipErrorInvalidValue;
-  hipError_t e = launch_bwd_rounds(a, bf16, BC, D, round_ptr_host, n_rounds, st);
+  hipError_t e = launch_gather_dO(a, bf16, D, n_packed, st);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_rounds(a, bf16, BC, D, round_ptr_host, n_rounds, st);
   if (e != hipSuccess) return e;
   if (n_chunks > 0) {
     e = launch_grad(a, bf16, BC, D, n_chunks, st);
