@@ -65,6 +65,10 @@ typedef struct {
   int64_t n_pos;       /* trajectory positions with a next-token target */
   int64_t n_expanded;  /* sum of trajectory lengths */
   size_t device_bytes; /* size of the device copy made by kda_plan_upload */
+  int32_t n_att_tiles; /* 64-row tiles of all segments (tree attention query / key tiles) */
+  int32_t n_att_items; /* dk / dv work items of the tree attention backward */
+  int32_t n_att_slots; /* partial dk / dv slots (per head) of split key tiles */
+  int32_t n_att_split; /* key tiles whose work is split over several items */
 } kda_plan_info_t;
 
 /*
@@ -130,6 +134,9 @@ enum {
   KDA_F_ROW_INDEX, KDA_F_OUT_ROW, KDA_F_BUF_SEQ, KDA_F_BUF_POS, KDA_F_BUF_CHUNK,
   KDA_F_BUF_CONS_PTR, KDA_F_BUF_CONS, KDA_F_POS_ROW, KDA_F_POS_NEXT_ROW, KDA_F_ROW_POS_PTR,
   KDA_F_ROW_POS_IDX, KDA_F_LEAF_SEG, KDA_F_ROOT_SEG,
+  KDA_F_ATT_ANC_PTR, KDA_F_ATT_ANC, KDA_F_ATT_SEG_TILE0, KDA_F_ATT_TILE_SEG, KDA_F_ATT_TILE_OFF,
+  KDA_F_ATT_QORDER, KDA_F_ATT_KQ_PTR, KDA_F_ATT_KQ, KDA_F_ATT_KW_TILE, KDA_F_ATT_KW_Q0,
+  KDA_F_ATT_KW_NQ, KDA_F_ATT_KW_SLOT,
   KDA_F_COUNT
 };
 int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64_t n);
@@ -247,6 +254,33 @@ int gather_logprobs_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32
                         const float* lse, const int32_t* row_pos_ptr,
                         const int32_t* row_pos_idx, const int32_t* pos_target,
                         const float* dlogp, void* dlogits, void* stream);
+
+/*
+ * Tree-ancestor softmax attention over the plan's compact rows (the full
+ * attention layers of the hybrid model: thelatestinai.com Figure 1(b), full
+ * attention reads ancestor keys and values; Figure C.1(c)).  The query of the
+ * row at offset i of segment v sees every row of every ancestor segment of v
+ * and the rows of v at offsets <= i -- its root path up to itself -- so one
+ * compact row serves every trajectory through it:
+ *     o_r = sum_j softmax_j(scale q_r . k_j) v_j,   lse_r = logsumexp_j(scale q_r . k_j)
+ * Multi-head, H heads of dimension d in {64, 128}.
+ *   q, k, v  [n_rows, H, d] bf16 (compact rows, as the plan's tree)
+ *   o        [n_rows, H, d] fp32;  lse [n_rows, H] fp32
+ * tree_attn_bwd: gradients of sum(dO * o): dO [n_rows, H, d] bf16, o and lse
+ *   from tree_attn_fwd; dq, dk, dv [n_rows, H, d] fp32, every element written;
+ *   ws of tree_attn_workspace_bytes(plan, H, d) bytes (row deltas and partial
+ *   sums of key tiles whose queries are split over several blocks; summed in
+ *   a fixed order, so results are deterministic).
+ * Errors: KDA_ERR_SHAPE for other head dims, KDA_ERR_ARG for null pointers,
+ * KDA_ERR_WORKSPACE for a small workspace, KDA_ERR_HIP for launch failures.
+ */
+size_t tree_attn_workspace_bytes(const kda_plan* plan, int32_t H, int32_t d);
+int tree_attn_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t d, float scale,
+                  const void* q, const void* k, const void* v, float* o, float* lse, void* stream);
+int tree_attn_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t d, float scale,
+                  const void* q, const void* k, const void* v, const float* o, const float* lse,
+                  const void* dO, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /*
  * Launch timing for benchmarks and profilers (not needed for computing).

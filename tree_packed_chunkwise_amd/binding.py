@@ -12,6 +12,7 @@ gather_logprobs, gather_logprobs_bwd.
 from __future__ import annotations
 
 import ctypes
+import math
 from pathlib import Path
 
 import numpy as np
@@ -27,6 +28,8 @@ FIELDS = [
     "SEQ_INIT_KIND", "SEQ_INIT_IDX", "CHUNK_SEQ", "CHUNK_ROW0", "CHUNK_LEN", "CHUNK_SAVE",
     "ROW_INDEX", "OUT_ROW", "BUF_SEQ", "BUF_POS", "BUF_CHUNK", "BUF_CONS_PTR", "BUF_CONS",
     "POS_ROW", "POS_NEXT_ROW", "ROW_POS_PTR", "ROW_POS_IDX", "LEAF_SEG", "ROOT_SEG",
+    "ATT_ANC_PTR", "ATT_ANC", "ATT_SEG_TILE0", "ATT_TILE_SEG", "ATT_TILE_OFF", "ATT_QORDER",
+    "ATT_KQ_PTR", "ATT_KQ", "ATT_KW_TILE", "ATT_KW_Q0", "ATT_KW_NQ", "ATT_KW_SLOT",
 ]
 FIELD_ID = {n: i for i, n in enumerate(FIELDS)}
 
@@ -36,6 +39,7 @@ EXPORTS = [
     "kda_plan_device_offset", "kda_saved_bytes", "kda_fwd_workspace_bytes",
     "kda_bwd_workspace_bytes", "kda_tree_fwd", "kda_tree_bwd", "gather_logprobs",
     "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
+    "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd",
 ]
 
 
@@ -48,7 +52,8 @@ class PlanInfo(ctypes.Structure):
         "n_seg", "n_rounds", "n_seq", "n_chunks", "n_buf", "n_leaf", "n_root", "chunk", "mode",
         "max_seq_per_round")] + [(n, ctypes.c_int64) for n in (
             "n_rows", "n_packed", "n_out_rows", "R", "n_pos", "n_expanded")] + [
-        ("device_bytes", ctypes.c_size_t)]
+        ("device_bytes", ctypes.c_size_t)] + [(n, ctypes.c_int32) for n in (
+            "n_att_tiles", "n_att_items", "n_att_slots", "n_att_split")]
 
 
 _LIB = None
@@ -88,6 +93,12 @@ def load_library(path: Path | str | None = None):
     L.gather_logprobs.restype = ctypes.c_int
     L.gather_logprobs_bwd.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
     L.gather_logprobs_bwd.restype = ctypes.c_int
+    L.tree_attn_workspace_bytes.argtypes = [vp, i32, i32]
+    L.tree_attn_workspace_bytes.restype = sz
+    L.tree_attn_fwd.argtypes = [vp, vp, i32, i32, f32] + [vp] * 5 + [vp]
+    L.tree_attn_fwd.restype = ctypes.c_int
+    L.tree_attn_bwd.argtypes = [vp, vp, i32, i32, f32] + [vp] * 10 + [sz, vp]
+    L.tree_attn_bwd.restype = ctypes.c_int
     L.kda_timing_enable.argtypes = [i32]
     L.kda_timing_enable.restype = ctypes.c_int
     L.kda_timing_read.argtypes = [i32, ctypes.c_char_p, i32, ctypes.POINTER(i64),
@@ -300,6 +311,42 @@ def gather_logprobs_bwd(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp
                                               _p(pos_target), _p(dlogp), _p(out),
                                               _stream(logits)))
     return out
+
+
+def tree_attn_fwd(plan: KDAPlan, q, k, v, scale=None, out=None):
+    """Tree-ancestor attention forward: q, k, v bf16 [rows, H, d] on the
+    plan's compact rows.  Returns (o fp32 [rows, H, d], lse fp32 [rows, H])."""
+    import torch
+    _need_cuda(q, k, v)
+    N, H, D = q.shape
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise KDAError("tree attention takes bf16 q, k, v")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = (torch.empty(N, H, D, dtype=torch.float32, device=q.device),
+               torch.empty(N, H, dtype=torch.float32, device=q.device))
+    o, lse = out
+    _check(load_library().tree_attn_fwd(plan.handle, _p(plan.device(q.device)), H, D, scale,
+                                        _p(q), _p(k), _p(v), _p(o), _p(lse), _stream(q)))
+    return o, lse
+
+
+def tree_attn_bwd(plan: KDAPlan, q, k, v, o, lse, dO, scale=None, out=None, ws=None):
+    """Gradients (dq, dk, dv) fp32 of sum(dO * o) for tree_attn_fwd; dO bf16."""
+    import torch
+    _need_cuda(q, k, v, o, lse, dO)
+    N, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = tuple(torch.empty(N, H, D, dtype=torch.float32, device=q.device) for _ in range(3))
+    nb = load_library().tree_attn_workspace_bytes(plan.handle, H, D)
+    if ws is None or ws.numel() < nb:
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = out
+    _check(load_library().tree_attn_bwd(plan.handle, _p(plan.device(q.device)), H, D, scale,
+                                        _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
+                                        _p(dk), _p(dv), _p(ws), ws.numel(), _stream(q)))
+    return dq, dk, dv
 
 
 def timing_enable(on: bool = True):

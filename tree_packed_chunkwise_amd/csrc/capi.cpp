@@ -1,8 +1,9 @@
 // capi.cpp -- extern "C" entry points of libkda_tree.so (declared in include/kda_tree.h).
 //
 // Argument checking, buffer carving and launch sequencing only; every step of
-// the computation runs in the HIP kernels of kda_fwd.hip, kda_bwd.hip and
-// gather.hip, enqueued on the caller's stream.
+// the computation runs in the HIP kernels (kda_prep.hip, kda_fwd.hip,
+// kda_bwd.hip, kda_grad.hip, kda_reduce.hip, attn.hip, gather.hip), enqueued
+// on the caller's stream.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -18,6 +19,9 @@ hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D,
                       int n_chunks, int64_t n_packed, const int* round_ptr_host, int n_rounds, int n_rep_rows,
                       int n_root, hipStream_t st);
+hipError_t launch_attn_fwd(const AttnArgs& a, int D, int n_tiles, hipStream_t st);
+hipError_t launch_attn_bwd(const AttnArgs& a, int D, int64_t n_rows, int n_tiles, int n_items,
+                           int n_split, hipStream_t st);
 hipError_t launch_gather_fwd(const void* logits, bool bf16, int64_t n_rows, int vocab,
                              const int* pos_row, const int* pos_tgt, int64_t n_pos, float* logp,
                              float* lse, hipStream_t st);
@@ -189,6 +193,10 @@ int kda_plan_info(const kda_plan* plan, kda_plan_info_t* info) {
   info->n_pos = (int64_t)p.pos_row.size();
   info->n_expanded = p.n_expanded;
   info->device_bytes = (size_t)p.dev.total * sizeof(int32_t);
+  info->n_att_tiles = (int32_t)p.att_tile_seg.size();
+  info->n_att_items = (int32_t)p.att_kw_tile.size();
+  info->n_att_slots = p.att_n_slots;
+  info->n_att_split = (int32_t)p.att_ks_tile.size();
   return KDA_OK;
 }
 
@@ -244,6 +252,18 @@ int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64
     case KDA_F_ROW_POS_IDX: return put32(p.row_pos_idx);
     case KDA_F_LEAF_SEG: return put32(p.leaf_seg);
     case KDA_F_ROOT_SEG: return put32(p.root_seg);
+    case KDA_F_ATT_ANC_PTR: return put32(p.att_anc_ptr);
+    case KDA_F_ATT_ANC: return put32(p.att_anc);
+    case KDA_F_ATT_SEG_TILE0: return put32(p.att_seg_tile0);
+    case KDA_F_ATT_TILE_SEG: return put32(p.att_tile_seg);
+    case KDA_F_ATT_TILE_OFF: return put32(p.att_tile_off);
+    case KDA_F_ATT_QORDER: return put32(p.att_qorder);
+    case KDA_F_ATT_KQ_PTR: return put32(p.att_kq_ptr);
+    case KDA_F_ATT_KQ: return put32(p.att_kq);
+    case KDA_F_ATT_KW_TILE: return put32(p.att_kw_tile);
+    case KDA_F_ATT_KW_Q0: return put32(p.att_kw_q0);
+    case KDA_F_ATT_KW_NQ: return put32(p.att_kw_nq);
+    case KDA_F_ATT_KW_SLOT: return put32(p.att_kw_slot);
     default: return fail(KDA_ERR_ARG, "unknown export field");
   }
 }
@@ -397,6 +417,99 @@ int gather_logprobs_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32
                                         row_pos_ptr, row_pos_idx, pos_target, dlogp, dlogits,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "gather_logprobs_bwd launch");
+  return KDA_OK;
+}
+
+// ---- tree-ancestor attention ----
+
+namespace {
+kda::AttnArgs make_attn_args(const kda::Plan& p, const void* dev, int H, float scale) {
+  const int32_t* b = (const int32_t*)dev;
+  const kda::DevLayout& d = p.dev;
+  kda::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.seg_row = b + d.att_seg_row;
+  a.seg_len = b + d.att_seg_len;
+  a.anc_ptr = b + d.att_anc_ptr;
+  a.anc = b + d.att_anc;
+  a.tile_seg = b + d.att_tile_seg;
+  a.tile_off = b + d.att_tile_off;
+  a.qorder = b + d.att_qorder;
+  a.kq_ptr = b + d.att_kq_ptr;
+  a.kq = b + d.att_kq;
+  a.kw_tile = b + d.att_kw_tile;
+  a.kw_q0 = b + d.att_kw_q0;
+  a.kw_nq = b + d.att_kw_nq;
+  a.kw_slot = b + d.att_kw_slot;
+  a.ks_tile = b + d.att_ks_tile;
+  a.ks_slot0 = b + d.att_ks_slot0;
+  a.ks_n = b + d.att_ks_n;
+  a.H = H;
+  a.scale = scale;
+  return a;
+}
+bool attn_shape_ok(int32_t H, int32_t d) { return H > 0 && (d == 64 || d == 128); }
+// ws = [row deltas [N][H] fp32 | partial dk, dv [n_slots][H][2][64][d] fp32]
+size_t attn_ws_carve(const kda::Plan& p, int H, int d, void* base, float** delta, float** part) {
+  Carver c(base);
+  float* x = c.take((size_t)p.n_rows * H);
+  float* y = c.take((size_t)p.att_n_slots * H * 2 * kda::ATT_TILE * d);
+  if (delta) *delta = x;
+  if (part) *part = y;
+  return c.off;
+}
+}  // namespace
+
+size_t tree_attn_workspace_bytes(const kda_plan* plan, int32_t H, int32_t d) {
+  if (!plan || !attn_shape_ok(H, d)) return 0;
+  return attn_ws_carve(plan->p, H, d, nullptr, nullptr, nullptr);
+}
+
+int tree_attn_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t d, float scale,
+                  const void* q, const void* k, const void* v, float* o, float* lse, void* stream) {
+  int rc = check_dev_plan(plan, dev_plan);
+  if (rc) return rc;
+  if (!attn_shape_ok(H, d)) return fail(KDA_ERR_SHAPE, "supported: head dim 64 or 128, H > 0");
+  if (!q || !k || !v || !o || !lse) return fail(KDA_ERR_ARG, "null tensor argument");
+  const kda::Plan& p = plan->p;
+  kda::AttnArgs a = make_attn_args(p, dev_plan, H, scale);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = o;
+  a.lse = lse;
+  hipError_t e = kda::launch_attn_fwd(a, d, (int)p.att_tile_seg.size(), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_attn_fwd launch");
+  return KDA_OK;
+}
+
+int tree_attn_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t d, float scale,
+                  const void* q, const void* k, const void* v, const float* o, const float* lse,
+                  const void* dO, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int rc = check_dev_plan(plan, dev_plan);
+  if (rc) return rc;
+  if (!attn_shape_ok(H, d)) return fail(KDA_ERR_SHAPE, "supported: head dim 64 or 128, H > 0");
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !ws)
+    return fail(KDA_ERR_ARG, "null tensor argument");
+  const kda::Plan& p = plan->p;
+  if (ws_bytes < attn_ws_carve(p, H, d, nullptr, nullptr, nullptr))
+    return fail(KDA_ERR_WORKSPACE, "attention workspace too small");
+  kda::AttnArgs a = make_attn_args(p, dev_plan, H, scale);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.oc = o;
+  a.lsec = lse;
+  a.dO = (const uint16_t*)dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  attn_ws_carve(p, H, d, ws, &a.delta, &a.part);
+  hipError_t e = kda::launch_attn_bwd(a, d, p.n_rows, (int)p.att_tile_seg.size(),
+                                      (int)p.att_kw_tile.size(), (int)p.att_ks_tile.size(),
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_attn_bwd launch");
   return KDA_OK;
 }
 

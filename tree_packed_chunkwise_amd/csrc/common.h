@@ -121,6 +121,41 @@ struct BwdArgs {
   float* rep_db;          // [n_replay,H]
 };
 
+// Tree-ancestor attention (attn.hip): plan tables (see plan.h) and tensors.
+struct AttnArgs {
+  const int* seg_row;
+  const int* seg_len;
+  const int* anc_ptr;
+  const int* anc;
+  const int* tile_seg;
+  const int* tile_off;
+  const int* qorder;
+  const int* kq_ptr;
+  const int* kq;
+  const int* kw_tile;
+  const int* kw_q0;
+  const int* kw_nq;
+  const int* kw_slot;
+  const int* ks_tile;
+  const int* ks_slot0;
+  const int* ks_n;
+  int H;
+  float scale;
+  const uint16_t* q;  // bf16 [N][H][D]
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o;           // [N][H][D]
+  float* lse;         // [N][H]
+  const uint16_t* dO; // bf16 [N][H][D]
+  const float* oc;    // forward output (backward input)
+  const float* lsec;
+  float* delta;       // [N][H]
+  float* dq;
+  float* dk;
+  float* dv;
+  float* part;        // [n_slots][H][2][64][D] partial dk, dv
+};
+
 inline __device__ float ld_in(const float* p, size_t i) { return p[i]; }
 inline __device__ float ld_in(const uint16_t* p, size_t i) {
   return __uint_as_float(((uint32_t)p[i]) << 16);

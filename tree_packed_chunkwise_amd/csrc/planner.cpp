@@ -446,6 +446,102 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     for (size_t pi = 0; pi < P.pos_row.size(); ++pi) P.row_pos_idx[fill[P.pos_row[pi]]++] = (int32_t)pi;
   }
 
+  // ---- tree-ancestor attention tables ----
+  {
+    P.att_seg_row.resize(n);
+    P.att_seg_len.resize(n);
+    for (int32_t i = 0; i < n; ++i) {
+      P.att_seg_row[i] = (int32_t)row0[i];
+      P.att_seg_len[i] = seg_len[i];
+    }
+    std::vector<int64_t> anc_rows(n, 0);
+    P.att_anc_ptr.push_back(0);
+    for (int32_t v = 0; v < n; ++v) {
+      std::vector<int32_t> path;
+      for (int32_t a = parent[v]; a >= 0; a = parent[a]) path.push_back(a);
+      for (auto it = path.rbegin(); it != path.rend(); ++it) {
+        P.att_anc.push_back(*it);
+        anc_rows[v] += seg_len[*it];
+      }
+      P.att_anc_ptr.push_back((int32_t)P.att_anc.size());
+    }
+    P.att_seg_tile0.push_back(0);
+    for (int32_t v = 0; v < n; ++v) {
+      for (int32_t off = 0; off < seg_len[v]; off += ATT_TILE) {
+        P.att_tile_seg.push_back(v);
+        P.att_tile_off.push_back(off);
+      }
+      P.att_seg_tile0.push_back((int32_t)P.att_tile_seg.size());
+    }
+    const int32_t nt = (int32_t)P.att_tile_seg.size();
+    // forward order: most keys first
+    {
+      std::vector<std::pair<int64_t, int32_t>> w(nt);
+      for (int32_t t = 0; t < nt; ++t) {
+        const int32_t v = P.att_tile_seg[t], off = P.att_tile_off[t];
+        w[t] = {-(anc_rows[v] + off + std::min(ATT_TILE, seg_len[v] - off)), t};
+      }
+      std::sort(w.begin(), w.end());
+      for (auto& x : w) P.att_qorder.push_back(x.second);
+    }
+    // query tiles seeing each key tile: own segment from the tile on, then the
+    // descendants (pre-order positions after v up to the end of its subtree)
+    std::vector<int32_t> pos(n), sub_end(n);
+    for (int32_t i = 0; i < n; ++i) pos[order[i]] = i;
+    for (int32_t i = n - 1; i >= 0; --i) {
+      const int32_t v = order[i];
+      int32_t end = i + 1;
+      for (int32_t j = child_ptr[v]; j < child_ptr[v + 1]; ++j) end = std::max(end, sub_end[child_list[j]]);
+      sub_end[v] = end;
+    }
+    P.att_kq_ptr.push_back(0);
+    for (int32_t t = 0; t < nt; ++t) {
+      const int32_t v = P.att_tile_seg[t];
+      for (int32_t u = t; u < P.att_seg_tile0[v + 1]; ++u) P.att_kq.push_back(u);
+      for (int32_t i = pos[v] + 1; i < sub_end[v]; ++i) {
+        const int32_t d = order[i];
+        for (int32_t u = P.att_seg_tile0[d]; u < P.att_seg_tile0[d + 1]; ++u) P.att_kq.push_back(u);
+      }
+      if ((int64_t)P.att_kq.size() >= (int64_t)INT32_MAX) {
+        err = "attention work lists too large";
+        return -1;
+      }
+      P.att_kq_ptr.push_back((int32_t)P.att_kq.size());
+    }
+    // work items of at most kw query tiles (at least ATT_KW_MIN, and about
+    // ATT_KW_TARGET items in all), most query tiles first; split tiles get
+    // consecutive slots
+    const int64_t total_kq = (int64_t)P.att_kq.size();
+    const int32_t kw = (int32_t)std::max<int64_t>(ATT_KW_MIN, (total_kq + ATT_KW_TARGET - 1) / ATT_KW_TARGET);
+    P.att_kw_max = kw;
+    struct Item { int32_t nq, tile, q0; };
+    std::vector<Item> items;
+    int32_t slot = 0;
+    std::vector<int32_t> tile_slot0(nt, -1);
+    for (int32_t t = 0; t < nt; ++t) {
+      const int32_t nq = P.att_kq_ptr[t + 1] - P.att_kq_ptr[t];
+      const int32_t nitem = (nq + kw - 1) / kw;
+      if (nitem > 1) {
+        tile_slot0[t] = slot;
+        P.att_ks_tile.push_back(t);
+        P.att_ks_slot0.push_back(slot);
+        P.att_ks_n.push_back(nitem);
+        slot += nitem;
+      }
+      for (int32_t i = 0; i < nitem; ++i)
+        items.push_back({std::min(kw, nq - i * kw), t, i * kw});
+    }
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& x, const Item& y) { return x.nq > y.nq; });
+    for (auto& it : items) {
+      P.att_kw_tile.push_back(it.tile);
+      P.att_kw_q0.push_back(it.q0);
+      P.att_kw_nq.push_back(it.nq);
+      P.att_kw_slot.push_back(tile_slot0[it.tile] < 0 ? -1 : tile_slot0[it.tile] + it.q0 / kw);
+    }
+    P.att_n_slots = slot;
+  }
+
   // ---- device block: int32 tables, each 64-element (256 B) aligned ----
   {
     DevLayout& d = P.dev;
@@ -464,6 +560,15 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
         {&d.root_seq_ptr, &P.root_seq_ptr},   {&d.root_seq, &P.root_seq},
         {&d.pos_row, &P.pos_row},             {&d.pos_next_row, &P.pos_next_row},
         {&d.row_pos_ptr, &P.row_pos_ptr},     {&d.row_pos_idx, &P.row_pos_idx},
+        {&d.att_seg_row, &P.att_seg_row},     {&d.att_seg_len, &P.att_seg_len},
+        {&d.att_anc_ptr, &P.att_anc_ptr},     {&d.att_anc, &P.att_anc},
+        {&d.att_seg_tile0, &P.att_seg_tile0}, {&d.att_tile_seg, &P.att_tile_seg},
+        {&d.att_tile_off, &P.att_tile_off},   {&d.att_qorder, &P.att_qorder},
+        {&d.att_kq_ptr, &P.att_kq_ptr},       {&d.att_kq, &P.att_kq},
+        {&d.att_kw_tile, &P.att_kw_tile},     {&d.att_kw_q0, &P.att_kw_q0},
+        {&d.att_kw_nq, &P.att_kw_nq},         {&d.att_kw_slot, &P.att_kw_slot},
+        {&d.att_ks_tile, &P.att_ks_tile},     {&d.att_ks_slot0, &P.att_ks_slot0},
+        {&d.att_ks_n, &P.att_ks_n},
     };
     for (auto& t : tabs) {
       *t.first = off;
