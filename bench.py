@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--expanded-steps", type=int, default=3)
+    ap.add_argument("--attn-steps", type=int, default=3,
+                    help="timed steps of the tree attention measurement (0: skip)")
+    ap.add_argument("--hybrid-steps", type=int, default=1,
+                    help="timed steps of the hybrid layer group (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel launch events in the timed region")
@@ -203,6 +207,114 @@ def cpu_baseline(spec, inp, dO, dhl_full, H, leaves):
 
 
 # ---------------------------------------------------------------------------
+# the config-4 pieces: tree attention (matrix-core bound) and the hybrid group
+# ---------------------------------------------------------------------------
+
+def attention_pairs(plan, seg_len):
+    """(query, key) pairs of the ancestor mask, per head."""
+    seg_len = np.asarray(seg_len, dtype=np.int64)
+    ptr = plan.export("ATT_ANC_PTR")
+    anc = plan.export("ATT_ANC")
+    pairs = 0
+    for v in range(len(seg_len)):
+        a_rows = int(seg_len[anc[ptr[v]:ptr[v + 1]]].sum())
+        pairs += int(seg_len[v]) * a_rows + int(seg_len[v]) * (int(seg_len[v]) + 1) // 2
+    return pairs
+
+
+def measure_attention(steps):
+    """Tree attention forward and backward on the hybrid group's tree (the
+    4-ary depth-3 tree of the forward workload), 16 heads, d = 128, bf16.
+    Algorithmic FLOPs: 4 d per (query, key) pair and head forward (QK^T and
+    PV), 10 d backward (recomputed QK^T, dP, dV, dK, dQ)."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    try:
+        w = synth.workload(4)
+        plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, 64)
+        N, H, D = plan.info["n_rows"], 16, 128
+        pairs = attention_pairs(plan, w.tree.seg_len)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(11)
+        mk = lambda: torch.randn(N, H, D, generator=gen, device="cuda").to(torch.bfloat16)
+        q, k, v, dO = mk(), mk(), mk(), mk()
+        o, lse = B.tree_attn_fwd(plan, q, k, v)
+        dq, dk, dv = B.tree_attn_bwd(plan, q, k, v, o, lse, dO)
+        torch.cuda.synchronize()
+        B.timing_enable(True)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(steps):
+            B.tree_attn_fwd(plan, q, k, v, out=(o, lse))
+        e[1].record()
+        for _ in range(steps):
+            B.tree_attn_bwd(plan, q, k, v, o, lse, dO, out=(dq, dk, dv))
+        e[2].record()
+        torch.cuda.synchronize()
+        kt = B.timing_read()
+        B.timing_enable(False)
+        fms, bms = e[0].elapsed_time(e[1]) / steps, e[1].elapsed_time(e[2]) / steps
+        ff, bf = 4 * pairs * D * H, 10 * pairs * D * H
+        kern = {n: round(ms / max(c, 1), 4) for n, (c, ms) in kt.items()}
+        fa = ff / (kern.get("tree_attn_fwd", fms) * 1e-3) / 1e12
+        return {"workload": f"{w.tree.name} tree, {N} rows, 16 heads, d=128, bf16",
+                "pairs_per_head": pairs, "fwd_ms": round(fms, 3), "bwd_ms": round(bms, 3),
+                "roofline": {"bound": "mfma", "kernel": "tree_attn_fwd", "achieved": round(fa, 1),
+                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(fa / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                "bwd_tflops": round(bf / (bms * 1e-3) / 1e12, 1),
+                "kernel_avg_ms": kern, "finite": bool(torch.isfinite(o).all())}
+    except Exception as exc:  # reported, never fatal to the headline line
+        return {"error": repr(exc)}
+
+
+def measure_hybrid(steps):
+    """The hybrid layer group (3 KDA layers, tree attention, log-prob gather,
+    hidden 2048, vocab 32000, bf16) forward + backward on the same tree."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    from tree_packed_chunkwise_amd.hybrid import HybridGroup, gather_maps
+    try:
+        w = synth.workload(4)
+        plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, 64)
+        N = plan.info["n_rows"]
+        model = HybridGroup(2048, 16, 128, 32000, n_kda=3, seed=0, dtype=torch.bfloat16,
+                            device="cuda")
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(12)
+        tokens = torch.randint(0, 32000, (N,), generator=gen, device="cuda")
+        maps = gather_maps(plan, tokens, "cuda")
+        dlogp = torch.randn(plan.info["n_pos"], generator=gen, device="cuda")
+
+        def step():
+            model.zero_grad(set_to_none=True)
+            logp = model(plan, tokens, maps)
+            (logp * dlogp).sum().backward()
+        step()
+        torch.cuda.synchronize()
+        B.timing_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        kt = B.timing_read()
+        B.timing_enable(False)
+        ms = e0.elapsed_time(e1) / steps
+        tree_ms = sum(t for _, t in kt.values()) / steps
+        return {"workload": f"{w.tree.name} tree, {N} rows, {plan.info['n_pos']} positions, "
+                            "hidden 2048, 16 heads d=128, vocab 32000, bf16",
+                "ms_per_step": round(ms, 2), "unique_tokens_per_s": round(N / (ms * 1e-3), 1),
+                "tree_kernels_ms": round(tree_ms, 2),
+                "dense_and_torch_ms": round(ms - tree_ms, 2)}
+    except Exception as exc:
+        return {"error": repr(exc)}
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     a = parse()
@@ -331,6 +443,9 @@ def main():
                     "expanded_rows": int(ei["n_packed"])}
         del efo, ebo, dOe
 
+    attention = measure_attention(a.attn_steps) if a.attn_steps > 0 else None
+    hybrid = measure_hybrid(a.hybrid_steps) if a.hybrid_steps > 0 else None
+
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "unique tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
@@ -349,6 +464,7 @@ def main():
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "plan_host_ms": round(plan_host_ms, 3), "plan_upload_ms": round(upload_ms, 3),
         "expanded": expanded, "kernels": kernels, "finite": ok,
+        "tree_attention": attention, "hybrid_group": hybrid,
     }
     print(json.dumps(out), flush=True)
 
