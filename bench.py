@@ -123,6 +123,7 @@ def kernel_bytes(name, info, H, D, in_bytes=2):
     B = info["chunk"]
     f = 4
     st = D * D * f                        # one state of one head
+    st16 = D * D * 2                      # the fp16 copies kept per chunk
     fimg, bimg = image_bytes(B, D, in_bytes)
     if name == "kda_chunk_decay":
         # reads q, k, v, g, beta; writes both chunk images
@@ -130,19 +131,19 @@ def kernel_bytes(name, info, H, D, in_bytes=2):
     if name == "kda_fwd_round":
         # reads the forward images; writes o (unique rows), the start state of
         # every chunk, handoff and leaf states
-        return (C * H * fimg + Nrow * H * D * f + C * H * st
+        return (C * H * fimg + Nrow * H * D * f + C * H * st16
                 + (info["n_buf"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_round":
         # reads the reverse images, packed dO, leaf-state gradients; writes dy,
         # the end-state gradient of every chunk, sequence start gradients
-        return (C * H * bimg + P * H * D * (in_bytes + f) + C * H * st
+        return (C * H * bimg + P * H * D * (in_bytes + f) + C * H * st16
                 + (info["n_seq"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_chunk_grad":
         # reads q, k, g, beta, dy, packed dO, A / Td / V of the forward image,
         # the start state and end-state gradient of every chunk; writes dq, dk,
         # dv, dg, dbeta
         return (P * H * (2 * D * in_bytes + D * f + f + D * f + D * in_bytes + 4 * D * f + f)
-                + C * H * ((B * (B + 8) + B * 24) * 2 + B * D * in_bytes + 2 * st))
+                + C * H * ((B * (B + 8) + B * 24) * 2 + B * D * in_bytes + 2 * st16))
     if name == "kda_bwd_gather_dO":
         return Nrow * H * D * in_bytes + P * H * D * in_bytes
     return None

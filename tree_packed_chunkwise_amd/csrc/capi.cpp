@@ -96,11 +96,11 @@ kda::DevPlan make_dev_plan(const kda::Plan& p, const void* dev) {
   return v;
 }
 
-// saved = [chunk start states | handoff states | forward chunk images |
+// saved = [chunk start states (fp16) | handoff states | forward chunk images |
 //          reverse chunk images]  (image layouts in common.h; the forward
 //          image reserves fp32 space for V whatever the input dtype)
 struct SavedView {
-  float* chunk_h;
+  _Float16* chunk_h;
   float* bufs;
   unsigned char* fimg;
   unsigned char* bimg;
@@ -109,7 +109,7 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
   Carver c(base);
   SavedView s;
   const size_t st = (size_t)H * D * D;
-  s.chunk_h = c.take((size_t)p.n_chunks() * st);
+  s.chunk_h = (_Float16*)c.take((size_t)p.n_chunks() * st / 2);
   s.bufs = c.take((size_t)p.n_buf() * st);
   const size_t nb = (size_t)p.n_chunks() * H;
   s.fimg = (unsigned char*)c.take(nb * kda::fwd_image_bytes(p.B, D) / 4);
@@ -119,9 +119,10 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
 }
 
 // bwd workspace = [dO in packed order (sized for fp32) | dy | chunk end-state
-//                  gradients | sequence start gradients | replay-row gradients]
+//                  gradients (fp16) | sequence start gradients | replay-row gradients]
 struct BwdWS {
-  float *dOp, *dy, *dhc, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
+  float *dOp, *dy, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
+  _Float16* dhc;
 };
 BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
@@ -129,7 +130,7 @@ BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) 
   const size_t nb = (size_t)p.n_chunks() * H;
   w.dOp = c.take((size_t)p.n_packed * H * D);
   w.dy = c.take((size_t)p.n_packed * H * D);
-  w.dhc = c.take(nb * D * D);
+  w.dhc = (_Float16*)c.take(nb * D * D / 2);
   w.slot = c.take((size_t)p.n_seq() * H * D * D);
   const size_t nrep = (size_t)p.R;
   w.rep_dq = c.take(nrep * H * D);

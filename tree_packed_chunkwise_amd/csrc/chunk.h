@@ -77,6 +77,32 @@ __device__ inline float row_sum16(float x) {
   return x;
 }
 
+// Sums of 16 values over the 16 lanes of a row at once: a butterfly of DPP
+// moves (row mirror, half-row mirror, quad swaps) in which each step keeps
+// half of the values and sends the other half to the partner lane.  Lane l
+// of the row returns sum over the row's lanes of x[l].
+__device__ inline float row_reduce16x16(const float (&x)[16]) {
+  const int i = threadIdx.x & 15;
+  float y8[8], y4[4], y2[2];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const bool hi = i & 8;
+    y8[n] = (hi ? x[8 + n] : x[n]) + dpp_mov<0x140>(hi ? x[n] : x[8 + n]);
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const bool hi = i & 4;
+    y4[n] = (hi ? y8[4 + n] : y8[n]) + dpp_mov<0x141>(hi ? y8[n] : y8[4 + n]);
+  }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const bool hi = i & 2;
+    y2[n] = (hi ? y4[2 + n] : y4[n]) + dpp_mov<0x4E>(hi ? y4[n] : y4[2 + n]);
+  }
+  const bool hi = i & 1;
+  return (hi ? y2[1] : y2[0]) + dpp_mov<0xB1>(hi ? y2[0] : y2[1]);
+}
+
 // B fragment from two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k step)
 __device__ inline f16x8 acc_pair(const f32x4& t0, const f32x4& t1) {
   f16x8 r;

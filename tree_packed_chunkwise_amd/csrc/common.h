@@ -83,7 +83,7 @@ struct FwdArgs {
   const float* h0;     // may be null
   float* o;
   float* h_leaf;
-  float* chunk_h;      // [n_chunks,H,D,D]
+  _Float16* chunk_h;   // [n_chunks,H,D,D] start state of every chunk (fp16 copy)
   float* bufs;         // [n_buf,H,D,D]
   unsigned char* fimg; // [n_chunks,H] forward images, stride fwd_image_bytes
   unsigned char* bimg; // [n_chunks,H] backward images, stride bwd_image_bytes
@@ -98,7 +98,7 @@ struct BwdArgs {
   const void* v;
   const float* g;
   const float* beta;
-  const float* chunk_h;   // saved start state per chunk [n_chunks,H,D,D]
+  const _Float16* chunk_h; // saved start state per chunk [n_chunks,H,D,D] (fp16 copy)
   const unsigned char* fimg;  // forward images (read: A, Td, V)
   const unsigned char* bimg;  // backward images
   const void* dO;
@@ -112,7 +112,7 @@ struct BwdArgs {
   float* dh_boundary;     // may be null
   void* dOp;              // [n_packed,H,D] dO in packed row order, zero on replay rows
   float* dy;              // [n_packed,H,D]
-  float* dhc;             // [n_chunks,H,D,D] gradient of each chunk's end state
+  _Float16* dhc;          // [n_chunks,H,D,D] gradient of each chunk's end state (fp16 copy)
   float* slot;            // [n_seq,H,D,D] gradient of each sequence's start state
   float* rep_dq;          // [n_replay,H,D] gradients of replayed rows
   float* rep_dk;

@@ -112,11 +112,11 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         }
       }
       {
-        float* dst = a.dhc + blk * DD;
+        _Float16* dst = a.dhc + blk * DD;  // fp16 copy for the chunk-local pass
 #pragma unroll
         for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = dh[C][r];
+          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = (_Float16)dh[C][r];
       }
       f16x8 dhb[KD];
 #pragma unroll

@@ -94,12 +94,13 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
     // ---- state phase: wave w < NV owns column block w of the slice ----
     if (sw) {
       const float sc = a.scale;
-      {  // start state of the chunk, kept for the reverse pass
-        float* dst = a.chunk_h + blk * DD;
+      {  // start state of the chunk, kept for the reverse pass (fp16: its only
+         // consumers feed it to fp16 matrix cores)
+        _Float16* dst = a.chunk_h + blk * DD;
 #pragma unroll
         for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = hs[C][r];
+          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = (_Float16)hs[C][r];
       }
       f16x8 hb[KD];
 #pragma unroll

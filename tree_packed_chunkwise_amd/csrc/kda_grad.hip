@@ -195,15 +195,15 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
   const int col = 16 * wave + l16;
   f32x4 hC[NCB], dhC[NCB], dyv[NB];
   if (vw) {
-    const float* hsrc = a.chunk_h + blk * DD;
-    const float* dhsrc = a.dhc + blk * DD;
+    const _Float16* hsrc = a.chunk_h + blk * DD;
+    const _Float16* dhsrc = a.dhc + blk * DD;
 #pragma unroll
     for (int C = 0; C < NCB; ++C)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const size_t o = (size_t)(16 * C + 4 * g + r) * D + col;
-        hC[C][r] = hsrc[o];
-        dhC[C][r] = dhsrc[o];
+        hC[C][r] = (float)hsrc[o];
+        dhC[C][r] = (float)dhsrc[o];
       }
 #pragma unroll
     for (int J = 0; J < NB; ++J)
@@ -310,14 +310,16 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
     }
   }
   if (vw) {
-    // deGC partial over this wave's 16 columns (lanes of equal g)
+    // deGC partial over this wave's 16 columns (lanes of equal g): channel
+    // 16 C + 4 g + r, 16 channels per butterfly (C in groups of four)
 #pragma unroll
-    for (int C = 0; C < NCB; ++C)
+    for (int C0 = 0; C0 < NCB; C0 += 4) {
+      float x[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = row_sum16(hC[C][r] * dhC[C][r]);
-        if (l16 == 0) s.redg[wave][16 * C + 4 * g + r] = x;
-      }
+      for (int n = 0; n < 16; ++n) x[n] = hC[C0 + n / 4][n % 4] * dhC[C0 + n / 4][n % 4];
+      const float y = row_reduce16x16(x);
+      s.redg[wave][16 * (C0 + l16 / 4) + 4 * g + l16 % 4] = y;
+    }
     // delta by block forward substitution with the diagonal inverses
     f32x4 d[NB];
 #pragma unroll
@@ -338,6 +340,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
     f16x8 db[KB];
 #pragma unroll
     for (int ks = 0; ks < KB; ++ks) db[ks] = HALF ? acc_half(d[0]) : acc_pair(d[2 * ks], d[2 * ks + 1]);
+    float ye[NB][4];  // dy * e
     // e = Z - A delta;  dbeta partial = sum over the columns of dy * e;  dV = beta dy
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
@@ -354,12 +357,26 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
         const float dy = dyv[I][r], b = s.beta[i];
-        const float x = row_sum16(dy * e[r]);
-        if (l16 == 0) s.redb[wave][i] = x;
+        ye[I][r] = dy * e[r];
         if (i < len) grad_dst(a, a.dv, a.rep_dv, rep0, s.orow[i], i, nrep, h, D)[col] = b * dy;
         s.u.p.nZ[i][col] = (_Float16)(-b * dy);
         s.u.p.dl[i][col] = (_Float16)d[I][r];
       }
+    }
+    // dbeta partial over this wave's 16 columns: row 16 I + 4 g + r
+    if constexpr (NB == 4) {
+      float x[16];
+#pragma unroll
+      for (int n = 0; n < 16; ++n) x[n] = ye[n / 4][n % 4];
+      s.redb[wave][16 * (l16 / 4) + 4 * g + l16 % 4] = row_reduce16x16(x);
+    } else {
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = row_sum16(ye[I][r]);
+          if (l16 == 0) s.redb[wave][16 * I + 4 * g + r] = x;
+        }
     }
   }
   __syncthreads();
