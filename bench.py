@@ -105,11 +105,11 @@ def measured_traffic(kernel, workload):
 
 
 def image_bytes(B, D, in_bytes):
-    """(forward image as used, reverse image) bytes of one chunk-head: the
-    padded fp16 LDS images of a chunk step (layouts in csrc/common.h)."""
+    """(image head, image as used) bytes of one chunk-head: the padded fp16
+    LDS image of a chunk step (layout in csrc/chunk.h); the head is
+    everything but V."""
     head = 2 * (2 * B * (D + 8) + D * (B + 8) + 2 * B * (B + 8) + B * 24) + 4 * D + 8 * B
-    bwd = 2 * (B * (D + 8) + 2 * D * (B + 8) + 2 * B * (B + 8) + B * 24) + 4 * D + 4 * B
-    return head + in_bytes * B * D, bwd
+    return head, head + in_bytes * B * D
 
 
 def kernel_bytes(name, info, H, D, in_bytes=2):
@@ -124,22 +124,22 @@ def kernel_bytes(name, info, H, D, in_bytes=2):
     f = 4
     st = D * D * f                        # one state of one head
     st16 = D * D * 2                      # the fp16 copies kept per chunk
-    fimg, bimg = image_bytes(B, D, in_bytes)
+    head, fimg = image_bytes(B, D, in_bytes)
     if name == "kda_chunk_decay":
-        # reads q, k, v, g, beta; writes both chunk images
-        return P * H * (3 * D * in_bytes + D * f + f) + C * H * (fimg + bimg)
+        # reads q, k, v, g, beta; writes the chunk images
+        return P * H * (3 * D * in_bytes + D * f + f) + C * H * fimg
     if name == "kda_fwd_round":
-        # reads the forward images; writes o (unique rows), the start state of
+        # reads the chunk images; writes o (unique rows), the start state of
         # every chunk, handoff and leaf states
         return (C * H * fimg + Nrow * H * D * f + C * H * st16
                 + (info["n_buf"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_round":
-        # reads the reverse images, packed dO, leaf-state gradients; writes dy,
+        # reads the image heads, packed dO, leaf-state gradients; writes dy,
         # the end-state gradient of every chunk, sequence start gradients
-        return (C * H * bimg + P * H * D * (in_bytes + f) + C * H * st16
+        return (C * H * head + P * H * D * (in_bytes + f) + C * H * st16
                 + (info["n_seq"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_chunk_grad":
-        # reads q, k, g, beta, dy, packed dO, A / Td / V of the forward image,
+        # reads q, k, g, beta, dy, packed dO, A / Td / V of the chunk image,
         # the start state and end-state gradient of every chunk; writes dq, dk,
         # dv, dg, dbeta
         return (P * H * (2 * D * in_bytes + D * f + f + D * f + D * in_bytes + 4 * D * f + f)

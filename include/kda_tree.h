@@ -157,9 +157,10 @@ int64_t kda_plan_device_offset(const kda_plan* plan, int32_t field);
 
 /*
  * Buffer sizes for kda_tree_fwd / kda_tree_bwd at head count H and head dims
- * dk, dv.  `saved` is written by the forward and read by the backward (the
- * start state of every chunk and every handoff state, fp32); `ws` is scratch
- * (any content on entry).  Both are in bytes; 0 for an unsupported shape.
+ * dk, dv.  `saved` is written by the forward and read by the backward (an
+ * fp16 copy of every chunk's start state, every handoff state in fp32, and
+ * each chunk's state-independent operands); `ws` is scratch (any content on
+ * entry).  Both are in bytes; 0 for an unsupported shape.
  */
 size_t kda_saved_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv);
 size_t kda_fwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int32_t dv);

@@ -96,14 +96,13 @@ kda::DevPlan make_dev_plan(const kda::Plan& p, const void* dev) {
   return v;
 }
 
-// saved = [chunk start states (fp16) | handoff states | forward chunk images |
-//          reverse chunk images]  (image layouts in common.h; the forward
-//          image reserves fp32 space for V whatever the input dtype)
+// saved = [chunk start states (fp16) | handoff states | chunk images]
+//         (image layout in chunk.h; the image reserves fp32 space for V
+//         whatever the input dtype)
 struct SavedView {
   _Float16* chunk_h;
   float* bufs;
   unsigned char* fimg;
-  unsigned char* bimg;
 };
 SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
@@ -113,7 +112,6 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
   s.bufs = c.take((size_t)p.n_buf() * st);
   const size_t nb = (size_t)p.n_chunks() * H;
   s.fimg = (unsigned char*)c.take(nb * kda::fwd_image_bytes(p.B, D) / 4);
-  s.bimg = (unsigned char*)c.take(nb * kda::bwd_image_bytes(p.B, D) / 4);
   if (total) *total = c.off;
   return s;
 }
@@ -340,7 +338,6 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.chunk_h = sv.chunk_h;
   a.bufs = sv.bufs;
   a.fimg = sv.fimg;
-  a.bimg = sv.bimg;
   hipError_t e = kda::launch_fwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
                                  p.round_seq_ptr.data(), p.n_rounds, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_fwd launch");
@@ -375,7 +372,6 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.chunk_h = sv.chunk_h;
   a.fimg = sv.fimg;
-  a.bimg = sv.bimg;
   a.dO = dO;
   a.dh_leaf = dh_leaf;
   a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;

@@ -135,6 +135,36 @@ __device__ inline f16x8 lds_a_perm(const _Float16* base, int pitch, int row, int
   return r;
 }
 
+// Fragments of X^T from a 16-bit row-major LDS array X[*][pitch] with the
+// transposing read ds_read_b64_tr_b16: within each 16-lane group, lane l gets
+// element l % 4 of the 8-byte chunk addressed by lane 4 e + l / 4, e = 0..3.
+// If lane s of group g addresses X[r0 + 4 g + s / 4][c0 + 4 (s % 4)], lane
+// (l16, g) receives X[r0 + 4 g + e][c0 + l16]: the 16x16x16 fragment of X^T
+// with rows c0 .. c0+15 and k = r0 + 4 g + e.  c0 and the pitch are multiples
+// of 4 halves (8-byte aligned chunks).
+__device__ inline f16x4 lds_tr4(const _Float16* X, int pitch, int r0, int c0) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
+  const _Float16* p = X + (r0 + 4 * g + (s >> 2)) * pitch + c0 + 4 * (s & 3);
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(f16x4, v);
+}
+// 32-deep A fragment of X^T in register k order (rows c0 + l16 of X^T, k =
+// r0 + {4g..4g+3, 16+4g..16+4g+3}); `half_only` zeroes the second half.
+__device__ inline f16x8 lds_a_perm_tr(const _Float16* X, int pitch, int r0, int c0,
+                                      bool half_only = false) {
+  const f16x4 lo = lds_tr4(X, pitch, r0, c0);
+  f16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  if (half_only) {
+    r[4] = r[5] = r[6] = r[7] = (_Float16)0.f;
+  } else {
+    const f16x4 hi = lds_tr4(X, pitch, r0 + 16, c0);
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  }
+  return r;
+}
+
 template <int BC, int D>
 struct Geom {
   static constexpr int NB = BC / 16;               // 16-row blocks of a chunk
@@ -171,22 +201,9 @@ template <int BC, int D, typename VT>
 struct FwdImage : FwdHead<BC, D> {
   VT V[BC][D];
 };
-template <int BC, int D>
-struct BwdImage {
-  _Float16 KhA[BC][D + 8];
-  _Float16 QtT[D][BC + 8];
-  _Float16 KnT[D][BC + 8];
-  _Float16 PT[BC][BC + 8];
-  _Float16 AT[BC][BC + 8];
-  _Float16 TdT[BC][24];
-  float gc[D];
-  float beta[BC];
-};
 static_assert(sizeof(FwdImage<64, 128, float>) == fwd_image_bytes(64, 128), "image layout");
 static_assert(sizeof(FwdImage<16, 64, uint16_t>) == fwd_image_used(16, 64, 2), "image layout");
 static_assert(sizeof(FwdHead<64, 128>) == fwd_image_head_bytes(64, 128), "image layout");
-static_assert(sizeof(BwdImage<64, 128>) == bwd_image_bytes(64, 128), "image layout");
-static_assert(sizeof(BwdImage<16, 64>) == bwd_image_bytes(16, 64), "image layout");
 
 // Asynchronous copy of `nvec` 16-byte vectors from global memory into LDS
 // (global_load_lds_dwordx4: the data goes straight to LDS, no registers).

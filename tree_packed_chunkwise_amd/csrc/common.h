@@ -65,11 +65,6 @@ constexpr __host__ __device__ size_t fwd_image_bytes(int BC, int D) {
 constexpr __host__ __device__ size_t fwd_image_used(int BC, int D, int elem) {
   return fwd_image_head_bytes(BC, D) + (size_t)elem * BC * D;
 }
-constexpr __host__ __device__ size_t bwd_image_bytes(int BC, int D) {
-  return (size_t)2 * ((size_t)BC * (D + 8) + 2 * (size_t)D * (BC + 8) + 2 * (size_t)BC * (BC + 8) +
-                      (size_t)BC * 24) +
-         4 * (size_t)D + 4 * (size_t)BC;
-}
 
 struct FwdArgs {
   DevPlan plan;
@@ -85,8 +80,7 @@ struct FwdArgs {
   float* h_leaf;
   _Float16* chunk_h;   // [n_chunks,H,D,D] start state of every chunk (fp16 copy)
   float* bufs;         // [n_buf,H,D,D]
-  unsigned char* fimg; // [n_chunks,H] forward images, stride fwd_image_bytes
-  unsigned char* bimg; // [n_chunks,H] backward images, stride bwd_image_bytes
+  unsigned char* fimg; // [n_chunks,H] chunk images, stride fwd_image_bytes
 };
 
 struct BwdArgs {
@@ -99,8 +93,7 @@ struct BwdArgs {
   const float* g;
   const float* beta;
   const _Float16* chunk_h; // saved start state per chunk [n_chunks,H,D,D] (fp16 copy)
-  const unsigned char* fimg;  // forward images (read: A, Td, V)
-  const unsigned char* bimg;  // backward images
+  const unsigned char* fimg;  // chunk images (the round reads the head, the gradient pass A, Td, V)
   const void* dO;
   const float* dh_leaf;   // may be null
   float* dq;

@@ -4,10 +4,12 @@
 // One block per (sequence, head, dv slice) of the round, rounds in reverse
 // order; the block walks its sequence's chunks backwards carrying dh, the
 // gradient of the state at the current chunk end (it starts from the leaf
-// state's gradient).  Per chunk it copies the chunk's reverse image (written
-// by the chunk-parallel pass, kda_prep.hip: k e^(Gam_C - Gam),
-// scale (q e^Gam)^T, -(k e^Gam)^T, scale P^T, A^T, Td^T, e^Gam_C, beta) into
-// LDS and runs:
+// state's gradient).  Per chunk it copies the head of the chunk's forward
+// image (written by the chunk-parallel pass, kda_prep.hip: q e^Gam,
+// -k e^Gam, (k e^(Gam_C - Gam))^T, A, P, Td, e^Gam_C, beta) into LDS; each
+// transposed operand below is read from it with the transposing LDS read
+// (lds_a_perm_tr / lds_tr4 in chunk.h), and the scale is folded into dO.
+// Then:
 //   at a handoff chunk end: dh += start gradients of every sequence that
 //        started from that state (later rounds, already final); the total is
 //        the handoff state's gradient (HARTS abstract: differentiable
@@ -29,7 +31,7 @@ namespace kda {
 template <typename TIn, int BC, int D, int NV>
 __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   using G = Geom<BC, D>;
-  using BI = BwdImage<BC, D>;
+  using BI = FwdHead<BC, D>;
   static_assert(NV <= NW, "one column block per wave");
   constexpr int KD = D / 32;
   constexpr int KB = (BC + 31) / 32;
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   const size_t DD = (size_t)D * D;
   const int cbeg = a.plan.seq_chunk_ptr[seq];
   const int cend = a.plan.seq_chunk_ptr[seq + 1];
-  auto image = [&](int cc) { return a.bimg + ((size_t)cc * H + h) * bwd_image_bytes(BC, D); };
+  auto image = [&](int cc) { return a.fimg + ((size_t)cc * H + h) * fwd_image_bytes(BC, D); };
 
   f32x4 dh[G::NCB];
   {
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
     for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dob[ks][e] = (_Float16)ld_in(&dor[ks][0], e);
+      for (int e = 0; e < 8; ++e) dob[ks][e] = (_Float16)(a.scale * ld_in(&dor[ks][0], e));
     if (c > cbeg) {
       lds_copy_async(&buf[(cend - c) & 1], image(c - 1), NVEC);
       load_do(c - 1);
@@ -129,10 +131,10 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
         for (int ks = 0; ks < KB; ++ks)
           if (32 * ks + 31 >= 16 * J)
-            dd[J] = mfma16(lds_a_perm(&s.PT[0][0], G::PB, 16 * J + l16, 32 * ks, g, HALF), dob[ks], dd[J]);
+            dd[J] = mfma16(lds_a_perm_tr(&s.P[0][0], G::PB, 32 * ks, 16 * J, HALF), dob[ks], dd[J]);
 #pragma unroll
         for (int ks = 0; ks < KD; ++ks)
-          dd[J] = mfma16(lds_a_perm(&s.KhA[0][0], G::PD, 16 * J + l16, 32 * ks, g), dhb[ks], dd[J]);
+          dd[J] = mfma16(lds_a_perm_tr(&s.KhT[0][0], G::PB, 32 * ks, 16 * J), dhb[ks], dd[J]);
       }
       // (I + diag(beta) A)^T dy = ddelta, from the last block up:
       // dy_I = Td_I^T (ddelta_I - sum_{J>I} A_JI^T diag(beta_J) dy_J)
@@ -142,12 +144,12 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         f32x4 rr = dd[I];
 #pragma unroll
         for (int J = G::NB - 1; J > I; --J) {
-          f16x4 la = *(const f16x4*)&s.AT[16 * I + l16][16 * J + 4 * g];
+          f16x4 la = lds_tr4(&s.L[0][0], G::PB, 16 * J, 16 * I);  // block (I, J) of A^T
 #pragma unroll
           for (int e = 0; e < 4; ++e) la[e] = -la[e];
           rr = mfma16k16(la, acc4(w[J]), rr);
         }
-        const f32x4 dy = mfma16k16(*(const f16x4*)&s.TdT[16 * I + l16][4 * g], acc4(rr),
+        const f32x4 dy = mfma16k16(lds_tr4(&s.Td[0][0], 24, 16 * I, 0), acc4(rr),
                                    (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -166,8 +168,8 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         for (int r = 0; r < 4; ++r) dh[C][r] *= s.gc[16 * C + 4 * g + r];
 #pragma unroll
         for (int ks = 0; ks < KB; ++ks) {
-          dh[C] = mfma16(lds_a_perm(&s.QtT[0][0], G::PB, 16 * C + l16, 32 * ks, g, HALF), dob[ks], dh[C]);
-          dh[C] = mfma16(lds_a_perm(&s.KnT[0][0], G::PB, 16 * C + l16, 32 * ks, g, HALF), wb[ks], dh[C]);
+          dh[C] = mfma16(lds_a_perm_tr(&s.Qt[0][0], G::PD, 32 * ks, 16 * C, HALF), dob[ks], dh[C]);
+          dh[C] = mfma16(lds_a_perm_tr(&s.Kn[0][0], G::PD, 32 * ks, 16 * C, HALF), wb[ks], dh[C]);
         }
       }
     }

@@ -10,8 +10,9 @@
 //   P_ij  = sum_c q_ic k_jc e^(Gam_ic - Gam_jc)   (j <= i)
 //   Td_I  = (I + diag(beta_I) A_II)^-1 for every 16-row diagonal block I
 // and the decayed operands q e^Gam, k e^Gam, k e^(Gam_C - Gam).  Everything
-// is written as the two chunk images (layouts in common.h): the LDS image of
-// a forward chunk step and that of a reverse chunk step, so that the round
+// is written as one chunk image (layout in chunk.h): the LDS image of a
+// forward chunk step, whose head the reverse chunk step reads as well (its
+// transposed operands come from transposing LDS reads), so that the round
 // kernels' sequential chain only copies an image and runs the state phase.
 // The state-dependent passes solve (I + diag(beta) A) delta = diag(beta) Z
 // (and its transpose) block by block with Td; the full inverse is never
@@ -43,7 +44,6 @@ template <typename TIn, int BC, int D>
 __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
   using G = Geom<BC, D>;
   using FI = FwdImage<BC, D, TIn>;
-  using BI = BwdImage<BC, D>;
   constexpr int NE = G::RPT * G::NHALF;
   __shared__ PrepSmem<BC, D> s;
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -52,7 +52,6 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
   const int row0 = a.plan.chunk_row0[c];
   const int len = a.plan.chunk_len[c];
   const int nrep = a.plan.chunk_nrep[c];
-  const float sc = a.scale;
   if (tid < BC) {
     const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
     s.tb.row[tid] = r;
@@ -77,14 +76,13 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
   }
   chunk_AP<BC, D>(s.tb, er, s.ap, &s.A[0][0], G::PB, &s.P[0][0], G::PB);
   FI* F = (FI*)(a.fimg + blk * fwd_image_bytes(BC, D));
-  BI* Bm = (BI*)(a.bimg + blk * bwd_image_bytes(BC, D));
 
   // decayed operands from the element mapping (channel c0 + 64 hf, rows r0..)
 #pragma unroll
   for (int hf = 0; hf < G::NHALF; ++hf) {
     const int cc = c0 + G::DH * hf;
     const float gcl = s.tb.gcl[cc];
-    _Float16 kht[G::RPT], qtt[G::RPT], knt[G::RPT];
+    _Float16 kht[G::RPT];
 #pragma unroll
     for (int t = 0; t < G::RPT; ++t) {
       const int n = hf * G::RPT + t, i = r0 + t;
@@ -93,50 +91,28 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
       F->Qt[i][cc] = (_Float16)(er.q[n] * e1);
       F->Kn[i][cc] = (_Float16)(-er.k[n] * e1);
       F->V[i][cc] = to_in<TIn>(vv[n]);
-      Bm->KhA[i][cc] = (_Float16)(er.k[n] * e2);
       kht[t] = (_Float16)(er.k[n] * e2);
-      qtt[t] = (_Float16)(sc * er.q[n] * e1);
-      knt[t] = (_Float16)(-er.k[n] * e1);
     }
     if constexpr (G::RPT == 8) {
-      f16x8 x, y, z;
+      f16x8 x;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) { x[t] = kht[t]; y[t] = qtt[t]; z[t] = knt[t]; }
+      for (int t = 0; t < 8; ++t) x[t] = kht[t];
       *(f16x8*)&F->KhT[cc][r0] = x;
-      *(f16x8*)&Bm->QtT[cc][r0] = y;
-      *(f16x8*)&Bm->KnT[cc][r0] = z;
     } else {
 #pragma unroll
-      for (int t = 0; t < G::RPT; ++t) {
-        F->KhT[cc][r0 + t] = kht[t];
-        Bm->QtT[cc][r0 + t] = qtt[t];
-        Bm->KnT[cc][r0 + t] = knt[t];
-      }
+      for (int t = 0; t < G::RPT; ++t) F->KhT[cc][r0 + t] = kht[t];
     }
   }
-  if (tid < D) {
-    F->gc[tid] = s.tb.gc[tid];
-    Bm->gc[tid] = s.tb.gc[tid];
-  }
+  if (tid < D) F->gc[tid] = s.tb.gc[tid];
   if (tid < BC) {
     F->beta[tid] = s.tb.beta[tid];
-    Bm->beta[tid] = s.tb.beta[tid];
     F->orow[tid] = s.tb.orow[tid];
   }
-  // A and P as they are (same pitch), and transposed for the reverse pass
+  // A and P as they are (same pitch)
   for (int e = tid; e < BC * BC / 8; e += NT) {
     const int i = e / (BC / 8), j0 = (e % (BC / 8)) * 8;
     *(f16x8*)&F->L[i][j0] = *(const f16x8*)&s.A[i][j0];
     *(f16x8*)&F->P[i][j0] = *(const f16x8*)&s.P[i][j0];
-    // row j = i of the transposes, columns j0 .. j0+7
-    f16x8 at, pt;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      at[m] = s.A[j0 + m][i];
-      pt[m] = (_Float16)(sc * (float)s.P[j0 + m][i]);
-    }
-    *(f16x8*)&Bm->AT[i][j0] = at;
-    *(f16x8*)&Bm->PT[i][j0] = pt;
   }
   // diagonal inverses: one lane per (block, column), forward substitution
   if (tid < 16 * G::NB) {
@@ -152,15 +128,8 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
       for (int m = 0; m < i; ++m) acc -= bi * (float)(m < 8 ? a0[m] : a1[m - 8]) * x[m];
       x[i] = (i >= j) ? acc : 0.f;
     }
-    f16x8 lo, hi;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const _Float16 v16 = (_Float16)x[i];
-      F->Td[b0 + i][j] = v16;
-      if (i < 8) lo[i] = v16; else hi[i - 8] = v16;
-    }
-    *(f16x8*)&Bm->TdT[b0 + j][0] = lo;
-    *(f16x8*)&Bm->TdT[b0 + j][8] = hi;
+    for (int i = 0; i < 16; ++i) F->Td[b0 + i][j] = (_Float16)x[i];
   }
 }
 
