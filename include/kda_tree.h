@@ -22,7 +22,9 @@
  *   - All device memory is owned by the caller.  Tensors are contiguous,
  *     row-major, with the row (token) dimension first: q,k [rows,H,dk];
  *     v [rows,H,dv]; g [rows,H,dk] fp32; beta [rows,H] fp32; o [rows,H,dv]
- *     fp32; states [*,H,dk,dv] fp32.
+ *     fp32; states [*,H,dk,dv] fp32.  Every device pointer (tensors,
+ *     `saved`, `ws`) is 16-byte aligned (KDA_ERR_ARG otherwise): rows move
+ *     in 16-byte vectors.
  *   - The library never allocates device memory and never synchronises the
  *     device.  Work is enqueued on `stream` (a hipStream_t; NULL = default
  *     stream) in stream order.

@@ -4,6 +4,7 @@
 // the computation runs in the HIP kernels (kda_prep.hip, kda_fwd.hip,
 // kda_bwd.hip, kda_grad.hip, kda_reduce.hip, attn.hip, gather.hip), enqueued
 // on the caller's stream.
+#include <initializer_list>
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -138,6 +139,13 @@ BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) 
   w.rep_db = c.take(nrep * H);
   if (total) *total = c.off;
   return w;
+}
+
+// kernels move tensor rows in 16-byte vectors
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (((uintptr_t)p) % 16) return false;
+  return true;
 }
 
 int check_dev_plan(const kda_plan* plan, const void* dev_plan) {
@@ -325,6 +333,8 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
     return fail(KDA_ERR_SHAPE, "in_dtype must be KDA_DTYPE_BF16 or KDA_DTYPE_FP32");
   if (!q || !k || !v || !g || !beta || !o || !h_leaf || !saved || !ws)
     return fail(KDA_ERR_ARG, "null tensor argument");
+  if (!aligned16({q, k, v, g, beta, h0, o, h_leaf, saved, ws}))
+    return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned");
   if (ws_bytes < kda_fwd_workspace_bytes(plan, H, dk, dv))
     return fail(KDA_ERR_WORKSPACE, "forward workspace too small");
   kda::FwdArgs a;
@@ -361,6 +371,8 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   if (!q || !k || !v || !g || !beta || !saved || !dO || !dq || !dk_ || !dv_ || !dg || !dbeta ||
       !dh0 || !ws)
     return fail(KDA_ERR_ARG, "null tensor argument");
+  if (!aligned16({q, k, v, g, beta, saved, dO, dh_leaf, dq, dk_, dv_, dg, dbeta, dh0, dh_boundary, ws}))
+    return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned");
   if (ws_bytes < kda_bwd_workspace_bytes(plan, H, dk, dv))
     return fail(KDA_ERR_WORKSPACE, "backward workspace too small");
   SavedView sv = carve_saved(p, H, dk, (void*)saved, nullptr);

@@ -103,6 +103,56 @@ __device__ inline float row_reduce16x16(const float (&x)[16]) {
   return (hi ? y2[1] : y2[0]) + dpp_mov<0xB1>(hi ? y2[0] : y2[1]);
 }
 
+// 4x4 transpose over the lanes of each DPP quad: afterwards lane 4a + b
+// holds in x[j] what lane 4a + j held in x[b].  Two exchange stages (lane
+// distance 2, then 1), each sending half of the values to the partner lane.
+//
+// Its use: an MFMA accumulator lane (l16 = 4a + b, g) holds rows R + 4g + r,
+// r = 0..3, of column c0 + l16; after the transpose it holds row R + 4g + b,
+// columns c0 + 4a .. c0 + 4a + 3, a contiguous piece of a row-major tile that
+// one vector load or store moves (quad_row / quad_col below).
+__device__ inline void quad_transpose(float (&x)[4]) {
+  const int b = threadIdx.x & 3;
+  {
+    const bool hi = b & 2;
+    const float r0 = dpp_mov<0x4E>(hi ? x[0] : x[2]);  // quad_perm [2,3,0,1]
+    const float r1 = dpp_mov<0x4E>(hi ? x[1] : x[3]);
+    if (hi) { x[0] = r0; x[1] = r1; } else { x[2] = r0; x[3] = r1; }
+  }
+  {
+    const bool odd = b & 1;
+    const float r0 = dpp_mov<0xB1>(odd ? x[0] : x[1]);  // quad_perm [1,0,3,2]
+    const float r1 = dpp_mov<0xB1>(odd ? x[2] : x[3]);
+    if (odd) { x[0] = r0; x[2] = r1; } else { x[1] = r0; x[3] = r1; }
+  }
+}
+__device__ inline void quad_transpose(f32x4& v) {
+  float x[4] = {v[0], v[1], v[2], v[3]};
+  quad_transpose(x);
+  v = (f32x4){x[0], x[1], x[2], x[3]};
+}
+// row offset (within a 16-row block) and column offset (within a 16-column
+// block) of this lane's piece after quad_transpose
+__device__ inline int quad_row() { return 4 * ((threadIdx.x & 63) >> 4) + (threadIdx.x & 3); }
+__device__ inline int quad_col() { return threadIdx.x & 12; }
+
+// four consecutive input elements (bf16 bits or fp32), one vector load
+template <typename TIn>
+using in4_t = TIn __attribute__((ext_vector_type(4)));
+__device__ inline f32x4 in4_to_f32(const in4_t<float>& v) { return v; }
+__device__ inline f32x4 in4_to_f32(const in4_t<uint16_t>& v) {
+  return (f32x4){__uint_as_float((unsigned)v[0] << 16), __uint_as_float((unsigned)v[1] << 16),
+                 __uint_as_float((unsigned)v[2] << 16), __uint_as_float((unsigned)v[3] << 16)};
+}
+// store four floats as fp16 (8 bytes) / load four fp16 as floats
+__device__ inline void st_h4(_Float16* p, const f32x4& v) {
+  *(f16x4*)p = (f16x4){(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+}
+__device__ inline f32x4 ld_h4(const _Float16* p) {
+  const f16x4 h = *(const f16x4*)p;
+  return (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
 // B fragment from two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k step)
 __device__ inline f16x8 acc_pair(const f32x4& t0, const f32x4& t1) {
   f16x8 r;

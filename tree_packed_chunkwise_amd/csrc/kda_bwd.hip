@@ -43,6 +43,8 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;
   const int col = 16 * (blockIdx.z * NV + wave) + l16;
+  const int cq = col - l16 + quad_col();     // first column of this lane's row piece
+  const int rq = quad_row();                 // its row within a 16-row block
   const int H = a.H;
   const TIn* dOp = (const TIn*)a.dOp;
   const size_t DD = (size_t)D * D;
@@ -59,18 +61,20 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       for (int r = 0; r < 4; ++r)
         dh[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
-  // dO of the chunk in flight, raw, in register k order (see chunk.h); packed
-  // dO is zero on replay rows
-  TIn dor[KB][8];
+  // dO of the chunk in flight, raw: this lane's row piece of the 16-row
+  // halves of every 32-deep k step (packed dO is zero on replay rows);
+  // quad_transpose turns it into register k order (chunk.h) when it is used
+  in4_t<TIn> dor[KB][2];
   auto load_do = [&](int cc) {
     const int r0c = a.plan.chunk_row0[cc], lenc = a.plan.chunk_len[cc];
 #pragma unroll
     for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 32 * ks + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-        dor[ks][e] = (TIn)0;
-        if (sw && i < BC && i < lenc) dor[ks][e] = dOp[((size_t)(r0c + i) * H + h) * D + col];
+      for (int hf = 0; hf < 2; ++hf) {
+        const int i = 32 * ks + 16 * hf + rq;
+        dor[ks][hf] = (in4_t<TIn>)0;
+        if (sw && i < BC && i < lenc)
+          dor[ks][hf] = *(const in4_t<TIn>*)&dOp[((size_t)(r0c + i) * H + h) * D + cq];
       }
   };
   if (cbeg < cend) {
@@ -84,17 +88,24 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
     __builtin_amdgcn_s_waitcnt(0);  // this chunk's image (and dO) have landed ...
     __syncthreads();                // ... for every wave; the other buffer is free
     const BI& s = buf[(cend - 1 - c) & 1];
-    f16x8 dob[KB];
+    f32x4 dof[KB][2];
 #pragma unroll
     for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dob[ks][e] = (_Float16)(a.scale * ld_in(&dor[ks][0], e));
+      for (int hf = 0; hf < 2; ++hf) dof[ks][hf] = a.scale * in4_to_f32(dor[ks][hf]);
     if (c > cbeg) {
       lds_copy_async(&buf[(cend - c) & 1], image(c - 1), NVEC);
       load_do(c - 1);
     }
 
     if (sw) {
+      f16x8 dob[KB];
+#pragma unroll
+      for (int ks = 0; ks < KB; ++ks) {
+        quad_transpose(dof[ks][0]);
+        quad_transpose(dof[ks][1]);
+        dob[ks] = acc_pair(dof[ks][0], dof[ks][1]);
+      }
       const int save = a.plan.chunk_save[c];
       if (save >= 0) {
         const int p0 = a.plan.buf_cons_ptr[save], p1 = a.plan.buf_cons_ptr[save + 1];
@@ -116,26 +127,68 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       {
         _Float16* dst = a.dhc + blk * DD;  // fp16 copy for the chunk-local pass
 #pragma unroll
-        for (int C = 0; C < G::NCB; ++C)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = (_Float16)dh[C][r];
+        for (int C = 0; C < G::NCB; ++C) {
+          f32x4 x = dh[C];
+          quad_transpose(x);
+          st_h4(dst + (size_t)(16 * C + rq) * D + cq, x);
+        }
       }
       f16x8 dhb[KD];
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) dhb[ks] = acc_pair(dh[2 * ks], dh[2 * ks + 1]);
+      // Every phase first issues all of its LDS fragment reads, then its
+      // MFMAs, so that the reads are in flight together.
       // ddelta = scale P^T dO + (K e^(Gam_C-Gam)) dh
+      f16x8 fa[G::NCB][KB > KD ? KB : KD];
+#pragma unroll
+      for (int J = 0; J < G::NB; ++J)
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) fa[J][ks] = lds_a_perm_tr(&s.KhT[0][0], G::PB, 32 * ks, 16 * J);
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 dd[G::NB];
 #pragma unroll
       for (int J = 0; J < G::NB; ++J) {
         dd[J] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks)
-          if (32 * ks + 31 >= 16 * J)
-            dd[J] = mfma16(lds_a_perm_tr(&s.P[0][0], G::PB, 32 * ks, 16 * J, HALF), dob[ks], dd[J]);
-#pragma unroll
-        for (int ks = 0; ks < KD; ++ks)
-          dd[J] = mfma16(lds_a_perm_tr(&s.KhT[0][0], G::PB, 32 * ks, 16 * J), dhb[ks], dd[J]);
+        for (int ks = 0; ks < KD; ++ks) dd[J] = mfma16(fa[J][ks], dhb[ks], dd[J]);
       }
+      // dh <- diag(e^Gam_C) dh + scale (Q e^Gam)^T dO (dhb holds the old dh)
+#pragma unroll
+      for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr(&s.Qt[0][0], G::PD, 32 * ks, 16 * C, HALF);
+      f32x4 gcv[G::NCB];
+#pragma unroll
+      for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gcv[C][r] = s.gc[16 * C + 4 * g + r];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int C = 0; C < G::NCB; ++C) {
+        dh[C] *= gcv[C];
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks) dh[C] = mfma16(fa[C][ks], dob[ks], dh[C]);
+      }
+      f16x8 fp[G::NB][KB];
+      f16x4 fl[G::NB][G::NB], ft[G::NB];
+      f32x4 bz[G::NB];
+#pragma unroll
+      for (int J = 0; J < G::NB; ++J) {
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks)
+          if (32 * ks + 31 >= 16 * J) fp[J][ks] = lds_a_perm_tr(&s.P[0][0], G::PB, 32 * ks, 16 * J, HALF);
+        ft[J] = lds_tr4(&s.Td[0][0], 24, 16 * J, 0);
+#pragma unroll
+        for (int I = 0; I < J; ++I) fl[I][J] = -lds_tr4(&s.L[0][0], G::PB, 16 * J, 16 * I);  // block (I, J) of A^T
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bz[J][r] = s.beta[16 * J + 4 * g + r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int J = 0; J < G::NB; ++J)
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks)
+          if (32 * ks + 31 >= 16 * J) dd[J] = mfma16(fp[J][ks], dob[ks], dd[J]);
       // (I + diag(beta) A)^T dy = ddelta, from the last block up:
       // dy_I = Td_I^T (ddelta_I - sum_{J>I} A_JI^T diag(beta_J) dy_J)
       f32x4 w[G::NB];
@@ -143,35 +196,25 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       for (int I = G::NB - 1; I >= 0; --I) {
         f32x4 rr = dd[I];
 #pragma unroll
-        for (int J = G::NB - 1; J > I; --J) {
-          f16x4 la = lds_tr4(&s.L[0][0], G::PB, 16 * J, 16 * I);  // block (I, J) of A^T
-#pragma unroll
-          for (int e = 0; e < 4; ++e) la[e] = -la[e];
-          rr = mfma16k16(la, acc4(w[J]), rr);
-        }
-        const f32x4 dy = mfma16k16(lds_tr4(&s.Td[0][0], 24, 16 * I, 0), acc4(rr),
-                                   (f32x4){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + 4 * g + r;
-          w[I][r] = dy[r] * s.beta[i];
-          if (i < len) a.dy[((size_t)(row0 + i) * H + h) * D + col] = dy[r];
-        }
+        for (int J = G::NB - 1; J > I; --J) rr = mfma16k16(fl[I][J], acc4(w[J]), rr);
+        f32x4 dy = mfma16k16(ft[I], acc4(rr), (f32x4){0.f, 0.f, 0.f, 0.f});
+        w[I] = dy * bz[I];
+        quad_transpose(dy);
+        if (16 * I + rq < len) *(f32x4*)&a.dy[((size_t)(row0 + 16 * I + rq) * H + h) * D + cq] = dy;
       }
       f16x8 wb[KB];
 #pragma unroll
       for (int ks = 0; ks < KB; ++ks) wb[ks] = HALF ? acc_half(w[0]) : acc_pair(w[2 * ks], w[2 * ks + 1]);
-      // dh <- diag(e^Gam_C) dh + scale (Q e^Gam)^T dO - (K e^Gam)^T diag(beta) dy
+      // dh -= (K e^Gam)^T diag(beta) dy
 #pragma unroll
-      for (int C = 0; C < G::NCB; ++C) {
+      for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dh[C][r] *= s.gc[16 * C + 4 * g + r];
+        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr(&s.Kn[0][0], G::PD, 32 * ks, 16 * C, HALF);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) {
-          dh[C] = mfma16(lds_a_perm_tr(&s.Qt[0][0], G::PD, 32 * ks, 16 * C, HALF), dob[ks], dh[C]);
-          dh[C] = mfma16(lds_a_perm_tr(&s.Kn[0][0], G::PD, 32 * ks, 16 * C, HALF), wb[ks], dh[C]);
-        }
-      }
+      for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks) dh[C] = mfma16(fa[C][ks], wb[ks], dh[C]);
     }
   }
   if (sw) {

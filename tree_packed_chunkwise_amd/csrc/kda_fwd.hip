@@ -43,6 +43,8 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;                 // this wave carries a column block of the state
   const int col = 16 * (blockIdx.z * NV + wave) + l16;
+  const int cq = col - l16 + quad_col();     // first column of this lane's row piece
+  const int rq = quad_row();                 // its row within a 16-row block
   const int H = a.H;
   const size_t DD = (size_t)D * D;
   const int cbeg = a.plan.seq_chunk_ptr[seq];
@@ -63,14 +65,15 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       for (int r = 0; r < 4; ++r)
         hs[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
-  // V of the chunk in flight, raw, for this lane's rows of column `col`
-  TIn vr[G::NB][4];
+  // V of the chunk in flight, raw: this lane's row piece of every 16-row
+  // block (one vector load each; quad_transpose turns it into the
+  // accumulator layout when it is used)
+  in4_t<TIn> vr[G::NB];
   auto load_v = [&](int cc) {
     const FI* F = (const FI*)image(cc);
 #pragma unroll
     for (int J = 0; J < G::NB; ++J)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vr[J][r] = sw ? F->V[16 * J + 4 * g + r][col] : (TIn)0;
+      vr[J] = sw ? *(const in4_t<TIn>*)&F->V[16 * J + rq][cq] : (in4_t<TIn>)0;
   };
   if (cbeg < cend) {
     lds_copy_async(&buf[0], image(cbeg), NVEC);
@@ -83,9 +86,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
     const FH& s = buf[(c - cbeg) & 1];
     f32x4 z[G::NB];
 #pragma unroll
-    for (int J = 0; J < G::NB; ++J)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) z[J][r] = ld_in(&vr[J][0], r);
+    for (int J = 0; J < G::NB; ++J) z[J] = in4_to_f32(vr[J]);
     if (c + 1 < cend) {
       lds_copy_async(&buf[(c - cbeg + 1) & 1], image(c + 1), NVEC);
       load_v(c + 1);
@@ -94,61 +95,97 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
     // ---- state phase: wave w < NV owns column block w of the slice ----
     if (sw) {
       const float sc = a.scale;
+#pragma unroll
+      for (int J = 0; J < G::NB; ++J) quad_transpose(z[J]);
       {  // start state of the chunk, kept for the reverse pass (fp16: its only
          // consumers feed it to fp16 matrix cores)
         _Float16* dst = a.chunk_h + blk * DD;
 #pragma unroll
-        for (int C = 0; C < G::NCB; ++C)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = (_Float16)hs[C][r];
+        for (int C = 0; C < G::NCB; ++C) {
+          f32x4 x = hs[C];
+          quad_transpose(x);
+          st_h4(dst + (size_t)(16 * C + rq) * D + cq, x);
+        }
       }
       f16x8 hb[KD];
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hs[2 * ks], hs[2 * ks + 1]);
+      // Every phase first issues all of its LDS fragment reads, then its
+      // MFMAs, so that the reads are in flight together.
       // Z = V - (K e^Gam) h
+      f16x8 fa[G::NB][KD];
 #pragma unroll
-      for (int J = 0; J < G::NB; ++J) {
+      for (int J = 0; J < G::NB; ++J)
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks)
-          z[J] = mfma16(lds_a_perm(&s.Kn[0][0], G::PD, 16 * J + l16, 32 * ks, g), hb[ks], z[J]);
+        for (int ks = 0; ks < KD; ++ks) fa[J][ks] = lds_a_perm(&s.Kn[0][0], G::PD, 16 * J + l16, 32 * ks, g);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+      for (int J = 0; J < G::NB; ++J)
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) z[J] = mfma16(fa[J][ks], hb[ks], z[J]);
+      // (Q e^Gam) h: independent of the solve below, so it overlaps it
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I)
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) fa[I][ks] = lds_a_perm(&s.Qt[0][0], G::PD, 16 * I + l16, 32 * ks, g);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 o[G::NB];
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I) {
+        o[I] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) o[I] = mfma16(fa[I][ks], hb[ks], o[I]);
       }
       // (I + diag(beta) A) delta = diag(beta) Z, block forward substitution with
       // the diagonal inverses: delta_I = Td_I diag(beta_I) (Z_I - sum_{J<I} A_IJ delta_J)
+      f16x4 fl[G::NB][G::NB], ft[G::NB];
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I) {
+        ft[I] = *(const f16x4*)&s.Td[16 * I + l16][4 * g];
+#pragma unroll
+        for (int J = 0; J < I; ++J) fl[I][J] = -*(const f16x4*)&s.L[16 * I + l16][16 * J + 4 * g];
+      }
+      f32x4 bz[G::NB];
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bz[I][r] = s.beta[16 * I + 4 * g + r];
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 d[G::NB];
 #pragma unroll
       for (int I = 0; I < G::NB; ++I) {
         f32x4 rr = z[I];
 #pragma unroll
-        for (int J = 0; J < I; ++J) {
-          f16x4 la = *(const f16x4*)&s.L[16 * I + l16][16 * J + 4 * g];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) la[e] = -la[e];
-          rr = mfma16k16(la, acc4(d[J]), rr);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rr[r] *= s.beta[16 * I + 4 * g + r];
-        d[I] = mfma16k16(*(const f16x4*)&s.Td[16 * I + l16][4 * g], acc4(rr),
-                         (f32x4){0.f, 0.f, 0.f, 0.f});
+        for (int J = 0; J < I; ++J) rr = mfma16k16(fl[I][J], acc4(d[J]), rr);
+        rr *= bz[I];
+        d[I] = mfma16k16(ft[I], acc4(rr), (f32x4){0.f, 0.f, 0.f, 0.f});
       }
       f16x8 db[KB];
 #pragma unroll
       for (int ks = 0; ks < KB; ++ks) db[ks] = HALF ? acc_half(d[0]) : acc_pair(d[2 * ks], d[2 * ks + 1]);
-      // O = scale (Q e^Gam h + P delta)
+      // O = scale ((Q e^Gam) h + P delta)
+      f16x8 fp[G::NB][KB];
 #pragma unroll
-      for (int I = 0; I < G::NB; ++I) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KD; ++ks)
-          o = mfma16(lds_a_perm(&s.Qt[0][0], G::PD, 16 * I + l16, 32 * ks, g), hb[ks], o);
+      for (int I = 0; I < G::NB; ++I)
 #pragma unroll
         for (int ks = 0; ks < KB; ++ks)
-          if (32 * ks <= 16 * I + 15)
-            o = mfma16(lds_a_perm(&s.P[0][0], G::PB, 16 * I + l16, 32 * ks, g, HALF), db[ks], o);
+          if (32 * ks <= 16 * I + 15) fp[I][ks] = lds_a_perm(&s.P[0][0], G::PB, 16 * I + l16, 32 * ks, g, HALF);
+      // (K e^(Gam_C-Gam))^T fragments for the state update
+      f16x8 fk[G::NCB][KB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int orow = s.orow[16 * I + 4 * g + r];
-          if (orow >= 0) a.o[((size_t)orow * H + h) * D + col] = sc * o[r];
-        }
+      for (int C = 0; C < G::NCB; ++C)
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks) fk[C][ks] = lds_a_perm(&s.KhT[0][0], G::PB, 16 * C + l16, 32 * ks, g, HALF);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int I = 0; I < G::NB; ++I) {
+#pragma unroll
+        for (int ks = 0; ks < KB; ++ks)
+          if (32 * ks <= 16 * I + 15) o[I] = mfma16(fp[I][ks], db[ks], o[I]);
+        o[I] *= sc;
+        quad_transpose(o[I]);
+        const int orow = s.orow[16 * I + rq];
+        if (orow >= 0) *(f32x4*)&a.o[((size_t)orow * H + h) * D + cq] = o[I];
       }
       // h' = diag(e^Gam_C) h + (K e^(Gam_C-Gam))^T delta
 #pragma unroll
@@ -156,9 +193,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) hs[C][r] *= s.gc[16 * C + 4 * g + r];
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks)
-          hs[C] = mfma16(lds_a_perm(&s.KhT[0][0], G::PB, 16 * C + l16, 32 * ks, g, HALF), db[ks],
-                         hs[C]);
+        for (int ks = 0; ks < KB; ++ks) hs[C] = mfma16(fk[C][ks], db[ks], hs[C]);
       }
       const int save = a.plan.chunk_save[c];
       if (save >= 0) {

@@ -139,7 +139,6 @@ struct GradSmem {
   float part[G::NRG][D];    // row-group sums (Gam, then the reverse scan)
   float degc[D];
   float beta[BC];
-  int row[BC];
   int orow[BC];
 };
 
@@ -174,60 +173,51 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
       (const FwdImage<BC, D, TIn>*)(a.fimg + blk * fwd_image_bytes(BC, D));
   const float sc = a.scale;
 
-  if (tid < BC) {
-    const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
-    s.row[tid] = r;
-    s.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
-    s.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
+  // ---- every global load is issued first (none waits on another, except
+  // the row-indexed ones on this thread's own row indices); the LDS writes
+  // and register layouts follow ----
+  const int c0 = tid % DH, rg = tid / DH, r0 = rg * RPT;  // element mapping: channel c0 + 64 hf, rows r0 ..
+  int rows[RPT];
+#pragma unroll
+  for (int t = 0; t < RPT; ++t) rows[t] = r0 + t < len ? a.plan.row_index[row0 + r0 + t] : -1;
+  int trow = -1, torow = -1;  // row table entries (tid < BC)
+  if (tid < BC && tid < len) {
+    trow = a.plan.row_index[row0 + tid];
+    torow = tid >= nrep ? a.plan.out_row[row0 + tid] : -1;
   }
-  {  // A and Td of the forward image
-    for (int e = tid; e < BC * BC / 8; e += NT) {
-      const int i = e / (BC / 8), j0 = (e % (BC / 8)) * 8;
-      *(f16x8*)&s.u.p.A[i][j0] = *(const f16x8*)&F->L[i][j0];
-    }
-    for (int e = tid; e < BC * 2; e += NT) {
-      const int i = e / 2, j0 = (e % 2) * 8;
-      *(f16x8*)&s.u.p.Td[i][j0] = *(const f16x8*)&F->Td[i][j0];
-    }
+  // A and Td of the forward image
+  constexpr int NAV = (BC * BC / 8 + NT - 1) / NT;
+  f16x8 av[NAV], tv;
+#pragma unroll
+  for (int n = 0; n < NAV; ++n) {
+    const int e = tid + NT * n;
+    if (e < BC * BC / 8) av[n] = *(const f16x8*)&F->L[e / (BC / 8)][(e % (BC / 8)) * 8];
   }
-  // ---- loads that need no row table: states and dy (wave layout) ----
+  if (tid < BC * 2) tv = *(const f16x8*)&F->Td[tid / 2][(tid % 2) * 8];
+  // states, dy and V as row pieces (one vector load each; quad_transpose
+  // turns them into the accumulator layout)
   const bool vw = wave < NCB;
   const int col = 16 * wave + l16;
-  f32x4 hC[NCB], dhC[NCB], dyv[NB];
+  const int cq = 16 * wave + quad_col(), rq = quad_row();
+  f32x4 hC[NCB], dhC[NCB], dyv[NB], z[NB];
+  in4_t<TIn> vraw[NB];
   if (vw) {
     const _Float16* hsrc = a.chunk_h + blk * DD;
     const _Float16* dhsrc = a.dhc + blk * DD;
 #pragma unroll
-    for (int C = 0; C < NCB; ++C)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const size_t o = (size_t)(16 * C + 4 * g + r) * D + col;
-        hC[C][r] = (float)hsrc[o];
-        dhC[C][r] = (float)dhsrc[o];
-      }
-#pragma unroll
-    for (int J = 0; J < NB; ++J)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * J + 4 * g + r;
-        dyv[J][r] = i < len ? a.dy[((size_t)(row0 + i) * H + h) * D + col] : 0.f;
-      }
-  }
-  __syncthreads();
-  // ---- loads through the row table ----
-  const int c0 = tid % DH, rg = tid / DH, r0 = rg * RPT;
-  float gm[NE], kk[NE], qq[NE];   // element mapping: channel c0 + 64 hf, rows r0 .. r0 + RPT - 1
-#pragma unroll
-  for (int hf = 0; hf < NHF; ++hf)
-#pragma unroll
-    for (int t = 0; t < RPT; ++t) {
-      const int n = hf * RPT + t, r = s.row[r0 + t];
-      const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf;
-      const float x = a.g[off], y = ld_in(k, off), w = ld_in(q, off);
-      gm[n] = r >= 0 ? x : 0.f;
-      kk[n] = r >= 0 ? y : 0.f;
-      qq[n] = r >= 0 ? w : 0.f;
+    for (int C = 0; C < NCB; ++C) {
+      const size_t o = (size_t)(16 * C + rq) * D + cq;
+      hC[C] = ld_h4(hsrc + o);
+      dhC[C] = ld_h4(dhsrc + o);
     }
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      const int i = 16 * J + rq;
+      dyv[J] = i < len ? *(const f32x4*)&a.dy[((size_t)(row0 + i) * H + h) * D + cq]
+                       : (f32x4){0.f, 0.f, 0.f, 0.f};
+      vraw[J] = *(const in4_t<TIn>*)&F->V[16 * J + rq][cq];
+    }
+  }
   Raw8<TIn> dov[NV8];   // packed dO is zero on replay rows
 #pragma unroll
   for (int n = 0; n < NV8; ++n) {
@@ -238,12 +228,43 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
       if (i < len) dov[n].load(dOp + ((size_t)(row0 + i) * H + h) * D + (e % (D / 8)) * 8);
     }
   }
-  f32x4 z[NB];
+  // through this thread's row indices: g, k, q; beta of the row table
+  float gm[NE], kk[NE], qq[NE];
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int n = hf * RPT + t, r = rows[t];
+      const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf;
+      const float x = a.g[off], y = ld_in(k, off), w = ld_in(q, off);
+      gm[n] = r >= 0 ? x : 0.f;
+      kk[n] = r >= 0 ? y : 0.f;
+      qq[n] = r >= 0 ? w : 0.f;
+    }
+  const float tbeta = trow >= 0 ? a.beta[(size_t)trow * H + h] : 0.f;
+  // LDS writes and register layouts
+  if (tid < BC) {
+    s.orow[tid] = torow;
+    s.beta[tid] = tbeta;
+  }
+#pragma unroll
+  for (int n = 0; n < NAV; ++n) {
+    const int e = tid + NT * n;
+    if (e < BC * BC / 8) *(f16x8*)&s.u.p.A[e / (BC / 8)][(e % (BC / 8)) * 8] = av[n];
+  }
+  if (tid < BC * 2) *(f16x8*)&s.u.p.Td[tid / 2][(tid % 2) * 8] = tv;
   if (vw) {
 #pragma unroll
-    for (int J = 0; J < NB; ++J)
+    for (int C = 0; C < NCB; ++C) {
+      quad_transpose(hC[C]);
+      quad_transpose(dhC[C]);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[J][r] = ld_in(&F->V[0][0], (size_t)(16 * J + 4 * g + r) * D + col);
+    for (int J = 0; J < NB; ++J) {
+      quad_transpose(dyv[J]);
+      z[J] = in4_to_f32(vraw[J]);
+      quad_transpose(z[J]);
+    }
   }
 
   // ---- Gam: running sums per row group, then their prefix ----
