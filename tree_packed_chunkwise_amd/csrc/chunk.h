@@ -291,7 +291,6 @@ struct ChunkTables {
   float part[Geom<BC, D>::NRG][D];           // per-row-group sums of g
   float dfac[(Geom<BC, D>::NOFF > 0 ? Geom<BC, D>::NOFF : 1)][D];  // e^(gref_I - gref_J)
   float beta[BC];
-  int row[BC];
   int orow[BC];
 };
 
@@ -313,18 +312,14 @@ struct ElemRegs {
   float lk[N], lq[N], rk[N];  // factored operands
 };
 
-// Issues the loads of k, q, g for the thread's elements (rows via tb.row;
-// zero past the chunk).  No synchronisation.
+// Issues the loads of k, q, g for the thread's elements (rows[t] = input row
+// of chunk row r0 + t, -1 past the chunk: zeros).  No synchronisation.
 template <typename TIn, int BC, int D>
 __device__ inline void elems_load(const TIn* q, const TIn* k, const float* g, int H, int h,
-                                  const ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) {
+                                  const int (&rows)[Geom<BC, D>::RPT], ElemRegs<BC, D>& er) {
   using G = Geom<BC, D>;
   const int tid = threadIdx.x;
   const int c0 = tid % G::DH;
-  const int r0 = (tid / G::DH) * G::RPT;
-  int rows[G::RPT];
-#pragma unroll
-  for (int t = 0; t < G::RPT; ++t) rows[t] = tb.row[r0 + t];
 #pragma unroll
   for (int hf = 0; hf < G::NHALF; ++hf)
 #pragma unroll

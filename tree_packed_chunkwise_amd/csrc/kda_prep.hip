@@ -52,16 +52,19 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
   const int row0 = a.plan.chunk_row0[c];
   const int len = a.plan.chunk_len[c];
   const int nrep = a.plan.chunk_nrep[c];
-  if (tid < BC) {
-    const int r = tid < len ? a.plan.row_index[row0 + tid] : -1;
-    s.tb.row[tid] = r;
-    s.tb.orow[tid] = (tid >= nrep && tid < len) ? a.plan.out_row[row0 + tid] : -1;
-    s.tb.beta[tid] = r >= 0 ? a.beta[(size_t)r * H + h] : 0.f;
-  }
-  __syncthreads();
-  ElemRegs<BC, D> er;
-  elems_load<TIn, BC, D>((const TIn*)a.q, (const TIn*)a.k, a.g, H, h, s.tb, er);
+  // every global load is issued first; each thread reads the row indices of
+  // its own element rows from the plan (no round trip through a shared table)
   const int c0 = tid % G::DH, r0 = (tid / G::DH) * G::RPT;
+  int rows[G::RPT];
+#pragma unroll
+  for (int t = 0; t < G::RPT; ++t) rows[t] = r0 + t < len ? a.plan.row_index[row0 + r0 + t] : -1;
+  int trow = -1, torow = -1;  // row table entries (tid < BC)
+  if (tid < BC && tid < len) {
+    trow = a.plan.row_index[row0 + tid];
+    torow = tid >= nrep ? a.plan.out_row[row0 + tid] : -1;
+  }
+  ElemRegs<BC, D> er;
+  elems_load<TIn, BC, D>((const TIn*)a.q, (const TIn*)a.k, a.g, H, h, rows, er);
   float vv[NE];
   {
     const TIn* v = (const TIn*)a.v;
@@ -69,11 +72,16 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
     for (int hf = 0; hf < G::NHALF; ++hf)
 #pragma unroll
       for (int t = 0; t < G::RPT; ++t) {
-        const int r = s.tb.row[r0 + t];
+        const int r = rows[t];
         const float x = ld_in(v, ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf);
         vv[hf * G::RPT + t] = r >= 0 ? x : 0.f;
       }
   }
+  if (tid < BC) {
+    s.tb.orow[tid] = torow;
+    s.tb.beta[tid] = trow >= 0 ? a.beta[(size_t)trow * H + h] : 0.f;
+  }
+  __syncthreads();
   chunk_AP<BC, D>(s.tb, er, s.ap, &s.A[0][0], G::PB, &s.P[0][0], G::PB);
   FI* F = (FI*)(a.fimg + blk * fwd_image_bytes(BC, D));
 
