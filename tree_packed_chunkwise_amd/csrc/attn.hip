@@ -84,100 +84,235 @@ __device__ inline void stage_rows(const uint16_t* src, int r0, int n, int H, int
   }
 }
 
+// ---- swizzled tiles ----
+// A 64-row tile of a bf16 [N][H][D] tensor in LDS, rows unpadded (2 D bytes);
+// the 16-byte chunk c of row r sits at chunk position c ^ swz(r).  The swizzle
+// keeps both fragment reads free of bank conflicts: a 16-byte row read by 16
+// lanes of distinct rows (swz is a bijection on r mod 16), and the transposing
+// 8-byte read, whose 16 lanes address four consecutive rows x two adjacent
+// chunks (swz differs between those rows above bit 0).
 template <int D>
-struct AttnFwdSmem {
-  uint16_t K[AT][D + 8];     // key rows (bf16)
-  uint16_t Vt[D][AT + 8];    // values, transposed (bf16)
+struct SwTile {
+  static constexpr int BYTES = AT * D * 2;
+  __device__ static int swz(int r) {
+    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
+  }
+  // byte offset of element (r, d)
+  __device__ static int off(int r, int d) {
+    return r * (2 * D) + ((((d >> 3) ^ swz(r))) << 4) + ((d & 7) << 1);
+  }
 };
 
+// Asynchronous copy of rows r0 .. r0+n-1 of a bf16 [N][H][D] tensor (head h)
+// into a swizzled tile (global_load_lds_dwordx4: straight to LDS).  Each 1 KB
+// piece of the tile is one wave instruction: lane l fills chunk position l of
+// the piece and so loads the chunk that the swizzle places there; rows past n
+// repeat row n-1 (their scores are masked).  Completion: s_waitcnt vmcnt(0)
+// and a barrier, by the caller.
+template <int D, int NWV>
+__device__ inline void tile_dma(unsigned char* dst, const uint16_t* src, int r0, int n, int H, int h) {
+  constexpr int LPR = (2 * D) / 16;   // lanes per tile row
+  constexpr int RPP = 64 / LPR;       // tile rows per 1 KB piece
+  constexpr int NP = AT / RPP;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rl = lane / LPR, pos = lane % LPR;
+#pragma unroll
+  for (int p = wave; p < NP; p += NWV) {
+    const int r = p * RPP + rl;
+    const int c = pos ^ SwTile<D>::swz(r);
+    const int gr = r0 + (r < n ? r : n - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(src + ((size_t)gr * H + h) * D + 8 * c),
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * p),
+                                     16, 0, 0);
+  }
+}
+
+// 16-byte row piece (8 consecutive k) of a swizzled tile: with r = row0 + l16
+// and d = 32 ks + 8 g it is the A fragment of rows row0 .. row0+15, k step ks
 template <int D>
-__global__ __launch_bounds__(ANT) void k_attn_fwd(AttnArgs a) {
+__device__ inline bf16x8 tile_row8(const unsigned char* t, int r, int d) {
+  return *(const bf16x8*)(t + SwTile<D>::off(r, d));
+}
+// A fragment of X^T in register k order (chunk.h) from a swizzled tile X:
+// rows c0 .. c0+15 of X^T (columns of X), k = rows r0 + {4g..4g+3, 16+4g..16+4g+3}
+// of X; two transposing 8-byte reads (chunk.h, lds_tr4)
+template <int D>
+__device__ inline bf16x8 tile_a_tr(const unsigned char* t, int r0, int c0) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, sl = lane & 15, g = lane >> 4;
+  const int d = c0 + 4 * (sl & 3);
+  const unsigned char* p0 = t + SwTile<D>::off(r0 + 4 * g + (sl >> 2), d);
+  const unsigned char* p1 = t + SwTile<D>::off(r0 + 16 + 4 * g + (sl >> 2), d);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p0);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p1);
+  // join the halves as 16-bit integers and bit-cast the whole vector (a
+  // __builtin_bit_cast of a single vector element reads element 0 with this
+  // compiler, whatever the index)
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Forward, one block (4 waves) per (query tile, head).  Wave w owns queries
+// 32 (w & 1) .. +31 of the tile and keys 32 (w >> 1) .. +31 of every key tile:
+// each wave runs its own online softmax over its half of the keys, and the two
+// halves are merged at the end (running maxima, sums and outputs, through
+// LDS).  Key tiles (every ancestor segment, then the own segment up to the
+// tile's end) are double-buffered by asynchronous copies.
+template <int D>
+__global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
+  using T = SwTile<D>;
   constexpr int KD = D / 32, NDB = D / 16;
-  __shared__ AttnFwdSmem<D> s;
+  __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][T::BYTES];  // [stage][K, V]
   const int t = a.qorder[blockIdx.x], h = blockIdx.y, H = a.H;
   const int seg = a.tile_seg[t], qoff = a.tile_off[t];
   const int slen = a.seg_len[seg], srow = a.seg_row[seg];
   const int qlen = min(AT, slen - qoff);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int qi = 16 * wave + l16;              // this lane's query (column of S^T)
-  const int qrow = srow + qoff + min(qi, qlen - 1);
-  const int qpos = qoff + qi;                  // offset of the query within its segment
-  const float sc = a.scale;
-  bf16x8 qb[KD];
+  const int qh = wave & 1, kh = wave >> 1;
+  const float sl2 = a.scale * 1.4426950408889634f;   // scores in log2 units
+  bf16x8 qf[2][KD];
+  int qpos[2];
 #pragma unroll
-  for (int ks = 0; ks < KD; ++ks) qb[ks] = *(const bf16x8*)(a.q + ((size_t)qrow * H + h) * D + 32 * ks + 8 * g);
-  f32x4 ot[NDB];
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = 32 * qh + 16 * qb + l16;
+    const int qrow = srow + qoff + min(qi, qlen - 1);
+    qpos[qb] = qoff + qi;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) ot[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+    for (int ks = 0; ks < KD; ++ks)
+      qf[qb][ks] = *(const bf16x8*)(a.q + ((size_t)qrow * H + h) * D + 32 * ks + 8 * g);
+  }
+  f32x4 ot[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) ot[db][0] = ot[db][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   const int a0 = a.anc_ptr[seg], na = a.anc_ptr[seg + 1] - a0;
-  for (int ri = 0; ri <= na; ++ri) {
+  auto seg_of = [&](int ri) { return ri == na ? seg : a.anc[a0 + ri]; };
+  auto len_of = [&](int ri) { return ri == na ? qoff + qlen : a.seg_len[seg_of(ri)]; };
+  auto stage = [&](int st, int ri, int k0) {
+    const int r0 = a.seg_row[seg_of(ri)] + k0, n = min(AT, len_of(ri) - k0);
+    tile_dma<D, ANT / 64>(sm[st][0], a.k, r0, n, H, h);
+    tile_dma<D, ANT / 64>(sm[st][1], a.v, r0, n, H, h);
+  };
+  int ri = 0, k0 = 0, st = 0;
+  stage(0, 0, 0);
+  for (;;) {
     const bool own = ri == na;
-    const int ksg = own ? seg : a.anc[a0 + ri];
-    const int r0 = a.seg_row[ksg];
-    const int rlen = own ? qoff + qlen : a.seg_len[ksg];
-    for (int k0 = 0; k0 < rlen; k0 += AT) {
-      const int klen = min(AT, rlen - k0);
-      __syncthreads();  // the previous tile's readers are done
-      stage_rows<D>(a.k, r0 + k0, klen, H, h, s.K, nullptr);
-      stage_rows<D>(a.v, r0 + k0, klen, H, h, nullptr, s.Vt);
-      __syncthreads();
-      f32x4 st[4];
+    const int rlen = len_of(ri), klen = min(AT, rlen - k0);
+    int nri = ri, nk0 = k0 + AT;
+    if (nk0 >= rlen) { nri = ri + 1; nk0 = 0; }
+    const bool more = nri <= na;
+    __builtin_amdgcn_s_waitcnt(0);  // this tile has landed ...
+    __syncthreads();                // ... for every wave; the other stage is free
+    if (more) stage(st ^ 1, nri, nk0);
+    const unsigned char* Kt = sm[st][0];
+    const unsigned char* Vt = sm[st][1];
+    bf16x8 kf[2][KD];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        st[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks)
-          st[kb] = mfmab(*(const bf16x8*)&s.K[16 * kb + l16][32 * ks + 8 * g], qb[ks], st[kb]);
+      for (int ks = 0; ks < KD; ++ks) kf[kb][ks] = tile_row8<D>(Kt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 sc[2][2];   // S^T tiles [key block][query block]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sc[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) sc[kb][qb] = mfmab(kf[kb][ks], qf[qb][ks], sc[kb][qb]);
       }
+    bf16x8 vf[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vf[db] = tile_a_tr<D>(Vt, 32 * kh, 16 * db);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       float mt = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = 16 * kb + 4 * g + r;
-          const bool vis = j < klen && (!own || k0 + j <= qpos);
-          const float x = vis ? st[kb][r] * sc : -INFINITY;
-          st[kb][r] = x;
+          const int j = 32 * kh + 16 * kb + 4 * g + r;
+          const bool vis = j < klen && (!own || k0 + j <= qpos[qb]);
+          const float x = vis ? sc[kb][qb][r] * sl2 : -INFINITY;
+          sc[kb][qb][r] = x;
           mt = xmax(mt, x);
         }
       mt = xmax(mt, __shfl_xor(mt, 16));
       mt = xmax(mt, __shfl_xor(mt, 32));
-      const float mn = xmax(m, mt);
-      const float alpha = mn == -INFINITY ? 1.f : __expf(m - mn);
+      const float mn = xmax(m[qb], mt);
+      const float alpha = mn == -INFINITY ? 1.f : exp2_(m[qb] - mn);
       float ps = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = st[kb][r] == -INFINITY ? 0.f : __expf(st[kb][r] - mn);
-          st[kb][r] = p;
+          const float p = mn == -INFINITY ? 0.f : exp2_(sc[kb][qb][r] - mn);
+          sc[kb][qb][r] = p;
           ps += p;
         }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l = l * alpha + ps;
-      m = mn;
-      bf16x8 ph0, pl0, ph1, pl1;
-      pair_hl(st[0], st[1], ph0, pl0);
-      pair_hl(st[2], st[3], ph1, pl1);
+      l[qb] = l[qb] * alpha + ps;   // this lane's keys; the 4 lanes of a query are summed at the end
+      m[qb] = mn;
+      bf16x8 ph, pl;
+      pair_hl(sc[0][qb], sc[1][qb], ph, pl);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ot[db][r] *= alpha;
-        ot[db] = mfma_hl(lds_a_perm_bf(&s.Vt[0][0], AT + 8, 16 * db + l16, 0, g), ph0, pl0, ot[db]);
-        ot[db] = mfma_hl(lds_a_perm_bf(&s.Vt[0][0], AT + 8, 16 * db + l16, 32, g), ph1, pl1, ot[db]);
+        ot[db][qb] *= alpha;
+        ot[db][qb] = mfma_hl(vf[db], ph, pl, ot[db][qb]);
       }
     }
+    if (!more) break;
+    ri = nri; k0 = nk0; st ^= 1;
   }
-  if (qi < qlen) {
-    const float inv = 1.f / l;
-    float* dst = a.o + ((size_t)qrow * H + h) * D;
+  // merge the two key halves: waves 2, 3 hand their state to waves 0, 1
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    l[qb] += __shfl_xor(l[qb], 16);
+    l[qb] += __shfl_xor(l[qb], 32);
+  }
+  __syncthreads();   // every wave is done with the tiles: reuse them
+  float* xo = (float*)&sm[0][0][0];               // [qh][NDB * 2 * 4][64]
+  float* xm = xo + 2 * NDB * 2 * 4 * 64;           // [qh][2][64]
+  float* xl = xm + 2 * 2 * 64;
+  if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      *(float4*)(dst + 16 * db + 4 * g) =
-          make_float4(ot[db][0] * inv, ot[db][1] * inv, ot[db][2] * inv, ot[db][3] * inv);
-    if (g == 0) a.lse[(size_t)qrow * H + h] = m + __logf(l);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane] = ot[db][qb][r];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      xm[(qh * 2 + qb) * 64 + lane] = m[qb];
+      xl[(qh * 2 + qb) * 64 + lane] = l[qb];
+    }
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qi = 32 * qh + 16 * qb + l16;
+      const float m2 = xm[(qh * 2 + qb) * 64 + lane], l2 = xl[(qh * 2 + qb) * 64 + lane];
+      const float mm = xmax(m[qb], m2);
+      const float w1 = m[qb] == -INFINITY ? 0.f : exp2_(m[qb] - mm);
+      const float w2 = m2 == -INFINITY ? 0.f : exp2_(m2 - mm);
+      const float lt = l[qb] * w1 + l2 * w2;
+      if (qi < qlen) {
+        const int qrow = srow + qoff + qi;
+        const float inv = 1.f / lt;
+        float* dst = a.o + ((size_t)qrow * H + h) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          float4 v;
+          float* vp = &v.x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            vp[r] = (ot[db][qb][r] * w1 + xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane] * w2) * inv;
+          *(float4*)(dst + 16 * db + 4 * g) = v;
+        }
+        if (g == 0) a.lse[(size_t)qrow * H + h] = (mm + __log2f(lt)) * 0.6931471805599453f;
+      }
+    }
   }
 }
 
