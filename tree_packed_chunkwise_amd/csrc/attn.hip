@@ -65,25 +65,6 @@ __device__ inline f32x4 mfma_hl(const bf16x8& a, const bf16x8& bh, const bf16x8&
 }
 __device__ inline float xmax(float a, float b) { return a > b ? a : b; }
 
-// 64 rows x D columns of a bf16 [N][H][D] tensor (rows r0 .. r0+n-1, zero past
-// n) into an LDS tile [64][D+8] and, when `tr` is given, transposed into
-// [D][72] (both bf16, exact).
-template <int D>
-__device__ inline void stage_rows(const uint16_t* src, int r0, int n, int H, int h,
-                                  uint16_t (*dst)[D + 8], uint16_t (*tr)[AT + 8]) {
-  for (int e = threadIdx.x; e < AT * D / 8; e += ANT) {
-    const int j = e / (D / 8), d0 = (e % (D / 8)) * 8;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (j < n) x = *(const uint4*)(src + ((size_t)(r0 + j) * H + h) * D + d0);
-    if (dst) *(uint4*)&dst[j][d0] = x;
-    if (tr) {
-      const uint16_t* xs = (const uint16_t*)&x;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) tr[d0 + m][j] = xs[m];
-    }
-  }
-}
-
 // ---- swizzled tiles ----
 // A 64-row tile of a bf16 [N][H][D] tensor in LDS, rows unpadded (2 D bytes);
 // the 16-byte chunk c of row r sits at chunk position c ^ swz(r).  The swizzle
@@ -152,6 +133,24 @@ __device__ inline bf16x8 tile_a_tr(const unsigned char* t, int r0, int c0) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 __device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+// maximum / sum over the four 16-lane rows of a wave, per column (lanes l,
+// l^16, l^32, l^48): gfx950 row swaps, no LDS round trip
+__device__ inline float max_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = xmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return xmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Running maximum of the online softmax (log2 units): it moves only when a
+// tile's maximum exceeds it by more than this, so probabilities stay below
+// 2^8 and most tiles skip the rescale of the accumulators.
+constexpr float ATT_MAX_SLACK = 8.f;
 
 // Forward, one block (4 waves) per (query tile, head).  Wave w owns queries
 // 32 (w & 1) .. +31 of the tile and keys 32 (w >> 1) .. +31 of every key tile:
@@ -199,6 +198,7 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
   for (;;) {
     const bool own = ri == na;
     const int rlen = len_of(ri), klen = min(AT, rlen - k0);
+    const bool full = !own && klen == AT;   // no masking needed
     int nri = ri, nk0 = k0 + AT;
     if (nk0 >= rlen) { nri = ri + 1; nk0 = 0; }
     const bool more = nri <= na;
@@ -228,20 +228,36 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mt = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 32 * kh + 16 * kb + 4 * g + r;
-          const bool vis = j < klen && (!own || k0 + j <= qpos[qb]);
-          const float x = vis ? sc[kb][qb][r] * sl2 : -INFINITY;
-          sc[kb][qb][r] = x;
-          mt = xmax(mt, x);
-        }
-      mt = xmax(mt, __shfl_xor(mt, 16));
-      mt = xmax(mt, __shfl_xor(mt, 32));
-      const float mn = xmax(m[qb], mt);
-      const float alpha = mn == -INFINITY ? 1.f : exp2_(m[qb] - mn);
+          for (int r = 0; r < 4; ++r) {
+            const float x = sc[kb][qb][r] * sl2;
+            sc[kb][qb][r] = x;
+            mt = xmax(mt, x);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 32 * kh + 16 * kb + 4 * g + r;
+            const bool vis = j < klen && (!own || k0 + j <= qpos[qb]);
+            const float x = vis ? sc[kb][qb][r] * sl2 : -INFINITY;
+            sc[kb][qb][r] = x;
+            mt = xmax(mt, x);
+          }
+      }
+      mt = max_rows4(mt);
+      const float mn = mt > m[qb] + ATT_MAX_SLACK ? mt : m[qb];
+      if (__builtin_amdgcn_ballot_w64(mn != m[qb])) {   // some query's reference moved
+        const float alpha = m[qb] == -INFINITY ? 0.f : exp2_(m[qb] - mn);
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) ot[db][qb] *= alpha;
+        m[qb] = mn;
+      }
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -251,25 +267,18 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
           sc[kb][qb][r] = p;
           ps += p;
         }
-      l[qb] = l[qb] * alpha + ps;   // this lane's keys; the 4 lanes of a query are summed at the end
-      m[qb] = mn;
+      l[qb] += ps;   // this lane's keys; the 4 lanes of a query are summed at the end
       bf16x8 ph, pl;
       pair_hl(sc[0][qb], sc[1][qb], ph, pl);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        ot[db][qb] *= alpha;
-        ot[db][qb] = mfma_hl(vf[db], ph, pl, ot[db][qb]);
-      }
+      for (int db = 0; db < NDB; ++db) ot[db][qb] = mfma_hl(vf[db], ph, pl, ot[db][qb]);
     }
     if (!more) break;
     ri = nri; k0 = nk0; st ^= 1;
   }
   // merge the two key halves: waves 2, 3 hand their state to waves 0, 1
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    l[qb] += __shfl_xor(l[qb], 16);
-    l[qb] += __shfl_xor(l[qb], 32);
-  }
+  for (int qb = 0; qb < 2; ++qb) l[qb] = sum_rows4(l[qb]);
   __syncthreads();   // every wave is done with the tiles: reuse them
   float* xo = (float*)&sm[0][0][0];               // [qh][NDB * 2 * 4][64]
   float* xm = xo + 2 * NDB * 2 * 4 * 64;           // [qh][2][64]
@@ -333,98 +342,173 @@ __global__ __launch_bounds__(ANT) void k_attn_delta(AttnArgs a, int64_t n_rh) {
   if (rh < n_rh && part == 0) a.delta[rh] = x;
 }
 
+// dq, one block (4 waves) per (query tile, head), over the same key tiles as
+// the forward.  Wave w owns queries 32 (w & 1) .. +31 and keys 32 (w >> 1) ..
+// +31 of every key tile:
+//   S^T = K Q^T, dP^T = V dO^T (bf16 matrix cores, exact inputs),
+//   P^T = 2^(S^T scale log2e - lse log2e), dS^T = P^T (dP^T - delta),
+//   dQ^T += K^T dS^T (K^T from the tile by transposing reads, dS^T hi/lo),
+// and the two key halves' partial dq are summed at the end.
 template <int D>
-struct AttnDqSmem {
-  uint16_t K[AT][D + 8];
-  uint16_t V[AT][D + 8];
-  uint16_t Kt[D][AT + 8];
-};
-
-template <int D>
-__global__ __launch_bounds__(ANT) void k_attn_dq(AttnArgs a) {
+__global__ __launch_bounds__(ANT, 2) void k_attn_dq(AttnArgs a) {
+  using T = SwTile<D>;
   constexpr int KD = D / 32, NDB = D / 16;
-  __shared__ AttnDqSmem<D> s;
+  __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][T::BYTES];  // [stage][K, V]
   const int t = a.qorder[blockIdx.x], h = blockIdx.y, H = a.H;
   const int seg = a.tile_seg[t], qoff = a.tile_off[t];
   const int slen = a.seg_len[seg], srow = a.seg_row[seg];
   const int qlen = min(AT, slen - qoff);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int qi = 16 * wave + l16;
-  const int qrow = srow + qoff + min(qi, qlen - 1);
-  const int qpos = qoff + qi;
-  const float sc = a.scale;
-  bf16x8 qb[KD], dob[KD];
+  const int qh = wave & 1, kh = wave >> 1;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  bf16x8 qf[2][KD], df[2][KD];
+  int qpos[2];
+  float lq[2], dl[2];
 #pragma unroll
-  for (int ks = 0; ks < KD; ++ks) {
-    qb[ks] = *(const bf16x8*)(a.q + ((size_t)qrow * H + h) * D + 32 * ks + 8 * g);
-    dob[ks] = *(const bf16x8*)(a.dO + ((size_t)qrow * H + h) * D + 32 * ks + 8 * g);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = 32 * qh + 16 * qb + l16;
+    const int qrow = srow + qoff + min(qi, qlen - 1);
+    qpos[qb] = qoff + qi;
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      qf[qb][ks] = *(const bf16x8*)(a.q + ((size_t)qrow * H + h) * D + 32 * ks + 8 * g);
+      df[qb][ks] = *(const bf16x8*)(a.dO + ((size_t)qrow * H + h) * D + 32 * ks + 8 * g);
+    }
+    lq[qb] = a.lsec[(size_t)qrow * H + h] * 1.4426950408889634f;
+    dl[qb] = a.delta[(size_t)qrow * H + h];
   }
-  const float lq = a.lsec[(size_t)qrow * H + h], dq_ = a.delta[(size_t)qrow * H + h];
-  f32x4 acc[NDB];
+  f32x4 acc[NDB][2];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int a0 = a.anc_ptr[seg], na = a.anc_ptr[seg + 1] - a0;
-  for (int ri = 0; ri <= na; ++ri) {
+  auto seg_of = [&](int ri) { return ri == na ? seg : a.anc[a0 + ri]; };
+  auto len_of = [&](int ri) { return ri == na ? qoff + qlen : a.seg_len[seg_of(ri)]; };
+  auto stage = [&](int st, int ri, int k0) {
+    const int r0 = a.seg_row[seg_of(ri)] + k0, n = min(AT, len_of(ri) - k0);
+    tile_dma<D, ANT / 64>(sm[st][0], a.k, r0, n, H, h);
+    tile_dma<D, ANT / 64>(sm[st][1], a.v, r0, n, H, h);
+  };
+  int ri = 0, k0 = 0, st = 0;
+  stage(0, 0, 0);
+  for (;;) {
     const bool own = ri == na;
-    const int ksg = own ? seg : a.anc[a0 + ri];
-    const int r0 = a.seg_row[ksg];
-    const int rlen = own ? qoff + qlen : a.seg_len[ksg];
-    for (int k0 = 0; k0 < rlen; k0 += AT) {
-      const int klen = min(AT, rlen - k0);
-      __syncthreads();
-      stage_rows<D>(a.k, r0 + k0, klen, H, h, s.K, s.Kt);
-      stage_rows<D>(a.v, r0 + k0, klen, H, h, s.V, nullptr);
-      __syncthreads();
-      f32x4 ds[4];
+    const int rlen = len_of(ri), klen = min(AT, rlen - k0);
+    const bool full = !own && klen == AT;
+    int nri = ri, nk0 = k0 + AT;
+    if (nk0 >= rlen) { nri = ri + 1; nk0 = 0; }
+    const bool more = nri <= na;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (more) stage(st ^ 1, nri, nk0);
+    const unsigned char* Kt = sm[st][0];
+    const unsigned char* Vt = sm[st][1];
+    f32x4 sc[2][2], dp[2][2];
+    {
+      bf16x8 kf[2][KD];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) {
-          st = mfmab(*(const bf16x8*)&s.K[16 * kb + l16][32 * ks + 8 * g], qb[ks], st);
-          dp = mfmab(*(const bf16x8*)&s.V[16 * kb + l16][32 * ks + 8 * g], dob[ks], dp);
+        for (int ks = 0; ks < KD; ++ks) kf[kb][ks] = tile_row8<D>(Kt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sc[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KD; ++ks) sc[kb][qb] = mfmab(kf[kb][ks], qf[qb][ks], sc[kb][qb]);
         }
+    }
+    {
+      bf16x8 vf[2][KD];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) vf[kb][ks] = tile_row8<D>(Vt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          dp[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KD; ++ks) dp[kb][qb] = mfmab(vf[kb][ks], df[qb][ks], dp[kb][qb]);
+        }
+    }
+    bf16x8 bh[2], bl[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = 16 * kb + 4 * g + r;
-          const bool vis = j < klen && (!own || k0 + j <= qpos);
-          const float p = vis ? __expf(st[r] * sc - lq) : 0.f;
-          ds[kb][r] = p * (dp[r] - dq_);
+          const int j = 32 * kh + 16 * kb + 4 * g + r;
+          const bool vis = full || (j < klen && (!own || k0 + j <= qpos[qb]));
+          const float p = vis ? exp2_(sc[kb][qb][r] * sl2 - lq[qb]) : 0.f;
+          sc[kb][qb][r] = p * (dp[kb][qb][r] - dl[qb]);   // dS^T
         }
-      }
-      bf16x8 bh0, bl0, bh1, bl1;
-      pair_hl(ds[0], ds[1], bh0, bl0);
-      pair_hl(ds[2], ds[3], bh1, bl1);
+      pair_hl(sc[0][qb], sc[1][qb], bh[qb], bl[qb]);
+    }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        acc[db] = mfma_hl(lds_a_perm_bf(&s.Kt[0][0], AT + 8, 16 * db + l16, 0, g), bh0, bl0, acc[db]);
-        acc[db] = mfma_hl(lds_a_perm_bf(&s.Kt[0][0], AT + 8, 16 * db + l16, 32, g), bh1, bl1, acc[db]);
+    for (int d0 = 0; d0 < NDB; d0 += 4) {
+      bf16x8 kt[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) kt[db] = tile_a_tr<D>(Kt, 32 * kh, 16 * (d0 + db));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) acc[d0 + db][qb] = mfma_hl(kt[db], bh[qb], bl[qb], acc[d0 + db][qb]);
+    }
+    if (!more) break;
+    ri = nri; k0 = nk0; st ^= 1;
+  }
+  // sum the two key halves: waves 2, 3 hand their partial dq to waves 0, 1
+  __syncthreads();
+  float* xo = (float*)&sm[0][0][0];   // [qh][NDB * 2 * 4][64]
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane] = acc[db][qb][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qi = 32 * qh + 16 * qb + l16;
+      if (qi < qlen) {
+        float* dst = a.dq + ((size_t)(srow + qoff + qi) * H + h) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          float4 v;
+          float* vp = &v.x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            vp[r] = a.scale * (acc[db][qb][r] + xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane]);
+          *(float4*)(dst + 16 * db + 4 * g) = v;
+        }
       }
     }
   }
-  if (qi < qlen) {
-    float* dst = a.dq + ((size_t)qrow * H + h) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *(float4*)(dst + 16 * db + 4 * g) =
-          make_float4(sc * acc[db][0], sc * acc[db][1], sc * acc[db][2], sc * acc[db][3]);
-  }
 }
 
+// dk / dv, one block (4 waves) per (work item, head): a key tile and a run of
+// the query tiles that see it (its own segment's tiles from the key tile on,
+// then every descendant segment's tiles).  Wave w owns keys 16 w .. +15 of the
+// key tile; per query tile (double-buffered asynchronous copies of its Q and
+// dO rows, and its lse and delta):
+//   S = Q K^T, dP = dO V^T (bf16 matrix cores; K and V of the wave's keys in
+//   registers), P = 2^(S scale log2e - lse log2e), dS = P (dP - delta),
+//   dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T by transposing reads; P, dS hi/lo).
 template <int D>
-struct AttnDkvSmem {
-  uint16_t Q[AT][D + 8];
-  uint16_t dO[AT][D + 8];
-  uint16_t Qt[D][AT + 8];
-  uint16_t dOt[D][AT + 8];
-  float lse[AT];
-  float delta[AT];
-};
-
-template <int D>
-__global__ __launch_bounds__(ANT) void k_attn_dkv(AttnArgs a) {
+__global__ __launch_bounds__(ANT, 2) void k_attn_dkv(AttnArgs a) {
+  using T = SwTile<D>;
   constexpr int KD = D / 32, NDB = D / 16;
-  __shared__ AttnDkvSmem<D> s;
+  __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][T::BYTES];  // [stage][Q, dO]
+  __shared__ float sld[2][2][AT];                                            // [stage][lse log2e, delta]
   const int item = blockIdx.x, h = blockIdx.y, H = a.H;
   const int t = a.kw_tile[item], q0 = a.kw_q0[item], nq = a.kw_nq[item], slot = a.kw_slot[item];
   const int seg = a.tile_seg[t], koff = a.tile_off[t];
@@ -432,7 +516,7 @@ __global__ __launch_bounds__(ANT) void k_attn_dkv(AttnArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int kj = 16 * wave + l16;              // this lane's key (column of S)
   const int krow = krow0 + min(kj, klen - 1);
-  const float sc = a.scale;
+  const float sl2 = a.scale * 1.4426950408889634f;
   bf16x8 kb[KD], vb[KD];
 #pragma unroll
   for (int ks = 0; ks < KD; ++ks) {
@@ -443,49 +527,90 @@ __global__ __launch_bounds__(ANT) void k_attn_dkv(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dkt[db] = dvt[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int e0 = a.kq_ptr[t] + q0;
-  for (int qi_ = 0; qi_ < nq; ++qi_) {
-    const int u = a.kq[e0 + qi_];
+  float rl = 0.f, rd = 0.f;   // lse / delta of row tid of the query tile in flight (tid < 64)
+  auto stage = [&](int st, int i) {
+    const int u = a.kq[e0 + i];
     const int qseg = a.tile_seg[u], qoff = a.tile_off[u];
     const int qlen = min(AT, a.seg_len[qseg] - qoff), qrow0 = a.seg_row[qseg] + qoff;
-    const bool own = qseg == seg;
-    __syncthreads();
-    stage_rows<D>(a.q, qrow0, qlen, H, h, s.Q, s.Qt);
-    stage_rows<D>(a.dO, qrow0, qlen, H, h, s.dO, s.dOt);
+    tile_dma<D, ANT / 64>(sm[st][0], a.q, qrow0, qlen, H, h);
+    tile_dma<D, ANT / 64>(sm[st][1], a.dO, qrow0, qlen, H, h);
     if (tid < AT) {
       const bool ok = tid < qlen;
-      s.lse[tid] = ok ? a.lsec[(size_t)(qrow0 + tid) * H + h] : 0.f;
-      s.delta[tid] = ok ? a.delta[(size_t)(qrow0 + tid) * H + h] : 0.f;
+      const size_t o = (size_t)(qrow0 + (ok ? tid : 0)) * H + h;
+      rl = ok ? a.lsec[o] * 1.4426950408889634f : 0.f;
+      rd = ok ? a.delta[o] : 0.f;
+    }
+  };
+  if (nq > 0) stage(0, 0);
+  for (int i = 0, st = 0; i < nq; ++i, st ^= 1) {
+    const int u = a.kq[e0 + i];
+    const int qseg = a.tile_seg[u], qoff = a.tile_off[u];
+    const int qlen = min(AT, a.seg_len[qseg] - qoff);
+    const bool own = qseg == seg;
+    const bool full = !own && qlen == AT && klen == AT;
+    __builtin_amdgcn_s_waitcnt(0);   // this query tile has landed (tiles and rl / rd)
+    if (tid < AT) {
+      sld[st][0][tid] = rl;
+      sld[st][1][tid] = rd;
     }
     __syncthreads();
-    f32x4 p[4], ds[4];
+    if (i + 1 < nq) stage(st ^ 1, i + 1);
+    const unsigned char* Qt = sm[st][0];
+    const unsigned char* Ot = sm[st][1];
+    f32x4 sp[4], dp[4];   // S and dP tiles [query block], then P and dS
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 fq[2][KD], fo[2][KD];
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) {
-        st = mfmab(*(const bf16x8*)&s.Q[16 * qb + l16][32 * ks + 8 * g], kb[ks], st);
-        dp = mfmab(*(const bf16x8*)&s.dO[16 * qb + l16][32 * ks + 8 * g], vb[ks], dp);
-      }
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = 16 * qb + 4 * g + r;    // query of this element (row of S)
-        const bool vis = qq < qlen && kj < klen && (!own || koff + kj <= qoff + qq);
-        const float pr = vis ? __expf(st[r] * sc - s.lse[qq]) : 0.f;
-        p[qb][r] = pr;
-        ds[qb][r] = pr * (dp[r] - s.delta[qq]);
+        for (int ks = 0; ks < KD; ++ks) {
+          fq[b][ks] = tile_row8<D>(Qt, 32 * half + 16 * b + l16, 32 * ks + 8 * g);
+          fo[b][ks] = tile_row8<D>(Ot, 32 * half + 16 * b + l16, 32 * ks + 8 * g);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) {
+          x = mfmab(fq[b][ks], kb[ks], x);
+          y = mfmab(fo[b][ks], vb[ks], y);
+        }
+        sp[2 * half + b] = x;
+        dp[2 * half + b] = y;
       }
     }
-    bf16x8 ph0, pl0, ph1, pl1, dh0, dl0, dh1, dl1;
-    pair_hl(p[0], p[1], ph0, pl0);
-    pair_hl(p[2], p[3], ph1, pl1);
-    pair_hl(ds[0], ds[1], dh0, dl0);
-    pair_hl(ds[2], ds[3], dh1, dl1);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      dvt[db] = mfma_hl(lds_a_perm_bf(&s.dOt[0][0], AT + 8, 16 * db + l16, 0, g), ph0, pl0, dvt[db]);
-      dvt[db] = mfma_hl(lds_a_perm_bf(&s.dOt[0][0], AT + 8, 16 * db + l16, 32, g), ph1, pl1, dvt[db]);
-      dkt[db] = mfma_hl(lds_a_perm_bf(&s.Qt[0][0], AT + 8, 16 * db + l16, 0, g), dh0, dl0, dkt[db]);
-      dkt[db] = mfma_hl(lds_a_perm_bf(&s.Qt[0][0], AT + 8, 16 * db + l16, 32, g), dh1, dl1, dkt[db]);
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qq = 16 * qb + 4 * g + r;   // query of this element (row of S)
+        const bool vis = full || (qq < qlen && kj < klen && (!own || koff + kj <= qoff + qq));
+        const float p = vis ? exp2_(sp[qb][r] * sl2 - sld[st][0][qq]) : 0.f;
+        sp[qb][r] = p;
+        dp[qb][r] = p * (dp[qb][r] - sld[st][1][qq]);
+      }
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {   // 32-deep k steps over the query tile's rows
+      bf16x8 ph, pl, dh, dlo;
+      pair_hl(sp[2 * kq], sp[2 * kq + 1], ph, pl);
+      pair_hl(dp[2 * kq], dp[2 * kq + 1], dh, dlo);
+#pragma unroll
+      for (int d0 = 0; d0 < NDB; d0 += 4) {
+        bf16x8 fo[4], fq[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          fo[db] = tile_a_tr<D>(Ot, 32 * kq, 16 * (d0 + db));
+          fq[db] = tile_a_tr<D>(Qt, 32 * kq, 16 * (d0 + db));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          dvt[d0 + db] = mfma_hl(fo[db], ph, pl, dvt[d0 + db]);
+          dkt[d0 + db] = mfma_hl(fq[db], dh, dlo, dkt[d0 + db]);
+        }
+      }
     }
   }
   // lane holds d = 16 db + 4 g + r of key kj
@@ -503,7 +628,7 @@ __global__ __launch_bounds__(ANT) void k_attn_dkv(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       *(float4*)(dk + 16 * db + 4 * g) =
-          make_float4(sc * dkt[db][0], sc * dkt[db][1], sc * dkt[db][2], sc * dkt[db][3]);
+          make_float4(a.scale * dkt[db][0], a.scale * dkt[db][1], a.scale * dkt[db][2], a.scale * dkt[db][3]);
       *(float4*)(dv + 16 * db + 4 * g) = make_float4(dvt[db][0], dvt[db][1], dvt[db][2], dvt[db][3]);
     }
   }
