@@ -52,7 +52,7 @@ enum {
   KDA_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed */
 };
 
-enum { KDA_MODE_MINCALL = 0, KDA_MODE_EXPANDED = 1 };
+enum { KDA_MODE_MINCALL = 0, KDA_MODE_EXPANDED = 1, KDA_MODE_NOREPLAY = 2, KDA_MODE_NODEWISE = 3 };
 enum { KDA_DTYPE_FP32 = 0, KDA_DTYPE_BF16 = 1 };
 
 typedef struct kda_plan kda_plan;
@@ -97,6 +97,18 @@ typedef struct {
  *   mode     KDA_MODE_MINCALL, or KDA_MODE_EXPANDED: one sequence per
  *            trajectory (leaf ascending), all in one round, no sharing; rows
  *            of o / dO / gradients are then the packed (expanded) rows.
+ *            Two ablations of the replay rule (thelatestinai.com Figure 5,
+ *            the no-replay variant; Figure 4, node-wise linear attention),
+ *            both on compact rows like MINCALL and with R = 0:
+ *            KDA_MODE_NOREPLAY: continuations as above, but every side child
+ *            starts at its own first position from the exact state there,
+ *            one round after its parent's sequence; the parent's chunk grid
+ *            is cut at that position (a short chunk) and the child's grid
+ *            starts there.  Continuations minimise rounds under that rule
+ *            (each side start costs one round).
+ *            KDA_MODE_NODEWISE: one sequence per segment, started from its
+ *            parent's end state, round = depth; a sequence ending at an
+ *            inner segment has no leaf (KDA_F_SEQ_LEAF = -1).
  *   out      receives the plan (immutable; free with kda_plan_destroy)
  * Host pointers.  Errors: KDA_ERR_TREE, KDA_ERR_ARG.
  */

@@ -144,7 +144,8 @@ def run_plan_fwd(plan: Plan, q, k, v, g, beta, h0, scale, n_leaf=None):
                 if plan.chunk_save[c] >= 0:
                     bufs[plan.chunk_save[c]] = hs
                     buf_round[plan.chunk_save[c]] = r
-            h_leaf[plan.seq_leaf[s]] = hs
+            if plan.seq_leaf[s] >= 0:   # a node-wise sequence may end at an inner segment
+                h_leaf[plan.seq_leaf[s]] = hs
     return dict(o=o, h_leaf=h_leaf, buffers=bufs, chunk_h=chunk_h)
 
 
@@ -169,7 +170,7 @@ def run_plan_bwd(plan: Plan, q, k, v, g, beta, h0, scale, dO, dh_leaf, fwd=None)
     dh_boundary = np.zeros((plan.n_buf,) + h0.shape[1:])
     for r in reversed(range(plan.n_rounds)):
         for s in range(plan.round_seq_ptr[r], plan.round_seq_ptr[r + 1]):
-            dh = dh_leaf[plan.seq_leaf[s]].copy()
+            dh = dh_leaf[plan.seq_leaf[s]].copy() if plan.seq_leaf[s] >= 0 else np.zeros(h0.shape[1:])
             for c in reversed(range(plan.seq_chunk_ptr[s], plan.seq_chunk_ptr[s + 1])):
                 b = plan.chunk_save[c]
                 if b >= 0:

@@ -56,6 +56,9 @@ from .tree import Tree
 
 MINCALL = 0
 EXPANDED = 1
+NOREPLAY = 2   # side branches start from their exact fork state (no replay)
+NODEWISE = 3   # one sequence per segment, started from its parent's end state
+EXACT_MODES = (NOREPLAY, NODEWISE)
 A_MODE, B_MODE = 0, 1
 
 
@@ -136,6 +139,57 @@ def simulate(tree: Tree, B: int, cont):
     return rounds, R, seg_round, chain_of, chain_head, b_head, init
 
 
+def dp_noreplay(tree: Tree):
+    """Continuations when a side branch starts from its exact fork state: that
+    state exists only once the call that makes it has returned, so every side
+    start costs one round and nothing is replayed.  G(v) = max(G(cont),
+    max over the other children c of 1 + G(c)); the continuation is the child
+    of largest G (ties as in dp_mincall: larger subtree, then smaller id).
+    Returns (cont, G, rounds)."""
+    n = tree.n
+    sub = tree.subtree_tokens()
+    G = [0] * n
+    cont = [-1] * n
+    for v in reversed(tree.preorder):
+        ch = tree.children[v]
+        if not ch:
+            continue
+        cstar = max(ch, key=lambda c: (G[c], int(sub[c]), -c))
+        cont[v] = cstar
+        G[v] = max([G[cstar]] + [1 + G[c] for c in ch if c != cstar])
+    return cont, G, 1 + max(G[r] for r in tree.roots)
+
+
+def simulate_exact(tree: Tree, cont):
+    """Sequences when side branches start from exact fork states: a side child
+    c of v starts at its own first position s_c, from the state that the
+    sequence holding v emits there, one round after that sequence's round.
+    Returns (rounds, seg_round, chain_of, chain_head, b_head, init) as
+    simulate does."""
+    n = tree.n
+    chain_of = [-1] * n
+    chain_head, b_head, chain_round, init = [], [], [], []
+    for v in tree.preorder:
+        p = int(tree.parent[v])
+        if p >= 0 and cont[p] == v:
+            chain_of[v] = chain_of[p]
+            continue
+        cid = len(chain_head)
+        chain_head.append(v)
+        if p < 0:
+            b_head.append(0)
+            chain_round.append(0)
+            init.append(("h0", tree.root_index[v]))
+        else:
+            S = chain_of[p]
+            b_head.append(int(tree.start[v]))
+            chain_round.append(chain_round[S] + 1)
+            init.append(("buf", S, int(tree.start[v])))
+        chain_of[v] = cid
+    seg_round = [chain_round[chain_of[v]] for v in range(n)]
+    return 1 + max(chain_round), seg_round, chain_of, chain_head, b_head, init
+
+
 def exhaustive_min_rounds(tree: Tree, B: int, limit: int = 200000):
     """Minimum rounds over every continuation assignment, where each internal
     node continues one of its children or none."""
@@ -182,7 +236,8 @@ class Plan:
     # per sequence
     seq_round: np.ndarray
     seq_head: np.ndarray
-    seq_leaf: np.ndarray          # leaf index (leaves ascending)
+    seq_leaf: np.ndarray          # leaf index (leaves ascending); -1 if the sequence ends at an
+                                  # inner segment (node-wise plans)
     seq_b_head: np.ndarray
     seq_replay: np.ndarray
     seq_row_ptr: np.ndarray       # [n_seq+1] into packed rows
@@ -237,8 +292,20 @@ def build_plan(tree: Tree, B: int, mode: int = MINCALL) -> Plan:
         n_rounds, R = 1, 0
         bufs = []
     else:
-        cont, _, rounds = dp_mincall(tree, B)
-        rounds_s, R, seg_round, chain_of, chain_head, b_head, init = simulate(tree, B, cont)
+        if mode == MINCALL:
+            cont, _, rounds = dp_mincall(tree, B)
+            rounds_s, R, seg_round, chain_of, chain_head, b_head, init = simulate(tree, B, cont)
+        elif mode == NOREPLAY:
+            cont, _, rounds = dp_noreplay(tree)
+            rounds_s, seg_round, chain_of, chain_head, b_head, init = simulate_exact(tree, cont)
+            R = 0
+        elif mode == NODEWISE:
+            cont = [-1] * n
+            rounds = 1 + max(tree.depth(v) for v in range(n))
+            rounds_s, seg_round, chain_of, chain_head, b_head, init = simulate_exact(tree, cont)
+            R = 0
+        else:
+            raise ValueError("unknown mode")
         assert rounds_s == rounds
         n_rounds = rounds
         nch = len(chain_head)
@@ -261,13 +328,16 @@ def build_plan(tree: Tree, B: int, mode: int = MINCALL) -> Plan:
             ini = init[c]
             if ini[0] == "buf":
                 ini = ("buf", seq_of_chain[ini[1]], ini[2])
-            seqs.append(dict(round=chain_round[c], head=h, leaf=tree.leaf_index[leaf],
+            seqs.append(dict(round=chain_round[c], head=h, leaf=tree.leaf_index.get(leaf, -1),
                              b=b_head[c], r=r, rows=np.concatenate([rep, own]), init=ini))
         seg_seq = _i64([seq_of_chain[chain_of[v]] for v in range(n)])
         seg_round = _i64(seg_round)
         seg_is_cont = _i64([0 if tree.parent[v] < 0 else int(cont[tree.parent[v]] == v)
                             for v in range(n)])
-        seg_b = _i64([-1 if seg_is_cont[v] else B * (int(tree.start[v]) // B) for v in range(n)])
+        if mode == MINCALL:
+            seg_b = _i64([-1 if seg_is_cont[v] else B * (int(tree.start[v]) // B) for v in range(n)])
+        else:
+            seg_b = _i64([-1 if seg_is_cont[v] else int(tree.start[v]) for v in range(n)])
         seg_rep = _i64([0 if seg_is_cont[v] else int(tree.start[v]) - int(seg_b[v])
                         for v in range(n)])
         bufs = sorted({(s["init"][1], s["init"][2]) for s in seqs if s["init"][0] == "buf"})
@@ -288,21 +358,35 @@ def build_plan(tree: Tree, B: int, mode: int = MINCALL) -> Plan:
             else:
                 out_row.append(int(rows[j]))
         seq_row_ptr.append(base + len(rows))
-        for c0 in range(0, len(rows), B):
-            L = min(B, len(rows) - c0)
+        # chunks: the sequence's own B-grid from its start; with exact starts
+        # the grid is also cut at every position a side branch starts from
+        cuts = sorted(pos - s["b"] for (sp, pos) in bufs if sp == si) if mode in EXACT_MODES else []
+        c0 = 0
+        while c0 < len(rows):
+            nxt = min(len(rows), (c0 // B + 1) * B)
+            for x in cuts:
+                if c0 < x < nxt:
+                    nxt = x
+                    break
+            L = nxt - c0
             chunk_seq.append(si)
             chunk_row0.append(base + c0)
             chunk_len.append(L)
             endpos = s["b"] + c0 + L
-            chunk_save.append(buf_id.get((si, endpos), -1) if L == B else -1)
+            if mode in EXACT_MODES or L == B:
+                chunk_save.append(buf_id.get((si, endpos), -1))
+            else:
+                chunk_save.append(-1)
+            c0 = nxt
         seq_chunk_ptr.append(len(chunk_seq))
     buf_seq = _i64([bk[0] for bk in bufs])
     buf_pos = _i64([bk[1] for bk in bufs])
     buf_chunk = []
     for (si, b) in bufs:
-        k = (b - seqs[si]["b"]) // B - 1
-        buf_chunk.append(seq_chunk_ptr[si] + k)
-        assert chunk_save[seq_chunk_ptr[si] + k] == buf_id[(si, b)]
+        hits = [c for c in range(seq_chunk_ptr[si], seq_chunk_ptr[si + 1])
+                if chunk_save[c] == buf_id[(si, b)]]
+        assert len(hits) == 1, "handoff buffer not at exactly one chunk end"
+        buf_chunk.append(hits[0])
     cons = [[] for _ in bufs]
     for si, s in enumerate(seqs):
         if s["init"][0] == "buf":

@@ -108,6 +108,10 @@ class Tree:
             v = int(self.parent[v])
         return p[::-1]
 
+    def depth(self, v: int) -> int:
+        """Number of ancestors of segment v (a root has depth 0)."""
+        return len(self.path(v)) - 1
+
     def seg_rows(self, v: int) -> np.ndarray:
         return np.arange(self.seg_row[v], self.seg_row[v] + self.seg_len[v], dtype=np.int64)
 

@@ -67,8 +67,19 @@ def oracle_tree(t: Tree, inp, dO, dhl, plan: B.KDAPlan | None = None, bwd=True):
         if plan is not None and plan.info["n_buf"]:
             bseq, bpos = plan.export("BUF_SEQ"), plan.export("BUF_POS")
             leaf_of_seq = plan.export("SEQ_LEAF")
+            head_of_seq = plan.export("SEQ_HEAD")
             leaves = plan.export("LEAF_SEG")
-            bounds = [(int(leaves[leaf_of_seq[s]]), int(p)) for s, p in zip(bseq, bpos)]
+
+            def leaf_on_path(s):
+                # a node-wise sequence (one segment) may end at an inner
+                # segment: any leaf below it has the same root path prefix
+                if leaf_of_seq[s] >= 0:
+                    return int(leaves[leaf_of_seq[s]])
+                v = int(head_of_seq[s])
+                while t.children[v]:
+                    v = t.children[v][0]
+                return v
+            bounds = [(leaf_on_path(s), int(p)) for s, p in zip(bseq, bpos)]
         g = okda.tree_bwd(t, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale, dO, dhl,
                           boundaries=bounds)
         res.update(dq=g["dq"], dk=g["dk"], dv=g["dv"], dg=g["dg"], dbeta=g["dbeta"],

@@ -22,18 +22,20 @@ from tree_packed_chunkwise_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("widx,heads", [(1, (0, 15)), (2, (0, 15)), (3, (5,))])
-def test_fullsize_trajectory_parity(widx, heads):
+@pytest.mark.parametrize("widx,heads,mode", [(1, (0, 15), B.MINCALL), (2, (0, 15), B.MINCALL),
+                                             (3, (5,), B.MINCALL), (2, (3,), B.NOREPLAY),
+                                             (2, (3,), B.NODEWISE), (3, (5,), B.NODEWISE)])
+def test_fullsize_trajectory_parity(widx, heads, mode):
     import torch
     w = synth.workload(widx)
     t = Tree(w.tree.parent, w.tree.seg_len, w.tree.seg_row)
-    plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk)
+    plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk, mode)
     info = plan.info
     N, H, D = info["n_rows"], w.H, w.dk
     leaves = [int(x) for x in plan.export("LEAF_SEG")]
     li = int(np.random.Generator(np.random.PCG64(100 + widx)).integers(len(leaves)))
     rows = t.path_rows(leaves[li])
-    print(f"case {w.name}: rows={N} rounds={info['n_rounds']} R={info['R']} "
+    print(f"case {w.name} mode {mode}: rows={N} rounds={info['n_rounds']} R={info['R']} "
           f"trajectory leaf={leaves[li]} length={len(rows)} heads={heads}", flush=True)
     dev = torch.device("cuda:0")
     inp = synth.make_kda_inputs_device(7000 + widx, N, H, D, D, dev, w.bf16)

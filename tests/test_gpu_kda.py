@@ -58,6 +58,22 @@ def test_random_forests(seed, D, chunk, bf16):
     _check(t, inp, plan, dO, dhl)
 
 
+@pytest.mark.parametrize("mode", [B.NOREPLAY, B.NODEWISE])
+@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("D,chunk,bf16", [(64, 16, False), (128, 64, True)])
+def test_exact_start_modes(mode, seed, D, chunk, bf16):
+    """The no-replay and node-wise plans (side branches start from their
+    exact fork states, chunk grids cut there) compute the same functions."""
+    rng = np.random.Generator(np.random.PCG64(40 + seed))
+    spec = synth.tree_random(rng, 10, 1, 3 * chunk, n_roots=1 + seed)
+    if seed:
+        spec = synth.shuffled_rows(spec, rng)
+    t, inp, plan, dO, dhl = make_case(spec, 2, D, bf16, 50 + seed, gate="weak", h0_mode="randn",
+                                      chunk=chunk, mode=mode)
+    assert plan.info["R"] == 0
+    _check(t, inp, plan, dO, dhl)
+
+
 @pytest.mark.parametrize("beta_mode", ["zero", "one"])
 def test_degenerate_beta(beta_mode):
     rng = np.random.Generator(np.random.PCG64(7))

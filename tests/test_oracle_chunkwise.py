@@ -88,3 +88,26 @@ def test_strong_decay_chunk_no_overflow():
     assert np.all(np.isfinite(O))
     np.testing.assert_allclose(O, o_ref[:, 0], rtol=1e-10, atol=1e-13)
     np.testing.assert_allclose(hn, S_ref[0], rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", [planner.NOREPLAY, planner.NODEWISE])
+@pytest.mark.parametrize("B", [4, 16, 64])
+@pytest.mark.parametrize("seed", range(3))
+def test_exact_mode_plans_equal_recurrence(mode, B, seed):
+    """Side branches started from exact fork states (no replay): the same
+    functions of the inputs, forward and reverse."""
+    t, inp, rng = _case(20 + seed, gate=("weak" if seed % 2 else "default"), n_roots=1 + seed % 2)
+    H, D = inp.q.shape[1], inp.q.shape[2]
+    p = planner.build_plan(t, B, mode)
+    o, hl = kda.tree_fwd(t, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale)
+    f = chunkwise.run_plan_fwd(p, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale,
+                               n_leaf=len(t.leaves))
+    np.testing.assert_allclose(f["o"], o, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(f["h_leaf"], hl, rtol=1e-11, atol=1e-12)
+    dO = rng.standard_normal((t.n_rows, H, D))
+    dhl = rng.standard_normal((len(t.leaves), H, D, D))
+    ref = kda.tree_bwd(t, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale, dO, dhl)
+    got = chunkwise.run_plan_bwd(p, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale, dO,
+                                 dhl, fwd=f)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        np.testing.assert_allclose(got[n], ref[n], rtol=1e-9, atol=1e-11)

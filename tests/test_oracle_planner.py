@@ -135,3 +135,86 @@ def test_malformed_trees_rejected():
         Tree([-1, 5], [1, 1])             # parent out of range
     with pytest.raises(TreeError):
         Tree([-1, 0], [2, 2], [0, 1])     # overlapping rows
+
+
+# ---- exact-state starts (the no-replay ablation and node-wise execution) ----
+
+def _exhaustive_exact_rounds(t, limit=200000):
+    """Minimum rounds over every continuation assignment when side branches
+    start from their exact fork states."""
+    import itertools
+    internal = [v for v in range(t.n) if t.children[v]]
+    choices = [[-1] + t.children[v] for v in internal]
+    total = 1
+    for c in choices:
+        total *= len(c)
+    assert total <= limit
+    best = None
+    for combo in itertools.product(*choices):
+        cont = [-1] * t.n
+        for v, c in zip(internal, combo):
+            cont[v] = c
+        r = planner.simulate_exact(t, cont)[0]
+        best = r if best is None else min(best, r)
+    return best
+
+
+def test_noreplay_dp_matches_exhaustive_search():
+    rng = np.random.Generator(np.random.PCG64(23))
+    for _ in range(300):
+        t = _rand_tree(rng)
+        cont, _, rounds = planner.dp_noreplay(t)
+        assert rounds == _exhaustive_exact_rounds(t)
+        assert planner.simulate_exact(t, cont)[0] == rounds
+
+
+def test_nodewise_rounds_are_depths():
+    rng = np.random.Generator(np.random.PCG64(29))
+    for _ in range(100):
+        t = _rand_tree(rng, 12)
+        p = planner.build_plan(t, 8, planner.NODEWISE)
+        assert p.n_rounds == 1 + max(t.depth(v) for v in range(t.n))
+        assert p.n_seq == t.n
+        assert list(p.seg_round) == [t.depth(v) for v in range(t.n)]
+        assert not np.any(p.seg_is_cont)
+
+
+def test_fig1_exact_modes():
+    # A40 -> {B30 -> {D25, E15}, C20}: no-replay continues A > B > D and starts
+    # C at 40 and E at 70 from their exact states one round later; node-wise
+    # runs one segment per sequence, a round per depth
+    t = Tree([-1, 0, 0, 1, 1], [40, 30, 20, 25, 15])
+    p = planner.build_plan(t, 16, planner.NOREPLAY)
+    assert p.n_rounds == 2 and p.R == 0
+    assert list(p.seg_is_cont) == [0, 1, 0, 1, 0]
+    assert list(p.seg_b[[2, 4]]) == [40, 70]
+    assert list(p.buf_pos) == [40, 70]
+    # the A > B > D sequence is cut at 40 and 70: chunk ends at 16, 32, 40, 48, 64, 70, 80, 95
+    s0 = p.seg_seq[0]
+    lens = p.chunk_len[p.seq_chunk_ptr[s0]:p.seq_chunk_ptr[s0 + 1]]
+    assert list(np.cumsum(lens)) == [16, 32, 40, 48, 64, 70, 80, 95]
+    q = planner.build_plan(t, 16, planner.NODEWISE)
+    assert q.n_rounds == 3 and q.n_seq == 5 and q.R == 0
+    assert list(q.seg_round) == [0, 1, 1, 2, 2]
+    assert list(q.seq_leaf[q.seg_seq[[0, 1]]]) == [-1, -1]   # A and B end at inner segments
+
+
+@pytest.mark.parametrize("mode", [planner.NOREPLAY, planner.NODEWISE])
+def test_exact_mode_structure(mode):
+    rng = np.random.Generator(np.random.PCG64(31 + mode))
+    for _ in range(100):
+        t = _rand_tree(rng, 12)
+        for B in (1, 4, 16):
+            p = planner.build_plan(t, B, mode)
+            assert p.R == 0 and p.n_packed == t.n_rows
+            assert sorted(p.row_index.tolist()) == list(range(t.n_rows))
+            assert np.all(p.out_row == p.row_index) and np.all(p.chunk_len <= B)
+            for s in range(p.n_seq):
+                if p.seq_init_kind[s] == 1:
+                    b = p.seq_init_idx[s]
+                    assert p.seq_round[p.buf_seq[b]] < p.seq_round[s]
+                    assert p.seq_b_head[s] == p.buf_pos[b] == t.start[p.seq_head[s]]
+                    c = p.buf_chunk[b]
+                    ps = p.buf_seq[b]
+                    end = p.seq_b_head[ps] + (p.chunk_row0[c] + p.chunk_len[c] - p.seq_row_ptr[ps])
+                    assert p.chunk_save[c] == b and end == p.buf_pos[b]

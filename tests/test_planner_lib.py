@@ -71,14 +71,15 @@ def test_random_forests_bit_exact(seed):
         if rng.integers(0, 2):
             spec = synth.shuffled_rows(spec, rng)
         for chunk in (1, 4, 16, 64):
-            for mode in (OP.MINCALL, OP.EXPANDED):
+            for mode in (OP.MINCALL, OP.EXPANDED, OP.NOREPLAY, OP.NODEWISE):
                 _compare(spec, chunk, mode)
 
 
 @pytest.mark.parametrize("idx", [0, 1, 3])
-def test_workload_trees_bit_exact(idx):
+@pytest.mark.parametrize("mode", [0, 2, 3])
+def test_workload_trees_bit_exact(idx, mode):
     w = synth.workload(idx)
-    _compare(w.tree, w.chunk, OP.MINCALL)
+    _compare(w.tree, w.chunk, mode)
 
 
 def test_workload_plan_shapes():

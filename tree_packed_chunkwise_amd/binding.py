@@ -19,7 +19,7 @@ import numpy as np
 
 LIB_PATH = Path(__file__).resolve().with_name("libkda_tree.so")
 
-MINCALL, EXPANDED = 0, 1
+MINCALL, EXPANDED, NOREPLAY, NODEWISE = 0, 1, 2, 3
 DT_FP32, DT_BF16 = 0, 1
 
 FIELDS = [

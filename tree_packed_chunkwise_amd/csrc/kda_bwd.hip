@@ -54,7 +54,8 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 
   f32x4 dh[G::NCB];
   {
-    const float* src = a.dh_leaf ? a.dh_leaf + ((size_t)a.plan.seq_leaf[seq] * H + h) * DD : nullptr;
+    const int leaf = a.plan.seq_leaf[seq];   // -1: the sequence ends at an inner segment
+    const float* src = (a.dh_leaf && leaf >= 0) ? a.dh_leaf + ((size_t)leaf * H + h) * DD : nullptr;
 #pragma unroll
     for (int C = 0; C < G::NCB; ++C)
 #pragma unroll

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       }
     }
   }
-  if (sw) {
+  if (sw && a.plan.seq_leaf[seq] >= 0) {   // node-wise sequences may end at an inner segment
     float* dst = a.h_leaf + ((size_t)a.plan.seq_leaf[seq] * H + h) * DD;
 #pragma unroll
     for (int C = 0; C < G::NCB; ++C)

@@ -55,10 +55,11 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     err = "chunk size must be positive";
     return -4;
   }
-  if (mode != 0 && mode != 1) {
+  if (mode < 0 || mode > 3) {
     err = "unknown mode";
     return -4;
   }
+  const bool exact = mode == 2 || mode == 3;   // side branches start from exact fork states
   const int32_t n = n_seg;
   P = Plan();
   P.mode = mode;
@@ -242,6 +243,64 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
       return -1;
     }
     P.n_rounds = rounds;
+  } else if (exact) {
+    // ---- exact-state starts: no replay ----
+    // A side branch starts at its own first position from the state that the
+    // sequence holding its parent emits there, one round after that
+    // sequence's round.  No-replay mode keeps the continuation structure,
+    // chosen by a one-mode DP (every side start costs one round):
+    // G(v) = max(G(cont), max over the other children of 1 + G(c)), the
+    // continuation being the child of largest G (ties: larger subtree, then
+    // smaller id).  Node-wise mode has no continuations: one sequence per
+    // segment, rounds by depth.
+    std::vector<int32_t> cont(n, -1);
+    if (mode == 2) {
+      std::vector<int64_t> sub(n);
+      for (int32_t i = 0; i < n; ++i) sub[i] = seg_len[i];
+      for (int32_t i = n - 1; i >= 0; --i) {
+        int32_t v = order[i];
+        if (parent[v] >= 0) sub[parent[v]] += sub[v];
+      }
+      std::vector<int32_t> G(n, 0);
+      for (int32_t i = n - 1; i >= 0; --i) {
+        int32_t v = order[i];
+        if (nchild(v) == 0) continue;
+        int32_t best = -1;
+        for (int32_t j = child_ptr[v]; j < child_ptr[v + 1]; ++j) {
+          int32_t c = child_list[j];
+          bool better = best < 0 || G[c] > G[best] || (G[c] == G[best] && sub[c] > sub[best]) ||
+                        (G[c] == G[best] && sub[c] == sub[best] && c < best);
+          if (better) best = c;
+        }
+        cont[v] = best;
+        int32_t gv = G[best];
+        for (int32_t j = child_ptr[v]; j < child_ptr[v + 1]; ++j)
+          if (child_list[j] != best) gv = std::max(gv, 1 + G[child_list[j]]);
+        G[v] = gv;
+      }
+    }
+    for (int32_t v : order) {
+      int32_t p = parent[v];
+      if (p >= 0 && cont[p] == v) {
+        chain_of[v] = chain_of[p];
+      } else {
+        Chain c;
+        c.head = v;
+        if (p < 0) {
+          c.round = 0; c.b_head = 0; c.init_kind = 0; c.init_a = root_index[v];
+        } else {
+          c.round = chains[chain_of[p]].round + 1;
+          c.b_head = s[v];
+          c.init_kind = 1; c.init_a = chain_of[p]; c.init_b = s[v];
+        }
+        chain_of[v] = (int32_t)chains.size();
+        chains.push_back(c);
+      }
+      chains[chain_of[v]].members.push_back(v);
+    }
+    int32_t maxr = 0;
+    for (auto& c : chains) maxr = std::max(maxr, c.round);
+    P.n_rounds = maxr + 1;
   } else {
     // ---- expanded: one sequence per trajectory ----
     for (int32_t li = 0; li < P.n_leaf; ++li) {
@@ -261,7 +320,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
   const int32_t nc = (int32_t)chains.size();
   std::vector<int32_t> seq_order(nc);
   for (int32_t i = 0; i < nc; ++i) seq_order[i] = i;
-  if (mode == 0)
+  if (mode != 1)
     std::sort(seq_order.begin(), seq_order.end(), [&](int32_t a, int32_t b) {
       if (chains[a].round != chains[b].round) return chains[a].round < chains[b].round;
       return chains[a].head < chains[b].head;
@@ -282,7 +341,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
   // ---- per-segment exports ----
   P.seg_round.assign(n, 0); P.seg_seq.assign(n, -1); P.seg_is_cont.assign(n, 0);
   P.seg_b.assign(n, -1); P.seg_replay.assign(n, 0);
-  if (mode == 0) {
+  if (mode != 1) {
     for (int32_t v = 0; v < n; ++v) {
       const Chain& c = chains[chain_of[v]];
       P.seg_round[v] = c.round;
@@ -306,10 +365,10 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     const Chain& c = chains[seq_order[si]];
     P.round_seq_ptr[c.round + 1]++;
     int32_t leaf = c.members.back();
-    int64_t r = (mode == 0) ? (s[c.head] - c.b_head) : 0;
+    int64_t r = (mode != 1) ? (s[c.head] - c.b_head) : 0;
     P.seq_round.push_back(c.round);
     P.seq_head.push_back(c.head);
-    P.seq_leaf.push_back(leaf_index[leaf]);
+    P.seq_leaf.push_back(leaf_index[leaf]);   // -1: a node-wise sequence ending at an inner segment
     P.seq_b_head.push_back((int32_t)c.b_head);
     P.seq_replay.push_back((int32_t)r);
     P.seq_init_kind.push_back(c.init_kind);
@@ -334,16 +393,25 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
       return -1;
     }
     for (int64_t j = r; j < len; ++j)
-      P.out_row[base + j] = (mode == 0) ? P.row_index[base + j] : (int32_t)(base + j);
+      P.out_row[base + j] = (mode != 1) ? P.row_index[base + j] : (int32_t)(base + j);
     P.seq_row_ptr.push_back((int32_t)packed);
-    for (int64_t c0 = 0; c0 < len; c0 += B) {
-      int32_t L = (int32_t)std::min<int64_t>(B, len - c0);
+    // chunks: the sequence's own B-grid from its start; with exact-state
+    // starts the grid is also cut at every position a side branch starts from
+    std::vector<int64_t> cuts;
+    if (exact)
+      for (auto it = buf_id.lower_bound({si, INT64_MIN}); it != buf_id.end() && it->first.first == si; ++it)
+        cuts.push_back(it->first.second - c.b_head);
+    for (int64_t c0 = 0, ci = 0; c0 < len;) {
+      int64_t nxt = std::min<int64_t>(len, (c0 / B + 1) * B);
+      while (ci < (int64_t)cuts.size() && cuts[ci] <= c0) ++ci;
+      if (ci < (int64_t)cuts.size() && cuts[ci] < nxt) nxt = cuts[ci];
+      int32_t L = (int32_t)(nxt - c0);
       P.chunk_seq.push_back(si);
       P.chunk_row0.push_back((int32_t)(base + c0));
       P.chunk_len.push_back(L);
       int64_t endpos = c.b_head + c0 + L;
       int32_t save = -1;
-      if (L == B) {
+      if (exact || L == B) {
         auto it = buf_id.find({si, endpos});
         if (it != buf_id.end()) save = it->second;
       }
@@ -352,6 +420,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
       P.chunk_nrep.push_back(nrep);
       P.chunk_rep0.push_back(rep_slots);
       rep_slots += nrep;
+      c0 = nxt;
     }
     P.seq_chunk_ptr.push_back((int32_t)P.chunk_seq.size());
   }
@@ -360,7 +429,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     P.round_seq_ptr[r + 1] += P.round_seq_ptr[r];
   }
   P.n_packed = packed;
-  P.n_out_rows = (mode == 0) ? n_rows : packed;
+  P.n_out_rows = (mode != 1) ? n_rows : packed;
 
   // ---- handoff buffers and their consumers ----
   P.buf_seq.assign(nbuf, 0); P.buf_pos.assign(nbuf, 0); P.buf_chunk.assign(nbuf, -1);
@@ -369,10 +438,11 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     int64_t b = kv.first.second;
     P.buf_seq[bi] = si;
     P.buf_pos[bi] = b;
-    int64_t k = (b - P.seq_b_head[si]) / B - 1;
-    int32_t ch = P.seq_chunk_ptr[si] + (int32_t)k;
-    if (k < 0 || ch >= P.seq_chunk_ptr[si + 1] || P.chunk_save[ch] != bi) {
-      err = "internal: handoff buffer not at a chunk end";
+    int32_t ch = -1, hits = 0;
+    for (int32_t cc = P.seq_chunk_ptr[si]; cc < P.seq_chunk_ptr[si + 1]; ++cc)
+      if (P.chunk_save[cc] == bi) { ch = cc; ++hits; }
+    if (hits != 1 || P.buf_pos[bi] != b) {
+      err = "internal: handoff buffer not at exactly one chunk end";
       return -1;
     }
     P.buf_chunk[bi] = ch;
