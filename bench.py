@@ -112,6 +112,56 @@ def image_bytes(B, D, in_bytes):
     return head, head + in_bytes * B * D
 
 
+def replay_ablation(dev, H=16, D=128):
+    """Replay versus exact-fork-state starts, per handoff depth (the synthetic
+    analogue of thelatestinai.com Figure 5): on a complete binary tree of
+    depth 5 (segments of 64-256 tokens, bf16 inputs), the forward output of
+    each plan mode against the trajectory-expanded run of the same kernels
+    (every trajectory on its own B-aligned grid), as relative L2 over the rows
+    at each handoff depth (side starts on the row's root path in the min-call
+    plan)."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    rng = np.random.Generator(np.random.PCG64(55))
+    spec = synth.tree_kary(2, 5, 64, 256, rng, name="binary_d5")
+    n_rows = int(np.sum(spec.seg_len))
+    inp = synth.make_kda_inputs_device(5500, n_rows, H, D, D, dev, True)
+    outs, plans = {}, {}
+    for name, mode in (("mincall", B.MINCALL), ("expanded", B.EXPANDED), ("noreplay", B.NOREPLAY),
+                       ("nodewise", B.NODEWISE)):
+        pl = B.KDAPlan(spec.parent, spec.seg_len, spec.seg_row, 64, mode)
+        f = B.kda_tree_fwd(pl, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], None, inp["scale"])
+        o = f["o"]
+        if mode == B.EXPANDED:   # packed rows -> compact rows (identical copies)
+            ri = torch.from_numpy(np.asarray(pl.export("ROW_INDEX"), np.int64)).to(dev)
+            oc = torch.empty(n_rows, H, D, device=dev)
+            oc[ri] = o
+            o = oc
+        outs[name], plans[name] = o.double(), pl
+    torch.cuda.synchronize()
+    p0 = plans["mincall"]
+    cont, parent = p0.export("SEG_IS_CONT"), spec.parent
+    hd = np.zeros(len(parent), np.int64)
+    for v in range(len(parent)):   # parents precede children in id order here
+        hd[v] = 0 if parent[v] < 0 else hd[parent[v]] + (0 if cont[v] else 1)
+    row_hd = np.repeat(hd, spec.seg_len)
+    res = {"tree": f"complete binary, depth 5, {len(parent)} segments, {n_rows} rows, "
+                   f"{H} heads, d={D}, bf16, chunk 64",
+           "reference": "trajectory-expanded run of the same kernels",
+           "handoff_depth": list(range(int(row_hd.max()) + 1)),
+           "rows": [int(np.sum(row_hd == d_)) for d_ in range(int(row_hd.max()) + 1)]}
+    ref = outs["expanded"]
+    for name in ("mincall", "noreplay", "nodewise"):
+        errs = []
+        for d_ in res["handoff_depth"]:
+            sel = torch.from_numpy(np.nonzero(row_hd == d_)[0]).to(dev)
+            a_, b_ = outs[name][sel], ref[sel]
+            errs.append(float(torch.linalg.norm(a_ - b_) / torch.linalg.norm(b_)))
+        res[f"{name}_rel_l2"] = [float(f"{e:.3e}") for e in errs]
+    return res
+
+
 def kernel_bytes(name, info, H, D, in_bytes=2):
     """Algorithmic bytes of all launches of one kernel class in one step: the
     tensors its role requires it to read and write once (documented per
@@ -417,33 +467,50 @@ def main():
                     "traffic": measured_traffic(dom, a.workload), "bytes_per_launch": int(per_launch),
                     "avg_launch_ms": round(kernels[dom]["avg_launch_ms"], 4)}
 
-    # trajectory-expanded execution of the same tree, same kernels
-    expanded = None
-    if a.expanded_steps > 0:
-        eplan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk, B.EXPANDED)
-        ei = eplan.info
-        eg = torch.Generator(device=dev)
-        eg.manual_seed(7)
-        dOe = torch.randn((ei["n_out_rows"], H, D), device=dev, generator=eg).to(dt)
-        efo = B.alloc_fwd(eplan, H, D, dev)
-        ebo = B.alloc_bwd(eplan, H, D, dev)
+    # the same tree and kernels under the other plan modes: trajectory-expanded
+    # execution (no sharing), and the two exact-fork-state ablations of the
+    # replay rule (no-replay: min-call packing with cut chunk grids;
+    # node-wise: one sequence per segment)
+    def time_mode(mode, steps, seed):
+        mplan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk, mode)
+        mi = mplan.info
+        mg = torch.Generator(device=dev)
+        mg.manual_seed(seed)
+        dOm = torch.randn((mi["n_out_rows"], H, D), device=dev, generator=mg).to(dt)
+        mfo = B.alloc_fwd(mplan, H, D, dev)
+        mbo = B.alloc_bwd(mplan, H, D, dev)
 
-        def estep():
-            B.kda_tree_fwd(eplan, q, k, v, g, beta, None, inp.scale, out=efo)
-            B.kda_tree_bwd(eplan, q, k, v, g, beta, efo["saved"], dOe, dhl, None, inp.scale,
-                           out=ebo)
-        estep()
+        def mstep():
+            B.kda_tree_fwd(mplan, q, k, v, g, beta, None, inp.scale, out=mfo)
+            B.kda_tree_bwd(mplan, q, k, v, g, beta, mfo["saved"], dOm, dhl, None, inp.scale,
+                           out=mbo)
+        mstep()
         torch.cuda.synchronize()
         e0.record()
-        for _ in range(a.expanded_steps):
-            estep()
+        for _ in range(steps):
+            mstep()
         e1.record()
         torch.cuda.synchronize()
-        ems = e0.elapsed_time(e1) / a.expanded_steps
+        mms = e0.elapsed_time(e1) / steps
+        del mfo, mbo, dOm
+        return mms, mi
+
+    expanded, modes = None, None
+    if a.expanded_steps > 0:
+        ems, ei = time_mode(B.EXPANDED, a.expanded_steps, 7)
         expanded = {"ms_per_step": round(ems, 3), "speedup": round(ems / ms, 3),
                     "expanded_rows": int(ei["n_packed"])}
-        del efo, ebo, dOe
+        modes = {"mincall": {"ms_per_step": round(ms, 3), "rounds": int(info["n_rounds"]),
+                             "sequences": int(info["n_seq"]), "chunks": int(info["n_chunks"]),
+                             "replay_rows": int(info["R"])}}
+        for name, mode in (("noreplay", B.NOREPLAY), ("nodewise", B.NODEWISE)):
+            mms, mi = time_mode(mode, a.expanded_steps, 9)
+            modes[name] = {"ms_per_step": round(mms, 3), "rounds": int(mi["n_rounds"]),
+                           "sequences": int(mi["n_seq"]), "chunks": int(mi["n_chunks"]),
+                           "replay_rows": int(mi["R"]),
+                           "unique_tokens_per_s": round(N / (mms / 1e3), 1)}
 
+    ablation = replay_ablation(dev) if a.expanded_steps > 0 else None
     attention = measure_attention(a.attn_steps) if a.attn_steps > 0 else None
     hybrid = measure_hybrid(a.hybrid_steps) if a.hybrid_steps > 0 else None
 
@@ -464,7 +531,8 @@ def main():
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_frac, 5)},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "plan_host_ms": round(plan_host_ms, 3), "plan_upload_ms": round(upload_ms, 3),
-        "expanded": expanded, "kernels": kernels, "finite": ok,
+        "expanded": expanded, "plan_modes": modes, "replay_ablation": ablation,
+        "kernels": kernels, "finite": ok,
         "tree_attention": attention, "hybrid_group": hybrid,
     }
     print(json.dumps(out), flush=True)
