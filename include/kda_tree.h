@@ -23,8 +23,8 @@
  *     row-major, with the row (token) dimension first: q,k [rows,H,dk];
  *     v [rows,H,dv]; g [rows,H,dk] fp32; beta [rows,H] fp32; o [rows,H,dv]
  *     fp32; states [*,H,dk,dv] fp32.  Every device pointer (tensors,
- *     `saved`, `ws`) is 16-byte aligned (KDA_ERR_ARG otherwise): rows move
- *     in 16-byte vectors.
+ *     `saved`, `ws`) is 16-byte aligned, beta and dbeta 4-byte aligned
+ *     (KDA_ERR_ARG otherwise): rows move in 16-byte vectors.
  *   - The library never allocates device memory and never synchronises the
  *     device.  Work is enqueued on `stream` (a hipStream_t; NULL = default
  *     stream) in stream order.
@@ -313,6 +313,32 @@ int kda_timing_read(int32_t idx, char* name, int32_t name_len, int64_t* launches
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* kda_last_error(void);
+
+/*
+ * Sharing windows (thelatestinai.com Figure 3; HARTS abstract): a producer
+ * call computes a shared prefix once and consumer microbatches start from its
+ * end states; within the window the gradients of the consumers' start states
+ * accumulate into the producer's end-state gradients before the one producer
+ * backward.  The calls are kda_tree_fwd / kda_tree_bwd on separate plans
+ * (consumer roots take their h0 from the producer's h_leaf); these two calls
+ * move and sum the states between them.  A state is `elems` floats (H*dk*dv,
+ * a multiple of 4); src and dst are device pointers, 16-byte aligned; index
+ * arrays are device int32 arrays.  Stream-ordered; no allocation.
+ *
+ * kda_state_copy: dst[dst_idx[i]] = src[src_idx[i]] for i < n (a NULL index
+ *   array is the identity).  Used to hand producer end states to consumer
+ *   roots and to scatter leaf states into a whole-tree array.
+ * kda_state_sum: dst[d] = (accumulate ? dst[d] : 0) + sum of src[idx[j]] over
+ *   j in [ptr[d], ptr[d+1]) in ascending j, for d < n_dst (an empty range
+ *   gives dst[d] or 0).  Fixed order: bitwise deterministic.  Used to
+ *   accumulate consumer start-state gradients into the producer's end-state
+ *   gradients, one microbatch after another.
+ * Errors: KDA_ERR_ARG (bad sizes, null or misaligned pointers), KDA_ERR_HIP.
+ */
+int kda_state_copy(const float* src, const int32_t* src_idx, float* dst, const int32_t* dst_idx,
+                   int32_t n, int64_t elems, void* stream);
+int kda_state_sum(const float* src, const int32_t* ptr, const int32_t* idx, int32_t n_dst,
+                  int64_t elems, int32_t accumulate, float* dst, void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,8 @@ EXPORTS = [
     "kda_plan_device_offset", "kda_saved_bytes", "kda_fwd_workspace_bytes",
     "kda_bwd_workspace_bytes", "kda_tree_fwd", "kda_tree_bwd", "gather_logprobs",
     "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
-    "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd",
+    "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "kda_state_copy",
+    "kda_state_sum",
 ]
 
 
@@ -99,6 +100,10 @@ def load_library(path: Path | str | None = None):
     L.tree_attn_fwd.restype = ctypes.c_int
     L.tree_attn_bwd.argtypes = [vp, vp, i32, i32, f32] + [vp] * 10 + [sz, vp]
     L.tree_attn_bwd.restype = ctypes.c_int
+    L.kda_state_copy.argtypes = [vp, vp, vp, vp, i32, i64, vp]
+    L.kda_state_copy.restype = ctypes.c_int
+    L.kda_state_sum.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp]
+    L.kda_state_sum.restype = ctypes.c_int
     L.kda_timing_enable.argtypes = [i32]
     L.kda_timing_enable.restype = ctypes.c_int
     L.kda_timing_read.argtypes = [i32, ctypes.c_char_p, i32, ctypes.POINTER(i64),
@@ -281,6 +286,26 @@ def kda_tree_bwd(plan: KDAPlan, q, k, v, g, beta, saved, dO, dh_leaf=None, h0=No
         _p(out["dh0"]), _p(out.get("dh_boundary")), _p(out["ws"]), out["ws"].numel(),
         _stream(q)))
     return out
+
+
+def kda_state_copy(src, src_idx, dst, dst_idx, n: int):
+    """dst[dst_idx[i]] = src[src_idx[i]] for i < n over [*, H, dk, dv] fp32 state
+    arrays (None index = identity; index arrays are device int32)."""
+    _need_cuda(src, src_idx, dst, dst_idx)
+    elems = int(np.prod(src.shape[1:]))
+    _check(load_library().kda_state_copy(_p(src), _p(src_idx), _p(dst), _p(dst_idx), int(n), elems,
+                                         _stream(src)))
+    return dst
+
+
+def kda_state_sum(src, ptr, idx, dst, accumulate: bool):
+    """dst[d] = (dst[d] if accumulate else 0) + sum of src[idx[j]], j in [ptr[d], ptr[d+1]),
+    in ascending j (ptr, idx device int32)."""
+    _need_cuda(src, ptr, idx, dst)
+    elems = int(np.prod(dst.shape[1:]))
+    _check(load_library().kda_state_sum(_p(src), _p(ptr), _p(idx), int(ptr.shape[0] - 1), elems,
+                                        1 if accumulate else 0, _p(dst), _stream(dst)))
+    return dst
 
 
 def gather_logprobs(logits, pos_row, pos_target, out=None):

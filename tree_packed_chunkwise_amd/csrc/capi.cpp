@@ -30,6 +30,10 @@ hipError_t launch_gather_bwd(const void* logits, bool bf16, int64_t n_rows, int 
                              const float* lse, const int* row_pos_ptr, const int* row_pos_idx,
                              const int* pos_tgt, const float* dlogp, void* dlogits,
                              hipStream_t st);
+hipError_t launch_state_copy(const float* src, const int* sidx, float* dst, const int* didx, int n,
+                             int64_t elems, hipStream_t st);
+hipError_t launch_state_sum(const float* src, const int* ptr, const int* idx, int n_dst,
+                            int64_t elems, int accumulate, float* dst, hipStream_t st);
 }  // namespace kda
 
 struct kda_plan {
@@ -333,8 +337,8 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
     return fail(KDA_ERR_SHAPE, "in_dtype must be KDA_DTYPE_BF16 or KDA_DTYPE_FP32");
   if (!q || !k || !v || !g || !beta || !o || !h_leaf || !saved || !ws)
     return fail(KDA_ERR_ARG, "null tensor argument");
-  if (!aligned16({q, k, v, g, beta, h0, o, h_leaf, saved, ws}))
-    return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned");
+  if (!aligned16({q, k, v, g, h0, o, h_leaf, saved, ws}) || ((uintptr_t)beta) % 4)
+    return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned (beta: 4-byte)");
   if (ws_bytes < kda_fwd_workspace_bytes(plan, H, dk, dv))
     return fail(KDA_ERR_WORKSPACE, "forward workspace too small");
   kda::FwdArgs a;
@@ -371,8 +375,9 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   if (!q || !k || !v || !g || !beta || !saved || !dO || !dq || !dk_ || !dv_ || !dg || !dbeta ||
       !dh0 || !ws)
     return fail(KDA_ERR_ARG, "null tensor argument");
-  if (!aligned16({q, k, v, g, beta, saved, dO, dh_leaf, dq, dk_, dv_, dg, dbeta, dh0, dh_boundary, ws}))
-    return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned");
+  if (!aligned16({q, k, v, g, saved, dO, dh_leaf, dq, dk_, dv_, dg, dh0, dh_boundary, ws}) ||
+      ((uintptr_t)beta) % 4 || ((uintptr_t)dbeta) % 4)
+    return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned (beta, dbeta: 4-byte)");
   if (ws_bytes < kda_bwd_workspace_bytes(plan, H, dk, dv))
     return fail(KDA_ERR_WORKSPACE, "backward workspace too small");
   SavedView sv = carve_saved(p, H, dk, (void*)saved, nullptr);
@@ -519,6 +524,29 @@ int tree_attn_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t
                                       (int)p.att_kw_tile.size(), (int)p.att_ks_tile.size(),
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tree_attn_bwd launch");
+  return KDA_OK;
+}
+
+int kda_state_copy(const float* src, const int32_t* src_idx, float* dst, const int32_t* dst_idx,
+                   int32_t n, int64_t elems, void* stream) {
+  if (n < 0 || elems < 0 || elems % 4) return fail(KDA_ERR_ARG, "n >= 0 and elems a multiple of 4");
+  if (n == 0 || elems == 0) return KDA_OK;
+  if (!src || !dst) return fail(KDA_ERR_ARG, "null state argument");
+  if (!aligned16({src, dst})) return fail(KDA_ERR_ARG, "state arguments must be 16-byte aligned");
+  hipError_t e = kda::launch_state_copy(src, src_idx, dst, dst_idx, n, elems, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_state_copy launch");
+  return KDA_OK;
+}
+
+int kda_state_sum(const float* src, const int32_t* ptr, const int32_t* idx, int32_t n_dst,
+                  int64_t elems, int32_t accumulate, float* dst, void* stream) {
+  if (n_dst < 0 || elems < 0 || elems % 4) return fail(KDA_ERR_ARG, "n_dst >= 0 and elems a multiple of 4");
+  if (n_dst == 0 || elems == 0) return KDA_OK;
+  if (!ptr || !dst) return fail(KDA_ERR_ARG, "null argument");
+  if (!aligned16({src, dst})) return fail(KDA_ERR_ARG, "state arguments must be 16-byte aligned");
+  hipError_t e = kda::launch_state_sum(src, ptr, idx, n_dst, elems, accumulate ? 1 : 0, dst,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_state_sum launch");
   return KDA_OK;
 }
 
