@@ -162,6 +162,42 @@ def replay_ablation(dev, H=16, D=128):
     return res
 
 
+def measure_window(w, dev, steps, ms_single):
+    """A sharing window on the benchmark tree: the producer call holds the
+    root and its children (depth <= 1), the 16 depth-2 subtrees run as 4
+    consumer microbatches started from the producer's end states, and their
+    start-state gradients accumulate before the producer backward.  Forward
+    and backward of the whole window per step; ms_single is the single packed
+    call on the same tree."""
+    import torch
+    from tree_packed_chunkwise_amd import synth
+    from tree_packed_chunkwise_amd.window import SharingWindow
+    win = SharingWindow(w.tree.parent, w.tree.seg_len, 1, 4, chunk=w.chunk)
+    N, H, D = win.n_rows, w.H, w.dk
+    inp = synth.make_kda_inputs_device(9100, N, H, D, D, dev, w.bf16)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9101)
+    dO = torch.randn(N, H, D, device=dev, generator=gen).to(inp["q"].dtype)
+    dhl = torch.randn(win.n_leaf, H, D, D, device=dev, generator=gen)
+
+    def step():
+        return win.run(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                       dO=dO, dh_leaf=dhl)
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"producer": "depth <= 1 (5 segments), %d rows" % win.rows_p,
+            "consumers": "16 depth-2 subtrees in 4 microbatches, rows %s" % [m["rows"] for m in win.micro],
+            "ms_per_step": round(ms, 3), "unique_tokens_per_s": round(N / (ms / 1e3), 1),
+            "vs_single_call": round(ms_single / ms, 3)}
+
+
 def kernel_bytes(name, info, H, D, in_bytes=2):
     """Algorithmic bytes of all launches of one kernel class in one step: the
     tensors its role requires it to read and write once (documented per
@@ -511,6 +547,7 @@ def main():
                            "unique_tokens_per_s": round(N / (mms / 1e3), 1)}
 
     ablation = replay_ablation(dev) if a.expanded_steps > 0 else None
+    window = measure_window(w, dev, a.expanded_steps, ms) if a.expanded_steps > 0 else None
     attention = measure_attention(a.attn_steps) if a.attn_steps > 0 else None
     hybrid = measure_hybrid(a.hybrid_steps) if a.hybrid_steps > 0 else None
 
@@ -531,7 +568,8 @@ def main():
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_frac, 5)},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "plan_host_ms": round(plan_host_ms, 3), "plan_upload_ms": round(upload_ms, 3),
-        "expanded": expanded, "plan_modes": modes, "replay_ablation": ablation,
+        "expanded": expanded, "plan_modes": modes, "sharing_window": window,
+        "replay_ablation": ablation,
         "kernels": kernels, "finite": ok,
         "tree_attention": attention, "hybrid_group": hybrid,
     }
