@@ -539,7 +539,8 @@ def main():
         modes = {"mincall": {"ms_per_step": round(ms, 3), "rounds": int(info["n_rounds"]),
                              "sequences": int(info["n_seq"]), "chunks": int(info["n_chunks"]),
                              "replay_rows": int(info["R"])}}
-        for name, mode in (("noreplay", B.NOREPLAY), ("nodewise", B.NODEWISE)):
+        for name, mode in (("noreplay", B.NOREPLAY), ("nodewise", B.NODEWISE),
+                           ("mincall_short", B.MINCALL_SHORT)):
             mms, mi = time_mode(mode, a.expanded_steps, 9)
             modes[name] = {"ms_per_step": round(mms, 3), "rounds": int(mi["n_rounds"]),
                            "sequences": int(mi["n_seq"]), "chunks": int(mi["n_chunks"]),

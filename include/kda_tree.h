@@ -52,7 +52,13 @@ enum {
   KDA_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed */
 };
 
-enum { KDA_MODE_MINCALL = 0, KDA_MODE_EXPANDED = 1, KDA_MODE_NOREPLAY = 2, KDA_MODE_NODEWISE = 3 };
+enum {
+  KDA_MODE_MINCALL = 0,
+  KDA_MODE_EXPANDED = 1,
+  KDA_MODE_NOREPLAY = 2,
+  KDA_MODE_NODEWISE = 3,
+  KDA_MODE_MINCALL_SHORT = 4
+};
 enum { KDA_DTYPE_FP32 = 0, KDA_DTYPE_BF16 = 1 };
 
 typedef struct kda_plan kda_plan;
@@ -109,6 +115,12 @@ typedef struct {
  *            KDA_MODE_NODEWISE: one sequence per segment, started from its
  *            parent's end state, round = depth; a sequence ending at an
  *            inner segment has no leaf (KDA_F_SEQ_LEAF = -1).
+ *            KDA_MODE_MINCALL_SHORT (not the pages' planner; a variant for
+ *            the GPU): the same minimum number of rounds and the same replay
+ *            rule, but a segment whose children can all be side-started
+ *            without adding a round continues none of them, so sequences end
+ *            sooner and the longest sequence of a round (what its call waits
+ *            for) shrinks, at the price of more replay rows.
  *   out      receives the plan (immutable; free with kda_plan_destroy)
  * Host pointers.  Errors: KDA_ERR_TREE, KDA_ERR_ARG.
  */

@@ -58,6 +58,7 @@ MINCALL = 0
 EXPANDED = 1
 NOREPLAY = 2   # side branches start from their exact fork state (no replay)
 NODEWISE = 3   # one sequence per segment, started from its parent's end state
+MINCALL_SHORT = 4   # minimum rounds; a continuation that costs no round is dropped
 EXACT_MODES = (NOREPLAY, NODEWISE)
 A_MODE, B_MODE = 0, 1
 
@@ -66,9 +67,15 @@ def _head_mode(s, e, B):
     return A_MODE if e // B == s // B else B_MODE
 
 
-def dp_mincall(tree: Tree, B: int):
+def dp_mincall(tree: Tree, B: int, short: bool = False):
     """Two-mode DP.  Returns (cont, G, rounds): cont[v] is the continuation
-    child of v (-1 for a leaf), G[v] = (G(v,A), G(v,B))."""
+    child of v (-1 for a leaf), G[v] = (G(v,A), G(v,B)).
+
+    short=True: where side-starting every child of v gives the same G(v, m)
+    for both modes as continuing the best one, v continues none of them.  The
+    round count is unchanged (G is unchanged everywhere); the sequences end
+    sooner, which shortens the longest sequence of later rounds (the chain a
+    round's call waits for) at the price of more replay rows."""
     n = tree.n
     sub = tree.subtree_tokens()
     G = [(0, 0)] * n
@@ -83,7 +90,7 @@ def dp_mincall(tree: Tree, B: int):
         cstar = max(ch, key=lambda c: (base[c], int(sub[c]), -c))
         cont[v] = cstar
         same_chunk = tree.end[cstar] // B == tree.start[cstar] // B
-        gv = []
+        gv, gnone = [], []
         for m in (A_MODE, B_MODE):
             d = 0 if m == A_MODE else 1
             cm = A_MODE if (m == A_MODE and same_chunk) else B_MODE
@@ -92,6 +99,9 @@ def dp_mincall(tree: Tree, B: int):
                 if c != cstar:
                     worst = max(worst, d + base[c])
             gv.append(worst)
+            gnone.append(max(d + base[c] for c in ch))
+        if short and gnone == gv:
+            cont[v] = -1
         G[v] = tuple(gv)
     rounds = 0
     for r in tree.roots:
@@ -292,8 +302,8 @@ def build_plan(tree: Tree, B: int, mode: int = MINCALL) -> Plan:
         n_rounds, R = 1, 0
         bufs = []
     else:
-        if mode == MINCALL:
-            cont, _, rounds = dp_mincall(tree, B)
+        if mode in (MINCALL, MINCALL_SHORT):
+            cont, _, rounds = dp_mincall(tree, B, short=(mode == MINCALL_SHORT))
             rounds_s, R, seg_round, chain_of, chain_head, b_head, init = simulate(tree, B, cont)
         elif mode == NOREPLAY:
             cont, _, rounds = dp_noreplay(tree)
@@ -334,7 +344,7 @@ def build_plan(tree: Tree, B: int, mode: int = MINCALL) -> Plan:
         seg_round = _i64(seg_round)
         seg_is_cont = _i64([0 if tree.parent[v] < 0 else int(cont[tree.parent[v]] == v)
                             for v in range(n)])
-        if mode == MINCALL:
+        if mode in (MINCALL, MINCALL_SHORT):
             seg_b = _i64([-1 if seg_is_cont[v] else B * (int(tree.start[v]) // B) for v in range(n)])
         else:
             seg_b = _i64([-1 if seg_is_cont[v] else int(tree.start[v]) for v in range(n)])

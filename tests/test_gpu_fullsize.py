@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("widx,heads,mode", [(1, (0, 15), B.MINCALL), (2, (0, 15), B.MINCALL),
                                              (3, (5,), B.MINCALL), (2, (3,), B.NOREPLAY),
-                                             (2, (3,), B.NODEWISE), (3, (5,), B.NODEWISE)])
+                                             (2, (3,), B.NODEWISE), (3, (5,), B.NODEWISE),
+                                             (2, (7,), B.MINCALL_SHORT)])
 def test_fullsize_trajectory_parity(widx, heads, mode):
     import torch
     w = synth.workload(widx)

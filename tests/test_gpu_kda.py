@@ -58,6 +58,17 @@ def test_random_forests(seed, D, chunk, bf16):
     _check(t, inp, plan, dO, dhl)
 
 
+@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("D,chunk,bf16", [(64, 16, False), (128, 64, True)])
+def test_short_chain_mode(seed, D, chunk, bf16):
+    """The short-chain variant of the min-call plan: same functions."""
+    rng = np.random.Generator(np.random.PCG64(60 + seed))
+    spec = synth.tree_kary(3, 3, chunk, 4 * chunk, rng)
+    t, inp, plan, dO, dhl = make_case(spec, 2, D, bf16, 70 + seed, gate="weak", h0_mode="randn",
+                                      chunk=chunk, mode=B.MINCALL_SHORT)
+    _check(t, inp, plan, dO, dhl)
+
+
 @pytest.mark.parametrize("mode", [B.NOREPLAY, B.NODEWISE])
 @pytest.mark.parametrize("seed", range(2))
 @pytest.mark.parametrize("D,chunk,bf16", [(64, 16, False), (128, 64, True)])
@@ -111,14 +122,16 @@ def test_expanded_mode_matches_expansion():
         assert rel_l2(got[n], np.concatenate([e[n] for e in exp])) <= TOL, n
 
 
-def test_tree_equals_expanded_bitwise_on_gpu():
+@pytest.mark.parametrize("mode", [B.MINCALL, B.MINCALL_SHORT])
+def test_tree_equals_expanded_bitwise_on_gpu(mode):
     """Replay keeps every trajectory's chunk grid: the packed tree run and the
     trajectory-expanded run compute the same chunks from the same states, so
-    outputs and leaf states agree bit for bit."""
+    outputs and leaf states agree bit for bit (with or without the short-chain
+    tie-break, which changes only which sequences carry which segments)."""
     rng = np.random.Generator(np.random.PCG64(31))
     spec = synth.tree_random(rng, 10, 20, 200, n_roots=1)
     t, inp, plan, dO, dhl = make_case(spec, 2, 128, True, 32, chunk=64, h0_mode="randn",
-                                      gate="weak")
+                                      gate="weak", mode=mode)
     tree = gpu_run(plan, inp)
     eplan = B.KDAPlan(spec.parent, spec.seg_len, spec.seg_row, 64, B.EXPANDED)
     exp = gpu_run(eplan, inp)

@@ -20,12 +20,13 @@ def _case(seed, gate="weak", n_seg=8, lo=1, hi=40, n_roots=1, H=2, D=6, h0="rand
     return t, inp, rng
 
 
+@pytest.mark.parametrize("mode", [planner.MINCALL, planner.MINCALL_SHORT])
 @pytest.mark.parametrize("B", [1, 4, 16, 64])
 @pytest.mark.parametrize("seed", range(4))
-def test_plan_forward_equals_recurrence(B, seed):
+def test_plan_forward_equals_recurrence(B, seed, mode):
     t, inp, _ = _case(seed, gate=("weak" if seed % 2 else "default"), n_roots=1 + seed % 2)
     o, hl = kda.tree_fwd(t, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale)
-    p = planner.build_plan(t, B)
+    p = planner.build_plan(t, B, mode)
     f = chunkwise.run_plan_fwd(p, inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0, inp.scale,
                                n_leaf=len(t.leaves))
     np.testing.assert_allclose(f["o"], o, rtol=1e-11, atol=1e-12)

@@ -218,3 +218,20 @@ def test_exact_mode_structure(mode):
                     ps = p.buf_seq[b]
                     end = p.seq_b_head[ps] + (p.chunk_row0[c] + p.chunk_len[c] - p.seq_row_ptr[ps])
                     assert p.chunk_save[c] == b and end == p.buf_pos[b]
+
+
+@pytest.mark.parametrize("B", [4, 8, 16])
+def test_short_chain_variant_keeps_minimum_rounds(B):
+    """The short-chain variant drops only continuations that cost no round:
+    the round count stays the exhaustive minimum, and its sequences are never
+    longer than the min-call plan's."""
+    rng = np.random.Generator(np.random.PCG64(40 + B))
+    for _ in range(200):
+        t = _rand_tree(rng)
+        cont, _, rounds = planner.dp_mincall(t, B, short=True)
+        assert rounds == planner.exhaustive_min_rounds(t, B)
+        assert planner.simulate(t, B, cont)[0] == rounds
+        p0 = planner.build_plan(t, B, planner.MINCALL)
+        p4 = planner.build_plan(t, B, planner.MINCALL_SHORT)
+        assert p4.n_rounds == p0.n_rounds
+        assert np.diff(p4.seq_row_ptr).max() <= np.diff(p0.seq_row_ptr).max() + B

@@ -71,12 +71,12 @@ def test_random_forests_bit_exact(seed):
         if rng.integers(0, 2):
             spec = synth.shuffled_rows(spec, rng)
         for chunk in (1, 4, 16, 64):
-            for mode in (OP.MINCALL, OP.EXPANDED, OP.NOREPLAY, OP.NODEWISE):
+            for mode in (OP.MINCALL, OP.EXPANDED, OP.NOREPLAY, OP.NODEWISE, OP.MINCALL_SHORT):
                 _compare(spec, chunk, mode)
 
 
 @pytest.mark.parametrize("idx", [0, 1, 3])
-@pytest.mark.parametrize("mode", [0, 2, 3])
+@pytest.mark.parametrize("mode", [0, 2, 3, 4])
 def test_workload_trees_bit_exact(idx, mode):
     w = synth.workload(idx)
     _compare(w.tree, w.chunk, mode)

@@ -19,7 +19,7 @@ import numpy as np
 
 LIB_PATH = Path(__file__).resolve().with_name("libkda_tree.so")
 
-MINCALL, EXPANDED, NOREPLAY, NODEWISE = 0, 1, 2, 3
+MINCALL, EXPANDED, NOREPLAY, NODEWISE, MINCALL_SHORT = 0, 1, 2, 3, 4
 DT_FP32, DT_BF16 = 0, 1
 
 FIELDS = [

@@ -55,11 +55,13 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     err = "chunk size must be positive";
     return -4;
   }
-  if (mode < 0 || mode > 3) {
+  if (mode < 0 || mode > 4) {
     err = "unknown mode";
     return -4;
   }
   const bool exact = mode == 2 || mode == 3;   // side branches start from exact fork states
+  const bool mincall = mode == 0 || mode == 4; // replay side starts, minimum rounds
+  const bool shortc = mode == 4;               // drop continuations that cost no round
   const int32_t n = n_seg;
   P = Plan();
   P.mode = mode;
@@ -172,7 +174,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
   std::vector<int32_t> chain_of(n, -1);
   int64_t R = 0;
 
-  if (mode == 0) {
+  if (mincall) {
     // ---- two-mode DP (children before parents) ----
     std::vector<int64_t> sub(n);
     for (int32_t i = 0; i < n; ++i) sub[i] = seg_len[i];
@@ -203,6 +205,9 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
       int32_t cB = gB[best];
       gA[v] = std::max(cA, other == INT_MIN ? 0 : other);
       gB[v] = std::max(cB, other == INT_MIN ? 0 : other + 1);
+      // short-chain variant: side-starting every child costs no round in
+      // either mode -> continue none (G unchanged, sequences end sooner)
+      if (shortc && top1 == gA[v] && top1 + 1 == gB[v]) cont[v] = -1;
     }
     int32_t rounds = 0;
     for (int32_t r : roots) {
