@@ -132,7 +132,7 @@ BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) 
   BwdWS w;
   const size_t nb = (size_t)p.n_chunks() * H;
   w.dOp = c.take((size_t)p.n_packed * H * D);
-  w.dy = c.take((size_t)p.n_packed * H * D);
+  w.dy = c.take(nb * p.B * D);   // per chunk-head 16x16 tiles
   w.dhc = (_Float16*)c.take(nb * D * D / 2);
   w.slot = c.take((size_t)p.n_seq() * H * D * D);
   const size_t nrep = (size_t)p.R;

@@ -152,6 +152,17 @@ __device__ inline f32x4 ld_h4(const _Float16* p) {
   const f16x4 h = *(const f16x4*)p;
   return (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
+// The fp16 state copies (chunk start states, chunk end-state gradients) and
+// the chunk-row gradients dy handed from the reverse rounds to the chunk pass
+// are kept as 16x16 tiles: tile (C, W) holds rows 16C .. 16C + 15 and columns
+// 16W .. 16W + 15 at elements (C (D/16) + W) 256, and inside it lane l of the
+// wave that carries column block W keeps its quad_transpose row piece
+// (quad_row, quad_col) at 4 l.  One wave's store or load of a tile thus moves
+// 512 (fp16) or 1024 (fp32) contiguous bytes.
+template <int D>
+__device__ inline size_t state_tile(int C, int W) {
+  return (size_t)(C * (D / 16) + W) * 256 + 4 * (threadIdx.x & 63);
+}
 
 // B fragment from two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k step)
 __device__ inline f16x8 acc_pair(const f32x4& t0, const f32x4& t1) {

@@ -104,7 +104,7 @@ struct BwdArgs {
   float* dh0;
   float* dh_boundary;     // may be null
   void* dOp;              // [n_packed,H,D] dO in packed row order, zero on replay rows
-  float* dy;              // [n_packed,H,D]
+  float* dy;              // [n_chunks,H] x (BC x D in 16x16 tiles, state_tile order)
   _Float16* dhc;          // [n_chunks,H,D,D] gradient of each chunk's end state (fp16 copy)
   float* slot;            // [n_seq,H,D,D] gradient of each sequence's start state
   float* rep_dq;          // [n_replay,H,D] gradients of replayed rows

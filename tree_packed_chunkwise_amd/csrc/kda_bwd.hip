@@ -131,7 +131,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         for (int C = 0; C < G::NCB; ++C) {
           f32x4 x = dh[C];
           quad_transpose(x);
-          st_h4(dst + (size_t)(16 * C + rq) * D + cq, x);
+          st_h4(dst + state_tile<D>(C, col >> 4), x);
         }
       }
       f16x8 dhb[KD];
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         f32x4 dy = mfma16k16(ft[I], acc4(rr), (f32x4){0.f, 0.f, 0.f, 0.f});
         w[I] = dy * bz[I];
         quad_transpose(dy);
-        if (16 * I + rq < len) *(f32x4*)&a.dy[((size_t)(row0 + 16 * I + rq) * H + h) * D + cq] = dy;
+        if (16 * I + rq < len) *(f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(I, col >> 4)] = dy;
       }
       f16x8 wb[KB];
 #pragma unroll

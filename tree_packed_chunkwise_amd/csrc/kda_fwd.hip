@@ -104,7 +104,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
         for (int C = 0; C < G::NCB; ++C) {
           f32x4 x = hs[C];
           quad_transpose(x);
-          st_h4(dst + (size_t)(16 * C + rq) * D + cq, x);
+          st_h4(dst + state_tile<D>(C, col >> 4), x);
         }
       }
       f16x8 hb[KD];

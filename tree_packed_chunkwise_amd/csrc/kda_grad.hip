@@ -206,14 +206,14 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
     const _Float16* dhsrc = a.dhc + blk * DD;
 #pragma unroll
     for (int C = 0; C < NCB; ++C) {
-      const size_t o = (size_t)(16 * C + rq) * D + cq;
+      const size_t o = state_tile<D>(C, wave);
       hC[C] = ld_h4(hsrc + o);
       dhC[C] = ld_h4(dhsrc + o);
     }
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
       const int i = 16 * J + rq;
-      dyv[J] = i < len ? *(const f32x4*)&a.dy[((size_t)(row0 + i) * H + h) * D + cq]
+      dyv[J] = i < len ? *(const f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(J, wave)]
                        : (f32x4){0.f, 0.f, 0.f, 0.f};
       vraw[J] = *(const in4_t<TIn>*)&F->V[16 * J + rq][cq];
     }
