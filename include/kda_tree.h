@@ -27,7 +27,12 @@
  *     (KDA_ERR_ARG otherwise): rows move in 16-byte vectors.
  *   - The library never allocates device memory and never synchronises the
  *     device.  Work is enqueued on `stream` (a hipStream_t; NULL = default
- *     stream) in stream order.
+ *     stream) in stream order.  kda_tree_fwd and kda_tree_bwd run part of
+ *     their kernels on a second stream of the current device (created on
+ *     the first such call, default priority, kept until the process ends),
+ *     forked from `stream` and joined back into it with events: all of
+ *     their work still follows earlier work on `stream` and precedes later
+ *     work on it, and the pattern is valid under stream capture.
  *   - Results are deterministic: bitwise identical from run to run (no
  *     floating-point atomics; every reduction has a fixed order).
  *   - Status codes: KDA_OK (0) or a negative KDA_ERR_*; on error nothing is

@@ -3,7 +3,8 @@
 // Argument checking, buffer carving and launch sequencing only; every step of
 // the computation runs in the HIP kernels (kda_prep.hip, kda_fwd.hip,
 // kda_bwd.hip, kda_grad.hip, kda_reduce.hip, attn.hip, gather.hip), enqueued
-// on the caller's stream.
+// on the caller's stream (the forward and reverse calls also fork a second
+// stream of the device and join it back before returning: schedule.cpp).
 #include <initializer_list>
 #include <hip/hip_runtime.h>
 
@@ -15,11 +16,8 @@
 #include "plan.h"
 
 namespace kda {
-hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
-                      const int* round_ptr_host, int n_rounds, hipStream_t st);
-hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D,
-                      int n_chunks, int64_t n_packed, const int* round_ptr_host, int n_rounds, int n_rep_rows,
-                      int n_root, hipStream_t st);
+hipError_t run_fwd(const FwdArgs& a, bool bf16, int BC, int D, const Plan& p, hipStream_t st);
+hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hipStream_t st);
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int n_tiles, hipStream_t st);
 hipError_t launch_attn_bwd(const AttnArgs& a, int D, int64_t n_rows, int n_tiles, int n_items,
                            int n_split, hipStream_t st);
@@ -352,8 +350,7 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.chunk_h = sv.chunk_h;
   a.bufs = sv.bufs;
   a.fimg = sv.fimg;
-  hipError_t e = kda::launch_fwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(),
-                                 p.round_seq_ptr.data(), p.n_rounds, (hipStream_t)stream);
+  hipError_t e = kda::run_fwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_fwd launch");
   return KDA_OK;
 }
@@ -399,9 +396,7 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.slot = w.slot;
   a.rep_dq = w.rep_dq; a.rep_dk = w.rep_dk; a.rep_dg = w.rep_dg; a.rep_dv = w.rep_dv;
   a.rep_db = w.rep_db;
-  hipError_t e = kda::launch_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p.n_chunks(), p.n_packed,
-                                 p.round_seq_ptr.data(), p.n_rounds, (int)p.rep_row.size(),
-                                 p.n_root, (hipStream_t)stream);
+  hipError_t e = kda::run_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_bwd launch");
   return KDA_OK;
 }

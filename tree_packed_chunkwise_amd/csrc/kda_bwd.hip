@@ -271,10 +271,10 @@ hipError_t launch_bround(const BwdArgs& a, int nseq, int seq0, int slices, hipSt
 }
 
 template <typename TIn, int BC, int D>
-hipError_t launch_brounds_t(const BwdArgs& a, const int* round_ptr_host, int n_rounds,
+hipError_t launch_brounds_t(const BwdArgs& a, const int* round_ptr_host, int r_begin, int r_end,
                             hipStream_t st) {
   constexpr int NCB = D / 16;
-  for (int r = n_rounds - 1; r >= 0; --r) {
+  for (int r = r_end - 1; r >= r_begin; --r) {
     const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
     if (nseq == 0) continue;
     const int sl = round_slices(nseq, a.H, D);
@@ -289,10 +289,12 @@ hipError_t launch_brounds_t(const BwdArgs& a, const int* round_ptr_host, int n_r
   return hipSuccess;
 }
 
+// rounds r_end - 1 down to r_begin
 hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
-                             int n_rounds, hipStream_t st) {
+                             int r_begin, int r_end, hipStream_t st) {
 #define KDA_BR_CASE(T, BCv, Dv) \
-  if (BC == BCv && D == Dv) return launch_brounds_t<T, BCv, Dv>(a, round_ptr_host, n_rounds, st);
+  if (BC == BCv && D == Dv) \
+    return launch_brounds_t<T, BCv, Dv>(a, round_ptr_host, r_begin, r_end, st);
   if (bf16) {
     KDA_BR_CASE(uint16_t, 64, 128)
     KDA_BR_CASE(uint16_t, 64, 64)

@@ -231,10 +231,10 @@ hipError_t launch_round(const FwdArgs& a, int nseq, int seq0, int slices, hipStr
 }
 
 template <typename TIn, int BC, int D>
-hipError_t launch_fwd2_t(const FwdArgs& a, const int* round_ptr_host, int n_rounds,
+hipError_t launch_fwd2_t(const FwdArgs& a, const int* round_ptr_host, int r_begin, int r_end,
                          hipStream_t st) {
   constexpr int NCB = D / 16;
-  for (int r = 0; r < n_rounds; ++r) {
+  for (int r = r_begin; r < r_end; ++r) {
     const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
     if (nseq == 0) continue;
     const int sl = round_slices(nseq, a.H, D);
@@ -249,14 +249,11 @@ hipError_t launch_fwd2_t(const FwdArgs& a, const int* round_ptr_host, int n_roun
   return hipSuccess;
 }
 
-hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st);
-
-hipError_t launch_fwd(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks,
-                      const int* round_ptr_host, int n_rounds, hipStream_t st) {
-  hipError_t e = launch_prep(a, bf16, BC, D, n_chunks, st);
-  if (e != hipSuccess) return e;
+// rounds r_begin .. r_end - 1, in order
+hipError_t launch_fwd_rounds(const FwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
+                             int r_begin, int r_end, hipStream_t st) {
 #define KDA_FWD_CASE(T, BCv, Dv) \
-  if (BC == BCv && D == Dv) return launch_fwd2_t<T, BCv, Dv>(a, round_ptr_host, n_rounds, st);
+  if (BC == BCv && D == Dv) return launch_fwd2_t<T, BCv, Dv>(a, round_ptr_host, r_begin, r_end, st);
   if (bf16) {
     KDA_FWD_CASE(uint16_t, 64, 128)
     KDA_FWD_CASE(uint16_t, 64, 64)

@@ -150,7 +150,7 @@ __device__ inline float* grad_dst(const BwdArgs& a, float* base, float* rep, int
 }
 
 template <typename TIn, int BC, int D>
-__global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
+__global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   using G = GradGeom<BC, D>;
   constexpr int NB = G::NB, NCB = G::NCB, KD = G::KD, NHF = G::NHF, NS = G::NS;
   constexpr int NG = G::NG, NTW = G::NTW, DH = G::DH, NRG = G::NRG, RPT = G::RPT;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
   constexpr bool HALF = (BC == 16);
   constexpr int NV8 = (BC * D / 8 + NT - 1) / NT;   // 8-element vectors of dO per thread
   __shared__ GradSmem<BC, D> s;
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int c = c_begin + blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int H = a.H;
   const size_t blk = (size_t)c * H + h;
@@ -599,15 +599,18 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a) {
 }
 
 template <typename TIn, int BC, int D>
-hipError_t launch_grad_t(const BwdArgs& a, int n_chunks, hipStream_t st) {
+hipError_t launch_grad_t(const BwdArgs& a, int c_begin, int n_chunks, hipStream_t st) {
   if (n_chunks <= 0) return hipSuccess;
-  KDA_LAUNCH("kda_bwd_chunk_grad", (k_bwd_grad<TIn, BC, D>), dim3(n_chunks, a.H), dim3(NT), st, a);
+  KDA_LAUNCH("kda_bwd_chunk_grad", (k_bwd_grad<TIn, BC, D>), dim3(n_chunks, a.H), dim3(NT), st, a,
+             c_begin);
   return hipGetLastError();
 }
 
-hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st) {
+// chunks c_begin .. c_begin + n_chunks - 1
+hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
+                       hipStream_t st) {
 #define KDA_GRAD_CASE(T, BCv, Dv) \
-  if (BC == BCv && D == Dv) return launch_grad_t<T, BCv, Dv>(a, n_chunks, st);
+  if (BC == BCv && D == Dv) return launch_grad_t<T, BCv, Dv>(a, c_begin, n_chunks, st);
   if (bf16) {
     KDA_GRAD_CASE(uint16_t, 64, 128)
     KDA_GRAD_CASE(uint16_t, 64, 64)

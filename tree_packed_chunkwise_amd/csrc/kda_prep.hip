@@ -41,12 +41,12 @@ __device__ inline uint16_t to_in<uint16_t>(float x) {  // exact: x holds a bf16 
 }
 
 template <typename TIn, int BC, int D>
-__global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
+__global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
   using G = Geom<BC, D>;
   using FI = FwdImage<BC, D, TIn>;
   constexpr int NE = G::RPT * G::NHALF;
   __shared__ PrepSmem<BC, D> s;
-  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int c = c_begin + blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int H = a.H;
   const size_t blk = (size_t)c * H + h;
   const int row0 = a.plan.chunk_row0[c];
@@ -142,15 +142,18 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a) {
 }
 
 template <typename TIn, int BC, int D>
-hipError_t launch_prep_t(const FwdArgs& a, int n_chunks, hipStream_t st) {
+hipError_t launch_prep_t(const FwdArgs& a, int c_begin, int n_chunks, hipStream_t st) {
   if (n_chunks <= 0) return hipSuccess;
-  KDA_LAUNCH("kda_chunk_decay", (k_chunk_prep<TIn, BC, D>), dim3(n_chunks, a.H), dim3(NT), st, a);
+  KDA_LAUNCH("kda_chunk_decay", (k_chunk_prep<TIn, BC, D>), dim3(n_chunks, a.H), dim3(NT), st, a,
+             c_begin);
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st) {
+// chunks c_begin .. c_begin + n_chunks - 1
+hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
+                       hipStream_t st) {
 #define KDA_PREP_CASE(T, BCv, Dv) \
-  if (BC == BCv && D == Dv) return launch_prep_t<T, BCv, Dv>(a, n_chunks, st);
+  if (BC == BCv && D == Dv) return launch_prep_t<T, BCv, Dv>(a, c_begin, n_chunks, st);
   if (bf16) {
     KDA_PREP_CASE(uint16_t, 64, 128)
     KDA_PREP_CASE(uint16_t, 64, 64)

@@ -1,14 +1,10 @@
-// kda_reduce.hip -- the reverse pass in full, and its two fixed-order reductions
-// (gfx950).
-//
-// Order of the reverse pass of a plan:
-//   0. dO gathered into packed row order (zero on replay rows);
-//   1. the state-gradient rounds, last round first (kda_bwd.hip);
-//   2. the chunk-local gradients of every chunk, fully parallel (kda_grad.hip);
-//   3. gradients of replayed rows (rows a side sequence recomputes from the
-//      start of its chunk, HARTS Figure 2(c)) added into their compact rows;
-//   4. dh0 of every root: the sum of the start-state gradients of the
-//      sequences that start from it.
+// kda_reduce.hip -- the two fixed-order reductions that close the reverse
+// pass (gfx950), after the state-gradient rounds and the chunk-local
+// gradients of every chunk (launch order in schedule.cpp):
+//   - gradients of replayed rows (rows a side sequence recomputes from the
+//     start of its chunk, HARTS Figure 2(c)) added into their compact rows;
+//   - dh0 of every root: the sum of the start-state gradients of the
+//     sequences that start from it.
 // Both reductions add in a fixed order, so results do not depend on timing.
 #include "common.h"
 #include "timing.h"
@@ -16,11 +12,6 @@
 namespace kda {
 
 constexpr int BT = 256;  // threads per block of the reductions
-
-hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
-                             int n_rounds, hipStream_t st);
-hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks, hipStream_t st);
-hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int D, int64_t n_packed, hipStream_t st);
 
 // replayed-row gradients added into their compact rows (fixed order)
 template <int D>
@@ -80,18 +71,8 @@ hipError_t launch_reduce_t(const BwdArgs& a, int n_rep_rows, int n_root, hipStre
   return hipSuccess;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks, int64_t n_packed,
-                      const int* round_ptr_host, int n_rounds, int n_rep_rows, int n_root,
-                      hipStream_t st) {
+hipError_t launch_reduce(const BwdArgs& a, int D, int n_rep_rows, int n_root, hipStream_t st) {
   if (D != 64 && D != 128) return hipErrorInvalidValue;
-  hipError_t e = launch_gather_dO(a, bf16, D, n_packed, st);
-  if (e != hipSuccess) return e;
-  e = launch_bwd_rounds(a, bf16, BC, D, round_ptr_host, n_rounds, st);
-  if (e != hipSuccess) return e;
-  if (n_chunks > 0) {
-    e = launch_grad(a, bf16, BC, D, n_chunks, st);
-    if (e != hipSuccess) return e;
-  }
   return D == 128 ? launch_reduce_t<128>(a, n_rep_rows, n_root, st)
                   : launch_reduce_t<64>(a, n_rep_rows, n_root, st);
 }
