@@ -80,14 +80,15 @@ def path_bytes_per_token(H, D, in_bytes=2):
     return fwd, bwd
 
 
-# HBM bytes per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-# scaled by a plain device copy's counts (profiles/*_hbm_traffic.md).  A figure
+# HBM bytes per launch of a kernel (mean over the launches of a call), from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a plain device copy's counts
+# (profiles/*_hbm_traffic.md).  A figure
 # holds only for the kernel sources and workload it was measured on: the
 # sources are hashed at run time and the figure is dropped when they differ.
 MEASURED_TRAFFIC = {
     "kda_bwd_chunk_grad": {"sources": ("kda_grad.hip", "chunk.h", "common.h"),
-                           "sha256_16": "d7c311cda4bc7022", "workload": 2,
-                           "bytes_per_launch": 8858676817},
+                           "sha256_16": "c2c9f948e01d6d89", "workload": 2,
+                           "bytes_per_launch": 2305659069},
 }
 
 
@@ -478,6 +479,30 @@ def main():
     fwd_ms, bwd_ms = ef[0].elapsed_time(ef[1]), ef[1].elapsed_time(ef[2])
     ok = bool(torch.isfinite(fo["o"]).all() and torch.isfinite(bo["dq"]).all())
 
+    # the same step with every kernel on the caller's stream (no overlap of the
+    # chunk passes with the round chains): per-kernel times without sharing
+    # the GPU, and the step time of that schedule
+    kt_seq, seq_ms = {}, None
+    if not a.no_timing:
+        B.set_overlap(False)
+        try:
+            step()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(2):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            seq_ms = e0.elapsed_time(e1) / 2
+            B.timing_enable(True)
+            for _ in range(2):
+                step()
+            torch.cuda.synchronize()
+            kt_seq = B.timing_read()
+            B.timing_enable(False)
+        finally:
+            B.set_overlap(True)
+
     value = N / (ms * 1e-3)
     fwd_b, bwd_b = path_bytes_per_token(H, D, 2 if w.bf16 else 4)
     st = H * D * D * 4
@@ -501,7 +526,15 @@ def main():
             roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                     "traffic": measured_traffic(dom, a.workload), "bytes_per_launch": int(per_launch),
-                    "avg_launch_ms": round(kernels[dom]["avg_launch_ms"], 4)}
+                    "avg_launch_ms": round(kernels[dom]["avg_launch_ms"], 4),
+                    "launches_per_step": lps}
+            if dom in kt_seq:
+                cnt_s, tot_s = kt_seq[dom]
+                ms_s = tot_s / 2   # per step
+                roof["single_stream"] = {
+                    "ms_per_step": round(ms_s, 4), "achieved": round(kb / (ms_s * 1e-3) / 1e9, 2),
+                    "frac": round(kb / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                    "step_ms": round(seq_ms, 4)}
 
     # the same tree and kernels under the other plan modes: trajectory-expanded
     # execution (no sharing), and the two exact-fork-state ablations of the

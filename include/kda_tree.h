@@ -32,7 +32,8 @@
  *     the first such call, default priority, kept until the process ends),
  *     forked from `stream` and joined back into it with events: all of
  *     their work still follows earlier work on `stream` and precedes later
- *     work on it, and the pattern is valid under stream capture.
+ *     work on it, and the pattern is valid under stream capture
+ *     (kda_set_overlap(0) keeps all work on `stream`).
  *   - Results are deterministic: bitwise identical from run to run (no
  *     floating-point atomics; every reduction has a fixed order).
  *   - Status codes: KDA_OK (0) or a negative KDA_ERR_*; on error nothing is
@@ -227,6 +228,18 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
                  int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
                  const float* g, const float* beta, const float* h0, float* o, float* h_leaf,
                  void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kda_set_overlap -- process-wide launch policy of kda_tree_fwd / kda_tree_bwd.
+ *
+ * With enable != 0 (the default) the chunk-parallel passes of a call run on a
+ * second stream of the device beside the sequential per-round passes (the
+ * rounds of Figure 2(c) form a chain; the chunk passes do not), forked from
+ * and joined back into the caller's stream.  With enable == 0 every kernel of
+ * a call runs on the caller's stream in order.  Results are bitwise the same
+ * either way.  Takes effect for calls made after it returns.  Returns KDA_OK.
+ */
+int kda_set_overlap(int32_t enable);
 
 /*
  * kda_tree_bwd -- reverse mode of kda_tree_fwd (rounds in reverse order).

@@ -148,3 +148,26 @@ def test_deterministic():
     b = gpu_run(plan, inp, dO, dhl)
     for n in ("o", "h_leaf", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_overlap_matches_single_stream():
+    """The chunk-parallel passes run on a second stream beside the round
+    chains by default; keeping every kernel on the caller's stream must give
+    the same bits (no kernel reads what a kernel beside it writes, and every
+    sum has a fixed order).  The tree has four rounds, so the forward runs
+    three chunk-pass groups beside the rounds and the reverse pass forks the
+    chunk-local gradients twice."""
+    rng = np.random.Generator(np.random.PCG64(53))
+    spec = synth.tree_kary(3, 3, 40, 260, rng)
+    t, inp, plan, dO, dhl = make_case(spec, 2, 128, True, 54, chunk=64, h0_mode="randn")
+    assert plan.info["n_rounds"] == 4
+    try:
+        B.set_overlap(False)
+        one = gpu_run(plan, inp, dO, dhl)
+    finally:
+        B.set_overlap(True)
+    two = gpu_run(plan, inp, dO, dhl)
+    for n in ALL:
+        if one.get(n) is None:
+            continue
+        assert np.array_equal(one[n], two[n]), n

@@ -40,7 +40,7 @@ EXPORTS = [
     "kda_bwd_workspace_bytes", "kda_tree_fwd", "kda_tree_bwd", "gather_logprobs",
     "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
     "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "kda_state_copy",
-    "kda_state_sum",
+    "kda_state_sum", "kda_set_overlap",
 ]
 
 
@@ -106,6 +106,8 @@ def load_library(path: Path | str | None = None):
     L.kda_state_sum.restype = ctypes.c_int
     L.kda_timing_enable.argtypes = [i32]
     L.kda_timing_enable.restype = ctypes.c_int
+    L.kda_set_overlap.argtypes = [i32]
+    L.kda_set_overlap.restype = ctypes.c_int
     L.kda_timing_read.argtypes = [i32, ctypes.c_char_p, i32, ctypes.POINTER(i64),
                                   ctypes.POINTER(ctypes.c_double)]
     L.kda_timing_read.restype = ctypes.c_int
@@ -372,6 +374,13 @@ def tree_attn_bwd(plan: KDAPlan, q, k, v, o, lse, dO, scale=None, out=None, ws=N
                                         _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
                                         _p(dk), _p(dv), _p(ws), ws.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def set_overlap(on: bool = True):
+    """Whether kda_tree_fwd / kda_tree_bwd run their chunk-parallel passes on a
+    second stream beside the round chains (default) or everything on the
+    caller's stream; results are bitwise the same."""
+    _check(load_library().kda_set_overlap(1 if on else 0))
 
 
 def timing_enable(on: bool = True):

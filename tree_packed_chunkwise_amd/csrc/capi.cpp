@@ -18,6 +18,7 @@
 namespace kda {
 hipError_t run_fwd(const FwdArgs& a, bool bf16, int BC, int D, const Plan& p, hipStream_t st);
 hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hipStream_t st);
+void set_overlap(bool on);
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int n_tiles, hipStream_t st);
 hipError_t launch_attn_bwd(const AttnArgs& a, int D, int64_t n_rows, int n_tiles, int n_items,
                            int n_split, hipStream_t st);
@@ -398,6 +399,11 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.rep_db = w.rep_db;
   hipError_t e = kda::run_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_bwd launch");
+  return KDA_OK;
+}
+
+int kda_set_overlap(int32_t enable) {
+  kda::set_overlap(enable != 0);
   return KDA_OK;
 }
 

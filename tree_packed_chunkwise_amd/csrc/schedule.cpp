@@ -17,10 +17,12 @@
 //             joined before the fixed-order reductions.
 // No kernel reads memory that a kernel running beside it writes, and every
 // sum is in a fixed order, so the results do not depend on how the two
-// streams interleave.  The fork/join sequence of a call is enqueued under a
+// streams interleave (kda_set_overlap(0) makes every call use the caller's
+// stream alone, with the same results).  The fork/join sequence of a call is enqueued under a
 // per-device lock (its events are reused from call to call).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -53,6 +55,7 @@ struct Side {
 
 std::mutex g_mu;
 std::map<int, Side*> g_side;
+std::atomic<int> g_overlap{1};
 
 hipError_t side_of_current_device(Side** out) {
   int dev = 0;
@@ -108,11 +111,13 @@ hipError_t group_event(Side* sd, size_t i, hipEvent_t* ev) {
 
 }  // namespace
 
+void set_overlap(bool on) { g_overlap.store(on ? 1 : 0); }
+
 hipError_t run_fwd(const FwdArgs& a, bool bf16, int BC, int D, const Plan& p, hipStream_t st) {
   const int R = p.n_rounds, nc = p.n_chunks();
   const int* rp = p.round_seq_ptr.data();
   const int c1 = R > 1 ? round_chunk_begin(p, 1) : nc;
-  if (c1 == 0 || c1 >= nc) {  // nothing to overlap
+  if (c1 == 0 || c1 >= nc || !g_overlap.load()) {  // nothing to overlap, or one stream asked for
     KDA_TRY(launch_prep(a, bf16, BC, D, 0, nc, st));
     return launch_fwd_rounds(a, bf16, BC, D, rp, 0, R, st);
   }
@@ -149,7 +154,7 @@ hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
   const int* rp = p.round_seq_ptr.data();
   KDA_TRY(launch_gather_dO(a, bf16, D, p.n_packed, st));
   Side* sd = nullptr;
-  if (R > 1 && nc > 0) KDA_TRY(side_of_current_device(&sd));
+  if (R > 1 && nc > 0 && g_overlap.load()) KDA_TRY(side_of_current_device(&sd));
   std::unique_lock<std::mutex> lk;
   if (sd) lk = std::unique_lock<std::mutex>(sd->mu);
   const int group = nc / 4 > 1 ? nc / 4 : 1;
