@@ -173,9 +173,10 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       (const FwdImage<BC, D, TIn>*)(a.fimg + blk * fwd_image_bytes(BC, D));
   const float sc = a.scale;
 
-  // ---- every global load is issued first (none waits on another, except
-  // the row-indexed ones on this thread's own row indices); the LDS writes
-  // and register layouts follow ----
+  // ---- global loads, issued in the order of their first use: loads return
+  // in issue order, so each phase waits only for what it reads while the
+  // later ones are still in flight.  LDS writes and register layouts come
+  // where they are needed. ----
   const int c0 = tid % DH, rg = tid / DH, r0 = rg * RPT;  // element mapping: channel c0 + 64 hf, rows r0 ..
   int rows[RPT];
 #pragma unroll
@@ -185,7 +186,40 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     trow = a.plan.row_index[row0 + tid];
     torow = tid >= nrep ? a.plan.out_row[row0 + tid] : -1;
   }
-  // A and Td of the forward image
+  // g, then k, through this thread's row indices (Gam, K e^Gam)
+  float gm[NE], kk[NE], qq[NE];
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int r = rows[t];
+      const float x = a.g[((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf];
+      gm[hf * RPT + t] = r >= 0 ? x : 0.f;
+    }
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int r = rows[t];
+      const float y = ld_in(k, ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf);
+      kk[hf * RPT + t] = r >= 0 ? y : 0.f;
+    }
+  // start state and V as row pieces (phase 1; quad_transpose turns them into
+  // the accumulator layout), A and Td of the forward image, beta
+  const bool vw = wave < NCB;
+  const int col = 16 * wave + l16;
+  const int cq = 16 * wave + quad_col(), rq = quad_row();
+  f16x4 hraw[NCB], dhraw[NCB];
+  f32x4 dyv[NB], z[NB];
+  in4_t<TIn> vraw[NB];
+  const _Float16* hsrc = a.chunk_h + blk * DD;
+  const _Float16* dhsrc = a.dhc + blk * DD;
+  if (vw) {
+#pragma unroll
+    for (int C = 0; C < NCB; ++C) hraw[C] = *(const f16x4*)(hsrc + state_tile<D>(C, wave));
+#pragma unroll
+    for (int J = 0; J < NB; ++J) vraw[J] = *(const in4_t<TIn>*)&F->V[16 * J + rq][cq];
+  }
   constexpr int NAV = (BC * BC / 8 + NT - 1) / NT;
   f16x8 av[NAV], tv;
 #pragma unroll
@@ -194,77 +228,37 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     if (e < BC * BC / 8) av[n] = *(const f16x8*)&F->L[e / (BC / 8)][(e % (BC / 8)) * 8];
   }
   if (tid < BC * 2) tv = *(const f16x8*)&F->Td[tid / 2][(tid % 2) * 8];
-  // states, dy and V as row pieces (one vector load each; quad_transpose
-  // turns them into the accumulator layout)
-  const bool vw = wave < NCB;
-  const int col = 16 * wave + l16;
-  const int cq = 16 * wave + quad_col(), rq = quad_row();
-  f32x4 hC[NCB], dhC[NCB], dyv[NB], z[NB];
-  in4_t<TIn> vraw[NB];
+  const float tbeta = trow >= 0 ? a.beta[(size_t)trow * H + h] : 0.f;
+  // dy (phase 1), dO (after Z), q (phase 3), the end-state gradient (end of phase 2)
   if (vw) {
-    const _Float16* hsrc = a.chunk_h + blk * DD;
-    const _Float16* dhsrc = a.dhc + blk * DD;
 #pragma unroll
-    for (int C = 0; C < NCB; ++C) {
-      const size_t o = state_tile<D>(C, wave);
-      hC[C] = ld_h4(hsrc + o);
-      dhC[C] = ld_h4(dhsrc + o);
-    }
-#pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      const int i = 16 * J + rq;
-      dyv[J] = i < len ? *(const f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(J, wave)]
-                       : (f32x4){0.f, 0.f, 0.f, 0.f};
-      vraw[J] = *(const in4_t<TIn>*)&F->V[16 * J + rq][cq];
-    }
+    for (int J = 0; J < NB; ++J)
+      dyv[J] = 16 * J + rq < len ? *(const f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(J, wave)]
+                                 : (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  Raw8<TIn> dov[NV8];   // packed dO is zero on replay rows
+  // packed dO (zero on replay rows): loaded without a branch (rows past the
+  // chunk read its first row and are zeroed where used), so that no wait for
+  // it is forced before the later loads are issued
+  Raw8<TIn> dov[NV8];
+  bool dok[NV8];
 #pragma unroll
   for (int n = 0; n < NV8; ++n) {
     const int e = tid + NT * n;
-    dov[n].zero();
-    if (e < BC * D / 8) {
-      const int i = e / (D / 8);
-      if (i < len) dov[n].load(dOp + ((size_t)(row0 + i) * H + h) * D + (e % (D / 8)) * 8);
-    }
+    const int i = e / (D / 8);
+    dok[n] = e < BC * D / 8 && i < len;
+    dov[n].load(dOp + ((size_t)(row0 + (dok[n] ? i : 0)) * H + h) * D + (e % (D / 8)) * 8);
   }
-  // through this thread's row indices: g, k, q; beta of the row table
-  float gm[NE], kk[NE], qq[NE];
 #pragma unroll
   for (int hf = 0; hf < NHF; ++hf)
 #pragma unroll
     for (int t = 0; t < RPT; ++t) {
-      const int n = hf * RPT + t, r = rows[t];
-      const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf;
-      const float x = a.g[off], y = ld_in(k, off), w = ld_in(q, off);
-      gm[n] = r >= 0 ? x : 0.f;
-      kk[n] = r >= 0 ? y : 0.f;
-      qq[n] = r >= 0 ? w : 0.f;
+      const int r = rows[t];
+      const float w = ld_in(q, ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf);
+      qq[hf * RPT + t] = r >= 0 ? w : 0.f;
     }
-  const float tbeta = trow >= 0 ? a.beta[(size_t)trow * H + h] : 0.f;
-  // LDS writes and register layouts
-  if (tid < BC) {
-    s.orow[tid] = torow;
-    s.beta[tid] = tbeta;
-  }
-#pragma unroll
-  for (int n = 0; n < NAV; ++n) {
-    const int e = tid + NT * n;
-    if (e < BC * BC / 8) *(f16x8*)&s.u.p.A[e / (BC / 8)][(e % (BC / 8)) * 8] = av[n];
-  }
-  if (tid < BC * 2) *(f16x8*)&s.u.p.Td[tid / 2][(tid % 2) * 8] = tv;
   if (vw) {
 #pragma unroll
-    for (int C = 0; C < NCB; ++C) {
-      quad_transpose(hC[C]);
-      quad_transpose(dhC[C]);
-    }
-#pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      quad_transpose(dyv[J]);
-      z[J] = in4_to_f32(vraw[J]);
-      quad_transpose(z[J]);
-    }
+    for (int C = 0; C < NCB; ++C) dhraw[C] = *(const f16x4*)(dhsrc + state_tile<D>(C, wave));
   }
 
   // ---- Gam: running sums per row group, then their prefix ----
@@ -302,17 +296,37 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     }
     if (rg == 0) s.degc[cc] = __expf(tot);   // e^Gam_C until deGC is formed
   }
+  if (tid < BC) {
+    s.orow[tid] = torow;
+    s.beta[tid] = tbeta;
+  }
+#pragma unroll
+  for (int n = 0; n < NAV; ++n) {
+    const int e = tid + NT * n;
+    if (e < BC * BC / 8) *(f16x8*)&s.u.p.A[e / (BC / 8)][(e % (BC / 8)) * 8] = av[n];
+  }
+  if (tid < BC * 2) *(f16x8*)&s.u.p.Td[tid / 2][(tid % 2) * 8] = tv;
   __syncthreads();
 
   // ---- phase 1: Z = V - (K e^Gam) h on column block `wave` ----
   if (vw) {
     f16x8 hb[KD];
+    {
+      f32x4 hC[NCB];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hC[2 * ks], hC[2 * ks + 1]);
+      for (int C = 0; C < NCB; ++C) {
+        *(f16x4*)&s.u.p.Hs[16 * C + rq][cq] = hraw[C];   // h as [c][v] fp16, from its row pieces
+        hC[C] = (f32x4){(float)hraw[C][0], (float)hraw[C][1], (float)hraw[C][2], (float)hraw[C][3]};
+        quad_transpose(hC[C]);
+      }
 #pragma unroll
-    for (int C = 0; C < NCB; ++C)
+      for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hC[2 * ks], hC[2 * ks + 1]);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s.u.p.Hs[16 * C + 4 * g + r][col] = (_Float16)hC[C][r];
+    for (int J = 0; J < NB; ++J) {
+      z[J] = in4_to_f32(vraw[J]);
+      quad_transpose(z[J]);
+    }
 #pragma unroll
     for (int J = 0; J < NB; ++J)
 #pragma unroll
@@ -326,21 +340,13 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     if (e < BC * D / 8) {
       f16x8 x;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) x[t] = (_Float16)(sc * dov[n].at(t));
+      for (int t = 0; t < 8; ++t) x[t] = (_Float16)(dok[n] ? sc * dov[n].at(t) : 0.f);
       *(f16x8*)&s.u.p.x.dO[e / (D / 8)][(e % (D / 8)) * 8] = x;
     }
   }
   if (vw) {
-    // deGC partial over this wave's 16 columns (lanes of equal g): channel
-    // 16 C + 4 g + r, 16 channels per butterfly (C in groups of four)
 #pragma unroll
-    for (int C0 = 0; C0 < NCB; C0 += 4) {
-      float x[16];
-#pragma unroll
-      for (int n = 0; n < 16; ++n) x[n] = hC[C0 + n / 4][n % 4] * dhC[C0 + n / 4][n % 4];
-      const float y = row_reduce16x16(x);
-      s.redg[wave][16 * (C0 + l16 / 4) + 4 * g + l16 % 4] = y;
-    }
+    for (int J = 0; J < NB; ++J) quad_transpose(dyv[J]);
     // delta by block forward substitution with the diagonal inverses
     f32x4 d[NB];
 #pragma unroll
@@ -407,9 +413,6 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     *grad_dst(a, a.dbeta, a.rep_db, rep0, s.orow[tid], tid, nrep, h, 1) = acc;
   }
   if (tid < D) {
-    float acc = 0.f;
-    for (int w = 0; w < NCB; ++w) acc += s.redg[w][tid];
-    s.degc[tid] *= acc;   // deGC e^Gam_C
     for (int I = 0; I < NB; ++I)
       for (int J = 0; J <= I; ++J)
         s.dfac[low_index(I, J)][tid] = __expf(s.gref[I][tid] - s.gref[J][tid]);
@@ -465,12 +468,37 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     split_tile(tp, Ph[sl], Pl[sl]);
     split_tile(ta, Ah[sl], Al[sl]);
   }
+  if (vw) {
+    // deGC partial over this wave's 16 columns: channel 16 C + rq, the sum
+    // over v of h dh' (h read back from its fp16 copy, which holds exactly
+    // the stored start state); the four lanes of a row piece differ in lane
+    // bits 2 and 3 (row rotations by 8 and 4)
+    float x[NCB];
+#pragma unroll
+    for (int C = 0; C < NCB; ++C) {
+      const f16x4 hv = *(const f16x4*)&s.u.p.Hs[16 * C + rq][cq];
+      x[C] = (float)hv[0] * (float)dhraw[C][0] + (float)hv[1] * (float)dhraw[C][1] +
+             (float)hv[2] * (float)dhraw[C][2] + (float)hv[3] * (float)dhraw[C][3];
+    }
+#pragma unroll
+    for (int C = 0; C < NCB; ++C) {
+      x[C] += dpp_mov<0x128>(x[C]);   // row_ror:8
+      x[C] += dpp_mov<0x124>(x[C]);   // row_ror:4
+    }
+    if ((lane & 12) == 0) {
+#pragma unroll
+      for (int C = 0; C < NCB; ++C) s.redg[wave][16 * C + rq] = x[C];
+    }
+  }
   __syncthreads();  // h is dead: dh' takes its place
   if (vw) {
 #pragma unroll
-    for (int C = 0; C < NCB; ++C)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s.u.p.Hs[16 * C + 4 * g + r][col] = (_Float16)dhC[C][r];
+    for (int C = 0; C < NCB; ++C) *(f16x4*)&s.u.p.Hs[16 * C + rq][cq] = dhraw[C];
+  }
+  if (tid < D) {
+    float acc = 0.f;
+    for (int w = 0; w < NCB; ++w) acc += s.redg[w][tid];
+    s.degc[tid] *= acc;   // deGC e^Gam_C
   }
   __syncthreads();
 #pragma unroll
