@@ -323,25 +323,40 @@ struct ElemRegs {
   float lk[N], lq[N], rk[N];  // factored operands
 };
 
-// Issues the loads of k, q, g for the thread's elements (rows[t] = input row
-// of chunk row r0 + t, -1 past the chunk: zeros).  No synchronisation.
+// Issues the loads of g, then k, then q for the thread's elements (rows[t] =
+// input row of chunk row r0 + t, -1 past the chunk: zeros), in the order the
+// chunk pass first needs them (loads return in issue order).  No
+// synchronisation.
 template <typename TIn, int BC, int D>
 __device__ inline void elems_load(const TIn* q, const TIn* k, const float* g, int H, int h,
                                   const int (&rows)[Geom<BC, D>::RPT], ElemRegs<BC, D>& er) {
   using G = Geom<BC, D>;
   const int tid = threadIdx.x;
   const int c0 = tid % G::DH;
+  auto off = [&](int hf, int t) {
+    const int r = rows[t];
+    return ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf;
+  };
 #pragma unroll
   for (int hf = 0; hf < G::NHALF; ++hf)
 #pragma unroll
     for (int t = 0; t < G::RPT; ++t) {
-      const int n = hf * G::RPT + t;
-      const int r = rows[t];
-      const size_t off = ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + G::DH * hf;
-      const float kk = ld_in(k, off), qq = ld_in(q, off), gg = g[off];
-      er.k[n] = r >= 0 ? kk : 0.f;
-      er.q[n] = r >= 0 ? qq : 0.f;
-      er.gam[n] = r >= 0 ? gg : 0.f;
+      const float x = g[off(hf, t)];
+      er.gam[hf * G::RPT + t] = rows[t] >= 0 ? x : 0.f;
+    }
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf)
+#pragma unroll
+    for (int t = 0; t < G::RPT; ++t) {
+      const float x = ld_in(k, off(hf, t));
+      er.k[hf * G::RPT + t] = rows[t] >= 0 ? x : 0.f;
+    }
+#pragma unroll
+  for (int hf = 0; hf < G::NHALF; ++hf)
+#pragma unroll
+    for (int t = 0; t < G::RPT; ++t) {
+      const float x = ld_in(q, off(hf, t));
+      er.q[hf * G::RPT + t] = rows[t] >= 0 ? x : 0.f;
     }
 }
 

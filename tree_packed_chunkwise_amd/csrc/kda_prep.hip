@@ -63,6 +63,11 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
     trow = a.plan.row_index[row0 + tid];
     torow = tid >= nrep ? a.plan.out_row[row0 + tid] : -1;
   }
+  // beta, then g, k, q (the A/P phase), then v (needed only for the image's
+  // V at the end); the row table goes to LDS after the A/P phase, so that no
+  // wait for the later loads comes before it
+  const float bx = a.beta[(size_t)(trow < 0 ? 0 : trow) * H + h];
+  const float tbeta = trow >= 0 ? bx : 0.f;
   ElemRegs<BC, D> er;
   elems_load<TIn, BC, D>((const TIn*)a.q, (const TIn*)a.k, a.g, H, h, rows, er);
   float vv[NE];
@@ -77,12 +82,11 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
         vv[hf * G::RPT + t] = r >= 0 ? x : 0.f;
       }
   }
+  chunk_AP<BC, D>(s.tb, er, s.ap, &s.A[0][0], G::PB, &s.P[0][0], G::PB);
   if (tid < BC) {
     s.tb.orow[tid] = torow;
-    s.tb.beta[tid] = trow >= 0 ? a.beta[(size_t)trow * H + h] : 0.f;
+    s.tb.beta[tid] = tbeta;
   }
-  __syncthreads();
-  chunk_AP<BC, D>(s.tb, er, s.ap, &s.A[0][0], G::PB, &s.P[0][0], G::PB);
   FI* F = (FI*)(a.fimg + blk * fwd_image_bytes(BC, D));
 
   // decayed operands from the element mapping (channel c0 + 64 hf, rows r0..)
@@ -122,6 +126,7 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
     *(f16x8*)&F->L[i][j0] = *(const f16x8*)&s.A[i][j0];
     *(f16x8*)&F->P[i][j0] = *(const f16x8*)&s.P[i][j0];
   }
+  __syncthreads();  // beta of every row
   // diagonal inverses: one lane per (block, column), forward substitution
   if (tid < 16 * G::NB) {
     const int I = tid >> 4, j = tid & 15, b0 = 16 * I;
