@@ -120,8 +120,9 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
   return s;
 }
 
-// bwd workspace = [dO in packed order (sized for fp32) | dy | chunk end-state
-//                  gradients (fp16) | sequence start gradients | replay-row gradients]
+// bwd workspace = [dO tiles per chunk-head (sized for fp32) | dy tiles | chunk
+//                  end-state gradients (fp16) | sequence start gradients |
+//                  replay-row gradients]
 struct BwdWS {
   float *dOp, *dy, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
   _Float16* dhc;
@@ -130,7 +131,7 @@ BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) 
   Carver c(base);
   BwdWS w;
   const size_t nb = (size_t)p.n_chunks() * H;
-  w.dOp = c.take((size_t)p.n_packed * H * D);
+  w.dOp = c.take(nb * p.B * D);  // per chunk-head 16x16 tiles
   w.dy = c.take(nb * p.B * D);   // per chunk-head 16x16 tiles
   w.dhc = (_Float16*)c.take(nb * D * D / 2);
   w.slot = c.take((size_t)p.n_seq() * H * D * D);

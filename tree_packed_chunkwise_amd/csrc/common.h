@@ -103,7 +103,8 @@ struct BwdArgs {
   float* dbeta;
   float* dh0;
   float* dh_boundary;     // may be null
-  void* dOp;              // [n_packed,H,D] dO in packed row order, zero on replay rows
+  void* dOp;              // [n_chunks,H] x (BC x D dO in 16x16 tiles, state_tile order),
+                          // zero on replay rows and past the chunk
   float* dy;              // [n_chunks,H] x (BC x D in 16x16 tiles, state_tile order)
   _Float16* dhc;          // [n_chunks,H,D,D] gradient of each chunk's end state (fp16 copy)
   float* slot;            // [n_seq,H,D,D] gradient of each sequence's start state
@@ -149,9 +150,14 @@ struct AttnArgs {
   float* part;        // [n_slots][H][2][64][D] partial dk, dv
 };
 
-inline __device__ float ld_in(const float* p, size_t i) { return p[i]; }
+// One input element as fp32, loaded through the global address space (every
+// input lives in device memory; the compiler cannot always infer that, and a
+// flat load counts against both wait counters).
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+inline __device__ float ld_in(const float* p, size_t i) { return ((gptr<float>)p)[i]; }
 inline __device__ float ld_in(const uint16_t* p, size_t i) {
-  return __uint_as_float(((uint32_t)p[i]) << 16);
+  return __uint_as_float(((uint32_t)((gptr<uint16_t>)p)[i]) << 16);
 }
 
 }  // namespace kda

@@ -63,19 +63,19 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         dh[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
   // dO of the chunk in flight, raw: this lane's row piece of the 16-row
-  // halves of every 32-deep k step (packed dO is zero on replay rows);
-  // quad_transpose turns it into register k order (chunk.h) when it is used
+  // halves of every 32-deep k step, from the chunk's dO tiles (zero on replay
+  // rows and past the chunk); quad_transpose turns it into register k order
+  // (chunk.h) when it is used
   in4_t<TIn> dor[KB][2];
   auto load_do = [&](int cc) {
-    const int r0c = a.plan.chunk_row0[cc], lenc = a.plan.chunk_len[cc];
+    const TIn* src = dOp + ((size_t)cc * H + h) * (BC * D);
 #pragma unroll
     for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int i = 32 * ks + 16 * hf + rq;
         dor[ks][hf] = (in4_t<TIn>)0;
-        if (sw && i < BC && i < lenc)
-          dor[ks][hf] = *(const in4_t<TIn>*)&dOp[((size_t)(r0c + i) * H + h) * D + cq];
+        if (sw && 32 * ks + 16 * hf < BC)
+          dor[ks][hf] = *(const in4_t<TIn>*)&src[state_tile<D>(2 * ks + hf, col >> 4)];
       }
   };
   if (cbeg < cend) {
@@ -227,38 +227,56 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   }
 }
 
-// dO in packed row order: dOp[p] = dO[out_row[p]] for rows with an output,
-// zero on replay rows (16-byte vectors).
-template <typename TIn, int D>
-__global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, const int* out_row, int H,
-                                                   int64_t n_packed, TIn* dOp) {
-  constexpr int PER = 16 / sizeof(TIn);  // elements per vector
-  const int64_t nvec = n_packed * H * (D / PER);
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < nvec; e += (int64_t)gridDim.x * 256) {
-    const int64_t rowh = e / (D / PER);
-    const int64_t p = rowh / H;
-    const int h = (int)(rowh % H);
-    const int o = out_row[p];
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (o >= 0) x = ((const uint4*)(dO + ((size_t)o * H + h) * D))[e % (D / PER)];
-    ((uint4*)dOp)[e] = x;
+// dO of every chunk-head in 16x16 tiles (state_tile order, chunk.h): row i
+// of chunk c holds dO[out_row[chunk_row0[c] + i]] for rows with an output,
+// zero on replay rows and past the chunk.  One thread per 16-byte piece of a
+// row (a wave reads whole rows), written as the one or two 4-element row
+// pieces of the tiles it holds.
+template <typename TIn, int BC, int D>
+__global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, DevPlan plan, int H,
+                                                   int64_t n_pieces, TIn* dOp) {
+  constexpr int PER = 16 / (int)sizeof(TIn);  // elements per 16-byte piece: 8 or 4
+  constexpr int PPR = D / PER;                // pieces per row
+  using V = TIn __attribute__((ext_vector_type(PER)));
+  using V4 = in4_t<TIn>;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n_pieces;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t blk = e / (BC * PPR);
+    const int r = (int)(e % (BC * PPR)), i = r / PPR, v0 = (r % PPR) * PER;
+    const int c = (int)(blk / H), h = (int)(blk % H);
+    const int o = i < plan.chunk_len[c] ? plan.out_row[plan.chunk_row0[c] + i] : -1;
+    V x = (V)0;
+    if (o >= 0) x = *(const V*)&dO[((size_t)o * H + h) * D + v0];
+    TIn* dst = dOp + (size_t)blk * (BC * D);
+#pragma unroll
+    for (int m = 0; m < PER / 4; ++m) {
+      const int v = v0 + 4 * m;
+      const int l = 16 * ((i & 15) >> 2) + (v & 12) + (i & 3);
+      *(V4*)&dst[(size_t)((i >> 4) * (D / 16) + (v >> 4)) * 256 + 4 * l] =
+          (V4){x[4 * m], x[4 * m + 1], x[4 * m + 2], x[4 * m + 3]};
+    }
   }
 }
 
-hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int D, int64_t n_packed, hipStream_t st) {
-  if (n_packed <= 0) return hipSuccess;
-  const int64_t nvec = n_packed * a.H * (D / (bf16 ? 8 : 4));
-  const int nb = (int)((nvec + 255) / 256 < 65536 ? (nvec + 255) / 256 : 65536);
-#define KDA_GDO(T, Dv)                                                                       \
-  KDA_LAUNCH("kda_bwd_gather_dO", (k_gather_dO<T, Dv>), dim3(nb), dim3(256), st, (const T*)a.dO, \
-             a.plan.out_row, a.H, n_packed, (T*)a.dOp)
+hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+                            hipStream_t st) {
+  if (n_chunks <= 0) return hipSuccess;
+  const int64_t n_pieces = (int64_t)n_chunks * a.H * BC * D / (bf16 ? 8 : 4);
+  const int nb = (int)((n_pieces + 255) / 256 < 65536 ? (n_pieces + 255) / 256 : 65536);
+#define KDA_GDO(T, BCv, Dv)                                                                    \
+  if (BC == BCv && D == Dv) {                                                                  \
+    KDA_LAUNCH("kda_bwd_gather_dO", (k_gather_dO<T, BCv, Dv>), dim3(nb), dim3(256), st,        \
+               (const T*)a.dO, a.plan, a.H, n_pieces, (T*)a.dOp);                              \
+    return hipGetLastError();                                                                  \
+  }
   if (bf16) {
-    if (D == 128) KDA_GDO(uint16_t, 128); else KDA_GDO(uint16_t, 64);
+    KDA_GDO(uint16_t, 64, 128) KDA_GDO(uint16_t, 64, 64) KDA_GDO(uint16_t, 16, 128)
+    KDA_GDO(uint16_t, 16, 64)
   } else {
-    if (D == 128) KDA_GDO(float, 128); else KDA_GDO(float, 64);
+    KDA_GDO(float, 64, 128) KDA_GDO(float, 64, 64) KDA_GDO(float, 16, 128) KDA_GDO(float, 16, 64)
   }
 #undef KDA_GDO
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 int round_slices(int nseq, int H, int D);

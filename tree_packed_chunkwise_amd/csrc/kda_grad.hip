@@ -63,28 +63,6 @@ __device__ inline f32x4 mma3(const s16x4& ah, const s16x4& al, const s16x4& bh, 
   return t;
 }
 
-// eight consecutive input elements (bf16 bit patterns or fp32)
-template <typename T> struct Raw8;
-template <> struct Raw8<uint16_t> {
-  uint4 x;
-  __device__ void load(const uint16_t* p) { x = *(const uint4*)p; }
-  __device__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
-  __device__ float at(int e) const {
-    const uint32_t w = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
-    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-  }
-};
-template <> struct Raw8<float> {
-  float4 x, y;
-  __device__ void load(const float* p) { x = *(const float4*)p; y = *(const float4*)(p + 4); }
-  __device__ void zero() { x = y = make_float4(0.f, 0.f, 0.f, 0.f); }
-  __device__ float at(int e) const {
-    const float4& v = e < 4 ? x : y;
-    const int k = e & 3;
-    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-  }
-};
-
 template <int BC, int D>
 struct GradGeom {
   static constexpr int NB = BC / 16;             // 16-row blocks of the chunk
@@ -140,6 +118,7 @@ struct GradSmem {
   float degc[D];
   float beta[BC];
   int orow[BC];
+  int irow[BC];   // input row of each chunk row (-1 past the chunk)
 };
 
 // destination of a row gradient: the output row, or the replay slot
@@ -157,7 +136,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   constexpr int NE = RPT * NHF;
   constexpr int KB = (BC + 31) / 32;
   constexpr bool HALF = (BC == 16);
-  constexpr int NV8 = (BC * D / 8 + NT - 1) / NT;   // 8-element vectors of dO per thread
+  constexpr int NV4 = (BC * D / 4 + NT - 1) / NT;   // 4-element pieces of dO per thread
   __shared__ GradSmem<BC, D> s;
   const int c = c_begin + blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -207,6 +186,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   // start state and V as row pieces (phase 1; quad_transpose turns them into
   // the accumulator layout), A and Td of the forward image, beta
   const bool vw = wave < NCB;
+  const int wv = vw ? wave : 0;   // column block the loads use (waves past D/16 load and drop one)
   const int col = 16 * wave + l16;
   const int cq = 16 * wave + quad_col(), rq = quad_row();
   f16x4 hraw[NCB], dhraw[NCB];
@@ -214,12 +194,10 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   in4_t<TIn> vraw[NB];
   const _Float16* hsrc = a.chunk_h + blk * DD;
   const _Float16* dhsrc = a.dhc + blk * DD;
-  if (vw) {
 #pragma unroll
-    for (int C = 0; C < NCB; ++C) hraw[C] = *(const f16x4*)(hsrc + state_tile<D>(C, wave));
+  for (int C = 0; C < NCB; ++C) hraw[C] = *(const f16x4*)(hsrc + state_tile<D>(C, wv));
 #pragma unroll
-    for (int J = 0; J < NB; ++J) vraw[J] = *(const in4_t<TIn>*)&F->V[16 * J + rq][cq];
-  }
+  for (int J = 0; J < NB; ++J) vraw[J] = *(const in4_t<TIn>*)&F->V[16 * J + rq][16 * wv + quad_col()];
   constexpr int NAV = (BC * BC / 8 + NT - 1) / NT;
   f16x8 av[NAV], tv;
 #pragma unroll
@@ -229,37 +207,26 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   }
   if (tid < BC * 2) tv = *(const f16x8*)&F->Td[tid / 2][(tid % 2) * 8];
   const float tbeta = trow >= 0 ? a.beta[(size_t)trow * H + h] : 0.f;
-  // dy (phase 1), dO (after Z), q (phase 3), the end-state gradient (end of phase 2)
-  if (vw) {
+  // dy (phase 1), dO (after Z), the end-state gradient (end of phase 2); q
+  // (phase 3) follows at the start of phase 1, which keeps the loads in
+  // flight here within what one wait count can track (63)
 #pragma unroll
-    for (int J = 0; J < NB; ++J)
-      dyv[J] = 16 * J + rq < len ? *(const f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(J, wave)]
-                                 : (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-  // packed dO (zero on replay rows): loaded without a branch (rows past the
-  // chunk read its first row and are zeroed where used), so that no wait for
-  // it is forced before the later loads are issued
-  Raw8<TIn> dov[NV8];
-  bool dok[NV8];
+  for (int J = 0; J < NB; ++J)   // (rows past the chunk are zeroed where used)
+    dyv[J] = *(const f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(J, wv)];
+  // dO from the chunk's tiles (zero on replay rows and past the chunk):
+  // piece e = tid + NT n is lane e % 64 of tile e / 64, one contiguous
+  // 512- or 1024-byte run per wave
+  // (no branch around a load: a branch that uses the loaded value makes the
+  // compiler wait for every earlier load there)
+  in4_t<TIn> dov[NV4];
 #pragma unroll
-  for (int n = 0; n < NV8; ++n) {
+  for (int n = 0; n < NV4; ++n) {
     const int e = tid + NT * n;
-    const int i = e / (D / 8);
-    dok[n] = e < BC * D / 8 && i < len;
-    dov[n].load(dOp + ((size_t)(row0 + (dok[n] ? i : 0)) * H + h) * D + (e % (D / 8)) * 8);
+    const int ec = (BC * D / 4) % NT == 0 || e < BC * D / 4 ? e : BC * D / 4 - 1;
+    dov[n] = *(const in4_t<TIn>*)&dOp[blk * (BC * D) + 4 * (size_t)ec];
   }
 #pragma unroll
-  for (int hf = 0; hf < NHF; ++hf)
-#pragma unroll
-    for (int t = 0; t < RPT; ++t) {
-      const int r = rows[t];
-      const float w = ld_in(q, ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf);
-      qq[hf * RPT + t] = r >= 0 ? w : 0.f;
-    }
-  if (vw) {
-#pragma unroll
-    for (int C = 0; C < NCB; ++C) dhraw[C] = *(const f16x4*)(dhsrc + state_tile<D>(C, wave));
-  }
+  for (int C = 0; C < NCB; ++C) dhraw[C] = *(const f16x4*)(dhsrc + state_tile<D>(C, wv));
 
   // ---- Gam: running sums per row group, then their prefix ----
 #pragma unroll
@@ -298,6 +265,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   }
   if (tid < BC) {
     s.orow[tid] = torow;
+    s.irow[tid] = trow;
     s.beta[tid] = tbeta;
   }
 #pragma unroll
@@ -307,6 +275,19 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   }
   if (tid < BC * 2) *(f16x8*)&s.u.p.Td[tid / 2][(tid % 2) * 8] = tv;
   __syncthreads();
+  // q (phase 3) through the input rows of the row table: addressed from LDS
+  // after the barrier, these loads stay behind the prologue's, whose waits
+  // then remain exact
+#pragma unroll
+  for (int t = 0; t < RPT; ++t) rows[t] = s.irow[r0 + t];
+#pragma unroll
+  for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int r = rows[t];
+      const float w = ld_in(q, ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf);
+      qq[hf * RPT + t] = r >= 0 ? w : 0.f;
+    }
 
   // ---- phase 1: Z = V - (K e^Gam) h on column block `wave` ----
   if (vw) {
@@ -335,18 +316,21 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   }
   __syncthreads();  // Kn is dead: dO takes its place
 #pragma unroll
-  for (int n = 0; n < NV8; ++n) {
+  for (int n = 0; n < NV4; ++n) {
     const int e = tid + NT * n;
-    if (e < BC * D / 8) {
-      f16x8 x;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) x[t] = (_Float16)(dok[n] ? sc * dov[n].at(t) : 0.f);
-      *(f16x8*)&s.u.p.x.dO[e / (D / 8)][(e % (D / 8)) * 8] = x;
+    if (e < BC * D / 4) {
+      const int t = e >> 6, l = e & 63;
+      const f32x4 x = sc * in4_to_f32(dov[n]);
+      *(f16x4*)&s.u.p.x.dO[16 * (t / (D / 16)) + 4 * (l >> 4) + (l & 3)][16 * (t % (D / 16)) + (l & 12)] =
+          (f16x4){(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
     }
   }
   if (vw) {
 #pragma unroll
-    for (int J = 0; J < NB; ++J) quad_transpose(dyv[J]);
+    for (int J = 0; J < NB; ++J) {
+      if (16 * J + rq >= len) dyv[J] = (f32x4){0.f, 0.f, 0.f, 0.f};   // never written there
+      quad_transpose(dyv[J]);
+    }
     // delta by block forward substitution with the diagonal inverses
     f32x4 d[NB];
 #pragma unroll

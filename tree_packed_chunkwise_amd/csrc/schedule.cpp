@@ -36,7 +36,8 @@ hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int c_begin, 
                        hipStream_t st);
 hipError_t launch_fwd_rounds(const FwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
                              int r_begin, int r_end, hipStream_t st);
-hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int D, int64_t n_packed, hipStream_t st);
+hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+                            hipStream_t st);
 hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
                              int r_begin, int r_end, hipStream_t st);
 hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
@@ -152,7 +153,7 @@ hipError_t run_fwd(const FwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
 hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hipStream_t st) {
   const int R = p.n_rounds, nc = p.n_chunks();
   const int* rp = p.round_seq_ptr.data();
-  KDA_TRY(launch_gather_dO(a, bf16, D, p.n_packed, st));
+  KDA_TRY(launch_gather_dO(a, bf16, BC, D, nc, st));
   Side* sd = nullptr;
   if (R > 1 && nc > 0 && g_overlap.load()) KDA_TRY(side_of_current_device(&sd));
   std::unique_lock<std::mutex> lk;
