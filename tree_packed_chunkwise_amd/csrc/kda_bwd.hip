@@ -229,44 +229,45 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 
 // dO of every chunk-head in 16x16 tiles (state_tile order, chunk.h): row i
 // of chunk c holds dO[out_row[chunk_row0[c] + i]] for rows with an output,
-// zero on replay rows and past the chunk.  One thread per 16-byte piece of a
-// row (a wave reads whole rows), written as the one or two 4-element row
-// pieces of the tiles it holds.
+// zero on replay rows and past the chunk.  One block per chunk-head: its rows
+// are read whole into LDS (16-byte pieces, a wave per 4 or 2 rows), then the
+// tiles are written in their own order (a wave per contiguous tile).
 template <typename TIn, int BC, int D>
-__global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, DevPlan plan, int H,
-                                                   int64_t n_pieces, TIn* dOp) {
+__global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, DevPlan plan, int H, TIn* dOp,
+                                                   int c_begin) {
   constexpr int PER = 16 / (int)sizeof(TIn);  // elements per 16-byte piece: 8 or 4
   constexpr int PPR = D / PER;                // pieces per row
+  constexpr int PITCH = D + PER;              // LDS row pitch, padded by one piece
   using V = TIn __attribute__((ext_vector_type(PER)));
   using V4 = in4_t<TIn>;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n_pieces;
-       e += (int64_t)gridDim.x * 256) {
-    const int64_t blk = e / (BC * PPR);
-    const int r = (int)(e % (BC * PPR)), i = r / PPR, v0 = (r % PPR) * PER;
-    const int c = (int)(blk / H), h = (int)(blk % H);
-    const int o = i < plan.chunk_len[c] ? plan.out_row[plan.chunk_row0[c] + i] : -1;
+  __shared__ __attribute__((aligned(16))) TIn rowsm[BC * PITCH];
+  const int c = c_begin + blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int row0 = plan.chunk_row0[c], len = plan.chunk_len[c];
+  for (int p = tid; p < BC * PPR; p += 256) {
+    const int i = p / PPR, j = p % PPR;
+    const int o = i < len ? plan.out_row[row0 + i] : -1;
     V x = (V)0;
-    if (o >= 0) x = *(const V*)&dO[((size_t)o * H + h) * D + v0];
-    TIn* dst = dOp + (size_t)blk * (BC * D);
-#pragma unroll
-    for (int m = 0; m < PER / 4; ++m) {
-      const int v = v0 + 4 * m;
-      const int l = 16 * ((i & 15) >> 2) + (v & 12) + (i & 3);
-      *(V4*)&dst[(size_t)((i >> 4) * (D / 16) + (v >> 4)) * 256 + 4 * l] =
-          (V4){x[4 * m], x[4 * m + 1], x[4 * m + 2], x[4 * m + 3]};
-    }
+    if (o >= 0) x = *(const V*)&dO[((size_t)o * H + h) * D + j * PER];
+    *(V*)&rowsm[i * PITCH + j * PER] = x;
+  }
+  __syncthreads();
+  TIn* dst = dOp + ((size_t)c * H + h) * (BC * D);
+  for (int q = tid; q < BC * D / 4; q += 256) {
+    const int t = q >> 6, l = q & 63;
+    const int i = 16 * (t / (D / 16)) + 4 * (l >> 4) + (l & 3);
+    const int v = 16 * (t % (D / 16)) + (l & 12);
+    *(V4*)&dst[4 * (size_t)q] = *(const V4*)&rowsm[i * PITCH + v];
   }
 }
 
-hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+// chunks c_begin .. c_begin + n_chunks - 1
+hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
                             hipStream_t st) {
   if (n_chunks <= 0) return hipSuccess;
-  const int64_t n_pieces = (int64_t)n_chunks * a.H * BC * D / (bf16 ? 8 : 4);
-  const int nb = (int)((n_pieces + 255) / 256 < 65536 ? (n_pieces + 255) / 256 : 65536);
 #define KDA_GDO(T, BCv, Dv)                                                                    \
   if (BC == BCv && D == Dv) {                                                                  \
-    KDA_LAUNCH("kda_bwd_gather_dO", (k_gather_dO<T, BCv, Dv>), dim3(nb), dim3(256), st,        \
-               (const T*)a.dO, a.plan, a.H, n_pieces, (T*)a.dOp);                              \
+    KDA_LAUNCH("kda_bwd_gather_dO", (k_gather_dO<T, BCv, Dv>), dim3(n_chunks, a.H), dim3(256), \
+               st, (const T*)a.dO, a.plan, a.H, (T*)a.dOp, c_begin);                           \
     return hipGetLastError();                                                                  \
   }
   if (bf16) {

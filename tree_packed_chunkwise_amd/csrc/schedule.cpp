@@ -10,16 +10,17 @@
 //             pass of the later rounds' chunks, run round group by round
 //             group (a group: consecutive rounds of at least an eighth of
 //             all chunks); each round waits only for its own group's pass.
-//   reverse:  dO gathered; rounds last to first; once the chunks whose
-//             rounds are done amount to a quarter of all chunks, their
-//             chunk-local gradients run on the second stream beside the
-//             remaining rounds; the rest after round 0; the second stream is
-//             joined before the fixed-order reductions.
+//   reverse:  dO of the last round's chunks gathered (the rest on the
+//             second stream beside that round); rounds last to first; once
+//             the chunks whose rounds are done amount to a quarter of all
+//             chunks, their chunk-local gradients run on the second stream
+//             beside the remaining rounds; the rest after round 0; the
+//             second stream is joined before the fixed-order reductions.
 // No kernel reads memory that a kernel running beside it writes, and every
 // sum is in a fixed order, so the results do not depend on how the two
 // streams interleave (kda_set_overlap(0) makes every call use the caller's
-// stream alone, with the same results).  The fork/join sequence of a call is enqueued under a
-// per-device lock (its events are reused from call to call).
+// stream alone, with the same results).  The fork/join sequence of a call is
+// enqueued under a per-device lock (its events are reused from call to call).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -36,7 +37,7 @@ hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int c_begin, 
                        hipStream_t st);
 hipError_t launch_fwd_rounds(const FwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
                              int r_begin, int r_end, hipStream_t st);
-hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int n_chunks,
+hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
                             hipStream_t st);
 hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
                              int r_begin, int r_end, hipStream_t st);
@@ -153,15 +154,28 @@ hipError_t run_fwd(const FwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
 hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hipStream_t st) {
   const int R = p.n_rounds, nc = p.n_chunks();
   const int* rp = p.round_seq_ptr.data();
-  KDA_TRY(launch_gather_dO(a, bf16, BC, D, nc, st));
   Side* sd = nullptr;
   if (R > 1 && nc > 0 && g_overlap.load()) KDA_TRY(side_of_current_device(&sd));
   std::unique_lock<std::mutex> lk;
   if (sd) lk = std::unique_lock<std::mutex>(sd->mu);
+  // dO tiles: the last round's chunks first; with a second stream the rest
+  // are gathered there while that round runs
+  const int cl = R > 0 ? round_chunk_begin(p, R - 1) : nc;
+  hipEvent_t gathered = nullptr;
+  if (sd && cl > 0) {
+    KDA_TRY(launch_gather_dO(a, bf16, BC, D, cl, nc - cl, st));
+    KDA_TRY(order_after(sd->fork, st, sd->s));
+    KDA_TRY(launch_gather_dO(a, bf16, BC, D, 0, cl, sd->s));
+    KDA_TRY(group_event(sd, 0, &gathered));
+    KDA_TRY(hipEventRecord(gathered, sd->s));
+  } else {
+    KDA_TRY(launch_gather_dO(a, bf16, BC, D, 0, nc, st));
+  }
   const int group = nc / 4 > 1 ? nc / 4 : 1;
   int ready_end = nc;   // chunks [ready_end, nc) have their gradients launched
   bool forked = false;
   for (int r = R - 1; r >= 0; --r) {
+    if (gathered && r == R - 2) KDA_TRY(hipStreamWaitEvent(st, gathered, 0));
     KDA_TRY(launch_bwd_rounds(a, bf16, BC, D, rp, r, r + 1, st));
     const int cb = round_chunk_begin(p, r);
     if (sd && r > 0 && ready_end - cb >= group) {
