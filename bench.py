@@ -221,15 +221,16 @@ def kernel_bytes(name, info, H, D, in_bytes=2):
         return (C * H * fimg + Nrow * H * D * f + C * H * st16
                 + (info["n_buf"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_round":
-        # reads the image heads, packed dO, leaf-state gradients; writes dy,
-        # the end-state gradient of every chunk, sequence start gradients
-        return (C * H * head + P * H * D * (in_bytes + f) + C * H * st16
+        # reads the image heads, packed dO, leaf-state gradients; writes dy
+        # (fp16), the end-state gradient of every chunk, sequence start
+        # gradients
+        return (C * H * head + P * H * D * (in_bytes + 2) + C * H * st16
                 + (info["n_seq"] + info["n_leaf"]) * H * st)
     if name == "kda_bwd_chunk_grad":
-        # reads q, k, g, beta, dy, packed dO, A / Td / V of the chunk image,
-        # the start state and end-state gradient of every chunk; writes dq, dk,
-        # dv, dg, dbeta
-        return (P * H * (2 * D * in_bytes + D * f + f + D * f + D * in_bytes + 4 * D * f + f)
+        # reads q, k, g, beta, dy (fp16), packed dO, A / Td / V of the chunk
+        # image, the start state and end-state gradient of every chunk;
+        # writes dq, dk, dv, dg, dbeta
+        return (P * H * (2 * D * in_bytes + D * f + f + D * 2 + D * in_bytes + 4 * D * f + f)
                 + C * H * ((B * (B + 8) + B * 24) * 2 + B * D * in_bytes + 2 * st16))
     if name == "kda_bwd_gather_dO":
         return Nrow * H * D * in_bytes + P * H * D * in_bytes

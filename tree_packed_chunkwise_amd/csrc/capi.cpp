@@ -124,15 +124,15 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
 //                  end-state gradients (fp16) | sequence start gradients |
 //                  replay-row gradients]
 struct BwdWS {
-  float *dOp, *dy, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
-  _Float16* dhc;
+  float *dOp, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
+  _Float16 *dy, *dhc;
 };
 BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
   BwdWS w;
   const size_t nb = (size_t)p.n_chunks() * H;
   w.dOp = c.take(nb * p.B * D);  // per chunk-head 16x16 tiles
-  w.dy = c.take(nb * p.B * D);   // per chunk-head 16x16 tiles
+  w.dy = (_Float16*)c.take(nb * p.B * D / 2);   // fp16, per chunk-head 16x16 tiles
   w.dhc = (_Float16*)c.take(nb * D * D / 2);
   w.slot = c.take((size_t)p.n_seq() * H * D * D);
   const size_t nrep = (size_t)p.R;

@@ -105,7 +105,7 @@ struct BwdArgs {
   float* dh_boundary;     // may be null
   void* dOp;              // [n_chunks,H] x (BC x D dO in 16x16 tiles, state_tile order),
                           // zero on replay rows and past the chunk
-  float* dy;              // [n_chunks,H] x (BC x D in 16x16 tiles, state_tile order)
+  _Float16* dy;           // [n_chunks,H] x (BC x D fp16 in 16x16 tiles, state_tile order)
   _Float16* dhc;          // [n_chunks,H,D,D] gradient of each chunk's end state (fp16 copy)
   float* slot;            // [n_seq,H,D,D] gradient of each sequence's start state
   float* rep_dq;          // [n_replay,H,D] gradients of replayed rows

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         f32x4 dy = mfma16k16(ft[I], acc4(rr), (f32x4){0.f, 0.f, 0.f, 0.f});
         w[I] = dy * bz[I];
         quad_transpose(dy);
-        if (16 * I + rq < len) *(f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(I, col >> 4)] = dy;
+        if (16 * I + rq < len) st_h4(a.dy + blk * (BC * D) + state_tile<D>(I, col >> 4), dy);
       }
       f16x8 wb[KB];
 #pragma unroll

@@ -190,6 +190,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   const int col = 16 * wave + l16;
   const int cq = 16 * wave + quad_col(), rq = quad_row();
   f16x4 hraw[NCB], dhraw[NCB];
+  f16x4 dyh[NB];
   f32x4 dyv[NB], z[NB];
   in4_t<TIn> vraw[NB];
   const _Float16* hsrc = a.chunk_h + blk * DD;
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   // flight here within what one wait count can track (63)
 #pragma unroll
   for (int J = 0; J < NB; ++J)   // (rows past the chunk are zeroed where used)
-    dyv[J] = *(const f32x4*)&a.dy[blk * (BC * D) + state_tile<D>(J, wv)];
+    dyh[J] = *(const f16x4*)&a.dy[blk * (BC * D) + state_tile<D>(J, wv)];
   // dO from the chunk's tiles (zero on replay rows and past the chunk):
   // piece e = tid + NT n is lane e % 64 of tile e / 64, one contiguous
   // 512- or 1024-byte run per wave
@@ -328,6 +329,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   if (vw) {
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
+      dyv[J] = (f32x4){(float)dyh[J][0], (float)dyh[J][1], (float)dyh[J][2], (float)dyh[J][3]};
       if (16 * J + rq >= len) dyv[J] = (f32x4){0.f, 0.f, 0.f, 0.f};   // never written there
       quad_transpose(dyv[J]);
     }
