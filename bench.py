@@ -358,6 +358,70 @@ def measure_attention(steps):
         return {"error": repr(exc)}
 
 
+def measure_router(steps):
+    """Occurrence-weighted MoE router statistics (forward: loads, probability
+    and z-loss sums, top-8 per row; reverse: logit gradients) over the compact
+    rows of the fwd+bwd workload's tree, 128 experts, bf16 logits; and the
+    same kernels over the trajectory-expanded rows (every position routed,
+    count 1) for comparison.  Algorithmic bytes: forward reads the logits
+    (2 B x 128) and the count (4 B) of every row and writes its top-8 indices
+    and probabilities (64 B); reverse reads logits and count and writes fp32
+    gradients (512 B)."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    try:
+        w = synth.workload(2)
+        plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, 64)
+        N, E, K = plan.info["n_rows"], 128, 8
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(13)
+        x = (2 * torch.randn(N, E, generator=gen, device="cuda")).to(torch.bfloat16)
+        g = torch.randn(E, generator=gen, device="cuda")
+        q = plan.device_table("ROW_MULT")
+        # trajectory-expanded rows: every root-to-leaf path in position order
+        par, ln, r0 = (np.asarray(a, np.int64) for a in (w.tree.parent, w.tree.seg_len, w.tree.seg_row))
+        rows = []
+        for leaf in plan.export("LEAF_SEG"):
+            path, v = [], int(leaf)
+            while v >= 0:
+                path.append(v)
+                v = int(par[v])
+            rows.append(np.concatenate([np.arange(r0[s], r0[s] + ln[s]) for s in reversed(path)]))
+        rows = torch.from_numpy(np.concatenate(rows)).cuda()
+        xe = x.index_select(0, rows).contiguous()
+        qe = torch.ones(xe.shape[0], dtype=torch.int32, device="cuda")
+
+        def timed(xx, qq):
+            out = B.moe_router_stats(xx, qq, K)
+            dx = B.moe_router_stats_bwd(xx, qq, g, 0.1)
+            torch.cuda.synchronize()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            for _ in range(steps):
+                B.moe_router_stats(xx, qq, K)
+            e[1].record()
+            for _ in range(steps):
+                B.moe_router_stats_bwd(xx, qq, g, 0.1, out=dx)
+            e[2].record()
+            torch.cuda.synchronize()
+            return out, e[0].elapsed_time(e[1]) / steps, e[1].elapsed_time(e[2]) / steps
+        out, fms, bms = timed(x, q)
+        oute, fe, be = timed(xe, qe)
+        same = bool(torch.equal(out["load"], oute["load"]) and torch.equal(out["n_tok"], oute["n_tok"]))
+        fb, bb = N * (E * 2 + 4 + K * 8), N * (E * 2 + 4 + E * 4)
+        return {"workload": f"{w.tree.name} tree, {N} rows, {int(xe.shape[0])} positions, "
+                            f"{E} experts, top-{K}, bf16 logits",
+                "fwd_ms": round(fms, 4), "bwd_ms": round(bms, 4),
+                "fwd_GBps": round(fb / (fms * 1e-3) / 1e9, 1),
+                "bwd_GBps": round(bb / (bms * 1e-3) / 1e9, 1),
+                "expanded_fwd_ms": round(fe, 4), "expanded_bwd_ms": round(be, 4),
+                "speedup": round((fe + be) / (fms + bms), 3),
+                "loads_equal_expanded": same}
+    except Exception as exc:  # reported, never fatal to the headline line
+        return {"error": repr(exc)}
+
+
 def measure_hybrid(steps):
     """The hybrid layer group (3 KDA layers, tree attention, log-prob gather,
     hidden 2048, vocab 32000, bf16) forward + backward on the same tree."""
@@ -584,6 +648,7 @@ def main():
     ablation = replay_ablation(dev) if a.expanded_steps > 0 else None
     window = measure_window(w, dev, a.expanded_steps, ms) if a.expanded_steps > 0 else None
     attention = measure_attention(a.attn_steps) if a.attn_steps > 0 else None
+    router = measure_router(10) if a.attn_steps > 0 else None
     hybrid = measure_hybrid(a.hybrid_steps) if a.hybrid_steps > 0 else None
 
     out = {
@@ -606,7 +671,7 @@ def main():
         "expanded": expanded, "plan_modes": modes, "sharing_window": window,
         "replay_ablation": ablation,
         "kernels": kernels, "finite": ok,
-        "tree_attention": attention, "hybrid_group": hybrid,
+        "tree_attention": attention, "hybrid_group": hybrid, "moe_router": router,
     }
     print(json.dumps(out), flush=True)
 

@@ -157,6 +157,8 @@ int kda_plan_info(const kda_plan* plan, kda_plan_info_t* info);
  *              0..L-2): row of the position and row of its next token;
  *   ROW_POS_PTR/IDX  positions of every compact row (CSR, ascending)
  *   LEAF_SEG, ROOT_SEG  leaf and root segment ids, ascending
+ *   ROW_MULT   per compact row: its occurrence count, the number of
+ *              root-to-leaf trajectories through it
  */
 enum {
   KDA_F_SEG_ROUND = 0, KDA_F_SEG_SEQ, KDA_F_SEG_IS_CONT, KDA_F_SEG_B, KDA_F_SEG_REPLAY,
@@ -168,7 +170,7 @@ enum {
   KDA_F_ROW_POS_IDX, KDA_F_LEAF_SEG, KDA_F_ROOT_SEG,
   KDA_F_ATT_ANC_PTR, KDA_F_ATT_ANC, KDA_F_ATT_SEG_TILE0, KDA_F_ATT_TILE_SEG, KDA_F_ATT_TILE_OFF,
   KDA_F_ATT_QORDER, KDA_F_ATT_KQ_PTR, KDA_F_ATT_KQ, KDA_F_ATT_KW_TILE, KDA_F_ATT_KW_Q0,
-  KDA_F_ATT_KW_NQ, KDA_F_ATT_KW_SLOT,
+  KDA_F_ATT_KW_NQ, KDA_F_ATT_KW_SLOT, KDA_F_ROW_MULT,
   KDA_F_COUNT
 };
 int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64_t n);
@@ -183,8 +185,8 @@ int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64
 int kda_plan_upload(const kda_plan* plan, void* dev, size_t bytes, void* stream);
 
 /* Byte offset of an int32 table (KDA_F_POS_ROW, KDA_F_POS_NEXT_ROW,
- * KDA_F_ROW_POS_PTR, KDA_F_ROW_POS_IDX, KDA_F_ROW_INDEX, KDA_F_OUT_ROW) inside
- * the uploaded device copy, or a negative KDA_ERR_*. */
+ * KDA_F_ROW_POS_PTR, KDA_F_ROW_POS_IDX, KDA_F_ROW_INDEX, KDA_F_OUT_ROW,
+ * KDA_F_ROW_MULT) inside the uploaded device copy, or a negative KDA_ERR_*. */
 int64_t kda_plan_device_offset(const kda_plan* plan, int32_t field);
 
 /*
@@ -299,6 +301,51 @@ int gather_logprobs_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32
                         const float* lse, const int32_t* row_pos_ptr,
                         const int32_t* row_pos_idx, const int32_t* pos_target,
                         const float* dlogp, void* dlogits, void* stream);
+
+/*
+ * moe_router_stats -- router statistics of the trajectory-expanded batch from
+ * compact rows weighted by their occurrence counts (HARTS abstract: with
+ * deterministic top-k routing and no token dropping, occurrence counts
+ * restore MoE objective weights and expert-load statistics; Figure 1
+ * caption, q_B = 2 for a row shared by two trajectories; Figure C.1(d)).
+ * A row read by q trajectory positions counts q times:
+ *   load[e]  = sum_r q_r [e in topk(x_r)]     (int64, exact)
+ *   psum[e]  = sum_r q_r softmax(x_r)[e]       (fp32)
+ *   zsum[0]  = sum_r q_r logsumexp(x_r)^2      (fp32)
+ *   n_tok[0] = sum_r q_r                       (int64: expanded positions)
+ * from which a load-balancing loss E sum_e load[e]/(k n_tok) psum[e]/n_tok
+ * and a z-loss zsum/n_tok follow.  topk(x): the top_k largest logits, equal
+ * logits by the lower expert index.  Every sum has a fixed order: the results
+ * are bitwise reproducible.
+ *
+ *   logits      [n_rows, n_experts] bf16 or fp32 (dtype), device
+ *   n_experts   64, 128, 256 or 512;  top_k in [1, min(32, n_experts)]
+ *   row_mult    [n_rows] int32 occurrence counts (device; the plan's
+ *               KDA_F_ROW_MULT table, see kda_plan_device_offset)
+ *   topk_idx    [n_rows, top_k] int32 out, or NULL: chosen experts, in order
+ *   topk_prob   [n_rows, top_k] fp32 out, or NULL: their softmax probabilities
+ *   load, psum  [n_experts] int64 / fp32 out (device);  zsum [1] fp32,
+ *               n_tok [1] int64 out (device)
+ *   ws          moe_router_workspace_bytes(n_rows, n_experts) bytes of scratch
+ * Errors: KDA_ERR_ARG, KDA_ERR_SHAPE, KDA_ERR_WORKSPACE, KDA_ERR_HIP.
+ */
+size_t moe_router_workspace_bytes(int64_t n_rows, int32_t n_experts);
+int moe_router_stats(const void* logits, int32_t dtype, int64_t n_rows, int32_t n_experts,
+                     int32_t top_k, const int32_t* row_mult, int32_t* topk_idx, float* topk_prob,
+                     int64_t* load, float* psum, float* zsum, int64_t* n_tok, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * moe_router_stats_bwd -- gradient of L = <g_psum, psum> + g_z * zsum with
+ * respect to the logits (top-k membership carries none):
+ *   dlogits[r, :] = q_r * p_r * (g_psum - <p_r, g_psum> + 2 g_z lse_r),
+ *   p_r = softmax(x_r), lse_r = logsumexp(x_r).
+ *   g_psum [n_experts] fp32 (device);  dlogits [n_rows, n_experts] fp32 out.
+ * Errors: KDA_ERR_ARG, KDA_ERR_SHAPE, KDA_ERR_HIP.
+ */
+int moe_router_stats_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32_t n_experts,
+                         const int32_t* row_mult, const float* g_psum, float g_z, float* dlogits,
+                         void* stream);
 
 /*
  * Tree-ancestor softmax attention over the plan's compact rows (the full

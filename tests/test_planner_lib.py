@@ -8,6 +8,7 @@ from pathlib import Path
 import numpy as np
 import pytest
 
+from oracle import moe
 from oracle import planner as OP
 from oracle.tree import Tree
 from tree_packed_chunkwise_amd import binding as B
@@ -48,6 +49,7 @@ def _compare(spec, chunk, mode):
     for f, a in MAP.items():
         got, ref = pc.export(f), getattr(po, a)
         assert got.shape == ref.shape and np.array_equal(got, ref), f
+    assert np.array_equal(pc.export("ROW_MULT"), moe.occurrence(t))
     pr, pn = t.gather_map()
     assert np.array_equal(pc.export("POS_ROW"), pr)
     assert np.array_equal(pc.export("POS_NEXT_ROW"), pn)

@@ -29,7 +29,7 @@ FIELDS = [
     "ROW_INDEX", "OUT_ROW", "BUF_SEQ", "BUF_POS", "BUF_CHUNK", "BUF_CONS_PTR", "BUF_CONS",
     "POS_ROW", "POS_NEXT_ROW", "ROW_POS_PTR", "ROW_POS_IDX", "LEAF_SEG", "ROOT_SEG",
     "ATT_ANC_PTR", "ATT_ANC", "ATT_SEG_TILE0", "ATT_TILE_SEG", "ATT_TILE_OFF", "ATT_QORDER",
-    "ATT_KQ_PTR", "ATT_KQ", "ATT_KW_TILE", "ATT_KW_Q0", "ATT_KW_NQ", "ATT_KW_SLOT",
+    "ATT_KQ_PTR", "ATT_KQ", "ATT_KW_TILE", "ATT_KW_Q0", "ATT_KW_NQ", "ATT_KW_SLOT", "ROW_MULT",
 ]
 FIELD_ID = {n: i for i, n in enumerate(FIELDS)}
 
@@ -40,7 +40,8 @@ EXPORTS = [
     "kda_bwd_workspace_bytes", "kda_tree_fwd", "kda_tree_bwd", "gather_logprobs",
     "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
     "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "kda_state_copy",
-    "kda_state_sum", "kda_set_overlap",
+    "kda_state_sum", "kda_set_overlap", "moe_router_workspace_bytes", "moe_router_stats",
+    "moe_router_stats_bwd",
 ]
 
 
@@ -90,6 +91,12 @@ def load_library(path: Path | str | None = None):
     L.kda_tree_fwd.restype = ctypes.c_int
     L.kda_tree_bwd.argtypes = [vp, vp, i32, i32, i32, i32, f32] + [vp] * 17 + [sz, vp]
     L.kda_tree_bwd.restype = ctypes.c_int
+    L.moe_router_workspace_bytes.argtypes = [i64, i32]
+    L.moe_router_workspace_bytes.restype = sz
+    L.moe_router_stats.argtypes = [vp, i32, i64, i32, i32] + [vp] * 8 + [sz, vp]
+    L.moe_router_stats.restype = ctypes.c_int
+    L.moe_router_stats_bwd.argtypes = [vp, i32, i64, i32, vp, vp, f32, vp, vp]
+    L.moe_router_stats_bwd.restype = ctypes.c_int
     L.gather_logprobs.argtypes = [vp, i32, i64, i32, vp, vp, i64, vp, vp, vp]
     L.gather_logprobs.restype = ctypes.c_int
     L.gather_logprobs_bwd.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -337,6 +344,47 @@ def gather_logprobs_bwd(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp
                                               _p(lse), _p(row_pos_ptr), _p(row_pos_idx),
                                               _p(pos_target), _p(dlogp), _p(out),
                                               _stream(logits)))
+    return out
+
+
+def moe_router_stats(logits, row_mult, top_k: int, with_topk: bool = True):
+    """Occurrence-weighted router statistics of compact rows (see
+    include/kda_tree.h).  row_mult: int32 device counts, e.g.
+    plan.device_table("ROW_MULT").  Returns dict(load, psum, zsum, n_tok[,
+    topk_idx, topk_prob])."""
+    import torch
+    _need_cuda(logits, row_mult)
+    n_rows, E = logits.shape
+    dev = logits.device
+    L = load_library()
+    ws = torch.empty(max(1, L.moe_router_workspace_bytes(n_rows, E)), dtype=torch.uint8, device=dev)
+    out = dict(load=torch.empty(E, dtype=torch.int64, device=dev),
+               psum=torch.empty(E, dtype=torch.float32, device=dev),
+               zsum=torch.empty(1, dtype=torch.float32, device=dev),
+               n_tok=torch.empty(1, dtype=torch.int64, device=dev))
+    ti = tp = None
+    if with_topk:
+        ti = torch.empty((n_rows, top_k), dtype=torch.int32, device=dev)
+        tp = torch.empty((n_rows, top_k), dtype=torch.float32, device=dev)
+        out.update(topk_idx=ti, topk_prob=tp)
+    _check(L.moe_router_stats(_p(logits), _dtype_code(logits), n_rows, E, top_k, _p(row_mult),
+                              _p(ti) if ti is not None else None,
+                              _p(tp) if tp is not None else None, _p(out["load"]),
+                              _p(out["psum"]), _p(out["zsum"]), _p(out["n_tok"]), _p(ws),
+                              ws.numel(), _stream(logits)))
+    return out
+
+
+def moe_router_stats_bwd(logits, row_mult, g_psum, g_z: float, out=None):
+    """dlogits of <g_psum, psum> + g_z * zsum (fp32 [n_rows, E])."""
+    import torch
+    _need_cuda(logits, row_mult, g_psum)
+    n_rows, E = logits.shape
+    if out is None:
+        out = torch.empty((n_rows, E), dtype=torch.float32, device=logits.device)
+    _check(load_library().moe_router_stats_bwd(_p(logits), _dtype_code(logits), n_rows, E,
+                                               _p(row_mult), _p(g_psum), float(g_z), _p(out),
+                                               _stream(logits)))
     return out
 
 

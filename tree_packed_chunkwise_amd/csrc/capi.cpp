@@ -29,6 +29,12 @@ hipError_t launch_gather_bwd(const void* logits, bool bf16, int64_t n_rows, int 
                              const float* lse, const int* row_pos_ptr, const int* row_pos_idx,
                              const int* pos_tgt, const float* dlogp, void* dlogits,
                              hipStream_t st);
+size_t router_ws_bytes(int64_t n_rows, int E);
+hipError_t launch_router_stats(const void* x, bool bf16, int64_t n_rows, int E, int k,
+                               const int* q, int* tidx, float* tprob, int64_t* load, float* psum,
+                               float* zsum, int64_t* n_tok, void* ws, hipStream_t st);
+hipError_t launch_router_bwd(const void* x, bool bf16, int64_t n_rows, int E, const int* q,
+                             const float* g, float gz, float* dx, hipStream_t st);
 hipError_t launch_state_copy(const float* src, const int* sidx, float* dst, const int* didx, int n,
                              int64_t elems, hipStream_t st);
 hipError_t launch_state_sum(const float* src, const int* ptr, const int* idx, int n_dst,
@@ -275,6 +281,7 @@ int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64
     case KDA_F_ATT_KW_Q0: return put32(p.att_kw_q0);
     case KDA_F_ATT_KW_NQ: return put32(p.att_kw_nq);
     case KDA_F_ATT_KW_SLOT: return put32(p.att_kw_slot);
+    case KDA_F_ROW_MULT: return put32(p.row_mult);
     default: return fail(KDA_ERR_ARG, "unknown export field");
   }
 }
@@ -301,6 +308,7 @@ int64_t kda_plan_device_offset(const kda_plan* plan, int32_t field) {
     case KDA_F_ROW_POS_IDX: return d.row_pos_idx * 4;
     case KDA_F_ROW_INDEX: return d.row_index * 4;
     case KDA_F_OUT_ROW: return d.out_row * 4;
+    case KDA_F_ROW_MULT: return d.row_mult * 4;
     default: return fail(KDA_ERR_ARG, "field has no device table");
   }
 }
@@ -405,6 +413,48 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
 
 int kda_set_overlap(int32_t enable) {
   kda::set_overlap(enable != 0);
+  return KDA_OK;
+}
+
+namespace {
+bool router_shape_ok(int32_t E) { return E == 64 || E == 128 || E == 256 || E == 512; }
+}  // namespace
+
+size_t moe_router_workspace_bytes(int64_t n_rows, int32_t n_experts) {
+  if (n_rows < 0 || !router_shape_ok(n_experts)) return 0;
+  return kda::router_ws_bytes(n_rows, n_experts);
+}
+
+int moe_router_stats(const void* logits, int32_t dtype, int64_t n_rows, int32_t n_experts,
+                     int32_t top_k, const int32_t* row_mult, int32_t* topk_idx, float* topk_prob,
+                     int64_t* load, float* psum, float* zsum, int64_t* n_tok, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32) return fail(KDA_ERR_SHAPE, "dtype");
+  if (!router_shape_ok(n_experts)) return fail(KDA_ERR_SHAPE, "n_experts must be 64, 128, 256 or 512");
+  if (top_k < 1 || top_k > 32 || top_k > n_experts) return fail(KDA_ERR_SHAPE, "top_k");
+  if (n_rows < 0 || n_rows >= (int64_t)INT32_MAX) return fail(KDA_ERR_ARG, "bad n_rows");
+  if ((n_rows > 0 && (!logits || !row_mult)) || !load || !psum || !zsum || !n_tok || !ws)
+    return fail(KDA_ERR_ARG, "null argument");
+  if (ws_bytes < kda::router_ws_bytes(n_rows, n_experts))
+    return fail(KDA_ERR_WORKSPACE, "router workspace too small");
+  hipError_t e = kda::launch_router_stats(logits, dtype == KDA_DTYPE_BF16, n_rows, n_experts, top_k,
+                                          row_mult, topk_idx, topk_prob, load, psum, zsum, n_tok,
+                                          ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_router_stats launch");
+  return KDA_OK;
+}
+
+int moe_router_stats_bwd(const void* logits, int32_t dtype, int64_t n_rows, int32_t n_experts,
+                         const int32_t* row_mult, const float* g_psum, float g_z, float* dlogits,
+                         void* stream) {
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32) return fail(KDA_ERR_SHAPE, "dtype");
+  if (!router_shape_ok(n_experts)) return fail(KDA_ERR_SHAPE, "n_experts must be 64, 128, 256 or 512");
+  if (n_rows < 0 || n_rows >= (int64_t)INT32_MAX) return fail(KDA_ERR_ARG, "bad n_rows");
+  if (n_rows > 0 && (!logits || !row_mult || !g_psum || !dlogits))
+    return fail(KDA_ERR_ARG, "null argument");
+  hipError_t e = kda::launch_router_bwd(logits, dtype == KDA_DTYPE_BF16, n_rows, n_experts, row_mult,
+                                        g_psum, g_z, dlogits, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_router_stats_bwd launch");
   return KDA_OK;
 }
 

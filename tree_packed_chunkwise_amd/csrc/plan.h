@@ -23,7 +23,7 @@ struct DevLayout {
   int64_t buf_cons_ptr, buf_cons, buf_chunk;
   int64_t rep_row, rep_ptr, rep_slot;
   int64_t root_seq_ptr, root_seq;
-  int64_t pos_row, pos_next_row, row_pos_ptr, row_pos_idx;
+  int64_t pos_row, pos_next_row, row_pos_ptr, row_pos_idx, row_mult;
   int64_t att_seg_row, att_seg_len, att_anc_ptr, att_anc, att_seg_tile0;
   int64_t att_tile_seg, att_tile_off, att_qorder, att_kq_ptr, att_kq;
   int64_t att_kw_tile, att_kw_q0, att_kw_nq, att_kw_slot, att_ks_tile, att_ks_slot0, att_ks_n;
@@ -59,6 +59,8 @@ struct Plan {
   std::vector<int32_t> root_seq_ptr, root_seq;
   // gather map
   std::vector<int32_t> pos_row, pos_next_row, row_pos_ptr, row_pos_idx;
+  // occurrence count of every compact row (trajectories through it)
+  std::vector<int32_t> row_mult;
   std::vector<int32_t> leaf_seg, root_seg;
   // tree-ancestor attention.  Tiles are ATT_TILE-row pieces of segments, in
   // canonical order (segment ascending, offset ascending; seg_tile0 is the

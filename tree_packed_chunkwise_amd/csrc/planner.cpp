@@ -163,6 +163,19 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
   P.n_rows = n_rows;
   P.seg_start = s;
   P.seg_end = e;
+  // occurrence count of every compact row: the trajectories through it, i.e.
+  // the leaves below its segment (children follow parents in pre-order)
+  {
+    std::vector<int32_t> below(n, 0);
+    for (auto it = order.rbegin(); it != order.rend(); ++it) {
+      const int32_t v = *it;
+      if (nchild(v) == 0) below[v] = 1;
+      if (parent[v] >= 0) below[parent[v]] += below[v];
+    }
+    P.row_mult.assign(n_rows, 0);
+    for (int32_t v = 0; v < n; ++v)
+      for (int64_t t = 0; t < seg_len[v]; ++t) P.row_mult[row0[v] + t] = below[v];
+  }
 
   // compact row of trajectory position `pos` on the root path of segment v
   auto row_at = [&](int32_t v, int64_t pos) -> int32_t {
@@ -635,6 +648,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
         {&d.root_seq_ptr, &P.root_seq_ptr},   {&d.root_seq, &P.root_seq},
         {&d.pos_row, &P.pos_row},             {&d.pos_next_row, &P.pos_next_row},
         {&d.row_pos_ptr, &P.row_pos_ptr},     {&d.row_pos_idx, &P.row_pos_idx},
+        {&d.row_mult, &P.row_mult},
         {&d.att_seg_row, &P.att_seg_row},     {&d.att_seg_len, &P.att_seg_len},
         {&d.att_anc_ptr, &P.att_anc_ptr},     {&d.att_anc, &P.att_anc},
         {&d.att_seg_tile0, &P.att_seg_tile0}, {&d.att_tile_seg, &P.att_tile_seg},
