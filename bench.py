@@ -422,6 +422,43 @@ def measure_router(steps):
         return {"error": repr(exc)}
 
 
+def measure_l1(seed=17):
+    """Compression-oriented microbatches (kda_l1_plan, host) for a synthetic
+    rollout batch: 48 trees shaped like the workload trees (4-ary, depth 2 or
+    3, segments of U{256..2048} tokens), 64k-token microbatch budget.  The
+    bound is the forest's own compression (no tree cut)."""
+    import time as _t
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    try:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        parents, lens = [], []
+        for i in range(48):
+            spec = synth.tree_kary(4, 2 + (i % 2), 256, 2048, rng)
+            off = len(parents)
+            parents += [int(p) + off if p >= 0 else -1 for p in spec.parent]
+            lens += [int(x) for x in spec.seg_len]
+        budget = 65536
+        t0 = _t.perf_counter()
+        r = B.l1_plan(parents, lens, budget)
+        ms = (_t.perf_counter() - t0) * 1e3
+        par = np.asarray(parents)
+        ln = np.asarray(lens, np.int64)
+        endp = np.zeros(len(par), np.int64)
+        for v in range(len(par)):   # parents precede children here
+            endp[v] = (endp[par[v]] if par[v] >= 0 else 0) + ln[v]
+        leaf = np.ones(len(par), bool)
+        leaf[par[par >= 0]] = False
+        return {"workload": f"48 trees (4-ary, depth 2-3, U{{256..2048}}), {int(ln.sum())} unique "
+                            f"tokens, {int(endp[leaf].sum())} trajectory tokens, budget {budget}",
+                "microbatches": int(len(r["unique"])), "compression": round(r["compression"], 4),
+                "balance": round(r["balance"], 4),
+                "bound": round(float(endp[leaf].sum() / ln.sum()), 4),
+                "plan_ms": round(ms, 3)}
+    except Exception as exc:  # reported, never fatal to the headline line
+        return {"error": repr(exc)}
+
+
 def measure_hybrid(steps):
     """The hybrid layer group (3 KDA layers, tree attention, log-prob gather,
     hidden 2048, vocab 32000, bf16) forward + backward on the same tree."""
@@ -649,6 +686,7 @@ def main():
     window = measure_window(w, dev, a.expanded_steps, ms) if a.expanded_steps > 0 else None
     attention = measure_attention(a.attn_steps) if a.attn_steps > 0 else None
     router = measure_router(10) if a.attn_steps > 0 else None
+    l1plan = measure_l1()
     hybrid = measure_hybrid(a.hybrid_steps) if a.hybrid_steps > 0 else None
 
     out = {
@@ -671,7 +709,7 @@ def main():
         "expanded": expanded, "plan_modes": modes, "sharing_window": window,
         "replay_ablation": ablation,
         "kernels": kernels, "finite": ok,
-        "tree_attention": attention, "hybrid_group": hybrid, "moe_router": router,
+        "tree_attention": attention, "hybrid_group": hybrid, "moe_router": router, "l1_planner": l1plan,
     }
     print(json.dumps(out), flush=True)
 

@@ -135,6 +135,30 @@ int kda_tree_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
 
 void kda_plan_destroy(kda_plan* plan);
 
+/*
+ * kda_l1_plan -- compression-oriented microbatches of whole trajectories
+ * (HARTS abstract and Figure 1(c): the first planner level builds
+ * compression-oriented microbatches; Table 4 measures compression and
+ * balance).  A microbatch's load is its unique token count (the union of
+ * its trajectories' rows) and stays within `budget` (a trajectory longer
+ * than the budget goes alone).  Trees that fit stay whole; larger trees are
+ * cut into groups of leaves in depth-first order; the items are packed
+ * first-fit decreasing, then placed on the least-loaded microbatch (kept
+ * when all fit).  Host only; deterministic.
+ *
+ *   parent, seg_len  as for kda_tree_plan (n_seg entries)
+ *   leaf_mb          [n_leaf] out: microbatch of each trajectory, leaves by
+ *                    ascending segment id
+ *   n_mb             out: number of microbatches (<= n_leaf)
+ *   mb_unique, mb_expanded  [n_leaf] out: per microbatch (first *n_mb used)
+ *                    its unique tokens and the summed lengths of its
+ *                    trajectories; compression = sum expanded / sum unique,
+ *                    balance = mean unique / max unique
+ * Errors: KDA_ERR_ARG, KDA_ERR_TREE (malformed tree, budget <= 0).
+ */
+int kda_l1_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len, int64_t budget,
+                int32_t* leaf_mb, int32_t* n_mb, int64_t* mb_unique, int64_t* mb_expanded);
+
 /* Sizes and counts of a plan.  Host pointers. */
 int kda_plan_info(const kda_plan* plan, kda_plan_info_t* info);
 

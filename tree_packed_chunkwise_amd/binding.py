@@ -41,7 +41,7 @@ EXPORTS = [
     "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
     "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "kda_state_copy",
     "kda_state_sum", "kda_set_overlap", "moe_router_workspace_bytes", "moe_router_stats",
-    "moe_router_stats_bwd",
+    "moe_router_stats_bwd", "kda_l1_plan",
 ]
 
 
@@ -91,6 +91,8 @@ def load_library(path: Path | str | None = None):
     L.kda_tree_fwd.restype = ctypes.c_int
     L.kda_tree_bwd.argtypes = [vp, vp, i32, i32, i32, i32, f32] + [vp] * 17 + [sz, vp]
     L.kda_tree_bwd.restype = ctypes.c_int
+    L.kda_l1_plan.argtypes = [i32, vp, vp, i64, vp, vp, vp, vp]
+    L.kda_l1_plan.restype = ctypes.c_int
     L.moe_router_workspace_bytes.argtypes = [i64, i32]
     L.moe_router_workspace_bytes.restype = sz
     L.moe_router_stats.argtypes = [vp, i32, i64, i32, i32] + [vp] * 8 + [sz, vp]
@@ -345,6 +347,29 @@ def gather_logprobs_bwd(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp
                                               _p(pos_target), _p(dlogp), _p(out),
                                               _stream(logits)))
     return out
+
+
+def l1_plan(parent, seg_len, budget: int) -> dict:
+    """Compression-oriented microbatches of whole trajectories (host; see
+    include/kda_tree.h).  Returns dict(leaf_mb [n_leaf], unique [n_mb],
+    expanded [n_mb], compression, balance)."""
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    seg_len = np.ascontiguousarray(seg_len, dtype=np.int32)
+    n = len(parent)
+    has_child = np.zeros(n, dtype=bool)
+    has_child[parent[parent >= 0]] = True
+    n_leaf = int((~has_child).sum())
+    leaf_mb = np.empty(n_leaf, dtype=np.int32)
+    n_mb = ctypes.c_int32(0)
+    uniq = np.empty(max(n_leaf, 1), dtype=np.int64)
+    expd = np.empty(max(n_leaf, 1), dtype=np.int64)
+    _check(load_library().kda_l1_plan(n, _np_ptr(parent), _np_ptr(seg_len), int(budget),
+                                      _np_ptr(leaf_mb), ctypes.byref(n_mb), _np_ptr(uniq),
+                                      _np_ptr(expd)))
+    m = n_mb.value
+    uniq, expd = uniq[:m].copy(), expd[:m].copy()
+    return dict(leaf_mb=leaf_mb, unique=uniq, expanded=expd,
+                compression=float(expd.sum() / uniq.sum()), balance=float(uniq.mean() / uniq.max()))
 
 
 def moe_router_stats(logits, row_mult, top_k: int, with_topk: bool = True):

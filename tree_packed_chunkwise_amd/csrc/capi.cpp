@@ -35,6 +35,9 @@ hipError_t launch_router_stats(const void* x, bool bf16, int64_t n_rows, int E, 
                                float* zsum, int64_t* n_tok, void* ws, hipStream_t st);
 hipError_t launch_router_bwd(const void* x, bool bf16, int64_t n_rows, int E, const int* q,
                              const float* g, float gz, float* dx, hipStream_t st);
+int l1_plan(int32_t n, const int32_t* parent, const int32_t* seg_len, int64_t budget,
+            std::vector<int32_t>& leaf_mb, std::vector<int64_t>& mb_unique,
+            std::vector<int64_t>& mb_expanded, std::string& err);
 hipError_t launch_state_copy(const float* src, const int* sidx, float* dst, const int* didx, int n,
                              int64_t elems, hipStream_t st);
 hipError_t launch_state_sum(const float* src, const int* ptr, const int* idx, int n_dst,
@@ -188,6 +191,23 @@ int kda_tree_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
 }
 
 void kda_plan_destroy(kda_plan* plan) { delete plan; }
+
+int kda_l1_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len, int64_t budget,
+                int32_t* leaf_mb, int32_t* n_mb, int64_t* mb_unique, int64_t* mb_expanded) {
+  if (!parent || !seg_len || !leaf_mb || !n_mb || !mb_unique || !mb_expanded)
+    return fail(KDA_ERR_ARG, "null argument");
+  std::vector<int32_t> lm;
+  std::vector<int64_t> mu, mx;
+  std::string err;
+  if (kda::l1_plan(n_seg, parent, seg_len, budget, lm, mu, mx, err) != 0)
+    return fail(KDA_ERR_TREE, err);
+  std::copy(lm.begin(), lm.end(), leaf_mb);
+  std::copy(mu.begin(), mu.end(), mb_unique);
+  std::copy(mx.begin(), mx.end(), mb_expanded);
+  *n_mb = (int32_t)mu.size();
+  g_err.clear();
+  return KDA_OK;
+}
 
 int kda_plan_info(const kda_plan* plan, kda_plan_info_t* info) {
   if (!plan || !info) return fail(KDA_ERR_ARG, "null argument");
