@@ -506,19 +506,40 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     __syncthreads();  // the previous phase's LDS readers are done
     {  // staging: channel c0 of the pass, rows r0 .. r0 + RPT - 1
       const int ch = DH * hf + c0;
+      if constexpr (RPT == 8) {   // the thread's 8 rows are one 16-byte run of each [c][i] array
+        bf16x8 rh8, rl8, qh8, ql8, kh8, kl8;
 #pragma unroll
-      for (int t = 0; t < RPT; ++t) {
-        const int n = hf * RPT + t, i = r0 + t;
-        const float ref = s.gref[i >> 4][ch];
-        const float f = __expf(gm[n] - ref), fi = __expf(ref - gm[n]);
-        __bf16 x, y;
-        split_bf16(kk[n] * fi, x, y);
-        s.u.d.rh[c0][i] = x; s.u.d.rl[c0][i] = y;
-        split_bf16(qq[n] * f, x, y);
-        s.u.d.qh[c0][i] = x; s.u.d.ql[c0][i] = y;
-        split_bf16(kk[n] * f, x, y);
-        s.u.d.kh[c0][i] = x; s.u.d.kl[c0][i] = y;
-        s.u.d.gam[c0][i] = gm[n];
+        for (int t = 0; t < 8; ++t) {
+          const int n = hf * RPT + t, i = r0 + t;
+          const float ref = s.gref[i >> 4][ch];
+          const float f = __expf(gm[n] - ref), fi = __expf(ref - gm[n]);
+          __bf16 x, y;
+          split_bf16(kk[n] * fi, x, y);
+          rh8[t] = x; rl8[t] = y;
+          split_bf16(qq[n] * f, x, y);
+          qh8[t] = x; ql8[t] = y;
+          split_bf16(kk[n] * f, x, y);
+          kh8[t] = x; kl8[t] = y;
+          s.u.d.gam[c0][i] = gm[n];
+        }
+        *(bf16x8*)&s.u.d.rh[c0][r0] = rh8; *(bf16x8*)&s.u.d.rl[c0][r0] = rl8;
+        *(bf16x8*)&s.u.d.qh[c0][r0] = qh8; *(bf16x8*)&s.u.d.ql[c0][r0] = ql8;
+        *(bf16x8*)&s.u.d.kh[c0][r0] = kh8; *(bf16x8*)&s.u.d.kl[c0][r0] = kl8;
+      } else {
+#pragma unroll
+        for (int t = 0; t < RPT; ++t) {
+          const int n = hf * RPT + t, i = r0 + t;
+          const float ref = s.gref[i >> 4][ch];
+          const float f = __expf(gm[n] - ref), fi = __expf(ref - gm[n]);
+          __bf16 x, y;
+          split_bf16(kk[n] * fi, x, y);
+          s.u.d.rh[c0][i] = x; s.u.d.rl[c0][i] = y;
+          split_bf16(qq[n] * f, x, y);
+          s.u.d.qh[c0][i] = x; s.u.d.ql[c0][i] = y;
+          split_bf16(kk[n] * f, x, y);
+          s.u.d.kh[c0][i] = x; s.u.d.kl[c0][i] = y;
+          s.u.d.gam[c0][i] = gm[n];
+        }
       }
     }
     __syncthreads();
