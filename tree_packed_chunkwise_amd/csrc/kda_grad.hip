@@ -32,6 +32,8 @@
 // column block, the channel factor between the two references applied to the
 // output rows), the gradients are combined, and dg is formed by a parallel
 // reverse scan.
+#include <type_traits>
+
 #include "chunk.h"
 #include "timing.h"
 
@@ -105,6 +107,7 @@ struct GradSmem {
       __bf16 qh[64][G::PB], ql[64][G::PB];   // Q e^(Gam - gref)   [c][i]
       __bf16 kh[64][G::PB], kl[64][G::PB];   // K e^(Gam - gref)   [c][i]
       float gam[64][G::PG];                  // Gam, replaced by dGam
+      __bf16 qraw[64][G::PB], kraw[64][G::PB];  // Q, K as read (bf16 inputs)  [c][i]
     } d;
   } u;
   __attribute__((aligned(16))) float dfac[G::NLOW][D];   // e^(gref_I - gref_J), J <= I
@@ -137,6 +140,9 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   constexpr int KB = (BC + 31) / 32;
   constexpr bool HALF = (BC == 16);
   constexpr int NV4 = (BC * D / 4 + NT - 1) / NT;   // 4-element pieces of dO per thread
+  // bf16 inputs: the combine of phase 3 rebuilds the decayed q, k from the
+  // inputs themselves (exact in bf16) instead of their hi/lo split products
+  constexpr bool RAWQK = std::is_same<TIn, uint16_t>::value;
   __shared__ GradSmem<BC, D> s;
   const int c = c_begin + blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -525,6 +531,16 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
         *(bf16x8*)&s.u.d.rh[c0][r0] = rh8; *(bf16x8*)&s.u.d.rl[c0][r0] = rl8;
         *(bf16x8*)&s.u.d.qh[c0][r0] = qh8; *(bf16x8*)&s.u.d.ql[c0][r0] = ql8;
         *(bf16x8*)&s.u.d.kh[c0][r0] = kh8; *(bf16x8*)&s.u.d.kl[c0][r0] = kl8;
+        if constexpr (RAWQK) {
+          bf16x8 q8, k8;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            q8[t] = (__bf16)qq[hf * RPT + t];
+            k8[t] = (__bf16)kk[hf * RPT + t];
+          }
+          *(bf16x8*)&s.u.d.qraw[c0][r0] = q8;
+          *(bf16x8*)&s.u.d.kraw[c0][r0] = k8;
+        }
       } else {
 #pragma unroll
         for (int t = 0; t < RPT; ++t) {
@@ -539,6 +555,10 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
           split_bf16(kk[n] * f, x, y);
           s.u.d.kh[c0][i] = x; s.u.d.kl[c0][i] = y;
           s.u.d.gam[c0][i] = gm[n];
+          if constexpr (RAWQK) {
+            s.u.d.qraw[c0][i] = (__bf16)qq[n];
+            s.u.d.kraw[c0][i] = (__bf16)kk[n];
+          }
         }
       }
     }
@@ -585,9 +605,17 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
           const float gam = s.u.d.gam[cl][i];
           const float ref = s.gref[tI][ch], er = s.eref[tI][ch], eg = s.ecg[tI][ch];
           const float lf = __expf(gam - ref), rf = __expf(ref - gam);
-          const float qd = bf16_val(s.u.d.qh[cl][i]) + bf16_val(s.u.d.ql[cl][i]);   // q e^(Gam-ref)
-          const float kd = bf16_val(s.u.d.kh[cl][i]) + bf16_val(s.u.d.kl[cl][i]);   // k e^(Gam-ref)
-          const float kr = bf16_val(s.u.d.rh[cl][i]) + bf16_val(s.u.d.rl[cl][i]);   // k e^(ref-Gam)
+          float qd, kd, kr;   // q e^(Gam-ref), k e^(Gam-ref), k e^(ref-Gam)
+          if constexpr (RAWQK) {
+            const float qv = bf16_val(s.u.d.qraw[cl][i]), kv = bf16_val(s.u.d.kraw[cl][i]);
+            qd = qv * lf;
+            kd = kv * lf;
+            kr = kv * rf;
+          } else {
+            qd = bf16_val(s.u.d.qh[cl][i]) + bf16_val(s.u.d.ql[cl][i]);
+            kd = bf16_val(s.u.d.kh[cl][i]) + bf16_val(s.u.d.kl[cl][i]);
+            kr = bf16_val(s.u.d.rh[cl][i]) + bf16_val(s.u.d.rl[cl][i]);
+          }
           const float xq = dQt[m][r] * er + rP[r];
           const float xk = dKt[m][r] * er + rA[r];
           const float kh2 = dKh[m][r] * kr * eg;
