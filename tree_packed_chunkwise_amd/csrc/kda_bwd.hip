@@ -280,7 +280,7 @@ hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int c_be
   return hipErrorInvalidValue;
 }
 
-int round_slices(int nseq, int H, int D);
+int round_slices(int nseq, int H, int D, int max_slices);
 
 template <typename TIn, int BC, int D, int NV>
 hipError_t launch_bround(const BwdArgs& a, int nseq, int seq0, int slices, hipStream_t st) {
@@ -291,12 +291,12 @@ hipError_t launch_bround(const BwdArgs& a, int nseq, int seq0, int slices, hipSt
 
 template <typename TIn, int BC, int D>
 hipError_t launch_brounds_t(const BwdArgs& a, const int* round_ptr_host, int r_begin, int r_end,
-                            hipStream_t st) {
+                            int max_slices, hipStream_t st) {
   constexpr int NCB = D / 16;
   for (int r = r_end - 1; r >= r_begin; --r) {
     const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
     if (nseq == 0) continue;
-    const int sl = round_slices(nseq, a.H, D);
+    const int sl = round_slices(nseq, a.H, D, max_slices);
     const int nv = NCB / sl;
     hipError_t e = hipErrorInvalidValue;
     if (nv == NCB) e = launch_bround<TIn, BC, D, NCB>(a, nseq, round_ptr_host[r], sl, st);
@@ -310,10 +310,10 @@ hipError_t launch_brounds_t(const BwdArgs& a, const int* round_ptr_host, int r_b
 
 // rounds r_end - 1 down to r_begin
 hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
-                             int r_begin, int r_end, hipStream_t st) {
+                             int r_begin, int r_end, int max_slices, hipStream_t st) {
 #define KDA_BR_CASE(T, BCv, Dv) \
   if (BC == BCv && D == Dv) \
-    return launch_brounds_t<T, BCv, Dv>(a, round_ptr_host, r_begin, r_end, st);
+    return launch_brounds_t<T, BCv, Dv>(a, round_ptr_host, r_begin, r_end, max_slices, st);
   if (bf16) {
     KDA_BR_CASE(uint16_t, 64, 128)
     KDA_BR_CASE(uint16_t, 64, 64)

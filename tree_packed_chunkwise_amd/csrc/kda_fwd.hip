@@ -215,9 +215,12 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
 }
 
 // Slices of a round: as many as keep every block on its own compute unit
-// (256 CUs) without exceeding D/16 column blocks.
-int round_slices(int nseq, int H, int D) {
-  const int maxs = D / 16;
+// (256 CUs) without exceeding D/16 column blocks or max_slices (<= 0: no
+// limit of its own).  A round that runs beside prep or gradient work on a
+// second stream takes fewer: its chain is bound by each block's own
+// bandwidth, so the compute units it leaves go to the throughput kernels.
+int round_slices(int nseq, int H, int D, int max_slices) {
+  const int maxs = max_slices > 0 && max_slices < D / 16 ? max_slices : D / 16;
   int sl = 1;
   while (sl * 2 <= maxs && (long)nseq * H * sl * 2 <= 256) sl *= 2;
   return sl;
@@ -232,12 +235,12 @@ hipError_t launch_round(const FwdArgs& a, int nseq, int seq0, int slices, hipStr
 
 template <typename TIn, int BC, int D>
 hipError_t launch_fwd2_t(const FwdArgs& a, const int* round_ptr_host, int r_begin, int r_end,
-                         hipStream_t st) {
+                         int max_slices, hipStream_t st) {
   constexpr int NCB = D / 16;
   for (int r = r_begin; r < r_end; ++r) {
     const int nseq = round_ptr_host[r + 1] - round_ptr_host[r];
     if (nseq == 0) continue;
-    const int sl = round_slices(nseq, a.H, D);
+    const int sl = round_slices(nseq, a.H, D, max_slices);
     const int nv = NCB / sl;
     hipError_t e = hipErrorInvalidValue;
     if (nv == NCB) e = launch_round<TIn, BC, D, NCB>(a, nseq, round_ptr_host[r], sl, st);
@@ -251,9 +254,9 @@ hipError_t launch_fwd2_t(const FwdArgs& a, const int* round_ptr_host, int r_begi
 
 // rounds r_begin .. r_end - 1, in order
 hipError_t launch_fwd_rounds(const FwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
-                             int r_begin, int r_end, hipStream_t st) {
+                             int r_begin, int r_end, int max_slices, hipStream_t st) {
 #define KDA_FWD_CASE(T, BCv, Dv) \
-  if (BC == BCv && D == Dv) return launch_fwd2_t<T, BCv, Dv>(a, round_ptr_host, r_begin, r_end, st);
+  if (BC == BCv && D == Dv) return launch_fwd2_t<T, BCv, Dv>(a, round_ptr_host, r_begin, r_end, max_slices, st);
   if (bf16) {
     KDA_FWD_CASE(uint16_t, 64, 128)
     KDA_FWD_CASE(uint16_t, 64, 64)

@@ -36,11 +36,11 @@ namespace kda {
 hipError_t launch_prep(const FwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
                        hipStream_t st);
 hipError_t launch_fwd_rounds(const FwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
-                             int r_begin, int r_end, hipStream_t st);
+                             int r_begin, int r_end, int max_slices, hipStream_t st);
 hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
                             hipStream_t st);
 hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const int* round_ptr_host,
-                             int r_begin, int r_end, hipStream_t st);
+                             int r_begin, int r_end, int max_slices, hipStream_t st);
 hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
                        hipStream_t st);
 hipError_t launch_reduce(const BwdArgs& a, int D, int n_rep_rows, int n_root, hipStream_t st);
@@ -58,6 +58,11 @@ struct Side {
 std::mutex g_mu;
 std::map<int, Side*> g_side;
 std::atomic<int> g_overlap{1};
+
+// Column slices per sequence of a round that runs beside another stream's
+// work (measured on the 4-ary tree workload: 2 beats 4 and 8 there, while a
+// lone round prefers all D/16).
+constexpr int kSlicesBeside = 2;
 
 hipError_t side_of_current_device(Side** out) {
   int dev = 0;
@@ -121,7 +126,7 @@ hipError_t run_fwd(const FwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
   const int c1 = R > 1 ? round_chunk_begin(p, 1) : nc;
   if (c1 == 0 || c1 >= nc || !g_overlap.load()) {  // nothing to overlap, or one stream asked for
     KDA_TRY(launch_prep(a, bf16, BC, D, 0, nc, st));
-    return launch_fwd_rounds(a, bf16, BC, D, rp, 0, R, st);
+    return launch_fwd_rounds(a, bf16, BC, D, rp, 0, R, 0, st);
   }
   Side* sd = nullptr;
   KDA_TRY(side_of_current_device(&sd));
@@ -143,10 +148,10 @@ hipError_t run_fwd(const FwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
     KDA_TRY(launch_prep(a, bf16, BC, D, cb, ce - cb, sd->s));
     KDA_TRY(hipEventRecord(ev, sd->s));
   }
-  KDA_TRY(launch_fwd_rounds(a, bf16, BC, D, rp, 0, 1, st));
+  KDA_TRY(launch_fwd_rounds(a, bf16, BC, D, rp, 0, 1, kSlicesBeside, st));
   for (size_t i = 0; i < ng; ++i) {
     KDA_TRY(hipStreamWaitEvent(st, sd->groups[i], 0));
-    KDA_TRY(launch_fwd_rounds(a, bf16, BC, D, rp, gr[i], gr[i + 1], st));
+    KDA_TRY(launch_fwd_rounds(a, bf16, BC, D, rp, gr[i], gr[i + 1], kSlicesBeside, st));
   }
   return hipSuccess;
 }
@@ -176,7 +181,7 @@ hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
   bool forked = false;
   for (int r = R - 1; r >= 0; --r) {
     if (gathered && r == R - 2) KDA_TRY(hipStreamWaitEvent(st, gathered, 0));
-    KDA_TRY(launch_bwd_rounds(a, bf16, BC, D, rp, r, r + 1, st));
+    KDA_TRY(launch_bwd_rounds(a, bf16, BC, D, rp, r, r + 1, sd ? kSlicesBeside : 0, st));
     const int cb = round_chunk_begin(p, r);
     if (sd && r > 0 && ready_end - cb >= group) {
       KDA_TRY(order_after(sd->fork, st, sd->s));
