@@ -87,8 +87,8 @@ def path_bytes_per_token(H, D, in_bytes=2):
 # sources are hashed at run time and the figure is dropped when they differ.
 MEASURED_TRAFFIC = {
     "kda_bwd_chunk_grad": {"sources": ("kda_grad.hip", "chunk.h", "common.h"),
-                           "sha256_16": "a7d59541b7c8dd6e", "workload": 2,
-                           "bytes_per_launch": 2313167770},
+                           "sha256_16": "ad568e4a46839379", "workload": 2,
+                           "bytes_per_launch": 2202106349},
 }
 
 
@@ -708,7 +708,10 @@ def main():
         "plan_host_ms": round(plan_host_ms, 3), "plan_upload_ms": round(upload_ms, 3),
         "expanded": expanded, "plan_modes": modes, "sharing_window": window,
         "replay_ablation": ablation,
-        "kernels": kernels, "finite": ok,
+        "kernels": kernels,
+        "kernels_single_stream": {n: {"launches_per_step": c / 2, "ms_per_step": round(t / 2, 4)}
+                                  for n, (c, t) in sorted(kt_seq.items())},
+        "finite": ok,
         "tree_attention": attention, "hybrid_group": hybrid, "moe_router": router, "l1_planner": l1plan,
     }
     print(json.dumps(out), flush=True)

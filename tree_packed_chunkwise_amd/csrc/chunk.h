@@ -152,16 +152,24 @@ __device__ inline f32x4 ld_h4(const _Float16* p) {
   const f16x4 h = *(const f16x4*)p;
   return (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
-// The fp16 state copies (chunk start states, chunk end-state gradients) and
-// the chunk-row gradients dy handed from the reverse rounds to the chunk pass
-// are kept as 16x16 tiles: tile (C, W) holds rows 16C .. 16C + 15 and columns
-// 16W .. 16W + 15 at elements (C (D/16) + W) 256, and inside it lane l of the
-// wave that carries column block W keeps its quad_transpose row piece
-// (quad_row, quad_col) at 4 l.  One wave's store or load of a tile thus moves
-// 512 (fp16) or 1024 (fp32) contiguous bytes.
+// The tiles that pass between the library's own kernels (the fp16 chunk
+// start states and end-state gradients, the chunk-row gradients dy, the
+// per-chunk dO, the V of a chunk image) are kept as 16x16 tiles in matrix-core
+// accumulator order: tile (C, W) holds rows 16C .. 16C + 15 and columns
+// 16W .. 16W + 15 at elements (C (D/16) + W) 256, and inside it lane
+// l = l16 + 16 g of the wave that carries column block W keeps what a 16x16
+// accumulator tile gives it, rows 16C + 4g .. 16C + 4g + 3 of column
+// 16W + l16, at 4 l .. 4 l + 3.  One wave's store or load of a tile thus
+// moves 512 (fp16) or 1024 (fp32) contiguous bytes, and neither the writer
+// nor a reader that works in accumulator layout moves values between lanes.
 template <int D>
 __device__ inline size_t state_tile(int C, int W) {
   return (size_t)(C * (D / 16) + W) * 256 + 4 * (threadIdx.x & 63);
+}
+// element offset of (row i, column c) of a [*][D] matrix kept in such tiles
+template <int D>
+__device__ inline size_t tile_elem(int i, int c) {
+  return (size_t)((i >> 4) * (D / 16) + (c >> 4)) * 256 + 4 * ((c & 15) + 16 * ((i & 15) >> 2)) + (i & 3);
 }
 
 // B fragment from two accumulator tiles (rows 0-15 and 16-31 of a 32-deep k step)
@@ -260,7 +268,7 @@ struct FwdHead {   // everything but V: what a forward chunk step keeps in LDS
 };
 template <int BC, int D, typename VT>
 struct FwdImage : FwdHead<BC, D> {
-  VT V[BC][D];
+  VT V[BC][D];   // in 16x16 accumulator-order tiles (state_tile), not row-major
 };
 static_assert(sizeof(FwdImage<64, 128, float>) == fwd_image_bytes(64, 128), "image layout");
 static_assert(sizeof(FwdImage<16, 64, uint16_t>) == fwd_image_used(16, 64, 2), "image layout");

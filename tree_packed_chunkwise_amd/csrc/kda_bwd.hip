@@ -43,8 +43,6 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;
   const int col = 16 * (blockIdx.z * NV + wave) + l16;
-  const int cq = col - l16 + quad_col();     // first column of this lane's row piece
-  const int rq = quad_row();                 // its row within a 16-row block
   const int H = a.H;
   const TIn* dOp = (const TIn*)a.dOp;
   const size_t DD = (size_t)D * D;
@@ -62,10 +60,9 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       for (int r = 0; r < 4; ++r)
         dh[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
-  // dO of the chunk in flight, raw: this lane's row piece of the 16-row
-  // halves of every 32-deep k step, from the chunk's dO tiles (zero on replay
-  // rows and past the chunk); quad_transpose turns it into register k order
-  // (chunk.h) when it is used
+  // dO of the chunk in flight, raw: this lane's accumulator piece of the
+  // 16-row halves of every 32-deep k step, from the chunk's dO tiles (zero on
+  // replay rows and past the chunk); two of them form a B fragment
   in4_t<TIn> dor[KB][2];
   auto load_do = [&](int cc) {
     const TIn* src = dOp + ((size_t)cc * H + h) * (BC * D);
@@ -102,11 +99,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
     if (sw) {
       f16x8 dob[KB];
 #pragma unroll
-      for (int ks = 0; ks < KB; ++ks) {
-        quad_transpose(dof[ks][0]);
-        quad_transpose(dof[ks][1]);
-        dob[ks] = acc_pair(dof[ks][0], dof[ks][1]);
-      }
+      for (int ks = 0; ks < KB; ++ks) dob[ks] = acc_pair(dof[ks][0], dof[ks][1]);
       const int save = a.plan.chunk_save[c];
       if (save >= 0) {
         const int p0 = a.plan.buf_cons_ptr[save], p1 = a.plan.buf_cons_ptr[save + 1];
@@ -128,11 +121,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       {
         _Float16* dst = a.dhc + blk * DD;  // fp16 copy for the chunk-local pass
 #pragma unroll
-        for (int C = 0; C < G::NCB; ++C) {
-          f32x4 x = dh[C];
-          quad_transpose(x);
-          st_h4(dst + state_tile<D>(C, col >> 4), x);
-        }
+        for (int C = 0; C < G::NCB; ++C) st_h4(dst + state_tile<D>(C, col >> 4), dh[C]);
       }
       f16x8 dhb[KD];
 #pragma unroll
@@ -200,8 +189,8 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
         for (int J = G::NB - 1; J > I; --J) rr = mfma16k16(fl[I][J], acc4(w[J]), rr);
         f32x4 dy = mfma16k16(ft[I], acc4(rr), (f32x4){0.f, 0.f, 0.f, 0.f});
         w[I] = dy * bz[I];
-        quad_transpose(dy);
-        if (16 * I + rq < len) st_h4(a.dy + blk * (BC * D) + state_tile<D>(I, col >> 4), dy);
+        // rows past the chunk are masked by the reader
+        if (16 * I < len) st_h4(a.dy + blk * (BC * D) + state_tile<D>(I, col >> 4), dy);
       }
       f16x8 wb[KB];
 #pragma unroll
@@ -252,11 +241,14 @@ __global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, DevPlan plan, 
   }
   __syncthreads();
   TIn* dst = dOp + ((size_t)c * H + h) * (BC * D);
-  for (int q = tid; q < BC * D / 4; q += 256) {
+  for (int q = tid; q < BC * D / 4; q += 256) {   // lane l of tile t: its accumulator piece
     const int t = q >> 6, l = q & 63;
-    const int i = 16 * (t / (D / 16)) + 4 * (l >> 4) + (l & 3);
-    const int v = 16 * (t % (D / 16)) + (l & 12);
-    *(V4*)&dst[4 * (size_t)q] = *(const V4*)&rowsm[i * PITCH + v];
+    const int i = 16 * (t / (D / 16)) + 4 * (l >> 4);
+    const int v = 16 * (t % (D / 16)) + (l & 15);
+    V4 x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = rowsm[(i + r) * PITCH + v];
+    *(V4*)&dst[4 * (size_t)q] = x;
   }
 }
 

@@ -65,15 +65,14 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       for (int r = 0; r < 4; ++r)
         hs[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
-  // V of the chunk in flight, raw: this lane's row piece of every 16-row
-  // block (one vector load each; quad_transpose turns it into the
-  // accumulator layout when it is used)
+  // V of the chunk in flight, raw: this lane's accumulator piece of every
+  // 16-row block (one vector load each from the image's V tiles)
   in4_t<TIn> vr[G::NB];
   auto load_v = [&](int cc) {
     const FI* F = (const FI*)image(cc);
 #pragma unroll
     for (int J = 0; J < G::NB; ++J)
-      vr[J] = sw ? *(const in4_t<TIn>*)&F->V[16 * J + rq][cq] : (in4_t<TIn>)0;
+      vr[J] = sw ? *(const in4_t<TIn>*)(&F->V[0][0] + state_tile<D>(J, col >> 4)) : (in4_t<TIn>)0;
   };
   if (cbeg < cend) {
     lds_copy_async(&buf[0], image(cbeg), NVEC);
@@ -95,17 +94,11 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
     // ---- state phase: wave w < NV owns column block w of the slice ----
     if (sw) {
       const float sc = a.scale;
-#pragma unroll
-      for (int J = 0; J < G::NB; ++J) quad_transpose(z[J]);
       {  // start state of the chunk, kept for the reverse pass (fp16: its only
          // consumers feed it to fp16 matrix cores)
         _Float16* dst = a.chunk_h + blk * DD;
 #pragma unroll
-        for (int C = 0; C < G::NCB; ++C) {
-          f32x4 x = hs[C];
-          quad_transpose(x);
-          st_h4(dst + state_tile<D>(C, col >> 4), x);
-        }
+        for (int C = 0; C < G::NCB; ++C) st_h4(dst + state_tile<D>(C, col >> 4), hs[C]);
       }
       f16x8 hb[KD];
 #pragma unroll

@@ -189,12 +189,11 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       const float y = ld_in(k, ((size_t)(r < 0 ? 0 : r) * H + h) * D + c0 + DH * hf);
       kk[hf * RPT + t] = r >= 0 ? y : 0.f;
     }
-  // start state and V as row pieces (phase 1; quad_transpose turns them into
-  // the accumulator layout), A and Td of the forward image, beta
+  // start state and V as accumulator pieces of their 16x16 tiles (phase 1),
+  // A and Td of the forward image, beta
   const bool vw = wave < NCB;
   const int wv = vw ? wave : 0;   // column block the loads use (waves past D/16 load and drop one)
   const int col = 16 * wave + l16;
-  const int cq = 16 * wave + quad_col(), rq = quad_row();
   f16x4 hraw[NCB], dhraw[NCB];
   f16x4 dyh[NB];
   f32x4 dyv[NB], z[NB];
@@ -204,7 +203,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
 #pragma unroll
   for (int C = 0; C < NCB; ++C) hraw[C] = *(const f16x4*)(hsrc + state_tile<D>(C, wv));
 #pragma unroll
-  for (int J = 0; J < NB; ++J) vraw[J] = *(const in4_t<TIn>*)&F->V[16 * J + rq][16 * wv + quad_col()];
+  for (int J = 0; J < NB; ++J) vraw[J] = *(const in4_t<TIn>*)(&F->V[0][0] + state_tile<D>(J, wv));
   constexpr int NAV = (BC * BC / 8 + NT - 1) / NT;
   f16x8 av[NAV], tv;
 #pragma unroll
@@ -303,18 +302,15 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       f32x4 hC[NCB];
 #pragma unroll
       for (int C = 0; C < NCB; ++C) {
-        *(f16x4*)&s.u.p.Hs[16 * C + rq][cq] = hraw[C];   // h as [c][v] fp16, from its row pieces
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.u.p.Hs[16 * C + 4 * g + r][col] = hraw[C][r];   // h as [c][v] fp16
         hC[C] = (f32x4){(float)hraw[C][0], (float)hraw[C][1], (float)hraw[C][2], (float)hraw[C][3]};
-        quad_transpose(hC[C]);
       }
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) hb[ks] = acc_pair(hC[2 * ks], hC[2 * ks + 1]);
     }
 #pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      z[J] = in4_to_f32(vraw[J]);
-      quad_transpose(z[J]);
-    }
+    for (int J = 0; J < NB; ++J) z[J] = in4_to_f32(vraw[J]);
 #pragma unroll
     for (int J = 0; J < NB; ++J)
 #pragma unroll
@@ -326,18 +322,19 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   for (int n = 0; n < NV4; ++n) {
     const int e = tid + NT * n;
     if (e < BC * D / 4) {
-      const int t = e >> 6, l = e & 63;
+      const int t = e >> 6, l = e & 63;   // lane l's piece of tile t: rows i0 .. i0 + 3 of column v
+      const int i0 = 16 * (t / (D / 16)) + 4 * (l >> 4), v = 16 * (t % (D / 16)) + (l & 15);
       const f32x4 x = sc * in4_to_f32(dov[n]);
-      *(f16x4*)&s.u.p.x.dO[16 * (t / (D / 16)) + 4 * (l >> 4) + (l & 3)][16 * (t % (D / 16)) + (l & 12)] =
-          (f16x4){(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s.u.p.x.dO[i0 + r][v] = (_Float16)x[r];
     }
   }
   if (vw) {
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
-      dyv[J] = (f32x4){(float)dyh[J][0], (float)dyh[J][1], (float)dyh[J][2], (float)dyh[J][3]};
-      if (16 * J + rq >= len) dyv[J] = (f32x4){0.f, 0.f, 0.f, 0.f};   // never written there
-      quad_transpose(dyv[J]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)   // rows past the chunk hold no gradient
+        dyv[J][r] = 16 * J + 4 * g + r < len ? (float)dyh[J][r] : 0.f;
     }
     // delta by block forward substitution with the diagonal inverses
     f32x4 d[NB];
@@ -461,31 +458,28 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
     split_tile(ta, Ah[sl], Al[sl]);
   }
   if (vw) {
-    // deGC partial over this wave's 16 columns: channel 16 C + rq, the sum
-    // over v of h dh' (h read back from its fp16 copy, which holds exactly
-    // the stored start state); the four lanes of a row piece differ in lane
-    // bits 2 and 3 (row rotations by 8 and 4)
-    float x[NCB];
+    // deGC partial over this wave's 16 columns: channel 16 C + 4 g + r, the
+    // sum over v of h dh' (h as its fp16 copy, which holds exactly the stored
+    // start state); the 16 lanes of a row group hold the 16 columns, summed
+    // by row_reduce16x16 (lane l16 ends with the sum of value l16)
+    static_assert(NCB == 4 || NCB == 8, "head dim 64 or 128");
+    float x0[16], x1[16];
 #pragma unroll
-    for (int C = 0; C < NCB; ++C) {
-      const f16x4 hv = *(const f16x4*)&s.u.p.Hs[16 * C + rq][cq];
-      x[C] = (float)hv[0] * (float)dhraw[C][0] + (float)hv[1] * (float)dhraw[C][1] +
-             (float)hv[2] * (float)dhraw[C][2] + (float)hv[3] * (float)dhraw[C][3];
-    }
+    for (int C = 0; C < NCB; ++C)
 #pragma unroll
-    for (int C = 0; C < NCB; ++C) {
-      x[C] += dpp_mov<0x128>(x[C]);   // row_ror:8
-      x[C] += dpp_mov<0x124>(x[C]);   // row_ror:4
-    }
-    if ((lane & 12) == 0) {
-#pragma unroll
-      for (int C = 0; C < NCB; ++C) s.redg[wave][16 * C + rq] = x[C];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const float p = (float)hraw[C][r] * (float)dhraw[C][r];
+        if (C < 4) x0[4 * C + r] = p; else x1[4 * (C - 4) + r] = p;
+      }
+    s.redg[wave][16 * (l16 >> 2) + 4 * g + (l16 & 3)] = row_reduce16x16(x0);
+    if constexpr (NCB == 8) s.redg[wave][16 * (4 + (l16 >> 2)) + 4 * g + (l16 & 3)] = row_reduce16x16(x1);
   }
   __syncthreads();  // h is dead: dh' takes its place
   if (vw) {
 #pragma unroll
-    for (int C = 0; C < NCB; ++C) *(f16x4*)&s.u.p.Hs[16 * C + rq][cq] = dhraw[C];
+    for (int C = 0; C < NCB; ++C)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s.u.p.Hs[16 * C + 4 * g + r][col] = dhraw[C][r];
   }
   if (tid < D) {
     float acc = 0.f;

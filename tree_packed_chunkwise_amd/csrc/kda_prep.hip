@@ -102,8 +102,20 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
       const float e2 = __expf(gcl - er.gam[n]);
       F->Qt[i][cc] = (_Float16)(er.q[n] * e1);
       F->Kn[i][cc] = (_Float16)(-er.k[n] * e1);
-      F->V[i][cc] = to_in<TIn>(vv[n]);
       kht[t] = (_Float16)(er.k[n] * e2);
+    }
+    TIn* Vt = &F->V[0][0];   // accumulator-order tiles
+    if constexpr (G::RPT % 4 == 0) {   // 4 rows of one column fill one lane's slot of a tile
+#pragma unroll
+      for (int t = 0; t < G::RPT; t += 4) {
+        in4_t<TIn> x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = to_in<TIn>(vv[hf * G::RPT + t + j]);
+        *(in4_t<TIn>*)&Vt[tile_elem<D>(r0 + t, cc)] = x;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < G::RPT; ++t) Vt[tile_elem<D>(r0 + t, cc)] = to_in<TIn>(vv[hf * G::RPT + t]);
     }
     if constexpr (G::RPT == 8) {
       f16x8 x;
