@@ -183,6 +183,10 @@ int kda_plan_info(const kda_plan* plan, kda_plan_info_t* info);
  *   LEAF_SEG, ROOT_SEG  leaf and root segment ids, ascending
  *   ROW_MULT   per compact row: its occurrence count, the number of
  *              root-to-leaf trajectories through it
+ *   SEQ_LPT    per round (indexed like the sequences): the round's sequence
+ *              ids in the order the round kernels launch them, most chunks
+ *              first, ties by id (a scheduling order only; results do not
+ *              depend on it)
  */
 enum {
   KDA_F_SEG_ROUND = 0, KDA_F_SEG_SEQ, KDA_F_SEG_IS_CONT, KDA_F_SEG_B, KDA_F_SEG_REPLAY,
@@ -194,7 +198,7 @@ enum {
   KDA_F_ROW_POS_IDX, KDA_F_LEAF_SEG, KDA_F_ROOT_SEG,
   KDA_F_ATT_ANC_PTR, KDA_F_ATT_ANC, KDA_F_ATT_SEG_TILE0, KDA_F_ATT_TILE_SEG, KDA_F_ATT_TILE_OFF,
   KDA_F_ATT_QORDER, KDA_F_ATT_KQ_PTR, KDA_F_ATT_KQ, KDA_F_ATT_KW_TILE, KDA_F_ATT_KW_Q0,
-  KDA_F_ATT_KW_NQ, KDA_F_ATT_KW_SLOT, KDA_F_ROW_MULT,
+  KDA_F_ATT_KW_NQ, KDA_F_ATT_KW_SLOT, KDA_F_ROW_MULT, KDA_F_SEQ_LPT,
   KDA_F_COUNT
 };
 int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64_t n);

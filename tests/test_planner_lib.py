@@ -58,6 +58,11 @@ def _compare(spec, chunk, mode):
     ptr, idx = pc.export("ROW_POS_PTR"), pc.export("ROW_POS_IDX")
     for r in range(0, t.n_rows, max(1, t.n_rows // 50)):
         assert np.array_equal(idx[ptr[r]:ptr[r + 1]], np.nonzero(pr == r)[0])
+    # launch order of the round kernels: each round's sequences, most chunks first
+    lpt, rp, nch = pc.export("SEQ_LPT"), pc.export("ROUND_SEQ_PTR"), np.diff(pc.export("SEQ_CHUNK_PTR"))
+    for r in range(len(rp) - 1):
+        want = sorted(range(rp[r], rp[r + 1]), key=lambda q: (-nch[q], q))
+        assert list(lpt[rp[r]:rp[r + 1]]) == want
     i = pc.info
     assert (i["n_rounds"], i["R"], i["n_packed"], i["n_out_rows"]) == \
         (po.n_rounds, po.R, po.n_packed, po.n_out_rows)

@@ -30,6 +30,7 @@ FIELDS = [
     "POS_ROW", "POS_NEXT_ROW", "ROW_POS_PTR", "ROW_POS_IDX", "LEAF_SEG", "ROOT_SEG",
     "ATT_ANC_PTR", "ATT_ANC", "ATT_SEG_TILE0", "ATT_TILE_SEG", "ATT_TILE_OFF", "ATT_QORDER",
     "ATT_KQ_PTR", "ATT_KQ", "ATT_KW_TILE", "ATT_KW_Q0", "ATT_KW_NQ", "ATT_KW_SLOT", "ROW_MULT",
+    "SEQ_LPT",
 ]
 FIELD_ID = {n: i for i, n in enumerate(FIELDS)}
 

@@ -90,6 +90,7 @@ kda::DevPlan make_dev_plan(const kda::Plan& p, const void* dev) {
   v.seq_init_kind = b + d.seq_init_kind;
   v.seq_init_idx = b + d.seq_init_idx;
   v.seq_leaf = b + d.seq_leaf;
+  v.seq_lpt = b + d.seq_lpt;
   v.chunk_seq = b + d.chunk_seq;
   v.chunk_row0 = b + d.chunk_row0;
   v.chunk_len = b + d.chunk_len;
@@ -302,6 +303,7 @@ int64_t kda_plan_export(const kda_plan* plan, int32_t field, int64_t* dst, int64
     case KDA_F_ATT_KW_NQ: return put32(p.att_kw_nq);
     case KDA_F_ATT_KW_SLOT: return put32(p.att_kw_slot);
     case KDA_F_ROW_MULT: return put32(p.row_mult);
+    case KDA_F_SEQ_LPT: return put32(p.seq_lpt);
     default: return fail(KDA_ERR_ARG, "unknown export field");
   }
 }

@@ -14,6 +14,7 @@ struct DevPlan {
   const int* seq_init_kind;
   const int* seq_init_idx;
   const int* seq_leaf;
+  const int* seq_lpt;      // launch order of a round's sequences (most chunks first)
   const int* chunk_seq;
   const int* chunk_row0;
   const int* chunk_len;

@@ -38,8 +38,9 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
   constexpr bool HALF = (BC == 16);          // chunk rows cover half a k step
   constexpr int NVEC = (int)(sizeof(FH) / 16);
   __shared__ FH buf[2];                      // this chunk's image and the next one's
-  const int seq = seq_begin + blockIdx.x;
-  const int h = blockIdx.y;
+  // blocks in the round's launch order: sequence rank major, head minor
+  const int seq = a.plan.seq_lpt[seq_begin + (int)blockIdx.x / a.H];
+  const int h = (int)blockIdx.x % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;                 // this wave carries a column block of the state
   const int col = 16 * (blockIdx.z * NV + wave) + l16;
@@ -221,7 +222,7 @@ int round_slices(int nseq, int H, int D, int max_slices) {
 
 template <typename TIn, int BC, int D, int NV>
 hipError_t launch_round(const FwdArgs& a, int nseq, int seq0, int slices, hipStream_t st) {
-  KDA_LAUNCH("kda_fwd_round", (k_fwd_round<TIn, BC, D, NV>), dim3(nseq, a.H, slices), dim3(NT),
+  KDA_LAUNCH("kda_fwd_round", (k_fwd_round<TIn, BC, D, NV>), dim3(nseq * a.H, 1, slices), dim3(NT),
              st, a, seq0);
   return hipGetLastError();
 }

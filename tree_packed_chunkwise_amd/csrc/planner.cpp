@@ -446,6 +446,17 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     P.max_seq_per_round = std::max(P.max_seq_per_round, P.round_seq_ptr[r + 1]);
     P.round_seq_ptr[r + 1] += P.round_seq_ptr[r];
   }
+  // launch order of each round's sequences: most chunks first (ties by id), so
+  // that when a round has more blocks than compute units the long chains start
+  // first; it changes no result (every block is independent)
+  P.seq_lpt.resize(P.seq_round.size());
+  for (int32_t r = 0; r < P.n_rounds; ++r) {
+    const int32_t b = P.round_seq_ptr[r], e = P.round_seq_ptr[r + 1];
+    for (int32_t si = b; si < e; ++si) P.seq_lpt[si] = si;
+    std::stable_sort(P.seq_lpt.begin() + b, P.seq_lpt.begin() + e, [&](int32_t x, int32_t y) {
+      return P.seq_chunk_ptr[x + 1] - P.seq_chunk_ptr[x] > P.seq_chunk_ptr[y + 1] - P.seq_chunk_ptr[y];
+    });
+  }
   P.n_packed = packed;
   P.n_out_rows = (mode != 1) ? n_rows : packed;
 
@@ -638,6 +649,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
         {&d.round_seq_ptr, &P.round_seq_ptr}, {&d.seq_chunk_ptr, &P.seq_chunk_ptr},
         {&d.seq_row_ptr, &P.seq_row_ptr},     {&d.seq_init_kind, &P.seq_init_kind},
         {&d.seq_init_idx, &P.seq_init_idx},   {&d.seq_leaf, &P.seq_leaf},
+        {&d.seq_lpt, &P.seq_lpt},
         {&d.chunk_seq, &P.chunk_seq},         {&d.chunk_row0, &P.chunk_row0},
         {&d.chunk_len, &P.chunk_len},         {&d.chunk_save, &P.chunk_save},
         {&d.chunk_nrep, &P.chunk_nrep},       {&d.chunk_rep0, &P.chunk_rep0},
