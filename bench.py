@@ -106,10 +106,10 @@ def measured_traffic(kernel, workload):
 
 
 def image_bytes(B, D, in_bytes):
-    """(image head, image as used) bytes of one chunk-head: the padded fp16
-    LDS image of a chunk step (layout in csrc/chunk.h); the head is
-    everything but V."""
-    head = 2 * (2 * B * (D + 8) + D * (B + 8) + 2 * B * (B + 8) + B * 24) + 4 * D + 8 * B
+    """(image head, image as used) bytes of one chunk-head: the fp16 LDS
+    image of a chunk step (layout in csrc/chunk.h); the head is everything
+    but V."""
+    head = 2 * (2 * B * D + D * B + 2 * B * B + B * 24) + 4 * D + 8 * B
     return head, head + in_bytes * B * D
 
 
@@ -231,7 +231,7 @@ def kernel_bytes(name, info, H, D, in_bytes=2):
         # image, the start state and end-state gradient of every chunk;
         # writes dq, dk, dv, dg, dbeta
         return (P * H * (2 * D * in_bytes + D * f + f + D * 2 + D * in_bytes + 4 * D * f + f)
-                + C * H * ((B * (B + 8) + B * 24) * 2 + B * D * in_bytes + 2 * st16))
+                + C * H * ((B * B + B * 24) * 2 + B * D * in_bytes + 2 * st16))
     if name == "kda_bwd_gather_dO":
         return Nrow * H * D * in_bytes + P * H * D * in_bytes
     return None

@@ -234,6 +234,69 @@ __device__ inline f16x8 lds_a_perm_tr(const _Float16* X, int pitch, int r0, int 
   return r;
 }
 
+// The chunk image's fp16 arrays are stored without padding; within a row of
+// W halves, the 8-byte piece q (halves 4q .. 4q + 3) of row r sits at piece
+// q ^ s(r), where s(r) takes the low four row bits with their two halves
+// swapped (masked to the row's piece count when a row has fewer than 16
+// pieces).  LDS serves 16 lanes of 8 bytes per cycle over 32 banks: the row
+// fragment reads (16 rows, one piece each) and the transposing reads (4 rows
+// x 4 consecutive pieces) then touch 16 distinct 8-byte bank pairs.
+template <int W>
+__device__ inline int swz_mask() {
+  return W / 4 < 16 ? W / 4 - 1 : 15;
+}
+__device__ inline int swz_rot(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+template <int W>
+__device__ inline int swz(int r, int c) {
+  return (((c >> 2) ^ (swz_rot(r) & swz_mask<W>())) << 2) | (c & 3);
+}
+// piece q0 (a compile-time multiple of 4 in the callers) XORed with the
+// lane's term t < 16: the high bits stay an immediate offset, only the low
+// four bits combine with t
+__device__ inline int swz_piece(int q0, int t) { return (q0 & ~15) | ((q0 & 15) ^ t); }
+// lds_a_perm on a swizzled [*][W] array; row = 16 J + l16 (J compile-time)
+template <int W>
+__device__ inline f16x8 lds_a_perm_sw(const _Float16* base, int row, int kb, int g,
+                                      bool half_only = false) {
+  const int t = (g ^ swz_rot(row)) & swz_mask<W>();   // kb / 4 is a multiple of 4: g fills bits 0-1
+  const _Float16* rp = base + row * W;
+  const f16x4 lo = *(const f16x4*)(rp + 4 * swz_piece(kb >> 2, t));
+  f16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  if (half_only) {
+    r[4] = r[5] = r[6] = r[7] = (_Float16)0.f;
+  } else {
+    const f16x4 hi = *(const f16x4*)(rp + 4 * swz_piece((kb + 16) >> 2, t));
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  }
+  return r;
+}
+// lds_tr4 / lds_a_perm_tr on a swizzled [*][W] array; r0 a multiple of 16,
+// c0 of 16 (both compile-time in the callers)
+template <int W>
+__device__ inline f16x4 lds_tr4_sw(const _Float16* X, int r0, int c0) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
+  const int rl = 4 * g + (s >> 2);                          // row within the 16-row block
+  const int t = ((s & 3) ^ swz_rot(rl)) & swz_mask<W>();
+  const _Float16* p = X + (r0 + rl) * W + 4 * swz_piece(c0 >> 2, t);
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(f16x4, v);
+}
+template <int W>
+__device__ inline f16x8 lds_a_perm_tr_sw(const _Float16* X, int r0, int c0, bool half_only = false) {
+  const f16x4 lo = lds_tr4_sw<W>(X, r0, c0);
+  f16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  if (half_only) {
+    r[4] = r[5] = r[6] = r[7] = (_Float16)0.f;
+  } else {
+    const f16x4 hi = lds_tr4_sw<W>(X, r0 + 16, c0);
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  }
+  return r;
+}
+
 template <int BC, int D>
 struct Geom {
   static constexpr int NB = BC / 16;               // 16-row blocks of a chunk
@@ -245,8 +308,7 @@ struct Geom {
   static constexpr int NRG = NT / DH;              // row groups of the element mapping
   static constexpr int RPT = BC / NRG;             // rows per thread in the element mapping
   static constexpr int PH = DH + 8;                // pitch (halves) of [row][DH] hi/lo arrays
-  static constexpr int PD = D + 8;                 // pitch (halves) of [row][D] fp16 arrays
-  static constexpr int PB = BC + 8;                // pitch (halves) of [*][BC] fp16 arrays
+  static constexpr int PB = BC + 8;                // pitch (halves) of the chunk pass's [*][BC] fp16 LDS arrays
   static constexpr int PF = BC + 1;                // pitch (floats) of [BC][BC] fp32 arrays
   static_assert(RPT >= 1 && BC % 16 == 0 && D % DH == 0, "geometry");
 };
@@ -256,11 +318,11 @@ struct Geom {
 // space for V, and an image with VT = uint16_t is a prefix of it.
 template <int BC, int D>
 struct FwdHead {   // everything but V: what a forward chunk step keeps in LDS
-  _Float16 Qt[BC][D + 8];
-  _Float16 Kn[BC][D + 8];
-  _Float16 KhT[D][BC + 8];
-  _Float16 L[BC][BC + 8];
-  _Float16 P[BC][BC + 8];
+  _Float16 Qt[BC][D];     // fp16 arrays: rows swizzled (swz), no padding
+  _Float16 Kn[BC][D];
+  _Float16 KhT[D][BC];
+  _Float16 L[BC][BC];
+  _Float16 P[BC][BC];
   _Float16 Td[BC][24];
   float gc[D];
   float beta[BC];

@@ -38,23 +38,22 @@ struct DevPlan {
 // (chunk, head) as the exact LDS image that a round kernel's state phase
 // reads: the round kernels copy it verbatim (16-byte vectors) and never touch
 // q, k, g or the exponentials on their sequential path.  fp16 arrays are
-// padded (pitch +8 halves) so that matrix-core fragment reads do not collide
-// in LDS banks; every array is a multiple of 16 bytes.
+// unpadded, their rows swizzled in 8-byte pieces (chunk.h swz) so that
+// matrix-core fragment reads do not collide in LDS banks; every array is a
+// multiple of 16 bytes.
 //
 // Forward image (BC rows, head dim D):
-//   Qt  [BC][D+8]   q e^Gam                 Kn  [BC][D+8]  -k e^Gam
-//   KhT [D][BC+8]   (k e^(Gam_C - Gam))^T   L   [BC][BC+8] A (strict lower)
-//   P   [BC][BC+8]  P (lower)               Td  [BC][24]   (I + diag(beta) A_II)^-1 per 16-row block
+//   Qt  [BC][D]     q e^Gam                 Kn  [BC][D]    -k e^Gam
+//   KhT [D][BC]     (k e^(Gam_C - Gam))^T   L   [BC][BC]   A (strict lower)
+//   P   [BC][BC]    P (lower)               Td  [BC][24]   (I + diag(beta) A_II)^-1 per 16-row block
 //   gc  [D] fp32    e^Gam_C                 beta [BC] fp32     orow [BC] int (-1: no output)
-//   V   [BC][D]     v in the input dtype (the region is sized for fp32)
-// Backward image:
-//   KhA [BC][D+8]   k e^(Gam_C - Gam)       QtT [D][BC+8]  scale (q e^Gam)^T
-//   KnT [D][BC+8]   -(k e^Gam)^T            PT  [BC][BC+8] scale P^T
-//   AT  [BC][BC+8]  A^T                     TdT [BC][24]   Td_I^T per block
-//   gc  [D] fp32, beta [BC] fp32
-// Rows past the chunk hold zeros (Gam, and so e^Gam, stays flat there).
+//   V   [BC][D]     v in the input dtype, in 16x16 accumulator-order tiles
+//                   (the region is sized for fp32)
+// The reverse pass reads the same image (its transposed operands through
+// transposing LDS reads).  Rows past the chunk hold zeros (Gam, and so e^Gam,
+// stays flat there).
 constexpr __host__ __device__ size_t fwd_image_head_bytes(int BC, int D) {
-  return (size_t)2 * (2 * (size_t)BC * (D + 8) + (size_t)D * (BC + 8) + 2 * (size_t)BC * (BC + 8) +
+  return (size_t)2 * (2 * (size_t)BC * D + (size_t)D * BC + 2 * (size_t)BC * BC +
                       (size_t)BC * 24) +
          4 * (size_t)D + 8 * (size_t)BC;
 }

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
       for (int J = 0; J < G::NB; ++J)
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) fa[J][ks] = lds_a_perm_tr(&s.KhT[0][0], G::PB, 32 * ks, 16 * J);
+        for (int ks = 0; ks < KD; ++ks) fa[J][ks] = lds_a_perm_tr_sw<BC>(&s.KhT[0][0], 32 * ks, 16 * J);
       __builtin_amdgcn_sched_barrier(0);
       f32x4 dd[G::NB];
 #pragma unroll
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
       for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr(&s.Qt[0][0], G::PD, 32 * ks, 16 * C, HALF);
+        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr_sw<D>(&s.Qt[0][0], 32 * ks, 16 * C, HALF);
       f32x4 gcv[G::NCB];
 #pragma unroll
       for (int C = 0; C < G::NCB; ++C)
@@ -167,10 +167,10 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       for (int J = 0; J < G::NB; ++J) {
 #pragma unroll
         for (int ks = 0; ks < KB; ++ks)
-          if (32 * ks + 31 >= 16 * J) fp[J][ks] = lds_a_perm_tr(&s.P[0][0], G::PB, 32 * ks, 16 * J, HALF);
+          if (32 * ks + 31 >= 16 * J) fp[J][ks] = lds_a_perm_tr_sw<BC>(&s.P[0][0], 32 * ks, 16 * J, HALF);
         ft[J] = lds_tr4(&s.Td[0][0], 24, 16 * J, 0);
 #pragma unroll
-        for (int I = 0; I < J; ++I) fl[I][J] = -lds_tr4(&s.L[0][0], G::PB, 16 * J, 16 * I);  // block (I, J) of A^T
+        for (int I = 0; I < J; ++I) fl[I][J] = -lds_tr4_sw<BC>(&s.L[0][0], 16 * J, 16 * I);  // block (I, J) of A^T
 #pragma unroll
         for (int r = 0; r < 4; ++r) bz[J][r] = s.beta[16 * J + 4 * g + r];
       }
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
       for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr(&s.Kn[0][0], G::PD, 32 * ks, 16 * C, HALF);
+        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr_sw<D>(&s.Kn[0][0], 32 * ks, 16 * C, HALF);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int C = 0; C < G::NCB; ++C)

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
 #pragma unroll
       for (int J = 0; J < G::NB; ++J)
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) fa[J][ks] = lds_a_perm(&s.Kn[0][0], G::PD, 16 * J + l16, 32 * ks, g);
+        for (int ks = 0; ks < KD; ++ks) fa[J][ks] = lds_a_perm_sw<D>(&s.Kn[0][0], 16 * J + l16, 32 * ks, g);
       __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
       for (int J = 0; J < G::NB; ++J)
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
 #pragma unroll
       for (int I = 0; I < G::NB; ++I)
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) fa[I][ks] = lds_a_perm(&s.Qt[0][0], G::PD, 16 * I + l16, 32 * ks, g);
+        for (int ks = 0; ks < KD; ++ks) fa[I][ks] = lds_a_perm_sw<D>(&s.Qt[0][0], 16 * I + l16, 32 * ks, g);
       __builtin_amdgcn_sched_barrier(0);
       f32x4 o[G::NB];
 #pragma unroll
@@ -137,7 +137,8 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       for (int I = 0; I < G::NB; ++I) {
         ft[I] = *(const f16x4*)&s.Td[16 * I + l16][4 * g];
 #pragma unroll
-        for (int J = 0; J < I; ++J) fl[I][J] = -*(const f16x4*)&s.L[16 * I + l16][16 * J + 4 * g];
+        for (int J = 0; J < I; ++J)   // columns 16 J + 4 g .. of the swizzled row
+          fl[I][J] = -*(const f16x4*)&s.L[16 * I + l16][4 * swz_piece(4 * J, (g ^ swz_rot(l16)) & swz_mask<BC>())];
       }
       f32x4 bz[G::NB];
 #pragma unroll
@@ -163,13 +164,13 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       for (int I = 0; I < G::NB; ++I)
 #pragma unroll
         for (int ks = 0; ks < KB; ++ks)
-          if (32 * ks <= 16 * I + 15) fp[I][ks] = lds_a_perm(&s.P[0][0], G::PB, 16 * I + l16, 32 * ks, g, HALF);
+          if (32 * ks <= 16 * I + 15) fp[I][ks] = lds_a_perm_sw<BC>(&s.P[0][0], 16 * I + l16, 32 * ks, g, HALF);
       // (K e^(Gam_C-Gam))^T fragments for the state update
       f16x8 fk[G::NCB][KB];
 #pragma unroll
       for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) fk[C][ks] = lds_a_perm(&s.KhT[0][0], G::PB, 16 * C + l16, 32 * ks, g, HALF);
+        for (int ks = 0; ks < KB; ++ks) fk[C][ks] = lds_a_perm_sw<BC>(&s.KhT[0][0], 16 * C + l16, 32 * ks, g, HALF);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int I = 0; I < G::NB; ++I) {

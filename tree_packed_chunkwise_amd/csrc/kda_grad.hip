@@ -204,12 +204,13 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   for (int C = 0; C < NCB; ++C) hraw[C] = *(const f16x4*)(hsrc + state_tile<D>(C, wv));
 #pragma unroll
   for (int J = 0; J < NB; ++J) vraw[J] = *(const in4_t<TIn>*)(&F->V[0][0] + state_tile<D>(J, wv));
-  constexpr int NAV = (BC * BC / 8 + NT - 1) / NT;
-  f16x8 av[NAV], tv;
+  constexpr int NAV = (BC * BC / 4 + NT - 1) / NT;   // 8-byte pieces of A (swizzled rows)
+  f16x4 av[NAV];
+  f16x8 tv;
 #pragma unroll
   for (int n = 0; n < NAV; ++n) {
-    const int e = tid + NT * n;
-    if (e < BC * BC / 8) av[n] = *(const f16x8*)&F->L[e / (BC / 8)][(e % (BC / 8)) * 8];
+    const int e = tid + NT * n, i = e / (BC / 4), j0 = (e % (BC / 4)) * 4;
+    if (e < BC * BC / 4) av[n] = *(const f16x4*)&F->L[i][swz<BC>(i, j0)];
   }
   if (tid < BC * 2) tv = *(const f16x8*)&F->Td[tid / 2][(tid % 2) * 8];
   const float tbeta = trow >= 0 ? a.beta[(size_t)trow * H + h] : 0.f;
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
 #pragma unroll
   for (int n = 0; n < NAV; ++n) {
     const int e = tid + NT * n;
-    if (e < BC * BC / 8) *(f16x8*)&s.u.p.A[e / (BC / 8)][(e % (BC / 8)) * 8] = av[n];
+    if (e < BC * BC / 4) *(f16x4*)&s.u.p.A[e / (BC / 4)][(e % (BC / 4)) * 4] = av[n];
   }
   if (tid < BC * 2) *(f16x8*)&s.u.p.Td[tid / 2][(tid % 2) * 8] = tv;
   __syncthreads();

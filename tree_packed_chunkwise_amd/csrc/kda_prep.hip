@@ -100,8 +100,8 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
       const int n = hf * G::RPT + t, i = r0 + t;
       const float e1 = __expf(er.gam[n]);
       const float e2 = __expf(gcl - er.gam[n]);
-      F->Qt[i][cc] = (_Float16)(er.q[n] * e1);
-      F->Kn[i][cc] = (_Float16)(-er.k[n] * e1);
+      F->Qt[i][swz<D>(i, cc)] = (_Float16)(er.q[n] * e1);
+      F->Kn[i][swz<D>(i, cc)] = (_Float16)(-er.k[n] * e1);
       kht[t] = (_Float16)(er.k[n] * e2);
     }
     TIn* Vt = &F->V[0][0];   // accumulator-order tiles
@@ -117,14 +117,17 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
 #pragma unroll
       for (int t = 0; t < G::RPT; ++t) Vt[tile_elem<D>(r0 + t, cc)] = to_in<TIn>(vv[hf * G::RPT + t]);
     }
-    if constexpr (G::RPT == 8) {
-      f16x8 x;
+    if constexpr (G::RPT % 4 == 0) {   // whole 8-byte pieces of the swizzled row
 #pragma unroll
-      for (int t = 0; t < 8; ++t) x[t] = kht[t];
-      *(f16x8*)&F->KhT[cc][r0] = x;
+      for (int t = 0; t < G::RPT; t += 4) {
+        f16x4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = kht[t + j];
+        *(f16x4*)&F->KhT[cc][swz<BC>(cc, r0 + t)] = x;
+      }
     } else {
 #pragma unroll
-      for (int t = 0; t < G::RPT; ++t) F->KhT[cc][r0 + t] = kht[t];
+      for (int t = 0; t < G::RPT; ++t) F->KhT[cc][swz<BC>(cc, r0 + t)] = kht[t];
     }
   }
   if (tid < D) F->gc[tid] = s.tb.gc[tid];
@@ -132,11 +135,11 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
     F->beta[tid] = s.tb.beta[tid];
     F->orow[tid] = s.tb.orow[tid];
   }
-  // A and P as they are (same pitch)
-  for (int e = tid; e < BC * BC / 8; e += NT) {
-    const int i = e / (BC / 8), j0 = (e % (BC / 8)) * 8;
-    *(f16x8*)&F->L[i][j0] = *(const f16x8*)&s.A[i][j0];
-    *(f16x8*)&F->P[i][j0] = *(const f16x8*)&s.P[i][j0];
+  // A and P in 8-byte pieces, into their swizzled places
+  for (int e = tid; e < BC * BC / 4; e += NT) {
+    const int i = e / (BC / 4), j0 = (e % (BC / 4)) * 4;
+    *(f16x4*)&F->L[i][swz<BC>(i, j0)] = *(const f16x4*)&s.A[i][j0];
+    *(f16x4*)&F->P[i][swz<BC>(i, j0)] = *(const f16x4*)&s.P[i][j0];
   }
   __syncthreads();  // beta of every row
   // diagonal inverses: one lane per (block, column), forward substitution
