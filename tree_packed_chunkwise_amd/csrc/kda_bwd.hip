@@ -127,38 +127,48 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       f16x8 dhb[KD];
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) dhb[ks] = acc_pair(dh[2 * ks], dh[2 * ks + 1]);
-      // Every phase first issues all of its LDS fragment reads, then its
-      // MFMAs, so that the reads are in flight together.
+      // Every phase first issues its LDS fragment reads, then its MFMAs, so
+      // that the reads are in flight together; the three largest phases run
+      // as two batches of eight fragments each, which keeps the kernel
+      // within its registers.
       // ddelta = scale P^T dO + (K e^(Gam_C-Gam)) dh
-      f16x8 fa[G::NCB][KB > KD ? KB : KD];
-#pragma unroll
-      for (int J = 0; J < G::NB; ++J)
-#pragma unroll
-        for (int ks = 0; ks < KD; ++ks) fa[J][ks] = lds_a_perm_tr_sw<BC>(&s.KhT[0][0], 32 * ks, 16 * J);
-      __builtin_amdgcn_sched_barrier(0);
+      constexpr int HB = G::NB > 1 ? G::NB / 2 : 1;   // row blocks per batch
+      constexpr int HC = G::NCB / 2;                  // column blocks per batch
       f32x4 dd[G::NB];
 #pragma unroll
-      for (int J = 0; J < G::NB; ++J) {
-        dd[J] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int J0 = 0; J0 < G::NB; J0 += HB) {
+        f16x8 fb[HB][KD];
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) dd[J] = mfma16(fa[J][ks], dhb[ks], dd[J]);
+        for (int j = 0; j < HB; ++j)
+#pragma unroll
+          for (int ks = 0; ks < KD; ++ks) fb[j][ks] = lds_a_perm_tr_sw<BC>(&s.KhT[0][0], 32 * ks, 16 * (J0 + j));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+          dd[J0 + j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KD; ++ks) dd[J0 + j] = mfma16(fb[j][ks], dhb[ks], dd[J0 + j]);
+        }
       }
       // dh <- diag(e^Gam_C) dh + scale (Q e^Gam)^T dO (dhb holds the old dh)
 #pragma unroll
-      for (int C = 0; C < G::NCB; ++C)
+      for (int C0 = 0; C0 < G::NCB; C0 += HC) {
+        f16x8 fb[HC][KB];
+        f32x4 gcv[HC];
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr_sw<D>(&s.Qt[0][0], 32 * ks, 16 * C, HALF);
-      f32x4 gcv[G::NCB];
+        for (int c = 0; c < HC; ++c) {
 #pragma unroll
-      for (int C = 0; C < G::NCB; ++C)
+          for (int ks = 0; ks < KB; ++ks) fb[c][ks] = lds_a_perm_tr_sw<D>(&s.Qt[0][0], 32 * ks, 16 * (C0 + c), HALF);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gcv[C][r] = s.gc[16 * C + 4 * g + r];
-      __builtin_amdgcn_sched_barrier(0);
+          for (int r = 0; r < 4; ++r) gcv[c][r] = s.gc[16 * (C0 + c) + 4 * g + r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int C = 0; C < G::NCB; ++C) {
-        dh[C] *= gcv[C];
+        for (int c = 0; c < HC; ++c) {
+          dh[C0 + c] *= gcv[c];
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) dh[C] = mfma16(fa[C][ks], dob[ks], dh[C]);
+          for (int ks = 0; ks < KB; ++ks) dh[C0 + c] = mfma16(fb[c][ks], dob[ks], dh[C0 + c]);
+        }
       }
       f16x8 fp[G::NB][KB];
       f16x4 fl[G::NB][G::NB], ft[G::NB];
@@ -198,14 +208,18 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       for (int ks = 0; ks < KB; ++ks) wb[ks] = HALF ? acc_half(w[0]) : acc_pair(w[2 * ks], w[2 * ks + 1]);
       // dh -= (K e^Gam)^T diag(beta) dy
 #pragma unroll
-      for (int C = 0; C < G::NCB; ++C)
+      for (int C0 = 0; C0 < G::NCB; C0 += HC) {
+        f16x8 fb[HC][KB];
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) fa[C][ks] = lds_a_perm_tr_sw<D>(&s.Kn[0][0], 32 * ks, 16 * C, HALF);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < HC; ++c)
 #pragma unroll
-      for (int C = 0; C < G::NCB; ++C)
+          for (int ks = 0; ks < KB; ++ks) fb[c][ks] = lds_a_perm_tr_sw<D>(&s.Kn[0][0], 32 * ks, 16 * (C0 + c), HALF);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KB; ++ks) dh[C] = mfma16(fa[C][ks], wb[ks], dh[C]);
+        for (int c = 0; c < HC; ++c)
+#pragma unroll
+          for (int ks = 0; ks < KB; ++ks) dh[C0 + c] = mfma16(fb[c][ks], wb[ks], dh[C0 + c]);
+      }
     }
   }
   if (sw) {
