@@ -75,7 +75,8 @@ struct GradGeom {
   static constexpr int NG = NW / NB;             // waves per row block
   static constexpr int NTW = (NCB / NG) > 0 ? NCB / NG : 1;  // output tiles per wave
   static constexpr int PD = D + 8;               // fp16 [*][D] pitch
-  static constexpr int PB = BC + 8;              // 16-bit [*][BC] pitch
+  static constexpr int PB = BC + 12;             // 16-bit [*][BC] pitch: 8-byte fragment reads by 16
+                                                 // rows hit distinct banks (rows 8-byte aligned)
   static constexpr int PG = BC + 1;              // fp32 [64][BC] pitch
   static constexpr int NLOW = NB * (NB + 1) / 2; // lower block pairs
   static constexpr int DH = 64;
@@ -83,6 +84,14 @@ struct GradGeom {
   static constexpr int RPT = BC / NRG;           // rows per thread in the element mapping
   static_assert(RPT >= 1 && NCB % 4 == 0, "geometry");
 };
+
+// eight bf16 values as two 8-byte stores (rows of the [*][PB] arrays are
+// 8-byte aligned)
+__device__ inline void put8(__bf16* p, const bf16x8& v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  *(bf16x4*)p = (bf16x4){v[0], v[1], v[2], v[3]};
+  *(bf16x4*)(p + 4) = (bf16x4){v[4], v[5], v[6], v[7]};
+}
 
 // lower block pair (I, J), J <= I -> I (I + 1) / 2 + J
 __device__ inline int low_index(int I, int J) { return I * (I + 1) / 2 + J; }
@@ -523,9 +532,9 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
           kh8[t] = x; kl8[t] = y;
           s.u.d.gam[c0][i] = gm[n];
         }
-        *(bf16x8*)&s.u.d.rh[c0][r0] = rh8; *(bf16x8*)&s.u.d.rl[c0][r0] = rl8;
-        *(bf16x8*)&s.u.d.qh[c0][r0] = qh8; *(bf16x8*)&s.u.d.ql[c0][r0] = ql8;
-        *(bf16x8*)&s.u.d.kh[c0][r0] = kh8; *(bf16x8*)&s.u.d.kl[c0][r0] = kl8;
+        put8(&s.u.d.rh[c0][r0], rh8); put8(&s.u.d.rl[c0][r0], rl8);
+        put8(&s.u.d.qh[c0][r0], qh8); put8(&s.u.d.ql[c0][r0], ql8);
+        put8(&s.u.d.kh[c0][r0], kh8); put8(&s.u.d.kl[c0][r0], kl8);
         if constexpr (RAWQK) {
           bf16x8 q8, k8;
 #pragma unroll
@@ -533,8 +542,8 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
             q8[t] = (__bf16)qq[hf * RPT + t];
             k8[t] = (__bf16)kk[hf * RPT + t];
           }
-          *(bf16x8*)&s.u.d.qraw[c0][r0] = q8;
-          *(bf16x8*)&s.u.d.kraw[c0][r0] = k8;
+          put8(&s.u.d.qraw[c0][r0], q8);
+          put8(&s.u.d.kraw[c0][r0], k8);
         }
       } else {
 #pragma unroll
