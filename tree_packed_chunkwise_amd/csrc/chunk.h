@@ -524,8 +524,9 @@ __device__ inline void elems_store(int hf, const ElemRegs<BC, D>& er, APOps<BC, 
 __device__ inline bf16x8 ld_bf8(const __bf16* p) { return *(const bf16x8*)p; }
 
 // Accumulates one 64-channel pass of A_IJ and P_IJ (block pair (I, J),
-// J <= I) on the calling wave; factors taken around gref_J:
-//   A_IJ += (Lk_I e^(gref_I - gref_J)) Rk_J^T,  P_IJ += (Lq_I e^(...)) Rk_J^T
+// J <= I) on the calling wave; factors taken around gref_J, the channel
+// factor between the two references applied once, to the shared operand:
+//   A_IJ += Lk_I (Rk_J e^(gref_I - gref_J))^T,  P_IJ += Lq_I (Rk_J e^(...))^T
 template <int BC, int D>
 __device__ inline void pair_pass(const APOps<BC, D>& ap, const ChunkTables<BC, D>& tb, int hf,
                                  int I, int J, f32x4& accA, f32x4& accP) {
@@ -538,18 +539,15 @@ __device__ inline void pair_pass(const APOps<BC, D>& ap, const ChunkTables<BC, D
 #pragma unroll
   for (int kb = 0; kb < Geom<BC, D>::DH; kb += 32) {
     const int c0 = kb + g8;
-    bf16x8 kh = ld_bf8(&ap.kh[ri][c0]), kl = ld_bf8(&ap.kl[ri][c0]);
-    bf16x8 qh = ld_bf8(&ap.qh[ri][c0]), ql = ld_bf8(&ap.ql[ri][c0]);
-    const bf16x8 rh = ld_bf8(&ap.rh[rj][c0]), rl = ld_bf8(&ap.rl[rj][c0]);
+    const bf16x8 kh = ld_bf8(&ap.kh[ri][c0]), kl = ld_bf8(&ap.kl[ri][c0]);
+    const bf16x8 qh = ld_bf8(&ap.qh[ri][c0]), ql = ld_bf8(&ap.ql[ri][c0]);
+    bf16x8 rh = ld_bf8(&ap.rh[rj][c0]), rl = ld_bf8(&ap.rl[rj][c0]);
     if (off) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float f = df[c0 + e];
         __bf16 h2, l2;
-        split_bf16(((float)kh[e] + (float)kl[e]) * f, h2, l2);
-        kh[e] = h2; kl[e] = l2;
-        split_bf16(((float)qh[e] + (float)ql[e]) * f, h2, l2);
-        qh[e] = h2; ql[e] = l2;
+        split_bf16(((float)rh[e] + (float)rl[e]) * df[c0 + e], h2, l2);
+        rh[e] = h2; rl[e] = l2;
       }
     }
     accA = mfmab(kh, rh, accA);

@@ -94,14 +94,17 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
   for (int hf = 0; hf < G::NHALF; ++hf) {
     const int cc = c0 + G::DH * hf;
     const float gcl = s.tb.gcl[cc];
+    _Float16* Fq = &F->Qt[0][0];
+    _Float16* Fk = &F->Kn[0][0];
     _Float16 kht[G::RPT];
 #pragma unroll
     for (int t = 0; t < G::RPT; ++t) {
       const int n = hf * G::RPT + t, i = r0 + t;
       const float e1 = __expf(er.gam[n]);
       const float e2 = __expf(gcl - er.gam[n]);
-      F->Qt[i][swz<D>(i, cc)] = (_Float16)(er.q[n] * e1);
-      F->Kn[i][swz<D>(i, cc)] = (_Float16)(-er.k[n] * e1);
+      const unsigned o = (unsigned)(i * D + swz<D>(i, cc));   // uniform base + 32-bit offset
+      Fq[o] = (_Float16)(er.q[n] * e1);
+      Fk[o] = (_Float16)(-er.k[n] * e1);
       kht[t] = (_Float16)(er.k[n] * e2);
     }
     TIn* Vt = &F->V[0][0];   // accumulator-order tiles
@@ -151,9 +154,10 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
       const f16x8 a0 = *(const f16x8*)&s.A[b0 + i][b0];
       const f16x8 a1 = *(const f16x8*)&s.A[b0 + i][b0 + 8];
       const float bi = s.tb.beta[b0 + i];
-      float acc = (i == j) ? 1.f : 0.f;
+      float sum = 0.f;   // sum_{m<i} A_im x_m (fp16 A enters the fma directly), then beta_i once
 #pragma unroll
-      for (int m = 0; m < i; ++m) acc -= bi * (float)(m < 8 ? a0[m] : a1[m - 8]) * x[m];
+      for (int m = 0; m < i; ++m) sum = __builtin_fmaf((float)(m < 8 ? a0[m] : a1[m - 8]), x[m], sum);
+      const float acc = ((i == j) ? 1.f : 0.f) - bi * sum;
       x[i] = (i >= j) ? acc : 0.f;
     }
 #pragma unroll
