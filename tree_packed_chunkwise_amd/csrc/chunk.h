@@ -390,7 +390,6 @@ template <int BC, int D>
 struct ElemRegs {
   static constexpr int N = Geom<BC, D>::RPT * Geom<BC, D>::NHALF;
   float k[N], q[N], gam[N];   // raw inputs, then Gam
-  float lk[N], lq[N], rk[N];  // factored operands
 };
 
 // Issues the loads of g, then k, then q for the thread's elements (rows[t] =
@@ -430,8 +429,8 @@ __device__ inline void elems_load(const TIn* q, const TIn* k, const float* g, in
     }
 }
 
-// Gam (cumulative log-decay over the chunk), the block tables and the
-// factored operands in registers.  Ends synchronised.
+// Gam (cumulative log-decay over the chunk) and the block tables.  Ends
+// synchronised.
 template <int BC, int D>
 __device__ inline void elems_gamma(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) {
   using G = Geom<BC, D>;
@@ -484,26 +483,14 @@ __device__ inline void elems_gamma(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) 
       for (int J = 0; J < I; ++J)
         tb.dfac[off_index(I, J)][tid] = __expf(tb.gref[I][tid] - tb.gref[J][tid]);
   }
-#pragma unroll
-  for (int hf = 0; hf < G::NHALF; ++hf) {
-    const int c = c0 + G::DH * hf;
-#pragma unroll
-    for (int t = 0; t < G::RPT; ++t) {
-      const int n = hf * G::RPT + t;
-      const float ref = tb.gref[(r0 + t) >> 4][c];
-      const float f = __expf(er.gam[n] - ref);
-      const float fi = __expf(ref - er.gam[n]);
-      er.lk[n] = er.k[n] * f;
-      er.lq[n] = er.q[n] * f;
-      er.rk[n] = er.k[n] * fi;
-    }
-  }
   __syncthreads();
 }
 
-// Writes the hi/lo operands of pass `hf` to LDS.  No synchronisation.
+// Forms the factored operands of pass `hf` (Lk, Lq, Rk around the row's block
+// reference) and writes their hi/lo parts to LDS.  No synchronisation.
 template <int BC, int D>
-__device__ inline void elems_store(int hf, const ElemRegs<BC, D>& er, APOps<BC, D>& ap) {
+__device__ inline void elems_store(int hf, const ElemRegs<BC, D>& er, const ChunkTables<BC, D>& tb,
+                                   APOps<BC, D>& ap) {
   using G = Geom<BC, D>;
   const int tid = threadIdx.x;
   const int c0 = tid % G::DH;
@@ -511,12 +498,15 @@ __device__ inline void elems_store(int hf, const ElemRegs<BC, D>& er, APOps<BC, 
 #pragma unroll
   for (int t = 0; t < G::RPT; ++t) {
     const int n = hf * G::RPT + t, i = r0 + t;
+    const float ref = tb.gref[i >> 4][c0 + G::DH * hf];
+    const float f = __expf(er.gam[n] - ref);
+    const float fi = __expf(ref - er.gam[n]);
     __bf16 hh, ll;
-    split_bf16(er.lk[n], hh, ll);
+    split_bf16(er.k[n] * f, hh, ll);
     ap.kh[i][c0] = hh; ap.kl[i][c0] = ll;
-    split_bf16(er.lq[n], hh, ll);
+    split_bf16(er.q[n] * f, hh, ll);
     ap.qh[i][c0] = hh; ap.ql[i][c0] = ll;
-    split_bf16(er.rk[n], hh, ll);
+    split_bf16(er.k[n] * fi, hh, ll);
     ap.rh[i][c0] = hh; ap.rl[i][c0] = ll;
   }
 }
@@ -576,7 +566,7 @@ __device__ inline void chunk_AP(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er, APO
 #pragma unroll
   for (int hf = 0; hf < G::NHALF; ++hf) {
     if (hf > 0) __syncthreads();
-    elems_store<BC, D>(hf, er, ap);
+    elems_store<BC, D>(hf, er, tb, ap);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
@@ -588,6 +578,7 @@ __device__ inline void chunk_AP(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er, APO
       }
     }
   }
+  __syncthreads();   // the outputs may take the operands' place
 #pragma unroll
   for (int m = 0; m < MAXP; ++m) {
     const int p = wave + NW * m;

@@ -25,10 +25,15 @@ namespace kda {
 template <int BC, int D>
 struct PrepSmem {
   using G = Geom<BC, D>;
-  APOps<BC, D> ap;
-  _Float16 A[BC][G::PB];
-  _Float16 P[BC][G::PB];
+  union {                     // the products' outputs replace their staged operands
+    APOps<BC, D> ap;
+    struct {
+      _Float16 A[BC][G::PB];
+      _Float16 P[BC][G::PB];
+    } o;
+  } u;
   ChunkTables<BC, D> tb;
+  int irow[BC];   // input row of each chunk row (-1 past the chunk)
 };
 
 template <typename TIn>
@@ -63,13 +68,20 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
     trow = a.plan.row_index[row0 + tid];
     torow = tid >= nrep ? a.plan.out_row[row0 + tid] : -1;
   }
-  // beta, then g, k, q (the A/P phase), then v (needed only for the image's
-  // V at the end); the row table goes to LDS after the A/P phase, so that no
-  // wait for the later loads comes before it
+  // beta, then g, k, q (the A/P phase); the row table goes to LDS after the
+  // A/P phase, so that no wait for the later loads comes before it
   const float bx = a.beta[(size_t)(trow < 0 ? 0 : trow) * H + h];
   const float tbeta = trow >= 0 ? bx : 0.f;
   ElemRegs<BC, D> er;
   elems_load<TIn, BC, D>((const TIn*)a.q, (const TIn*)a.k, a.g, H, h, rows, er);
+  if (tid < BC) s.irow[tid] = trow;
+  chunk_AP<BC, D>(s.tb, er, s.u.ap, &s.u.o.A[0][0], G::PB, &s.u.o.P[0][0], G::PB);
+  // v, needed only for the image's V, after the A/P phase (whose final
+  // barrier completes the row table): its registers stay free during that
+  // phase, and reading the rows back keeps their addresses out of it, so
+  // that two blocks fit on a compute unit
+#pragma unroll
+  for (int t = 0; t < G::RPT; ++t) rows[t] = s.irow[r0 + t];
   float vv[NE];
   {
     const TIn* v = (const TIn*)a.v;
@@ -82,7 +94,6 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
         vv[hf * G::RPT + t] = r >= 0 ? x : 0.f;
       }
   }
-  chunk_AP<BC, D>(s.tb, er, s.ap, &s.A[0][0], G::PB, &s.P[0][0], G::PB);
   if (tid < BC) {
     s.tb.orow[tid] = torow;
     s.tb.beta[tid] = tbeta;
@@ -141,8 +152,8 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
   // A and P in 8-byte pieces, into their swizzled places
   for (int e = tid; e < BC * BC / 4; e += NT) {
     const int i = e / (BC / 4), j0 = (e % (BC / 4)) * 4;
-    *(f16x4*)&F->L[i][swz<BC>(i, j0)] = *(const f16x4*)&s.A[i][j0];
-    *(f16x4*)&F->P[i][swz<BC>(i, j0)] = *(const f16x4*)&s.P[i][j0];
+    *(f16x4*)&F->L[i][swz<BC>(i, j0)] = *(const f16x4*)&s.u.o.A[i][j0];
+    *(f16x4*)&F->P[i][swz<BC>(i, j0)] = *(const f16x4*)&s.u.o.P[i][j0];
   }
   __syncthreads();  // beta of every row
   // diagonal inverses: one lane per (block, column), forward substitution
@@ -151,8 +162,8 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const f16x8 a0 = *(const f16x8*)&s.A[b0 + i][b0];
-      const f16x8 a1 = *(const f16x8*)&s.A[b0 + i][b0 + 8];
+      const f16x8 a0 = *(const f16x8*)&s.u.o.A[b0 + i][b0];
+      const f16x8 a1 = *(const f16x8*)&s.u.o.A[b0 + i][b0 + 8];
       const float bi = s.tb.beta[b0 + i];
       float sum = 0.f;   // sum_{m<i} A_im x_m (fp16 A enters the fma directly), then beta_i once
 #pragma unroll
