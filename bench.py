@@ -173,7 +173,10 @@ def measure_window(w, dev, steps, ms_single):
     import torch
     from tree_packed_chunkwise_amd import synth
     from tree_packed_chunkwise_amd.window import SharingWindow
-    win = SharingWindow(w.tree.parent, w.tree.seg_len, 1, 4, chunk=w.chunk)
+    try:
+        win = SharingWindow(w.tree.parent, w.tree.seg_len, 1, 4, chunk=w.chunk)
+    except ValueError as exc:   # e.g. a trunk tree with fewer than 4 subtrees below depth 1
+        return {"skipped": str(exc)}
     N, H, D = win.n_rows, w.H, w.dk
     inp = synth.make_kda_inputs_device(9100, N, H, D, D, dev, w.bf16)
     gen = torch.Generator(device=dev)
@@ -666,16 +669,36 @@ def main():
         del mfo, mbo, dOm
         return mms, mi
 
+    def fits(mode):
+        """Whether the plan mode's outputs and workspaces fit in free device
+        memory (the trajectory-expanded run of the step-wise tree does not:
+        ~4.8 M rows)."""
+        mp = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk, mode)
+        mi = mp.info
+        rows = mi["n_out_rows"] * H * D
+        need = (mp.saved_bytes(H, D) + mp.fwd_ws_bytes(H, D) + mp.bwd_ws_bytes(H, D)
+                + rows * (5 * 4 + 2))   # o, dq, dk, dv, dg (fp32) and dO (bf16)
+        free, _ = torch.cuda.mem_get_info(dev)
+        return need < 0.9 * free, mi
+
     expanded, modes = None, None
     if a.expanded_steps > 0:
-        ems, ei = time_mode(B.EXPANDED, a.expanded_steps, 7)
-        expanded = {"ms_per_step": round(ems, 3), "speedup": round(ems / ms, 3),
-                    "expanded_rows": int(ei["n_packed"])}
+        ok_e, ei = fits(B.EXPANDED)
+        if ok_e:
+            ems, ei = time_mode(B.EXPANDED, a.expanded_steps, 7)
+            expanded = {"ms_per_step": round(ems, 3), "speedup": round(ems / ms, 3),
+                        "expanded_rows": int(ei["n_packed"])}
+        else:
+            expanded = {"skipped": "does not fit in device memory in one call",
+                        "expanded_rows": int(ei["n_packed"])}
         modes = {"mincall": {"ms_per_step": round(ms, 3), "rounds": int(info["n_rounds"]),
                              "sequences": int(info["n_seq"]), "chunks": int(info["n_chunks"]),
                              "replay_rows": int(info["R"])}}
         for name, mode in (("noreplay", B.NOREPLAY), ("nodewise", B.NODEWISE),
                            ("mincall_short", B.MINCALL_SHORT)):
+            if not fits(mode)[0]:
+                modes[name] = {"skipped": "does not fit in device memory in one call"}
+                continue
             mms, mi = time_mode(mode, a.expanded_steps, 9)
             modes[name] = {"ms_per_step": round(mms, 3), "rounds": int(mi["n_rounds"]),
                            "sequences": int(mi["n_seq"]), "chunks": int(mi["n_chunks"]),
