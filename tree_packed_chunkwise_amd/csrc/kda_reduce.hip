@@ -11,16 +11,18 @@
 
 namespace kda {
 
-constexpr int BT = 256;  // threads per block of the reductions
+constexpr int BT = 256;  // threads per block of the dh0 reduction
 
-// replayed-row gradients added into their compact rows (fixed order)
+// replayed-row gradients added into their compact rows (fixed order); one
+// thread per channel
 template <int D>
-__global__ __launch_bounds__(BT) void k_reduce_rep(BwdArgs a) {
+__global__ __launch_bounds__(D) void k_reduce_rep(BwdArgs a) {
   const int e = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int H = a.H;
   const int row = a.plan.rep_row[e];
   const int p0 = a.plan.rep_ptr[e], p1 = a.plan.rep_ptr[e + 1];
-  for (int ch = tid; ch < D; ch += BT) {
+  {
+    const int ch = tid;
     const size_t o = ((size_t)row * H + h) * D + ch;
     float sq = a.dq[o], sk = a.dk[o], sg = a.dg[o], sv = a.dv[o];
     for (int p = p0; p < p1; ++p) {
@@ -42,29 +44,36 @@ __global__ __launch_bounds__(BT) void k_reduce_rep(BwdArgs a) {
   }
 }
 
-// dh0 of every root: sum of the start gradients of its sequences (fixed order)
+// dh0 of every root: sum of the start gradients of its sequences (fixed
+// order); one float4 of one (root, head) state per thread
 template <int D>
 __global__ __launch_bounds__(BT) void k_reduce_dh0(BwdArgs a) {
-  const int rt = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int H = a.H;
+  constexpr int DD4 = D * D / 4;
+  const int rh = blockIdx.y, H = a.H, rt = rh / H, h = rh % H;
+  const int e4 = blockIdx.x * BT + threadIdx.x;   // grid.x * BT == DD4
   const int p0 = a.plan.root_seq_ptr[rt], p1 = a.plan.root_seq_ptr[rt + 1];
-  const size_t DD = (size_t)D * D;
-  for (int e = tid; e < D * D; e += BT) {
-    float acc = 0.f;
-    for (int p = p0; p < p1; ++p) acc += a.slot[((size_t)a.plan.root_seq[p] * H + h) * DD + e];
-    a.dh0[((size_t)rt * H + h) * DD + e] = acc;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = p0; p < p1; ++p) {
+    const float4 x = ((const float4*)(a.slot + ((size_t)a.plan.root_seq[p] * H + h) * (4 * DD4)))[e4];
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
   }
+  ((float4*)(a.dh0 + ((size_t)rt * H + h) * (4 * DD4)))[e4] = acc;
 }
 
 template <int D>
 hipError_t launch_reduce_t(const BwdArgs& a, int n_rep_rows, int n_root, hipStream_t st) {
   if (n_rep_rows > 0) {
-    KDA_LAUNCH("kda_bwd_reduce_replay", (k_reduce_rep<D>), dim3(n_rep_rows, a.H), dim3(BT), st, a);
+    KDA_LAUNCH("kda_bwd_reduce_replay", (k_reduce_rep<D>), dim3(n_rep_rows, a.H), dim3(D), st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n_root > 0) {
-    KDA_LAUNCH("kda_bwd_reduce_dh0", (k_reduce_dh0<D>), dim3(n_root, a.H), dim3(BT), st, a);
+    static_assert((D * D / 4) % BT == 0, "whole blocks");
+    KDA_LAUNCH("kda_bwd_reduce_dh0", (k_reduce_dh0<D>), dim3(D * D / 4 / BT, n_root * a.H), dim3(BT),
+               st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
