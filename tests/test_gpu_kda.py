@@ -46,7 +46,7 @@ def test_tiny_weak_gates_handoff(h0_mode, dhl):
 
 @pytest.mark.parametrize("seed", range(3))
 @pytest.mark.parametrize("D,chunk,bf16", [(64, 16, False), (128, 64, True), (64, 64, True),
-                                          (128, 16, False)])
+                                          (128, 16, False), (128, 64, False), (64, 16, True)])
 def test_random_forests(seed, D, chunk, bf16):
     rng = np.random.Generator(np.random.PCG64(seed))
     spec = synth.tree_random(rng, 9, 1, 3 * chunk, n_roots=1 + seed % 2)
