@@ -16,7 +16,7 @@
 // kernels' sequential chain only copies an image and runs the state phase.
 // The state-dependent passes solve (I + diag(beta) A) delta = diag(beta) Z
 // (and its transpose) block by block with Td; the full inverse is never
-// formed.
+// formed.  Two blocks share a compute unit (63 KB of LDS, 128 registers).
 #include "chunk.h"
 #include "timing.h"
 
@@ -57,8 +57,9 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
   const int row0 = a.plan.chunk_row0[c];
   const int len = a.plan.chunk_len[c];
   const int nrep = a.plan.chunk_nrep[c];
-  // every global load is issued first; each thread reads the row indices of
-  // its own element rows from the plan (no round trip through a shared table)
+  // the A/P phase's global loads are issued first (v follows that phase);
+  // each thread reads the row indices of its own element rows from the plan
+  // (no round trip through a shared table)
   const int c0 = tid % G::DH, r0 = (tid / G::DH) * G::RPT;
   int rows[G::RPT];
 #pragma unroll
