@@ -247,7 +247,7 @@ size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int3
  *   h0              [n_root,H,dk,dv] fp32 initial states, or NULL for zeros
  *   o               [n_out_rows,H,dv] fp32 outputs (replay rows write nothing)
  *   h_leaf          [n_leaf,H,dk,dv] fp32 final state per leaf (leaves ascending)
- *   saved           kda_saved_bytes(...) bytes, kept for kda_tree_bwd
+ *   saved, saved_bytes  at least kda_saved_bytes(...) bytes, kept for kda_tree_bwd
  *   ws, ws_bytes    scratch of kda_fwd_workspace_bytes(...) bytes
  * Supported gate range: the chunk math factors per-pair decays through the
  * first row of each 16-row block; sum(|g|) over any 15 consecutive rows of a
@@ -257,7 +257,7 @@ size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int3
 int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
                  int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
                  const float* g, const float* beta, const float* h0, float* o, float* h_leaf,
-                 void* saved, void* ws, size_t ws_bytes, void* stream);
+                 void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * kda_set_overlap -- process-wide launch policy of kda_tree_fwd / kda_tree_bwd.
@@ -282,7 +282,8 @@ int kda_set_overlap(int32_t enable);
  * fixed order.
  *
  *   q..h0      the forward's inputs (same pointers or equal contents)
- *   saved      as written by kda_tree_fwd with the same inputs
+ *   saved, saved_bytes  as written by kda_tree_fwd with the same inputs (size
+ *              at least kda_saved_bytes(...))
  *   dO         [n_out_rows,H,dv] output gradients, dtype in_dtype
  *   dh_leaf    [n_leaf,H,dk,dv] fp32 gradient of each leaf state, or NULL for zeros
  *   dq, dk     [n_out_rows,H,dk] fp32;  dv [n_out_rows,H,dv] fp32
@@ -295,8 +296,8 @@ int kda_set_overlap(int32_t enable);
 int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
                  int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
                  const float* g, const float* beta, const float* h0, const void* saved,
-                 const void* dO, const float* dh_leaf, float* dq, float* dk_, float* dv_,
-                 float* dg, float* dbeta, float* dh0, float* dh_boundary, void* ws,
+                 size_t saved_bytes, const void* dO, const float* dh_leaf, float* dq, float* dk_,
+                 float* dv_, float* dg, float* dbeta, float* dh0, float* dh_boundary, void* ws,
                  size_t ws_bytes, void* stream);
 
 /*

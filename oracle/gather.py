@@ -10,9 +10,15 @@ vocabulary-sized logits).
     logp[pos] = z[row(pos), tgt(pos)] - logsumexp(z[row(pos), :])
     dz[row, :] = sum_{pos -> row} dlogp[pos] * (onehot(tgt(pos)) - softmax(z[row]))
 
+Masked entries (the pages leave them open; reading taken): a logit of -inf
+has probability zero.  A row whose every entry is -inf has lse = -inf, its
+positions get logp = -inf, and its softmax is taken as all zeros, so only the
+target columns of its gradient are nonzero.
+
 Pins (tests/test_oracle_gather.py): uniform logits give -ln V exactly;
 agreement with scipy.special.log_softmax applied to expanded rows; the
-backward agrees with central finite differences.
+backward agrees with central finite differences; a row with masked entries
+equals log_softmax over its unmasked entries alone.
 """
 from __future__ import annotations
 
@@ -28,7 +34,9 @@ def row_lse(z):
     for r0 in range(0, n, BLOCK):
         blk = np.asarray(z[r0:r0 + BLOCK], dtype=np.float64)
         m = blk.max(axis=1)
-        out[r0:r0 + BLOCK] = m + np.log(np.exp(blk - m[:, None]).sum(axis=1))
+        m = np.where(np.isfinite(m), m, 0.0)   # an all -inf row sums to 0: lse = -inf
+        with np.errstate(divide="ignore"):
+            out[r0:r0 + BLOCK] = m + np.log(np.exp(blk - m[:, None]).sum(axis=1))
     return out
 
 
@@ -38,7 +46,10 @@ def gather_fwd(z, pos_row, pos_tgt):
     pos_row = np.asarray(pos_row, dtype=np.int64)
     pos_tgt = np.asarray(pos_tgt, dtype=np.int64)
     zt = np.asarray(z[pos_row, pos_tgt], dtype=np.float64)
-    return zt - lse[pos_row], lse
+    lr = lse[pos_row]
+    with np.errstate(invalid="ignore"):
+        logp = np.where(lr == -np.inf, -np.inf, zt - lr)
+    return logp, lse
 
 
 def gather_bwd(z, pos_row, pos_tgt, dlogp, rows=None):
@@ -52,8 +63,10 @@ def gather_bwd(z, pos_row, pos_tgt, dlogp, rows=None):
     np.add.at(wsum, pos_row, dlogp)
     zr = np.asarray(z[rows], dtype=np.float64)
     m = zr.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
     p = np.exp(zr - m)
-    p /= p.sum(axis=1, keepdims=True)
+    tot = p.sum(axis=1, keepdims=True)
+    p = np.divide(p, tot, out=np.zeros_like(p), where=tot > 0)   # all masked: softmax 0
     dz = -p * wsum[rows][:, None]
     where = {int(r): i for i, r in enumerate(rows)}
     for pi in range(pos_row.shape[0]):

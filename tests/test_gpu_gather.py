@@ -61,6 +61,50 @@ def test_gather_small(spec_name, vocab, bf16):
     assert np.isfinite(dz.float().cpu().numpy()).all()
 
 
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_gather_masked_entries(bf16):
+    """Rows with masked (-inf) vocabulary entries: one row whose first 256
+    entries are masked, rows with scattered masks, an all-masked row, and a
+    masked target.  Finite values compare at 2e-3; -inf values must match."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(77))
+    spec = synth.tree_fig1()
+    plan = B.KDAPlan(spec.parent, spec.seg_len, spec.seg_row, 16)
+    N, vocab = plan.info["n_rows"], 1000
+    pos_row, pos_next, rp_ptr, rp_idx = _maps(plan)
+    z = rng.standard_normal((N, vocab), dtype=np.float32) * np.float32(3.0)
+    z = synth.round_bf16(z) if bf16 else z
+    z[0, :256] = -np.inf
+    for r in range(1, N, 3):
+        z[r, rng.choice(vocab, 300, replace=False)] = -np.inf
+    z[5, :] = -np.inf
+    tokens = rng.integers(256, vocab, N)
+    tgt = tokens[pos_next]
+    masked_tgt = np.flatnonzero(~np.isfinite(z[pos_row, tgt]))
+    assert len(masked_tgt) > 0
+    dlogp = rng.standard_normal(len(pos_row)).astype(np.float32)
+    print(f"case gather masked rows={N} vocab={vocab} bf16={bf16}", flush=True)
+    zt = torch.from_numpy(z).cuda().to(torch.bfloat16 if bf16 else torch.float32)
+    logp, lse = B.gather_logprobs(zt, _dev_i32(pos_row), _dev_i32(tgt))
+    dz = B.gather_logprobs_bwd(zt, lse, _dev_i32(rp_ptr), _dev_i32(rp_idx), _dev_i32(tgt),
+                               torch.from_numpy(dlogp).cuda())
+    torch.cuda.synchronize()
+    ref_logp, ref_lse = og.gather_fwd(z, pos_row, tgt)
+    ref_dz = og.gather_bwd(z, pos_row, tgt, dlogp)
+    got_logp, got_lse, got_dz = logp.cpu().numpy(), lse.cpu().numpy(), dz.float().cpu().numpy()
+    for got, ref in ((got_logp, ref_logp), (got_lse, ref_lse)):
+        assert not np.isnan(got).any()
+        assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref_logp)
+    errs = {"logp": rel_l2(got_logp[fin], ref_logp[fin]),
+            "lse": rel_l2(got_lse[np.isfinite(ref_lse)], ref_lse[np.isfinite(ref_lse)]),
+            "dlogits": rel_l2(got_dz, ref_dz)}
+    print("  rel L2:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert np.isfinite(got_dz).all()
+    assert all(e <= TOL for e in errs.values()), errs
+
+
 def test_gather_fullsize_sampled_rows():
     import torch
     w = synth.workload(1)

@@ -127,11 +127,20 @@ def test_bad_arguments(lib):
     p = B.KDAPlan(par, ln, None, 16)
     # unsupported shapes report zero sizes and are rejected before any launch
     assert p.saved_bytes(2, 96) == 0
-    assert lib.kda_tree_fwd(p.handle, ctypes.c_void_p(256), 2, 96, 96, 0, 1.0, *([None] * 10), 0,
-                            None) == -2
-    assert lib.kda_tree_fwd(p.handle, None, 2, 64, 64, 0, 1.0, *([None] * 10), 0, None) == -4
-    assert lib.kda_tree_fwd(p.handle, ctypes.c_void_p(256), 2, 64, 64, 0, 1.0,
-                            *([ctypes.c_void_p(256)] * 10), 0, None) == -3
+    assert lib.kda_tree_fwd(p.handle, ctypes.c_void_p(256), 2, 96, 96, 0, 1.0, *([None] * 9), 0,
+                            None, 0, None) == -2
+    assert lib.kda_tree_fwd(p.handle, None, 2, 64, 64, 0, 1.0, *([None] * 9), 0, None, 0,
+                            None) == -4
+    dev = ctypes.c_void_p(256)
+    # an undersized `saved` or workspace is refused before any launch
+    assert lib.kda_tree_fwd(p.handle, dev, 2, 64, 64, 0, 1.0, *([dev] * 9), 0, dev, 1 << 40,
+                            None) == -3
+    assert b"saved" in lib.kda_last_error()
+    assert lib.kda_tree_fwd(p.handle, dev, 2, 64, 64, 0, 1.0, *([dev] * 9), 1 << 40, dev, 0,
+                            None) == -3
     assert b"workspace" in lib.kda_last_error()
+    assert lib.kda_tree_bwd(p.handle, dev, 2, 64, 64, 0, 1.0, *([dev] * 7), 0, *([dev] * 10),
+                            1 << 40, None) == -3
+    assert b"saved" in lib.kda_last_error()
     p64 = B.KDAPlan(par, ln, None, 32)
     assert p64.fwd_ws_bytes(2, 64) == 0

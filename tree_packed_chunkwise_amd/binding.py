@@ -88,9 +88,10 @@ def load_library(path: Path | str | None = None):
     for n in ("kda_saved_bytes", "kda_fwd_workspace_bytes", "kda_bwd_workspace_bytes"):
         getattr(L, n).argtypes = [vp, i32, i32, i32]
         getattr(L, n).restype = sz
-    L.kda_tree_fwd.argtypes = [vp, vp, i32, i32, i32, i32, f32] + [vp] * 10 + [sz, vp]
+    L.kda_tree_fwd.argtypes = [vp, vp, i32, i32, i32, i32, f32] + [vp] * 9 + [sz, vp, sz, vp]
     L.kda_tree_fwd.restype = ctypes.c_int
-    L.kda_tree_bwd.argtypes = [vp, vp, i32, i32, i32, i32, f32] + [vp] * 17 + [sz, vp]
+    L.kda_tree_bwd.argtypes = ([vp, vp, i32, i32, i32, i32, f32] + [vp] * 7 + [sz] + [vp] * 10
+                               + [sz, vp])
     L.kda_tree_bwd.restype = ctypes.c_int
     L.kda_l1_plan.argtypes = [i32, vp, vp, i64, vp, vp, vp, vp]
     L.kda_l1_plan.restype = ctypes.c_int
@@ -241,6 +242,56 @@ def _need_cuda(*ts):
             raise KDAError("tensors must be contiguous")
 
 
+def _expect(name, t, shape, dtypes, optional=False):
+    """Refuses a tensor whose shape or dtype is not what the kernels index:
+    a wrong size or element type would become an out-of-bounds device access,
+    so it is caught here, before any launch."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise KDAError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise KDAError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise KDAError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _expect_bytes(name, t, nbytes):
+    if t is None:
+        raise KDAError(f"{name} is required")
+    have = t.numel() * t.element_size()
+    if have < int(nbytes):
+        raise KDAError(f"{name} holds {have} bytes, needs {int(nbytes)}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise KDAError(f"tensors on several devices: {sorted(map(str, devs))}")
+
+
+def _check_inputs(plan: "KDAPlan", q, k, v, g, beta, h0):
+    """q, k, v, g, beta and h0 against the plan's row and root counts."""
+    import torch
+    if q is None or q.dim() != 3:
+        raise KDAError("q must be [rows, H, dk]")
+    N, H, D = q.shape
+    i = plan.info
+    if N != i["n_rows"]:
+        raise KDAError(f"q has {N} rows, the plan has {i['n_rows']} compact rows")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise KDAError(f"q has dtype {q.dtype}: bf16 or fp32")
+    _expect("q", q, (N, H, D), None)
+    _expect("k", k, (N, H, D), (q.dtype,))
+    _expect("v", v, (N, H, D), (q.dtype,))
+    _expect("g", g, (N, H, D), (torch.float32,))
+    _expect("beta", beta, (N, H), (torch.float32,))
+    _expect("h0", h0, (i["n_root"], H, D, D), (torch.float32,), optional=True)
+    _same_device(q, k, v, g, beta, h0)
+    return N, H, D
+
+
 def alloc_fwd(plan: KDAPlan, H: int, D: int, device):
     """Output and scratch buffers of kda_tree_fwd (torch allocations)."""
     import torch
@@ -255,15 +306,25 @@ def alloc_fwd(plan: KDAPlan, H: int, D: int, device):
 
 def kda_tree_fwd(plan: KDAPlan, q, k, v, g, beta, h0=None, scale=None, out=None):
     """Forward pass; returns dict(o, h_leaf, saved[, ws])."""
+    import torch
+    N, H, D = _check_inputs(plan, q, k, v, g, beta, h0)
     _need_cuda(q, k, v, g, beta, h0)
-    N, H, D = q.shape
     if out is None:
         out = alloc_fwd(plan, H, D, q.device)
+    i = plan.info
+    _expect("o", out["o"], (i["n_out_rows"], H, D), (torch.float32,))
+    _expect("h_leaf", out["h_leaf"], (i["n_leaf"], H, D, D), (torch.float32,))
+    _expect_bytes("saved", out["saved"], plan.saved_bytes(H, D))
+    _expect_bytes("ws", out["ws"], plan.fwd_ws_bytes(H, D))
+    _need_cuda(out["o"], out["h_leaf"], out["saved"], out["ws"])
+    _same_device(q, out["o"], out["h_leaf"], out["saved"], out["ws"])
     sc = float(scale) if scale is not None else 1.0 / float(np.sqrt(D))
+    sv = out["saved"]
     _check(load_library().kda_tree_fwd(
         plan.handle, _p(plan.device(q.device)), H, D, v.shape[2], _dtype_code(q), sc,
         _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), _p(out["o"]), _p(out["h_leaf"]),
-        _p(out["saved"]), _p(out["ws"]), out["ws"].numel(), _stream(q)))
+        _p(sv), sv.numel() * sv.element_size(), _p(out["ws"]),
+        out["ws"].numel() * out["ws"].element_size(), _stream(q)))
     return out
 
 
@@ -284,26 +345,58 @@ def alloc_bwd(plan: KDAPlan, H: int, D: int, device, boundary=True):
 def kda_tree_bwd(plan: KDAPlan, q, k, v, g, beta, saved, dO, dh_leaf=None, h0=None, scale=None,
                  out=None, boundary=True):
     """Reverse mode; returns dict(dq, dk, dv, dg, dbeta, dh0, dh_boundary[, ws])."""
+    import torch
+    N, H, D = _check_inputs(plan, q, k, v, g, beta, h0)
+    i = plan.info
+    n = i["n_out_rows"]
+    _expect("dO", dO, (n, H, D), (q.dtype,))
+    _expect("dh_leaf", dh_leaf, (i["n_leaf"], H, D, D), (torch.float32,), optional=True)
+    _expect_bytes("saved", saved, plan.saved_bytes(H, D))
     _need_cuda(q, k, v, g, beta, saved, dO, dh_leaf, h0)
-    N, H, D = q.shape
-    if dO.dtype != q.dtype:
-        raise KDAError("dO must have the dtype of q/k/v")
     if out is None:
         out = alloc_bwd(plan, H, D, q.device, boundary)
+    f32 = (torch.float32,)
+    for name in ("dq", "dk", "dv", "dg"):
+        _expect(name, out[name], (n, H, D), f32)
+    _expect("dbeta", out["dbeta"], (n, H), f32)
+    _expect("dh0", out["dh0"], (i["n_root"], H, D, D), f32)
+    _expect("dh_boundary", out.get("dh_boundary"), (i["n_buf"], H, D, D), f32, optional=True)
+    _expect_bytes("ws", out["ws"], plan.bwd_ws_bytes(H, D))
+    _need_cuda(*[out.get(x) for x in ("dq", "dk", "dv", "dg", "dbeta", "dh0", "dh_boundary", "ws")])
+    _same_device(q, dO, dh_leaf, saved, *[out.get(x) for x in
+                                          ("dq", "dk", "dv", "dg", "dbeta", "dh0", "dh_boundary",
+                                           "ws")])
     sc = float(scale) if scale is not None else 1.0 / float(np.sqrt(D))
     _check(load_library().kda_tree_bwd(
         plan.handle, _p(plan.device(q.device)), H, D, v.shape[2], _dtype_code(q), sc,
-        _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), _p(saved), _p(dO), _p(dh_leaf),
+        _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0), _p(saved),
+        saved.numel() * saved.element_size(), _p(dO), _p(dh_leaf),
         _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dg"]), _p(out["dbeta"]),
-        _p(out["dh0"]), _p(out.get("dh_boundary")), _p(out["ws"]), out["ws"].numel(),
-        _stream(q)))
+        _p(out["dh0"]), _p(out.get("dh_boundary")), _p(out["ws"]),
+        out["ws"].numel() * out["ws"].element_size(), _stream(q)))
     return out
 
 
 def kda_state_copy(src, src_idx, dst, dst_idx, n: int):
     """dst[dst_idx[i]] = src[src_idx[i]] for i < n over [*, H, dk, dv] fp32 state
     arrays (None index = identity; index arrays are device int32)."""
+    import torch
+    f32, i32 = (torch.float32,), (torch.int32,)
+    if src is None or dst is None or src.dim() < 2 or tuple(src.shape[1:]) != tuple(dst.shape[1:]):
+        raise KDAError("src and dst must be [*, H, dk, dv] state arrays of one state shape")
+    _expect("src", src, tuple(src.shape), f32)
+    _expect("dst", dst, tuple(dst.shape), f32)
+    n = int(n)
+    for name, t, full in (("src_idx", src_idx, src), ("dst_idx", dst_idx, dst)):
+        if t is None:
+            if n > full.shape[0]:
+                raise KDAError(f"n = {n} exceeds the {full.shape[0]} states of the identity map")
+        else:
+            _expect(name, t, (t.shape[0],) if t.dim() == 1 else (-1,), i32)
+            if t.shape[0] < n:
+                raise KDAError(f"{name} holds {t.shape[0]} entries, needs {n}")
     _need_cuda(src, src_idx, dst, dst_idx)
+    _same_device(src, src_idx, dst, dst_idx)
     elems = int(np.prod(src.shape[1:]))
     _check(load_library().kda_state_copy(_p(src), _p(src_idx), _p(dst), _p(dst_idx), int(n), elems,
                                          _stream(src)))
@@ -313,7 +406,23 @@ def kda_state_copy(src, src_idx, dst, dst_idx, n: int):
 def kda_state_sum(src, ptr, idx, dst, accumulate: bool):
     """dst[d] = (dst[d] if accumulate else 0) + sum of src[idx[j]], j in [ptr[d], ptr[d+1]),
     in ascending j (ptr, idx device int32)."""
+    import torch
+    f32, i32 = (torch.float32,), (torch.int32,)
+    if dst is None or dst.dim() < 2 or ptr is None or ptr.dim() != 1:
+        raise KDAError("dst must be [n_dst, H, dk, dv] and ptr [n_dst + 1]")
+    n_dst = ptr.shape[0] - 1
+    if n_dst > dst.shape[0]:
+        raise KDAError(f"ptr describes {n_dst} sums, dst holds {dst.shape[0]} states")
+    _expect("ptr", ptr, (n_dst + 1,), i32)
+    _expect("dst", dst, tuple(dst.shape), f32)
+    if src is not None:
+        if tuple(src.shape[1:]) != tuple(dst.shape[1:]):
+            raise KDAError("src and dst must hold states of one shape")
+        _expect("src", src, tuple(src.shape), f32)
+    if idx is not None:
+        _expect("idx", idx, (idx.shape[0],) if idx.dim() == 1 else (-1,), i32)
     _need_cuda(src, ptr, idx, dst)
+    _same_device(src, ptr, idx, dst)
     elems = int(np.prod(dst.shape[1:]))
     _check(load_library().kda_state_sum(_p(src), _p(ptr), _p(idx), int(ptr.shape[0] - 1), elems,
                                         1 if accumulate else 0, _p(dst), _stream(dst)))
@@ -324,13 +433,24 @@ def gather_logprobs(logits, pos_row, pos_target, out=None):
     """logp[p] = logits[pos_row[p], pos_target[p]] - logsumexp(logits[pos_row[p]]).
     Returns (logp, lse)."""
     import torch
-    _need_cuda(logits, pos_row, pos_target)
+    if logits is None or logits.dim() != 2:
+        raise KDAError("logits must be [rows, vocab]")
     n_rows, vocab = logits.shape
+    _expect("logits", logits, (n_rows, vocab), (torch.bfloat16, torch.float32))
+    if pos_row is None or pos_row.dim() != 1:
+        raise KDAError("pos_row must be [n_pos]")
     n_pos = pos_row.shape[0]
+    _expect("pos_row", pos_row, (n_pos,), (torch.int32,))
+    _expect("pos_target", pos_target, (n_pos,), (torch.int32,))
+    _need_cuda(logits, pos_row, pos_target)
     if out is None:
         out = (torch.empty(n_pos, dtype=torch.float32, device=logits.device),
                torch.empty(n_rows, dtype=torch.float32, device=logits.device))
     logp, lse = out
+    _expect("logp", logp, (n_pos,), (torch.float32,))
+    _expect("lse", lse, (n_rows,), (torch.float32,))
+    _need_cuda(logp, lse)
+    _same_device(logits, pos_row, pos_target, logp, lse)
     _check(load_library().gather_logprobs(_p(logits), _dtype_code(logits), n_rows, vocab,
                                           _p(pos_row), _p(pos_target), n_pos, _p(logp), _p(lse),
                                           _stream(logits)))
@@ -339,10 +459,24 @@ def gather_logprobs(logits, pos_row, pos_target, out=None):
 
 def gather_logprobs_bwd(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp, out=None):
     import torch
-    _need_cuda(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp)
+    if logits is None or logits.dim() != 2:
+        raise KDAError("logits must be [rows, vocab]")
     n_rows, vocab = logits.shape
+    _expect("logits", logits, (n_rows, vocab), (torch.bfloat16, torch.float32))
+    _expect("lse", lse, (n_rows,), (torch.float32,))
+    _expect("row_pos_ptr", row_pos_ptr, (n_rows + 1,), (torch.int32,))
+    if pos_target is None or pos_target.dim() != 1:
+        raise KDAError("pos_target must be [n_pos]")
+    n_pos = pos_target.shape[0]
+    _expect("row_pos_idx", row_pos_idx, (n_pos,), (torch.int32,))
+    _expect("pos_target", pos_target, (n_pos,), (torch.int32,))
+    _expect("dlogp", dlogp, (n_pos,), (torch.float32,))
+    _need_cuda(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp)
     if out is None:
         out = torch.empty_like(logits)
+    _expect("dlogits", out, (n_rows, vocab), (logits.dtype,))
+    _need_cuda(out)
+    _same_device(logits, lse, row_pos_ptr, row_pos_idx, pos_target, dlogp, out)
     _check(load_library().gather_logprobs_bwd(_p(logits), _dtype_code(logits), n_rows, vocab,
                                               _p(lse), _p(row_pos_ptr), _p(row_pos_idx),
                                               _p(pos_target), _p(dlogp), _p(out),
@@ -379,8 +513,13 @@ def moe_router_stats(logits, row_mult, top_k: int, with_topk: bool = True):
     plan.device_table("ROW_MULT").  Returns dict(load, psum, zsum, n_tok[,
     topk_idx, topk_prob])."""
     import torch
-    _need_cuda(logits, row_mult)
+    if logits is None or logits.dim() != 2:
+        raise KDAError("logits must be [rows, n_experts]")
     n_rows, E = logits.shape
+    _expect("logits", logits, (n_rows, E), (torch.bfloat16, torch.float32))
+    _expect("row_mult", row_mult, (n_rows,), (torch.int32,))
+    _need_cuda(logits, row_mult)
+    _same_device(logits, row_mult)
     dev = logits.device
     L = load_library()
     ws = torch.empty(max(1, L.moe_router_workspace_bytes(n_rows, E)), dtype=torch.uint8, device=dev)
@@ -404,29 +543,51 @@ def moe_router_stats(logits, row_mult, top_k: int, with_topk: bool = True):
 def moe_router_stats_bwd(logits, row_mult, g_psum, g_z: float, out=None):
     """dlogits of <g_psum, psum> + g_z * zsum (fp32 [n_rows, E])."""
     import torch
-    _need_cuda(logits, row_mult, g_psum)
+    if logits is None or logits.dim() != 2:
+        raise KDAError("logits must be [rows, n_experts]")
     n_rows, E = logits.shape
+    _expect("logits", logits, (n_rows, E), (torch.bfloat16, torch.float32))
+    _expect("row_mult", row_mult, (n_rows,), (torch.int32,))
+    _expect("g_psum", g_psum, (E,), (torch.float32,))
+    _need_cuda(logits, row_mult, g_psum)
     if out is None:
         out = torch.empty((n_rows, E), dtype=torch.float32, device=logits.device)
+    _expect("dlogits", out, (n_rows, E), (torch.float32,))
+    _need_cuda(out)
+    _same_device(logits, row_mult, g_psum, out)
     _check(load_library().moe_router_stats_bwd(_p(logits), _dtype_code(logits), n_rows, E,
                                                _p(row_mult), _p(g_psum), float(g_z), _p(out),
                                                _stream(logits)))
     return out
 
 
+def _attn_shape(plan: KDAPlan, q):
+    if q is None or q.dim() != 3:
+        raise KDAError("q must be [rows, H, d]")
+    N, H, D = q.shape
+    if N != plan.info["n_rows"]:
+        raise KDAError(f"q has {N} rows, the plan has {plan.info['n_rows']} compact rows")
+    return N, H, D
+
+
 def tree_attn_fwd(plan: KDAPlan, q, k, v, scale=None, out=None):
     """Tree-ancestor attention forward: q, k, v bf16 [rows, H, d] on the
     plan's compact rows.  Returns (o fp32 [rows, H, d], lse fp32 [rows, H])."""
     import torch
+    N, H, D = _attn_shape(plan, q)
+    bf = (torch.bfloat16,)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(name, t, (N, H, D), bf)
     _need_cuda(q, k, v)
-    N, H, D = q.shape
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise KDAError("tree attention takes bf16 q, k, v")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = (torch.empty(N, H, D, dtype=torch.float32, device=q.device),
                torch.empty(N, H, dtype=torch.float32, device=q.device))
     o, lse = out
+    _expect("o", o, (N, H, D), (torch.float32,))
+    _expect("lse", lse, (N, H), (torch.float32,))
+    _need_cuda(o, lse)
+    _same_device(q, k, v, o, lse)
     _check(load_library().tree_attn_fwd(plan.handle, _p(plan.device(q.device)), H, D, scale,
                                         _p(q), _p(k), _p(v), _p(o), _p(lse), _stream(q)))
     return o, lse
@@ -435,18 +596,28 @@ def tree_attn_fwd(plan: KDAPlan, q, k, v, scale=None, out=None):
 def tree_attn_bwd(plan: KDAPlan, q, k, v, o, lse, dO, scale=None, out=None, ws=None):
     """Gradients (dq, dk, dv) fp32 of sum(dO * o) for tree_attn_fwd; dO bf16."""
     import torch
+    N, H, D = _attn_shape(plan, q)
+    bf, f32 = (torch.bfloat16,), (torch.float32,)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dO", dO)):
+        _expect(name, t, (N, H, D), bf)
+    _expect("o", o, (N, H, D), f32)
+    _expect("lse", lse, (N, H), f32)
     _need_cuda(q, k, v, o, lse, dO)
-    N, H, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = tuple(torch.empty(N, H, D, dtype=torch.float32, device=q.device) for _ in range(3))
     nb = load_library().tree_attn_workspace_bytes(plan.handle, H, D)
-    if ws is None or ws.numel() < nb:
+    if ws is None or ws.numel() * ws.element_size() < nb:
         ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = out
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(name, t, (N, H, D), f32)
+    _need_cuda(dq, dk, dv, ws)
+    _same_device(q, k, v, o, lse, dO, dq, dk, dv, ws)
     _check(load_library().tree_attn_bwd(plan.handle, _p(plan.device(q.device)), H, D, scale,
                                         _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dO), _p(dq),
-                                        _p(dk), _p(dv), _p(ws), ws.numel(), _stream(q)))
+                                        _p(dk), _p(dv), _p(ws), ws.numel() * ws.element_size(),
+                                        _stream(q)))
     return dq, dk, dv
 
 

@@ -357,7 +357,7 @@ size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int3
 int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
                  int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
                  const float* g, const float* beta, const float* h0, float* o, float* h_leaf,
-                 void* saved, void* ws, size_t ws_bytes, void* stream) {
+                 void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dev_plan(plan, dev_plan);
   if (rc) return rc;
   const kda::Plan& p = plan->p;
@@ -369,6 +369,8 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
     return fail(KDA_ERR_ARG, "null tensor argument");
   if (!aligned16({q, k, v, g, h0, o, h_leaf, saved, ws}) || ((uintptr_t)beta) % 4)
     return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned (beta: 4-byte)");
+  if (saved_bytes < kda_saved_bytes(plan, H, dk, dv))
+    return fail(KDA_ERR_WORKSPACE, "saved buffer too small");
   if (ws_bytes < kda_fwd_workspace_bytes(plan, H, dk, dv))
     return fail(KDA_ERR_WORKSPACE, "forward workspace too small");
   kda::FwdArgs a;
@@ -390,8 +392,8 @@ int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
 int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,
                  int32_t in_dtype, float scale, const void* q, const void* k, const void* v,
                  const float* g, const float* beta, const float* h0, const void* saved,
-                 const void* dO, const float* dh_leaf, float* dq, float* dk_, float* dv_,
-                 float* dg, float* dbeta, float* dh0, float* dh_boundary, void* ws,
+                 size_t saved_bytes, const void* dO, const float* dh_leaf, float* dq, float* dk_,
+                 float* dv_, float* dg, float* dbeta, float* dh0, float* dh_boundary, void* ws,
                  size_t ws_bytes, void* stream) {
   (void)h0;  // the start states of all chunks are in `saved`
   int rc = check_dev_plan(plan, dev_plan);
@@ -407,6 +409,8 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   if (!aligned16({q, k, v, g, saved, dO, dh_leaf, dq, dk_, dv_, dg, dh0, dh_boundary, ws}) ||
       ((uintptr_t)beta) % 4 || ((uintptr_t)dbeta) % 4)
     return fail(KDA_ERR_ARG, "tensor arguments must be 16-byte aligned (beta, dbeta: 4-byte)");
+  if (saved_bytes < kda_saved_bytes(plan, H, dk, dv))
+    return fail(KDA_ERR_WORKSPACE, "saved buffer too small");
   if (ws_bytes < kda_bwd_workspace_bytes(plan, H, dk, dv))
     return fail(KDA_ERR_WORKSPACE, "backward workspace too small");
   SavedView sv = carve_saved(p, H, dk, (void*)saved, nullptr);

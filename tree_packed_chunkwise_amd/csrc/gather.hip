@@ -13,6 +13,12 @@
 //               columns get their exact value (-softmax*w + sum of dlogp of the
 //               positions targeting that column), written by one thread.
 // HBM-bound: each logit is read once per pass and each gradient written once.
+//
+// Masked entries: a logit of -inf has probability zero (it adds nothing to
+// the row's sum of exponentials and its softmax value is 0).  A row whose
+// every entry is -inf has lse = -inf, every position on it gets logp = -inf,
+// and its softmax is taken as all zeros (only the target columns of its
+// gradient are nonzero).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,11 +37,13 @@ __device__ inline void st_logit(uint16_t* p, size_t i, float x) {
   p[i] = __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// running (max, sum of exp(x - max)); (-inf, 0) until a finite logit arrives,
+// and -inf logits add nothing (exp(-inf - m) would be NaN while m = -inf)
 __device__ inline void online_add(float& m, float& s, float x) {
   if (x > m) {
     s = s * __expf(m - x) + 1.f;
     m = x;
-  } else {
+  } else if (x > -INFINITY) {
     s += __expf(x - m);
   }
 }
@@ -100,7 +108,8 @@ __global__ void k_pos_logp(const T* logits, int vocab, const int* pos_row, const
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= n_pos) return;
   const int r = pos_row[p];
-  logp[p] = ld_logit(logits, (size_t)r * vocab + pos_tgt[p]) - lse[r];
+  const float l = lse[r];
+  logp[p] = l == -INFINITY ? -INFINITY : ld_logit(logits, (size_t)r * vocab + pos_tgt[p]) - l;
 }
 
 template <typename T>
@@ -114,14 +123,16 @@ __global__ __launch_bounds__(GT) void k_row_grad(const T* logits, int vocab, con
   float w = 0.f;
   for (int p = p0; p < p1; ++p) w += dlogp[row_pos_idx[p]];
   const float l = lse[row];
+  const bool dead = l == -INFINITY;   // every entry masked: softmax taken as 0
   const T* z = logits + row * vocab;
   T* dz = dlogits + row * vocab;
-  for (int i = tid; i < vocab; i += GT) st_logit(dz, i, -__expf(ld_logit(z, i) - l) * w);
+  for (int i = tid; i < vocab; i += GT)
+    st_logit(dz, i, dead ? 0.f : -__expf(ld_logit(z, i) - l) * w);
   __syncthreads();
   if (tid == 0) {
     for (int p = p0; p < p1; ++p) {
       const int t = pos_tgt[row_pos_idx[p]];
-      float acc = -__expf(ld_logit(z, t) - l) * w;
+      float acc = dead ? 0.f : -__expf(ld_logit(z, t) - l) * w;
       for (int p2 = p0; p2 < p1; ++p2)
         if (pos_tgt[row_pos_idx[p2]] == t) acc += dlogp[row_pos_idx[p2]];
       st_logit(dz, t, acc);
