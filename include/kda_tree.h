@@ -249,9 +249,11 @@ size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int3
  *   h_leaf          [n_leaf,H,dk,dv] fp32 final state per leaf (leaves ascending)
  *   saved, saved_bytes  at least kda_saved_bytes(...) bytes, kept for kda_tree_bwd
  *   ws, ws_bytes    scratch of kda_fwd_workspace_bytes(...) bytes
- * Supported gate range: the chunk math factors per-pair decays through the
- * first row of each 16-row block; sum(|g|) over any 15 consecutive rows of a
- * chunk must stay below 80 per channel (fp32 exponent range).
+ * Gates: any finite g <= 0.  The chunk math factors per-pair decays through
+ * the first row of each 16-row block; rows whose decay from that row exceeds
+ * 64 (from the first such row of a chunk on) take exact per-pair
+ * exponentials instead, chosen from the rows up to them, so replayed chunks
+ * still give the trajectory-expanded bits.
  * Errors: KDA_ERR_SHAPE, KDA_ERR_WORKSPACE, KDA_ERR_ARG, KDA_ERR_HIP.
  */
 int kda_tree_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,

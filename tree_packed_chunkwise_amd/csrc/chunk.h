@@ -21,10 +21,18 @@
 // Decay factors: e^(Gam_i - Gam_j) (j <= i) is split around a reference m per
 // 16-row block pair (I, J) as e^(Gam_i - m) e^(m - Gam_j), m = Gam at the
 // first row of block J.  The left factor is <= 1; the right one is bounded by
-// the decay of at most 15 consecutive rows.  The reference never lies after
-// either row of the pair, so an output row depends only on the rows up to it:
-// a chunk shared by two trajectories up to a fork gives the same bits before
-// the fork in both.
+// the decay from the first row of block J to row j.  The reference never lies
+// after either row of the pair, so an output row depends only on the rows up
+// to it: a chunk shared by two trajectories up to a fork gives the same bits
+// before the fork in both.
+//
+// Any gate g <= 0 is supported.  A row j whose decay from its block's first
+// row exceeds kExactDecay in some channel would push the right factor out of
+// the range where the split keeps its precision (and past fp32 from about
+// 88).  From the first such row of a chunk on, every row's A and P entries
+// are recomputed pair by pair with exact exponentials e^(Gam_i - Gam_j) <= 1
+// (chunk_AP_exact).  Which rows take that path is decided by the rows up to
+// them, so the causal property above still holds.
 #pragma once
 
 #include "common.h"
@@ -33,6 +41,9 @@ namespace kda {
 
 constexpr int NT = 512;  // threads per block
 constexpr int NW = 8;    // waves per block
+// largest decay (Gam at a block's first row minus Gam at a later row of the
+// block) that the factored products take; rows past it use exact pairs
+constexpr float kExactDecay = 64.f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -373,6 +384,7 @@ struct ChunkTables {
   float dfac[(Geom<BC, D>::NOFF > 0 ? Geom<BC, D>::NOFF : 1)][D];  // e^(gref_I - gref_J)
   float beta[BC];
   int orow[BC];
+  int first_bad;   // first row whose in-block decay exceeds kExactDecay (BC: none)
 };
 
 // hi/lo operands of the decay-factored products for one 64-channel pass:
@@ -448,6 +460,7 @@ __device__ inline void elems_gamma(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) 
     }
     tb.part[rg][c0 + G::DH * hf] = run;
   }
+  if (tid == 0) tb.first_bad = BC;
   __syncthreads();
 #pragma unroll
   for (int hf = 0; hf < G::NHALF; ++hf) {
@@ -467,6 +480,17 @@ __device__ inline void elems_gamma(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er) 
     }
   }
   __syncthreads();
+  {  // rows whose decay from their block's first row leaves the factored range
+    int bad = BC;
+#pragma unroll
+    for (int hf = 0; hf < G::NHALF; ++hf)
+#pragma unroll
+      for (int t = G::RPT - 1; t >= 0; --t) {
+        const int i = r0 + t;
+        if (tb.gref[i >> 4][c0 + G::DH * hf] - er.gam[hf * G::RPT + t] > kExactDecay) bad = i;
+      }
+    if (bad < BC) atomicMin(&tb.first_bad, bad);
+  }
   if (rg == G::NRG - 1) {
 #pragma unroll
     for (int hf = 0; hf < G::NHALF; ++hf) {
@@ -599,6 +623,76 @@ __device__ inline void chunk_AP(ChunkTables<BC, D>& tb, ElemRegs<BC, D>& er, APO
     if ((j >> 4) > (i >> 4)) {
       Aout[i * pa + j] = (_Float16)0.f;
       Pout[i * pp + j] = (_Float16)0.f;
+    }
+  }
+  __syncthreads();
+}
+
+// Exact A and P entries for the rows i >= first_bad (called when that row
+// exists):
+//   A_ij = sum_c k_ic k_jc e^(Gam_ic - Gam_jc)  (j < i),  P_ij = the same with q_i (j <= i),
+// every exponential taken of a non-positive difference.  It re-reads q, k and
+// g of the chunk's rows (irow: input row per chunk row, -1 past the chunk)
+// so that it holds none of the caller's registers; the channels go through
+// LDS in passes of CP (stage: 3 BC (CP + 1) floats, not overlapping Aout /
+// Pout), Gam as a running sum down each channel; thread t owns the pairs
+// e = t + NT m (i = e / BC, j = e % BC).  Overwrites those rows of Aout /
+// Pout.  Ends synchronised.
+template <typename TIn, int BC, int D>
+__device__ inline void chunk_AP_exact(const TIn* q, const TIn* k, const float* g,
+                                                         int H, int h, const int* irow,
+                                                         int first_bad, float* stage,
+                                                         _Float16* Aout, int pa, _Float16* Pout,
+                                                         int pp) {
+  constexpr int CP = 32, SP = CP + 1;
+  constexpr int NPR = (BC * BC + NT - 1) / NT;
+  float* kx = stage;
+  float* qx = stage + BC * SP;
+  float* gx = stage + 2 * BC * SP;
+  const int tid = threadIdx.x;
+  float a[NPR], p[NPR];
+#pragma unroll
+  for (int m = 0; m < NPR; ++m) a[m] = p[m] = 0.f;
+  for (int cp0 = 0; cp0 < D; cp0 += CP) {
+    for (int e = tid; e < BC * CP; e += NT) {
+      const int i = e / CP, c = e % CP, r = irow[i];
+      const size_t o = ((size_t)(r < 0 ? 0 : r) * H + h) * D + cp0 + c;
+      kx[i * SP + c] = r >= 0 ? ld_in(k, o) : 0.f;
+      qx[i * SP + c] = r >= 0 ? ld_in(q, o) : 0.f;
+      gx[i * SP + c] = r >= 0 ? g[o] : 0.f;
+    }
+    __syncthreads();
+    if (tid < CP) {   // Gam: running sum down the rows of channel cp0 + tid
+      float run = 0.f;
+      for (int i = 0; i < BC; ++i) {
+        run += gx[i * SP + tid];
+        gx[i * SP + tid] = run;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NPR; ++m) {
+      const int e = tid + NT * m, i = e / BC, j = e % BC;
+      if (e < BC * BC && i >= first_bad && j <= i) {
+        float sa = 0.f, sp = 0.f;
+#pragma unroll 2
+        for (int c = 0; c < CP; ++c) {
+          const float t = kx[j * SP + c] * __expf(gx[i * SP + c] - gx[j * SP + c]);
+          sa = __builtin_fmaf(kx[i * SP + c], t, sa);
+          sp = __builtin_fmaf(qx[i * SP + c], t, sp);
+        }
+        a[m] += sa;
+        p[m] += sp;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int m = 0; m < NPR; ++m) {
+    const int e = tid + NT * m, i = e / BC, j = e % BC;
+    if (e < BC * BC && i >= first_bad && j <= i) {
+      Aout[i * pa + j] = (_Float16)(j < i ? a[m] : 0.f);
+      Pout[i * pp + j] = (_Float16)p[m];
     }
   }
   __syncthreads();

@@ -32,6 +32,11 @@
 // column block, the channel factor between the two references applied to the
 // output rows), the gradients are combined, and dg is formed by a parallel
 // reverse scan.
+//
+// Chunks with decays past the range of the factored products (a row more than
+// kExactDecay below its block's first row, or a single step of more than
+// kExactStep) run phase 3 on exact per-pair exponentials instead
+// (phase3_exact_*): any gate g <= 0 is supported.
 #include <type_traits>
 
 #include "chunk.h"
@@ -118,6 +123,13 @@ struct GradSmem {
       float gam[64][G::PG];                  // Gam, replaced by dGam
       __bf16 qraw[64][G::PB], kraw[64][G::PB];  // Q, K as read (bf16 inputs)  [c][i]
     } d;
+    struct {                       // phase 3 of a chunk with exact pairs (decays past the
+                                   // factored range), one 64-channel pass, transposed
+      float dgam[64][G::PG];       // dGam of the pass           [c][i]
+      float gam[64][G::PG];        // Gam                        [c][i]
+      float qf[64][G::PG], kf[64][G::PG];   // q, k as read     [c][i]
+      float dP[BC][G::PG], dA[BC][G::PG];   // dP, dA (lower)    [i][j]
+    } e;
   } u;
   __attribute__((aligned(16))) float dfac[G::NLOW][D];   // e^(gref_I - gref_J), J <= I
   __attribute__((aligned(16))) float gref[G::NB][D];     // Gam at the first row of each block
@@ -128,9 +140,11 @@ struct GradSmem {
   float redg[NW][D];        // deGC partials per wave
   float part[G::NRG][D];    // row-group sums (Gam, then the reverse scan)
   float degc[D];
+  float gcl[D];             // Gam_C
   float beta[BC];
   int orow[BC];
   int irow[BC];   // input row of each chunk row (-1 past the chunk)
+  int bad;        // some row's decay from its block's first row exceeds kExactDecay
 };
 
 // destination of a row gradient: the output row, or the replay slot
@@ -139,6 +153,112 @@ __device__ inline float* grad_dst(const BwdArgs& a, float* base, float* rep, int
   if (i < nrep) return rep + ((size_t)(rep0 + i) * a.H + h) * width;
   return base + ((size_t)orow * a.H + h) * width;
 }
+
+// Phase 3 of a chunk with exact pairs: staging.  Channel c0 of pass hf, rows
+// r0 .. r0 + RPT - 1: Gam, q and k as read; on the first pass the waves of
+// the first column group also store their dP / dA blocks (tI, J <= tI) as
+// fp32 [i][j] (hi + lo of the B fragments, the values the factored path
+// uses; entries above the diagonal are never read).
+template <int BC, int D, int NS, int NE>
+__device__ inline void phase3_exact_stage(GradSmem<BC, D>& s, int hf, const float (&gm)[NE],
+                                          const float (&qq)[NE], const float (&kk)[NE],
+                                          const s16x4 (&Ph)[NS], const s16x4 (&Pl)[NS],
+                                          const s16x4 (&Ah)[NS], const s16x4 (&Al)[NS], int tI,
+                                          int tu) {
+  using G = GradGeom<BC, D>;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int c0 = tid % G::DH, r0 = (tid / G::DH) * G::RPT;
+#pragma unroll
+  for (int t = 0; t < G::RPT; ++t) {
+    const int n = hf * G::RPT + t, i = r0 + t;
+    s.u.e.gam[c0][i] = gm[n];
+    s.u.e.qf[c0][i] = qq[n];
+    s.u.e.kf[c0][i] = kk[n];
+  }
+  if (hf == 0 && tu == 0) {
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      if (sl <= tI) {   // tile (tI, J = sl) as [j][i]: lane holds j = 16 sl + 4 g + r, i = 16 tI + l16
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const int i = 16 * tI + l16;
+        // whole-vector bit casts (a cast of one vector element is not used)
+        const bf16x4 ph = __builtin_bit_cast(bf16x4, Ph[sl]), pl = __builtin_bit_cast(bf16x4, Pl[sl]);
+        const bf16x4 ah = __builtin_bit_cast(bf16x4, Ah[sl]), al = __builtin_bit_cast(bf16x4, Al[sl]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * sl + 4 * g + r;
+          s.u.e.dP[i][j] = bf16_val(ph[r]) + bf16_val(pl[r]);
+          s.u.e.dA[i][j] = bf16_val(ah[r]) + bf16_val(al[r]);
+        }
+      }
+    }
+  }
+}
+
+// Phase 3 of a chunk with exact pairs: the decay-weighted sums and the
+// combine of output tile C (channels 16 C ..) x row block tI, lane element
+// (channel 16 C + 4 g + r, row i = 16 tI + l16):
+//   rowP = sum_{j<i} dP_ij k_j e^(Gam_i-Gam_j)    rowA = sum_{j<i} dA_ij k_j e^(..)
+//   colP = sum_{j>i} dP_ji q_j e^(Gam_j-Gam_i)    colA = sum_{j>i} dA_ji k_j e^(..)
+// every exponent negative, and the pair (i, i) (factor 1) apart; then dq, dk
+// and dGam as in the factored path.  Terms whose decay spans no row -- the
+// pair (i, i) on both sides, and k e^(Gam_C - Gam) of the chunk's last row
+// against the Gam_C term -- cancel exactly in dGam and are left out of it:
+// with decays this strong dg itself is tiny, and their rounding would swamp it.
+template <int BC, int D>
+__device__ inline void phase3_exact_tile(const BwdArgs& a, GradSmem<BC, D>& s, int hf, int C,
+                                         int tI, const f32x4& dQt, const f32x4& dKt,
+                                         const f32x4& dKh, int rep0, int nrep, int len, int h) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const int cb = 16 * (C % 4), cf = 64 * hf + cb + 4 * g;
+  const int i = 16 * tI + l16;
+  float4 vq, vk;
+  float cs[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int cl = cb + 4 * g + r;
+    const float* Gc = &s.u.e.gam[cl][0];
+    const float* Kc = &s.u.e.kf[cl][0];
+    const float* Qc = &s.u.e.qf[cl][0];
+    const float gi = Gc[i];
+    float rowP = 0.f, rowA = 0.f, colP = 0.f, colA = 0.f;
+    for (int j = 0; j < BC; ++j) {
+      const float gj = Gc[j], kj = Kc[j], qj = Qc[j];
+      const float E = __expf(j < i ? gi - gj : gj - gi);
+      const float pr = s.u.e.dP[i][j], ar = s.u.e.dA[i][j];   // row side (j < i)
+      const float pc = s.u.e.dP[j][i], ac = s.u.e.dA[j][i];   // column side (j > i)
+      rowP += j < i ? pr * kj * E : 0.f;
+      rowA += j < i ? ar * kj * E : 0.f;
+      colP += j > i ? pc * qj * E : 0.f;
+      colA += j > i ? ac * kj * E : 0.f;
+    }
+    const float ki = Kc[i], qi = Qc[i];
+    const float dPii = s.u.e.dP[i][i];
+    const float eg = __expf(gi), ec = __expf(s.gcl[cf + r] - gi);
+    const float xq = dQt[r] * eg + rowP;
+    const float xk = dKt[r] * eg + rowA;
+    const float kh2 = i < len - 1 ? dKh[r] * ki * ec : 0.f;   // the last row's cancels
+    cs[r] = kh2;
+    s.u.e.dgam[cl][i] = qi * xq + ki * xk - kh2 - ki * (colP + colA);
+    (&vq.x)[r] = xq + dPii * ki;
+    (&vk.x)[r] = xk + dKh[r] * ec + colP + colA + dPii * qi;
+  }
+  if (i < len) {
+    const int orow = s.orow[i];
+    *(float4*)(grad_dst(a, a.dq, a.rep_dq, rep0, orow, i, nrep, h, D) + cf) = vq;
+    *(float4*)(grad_dst(a, a.dk, a.rep_dk, rep0, orow, i, nrep, h, D) + cf) = vk;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float x = row_sum16(cs[r]);
+    if (l16 == 0) s.csum[tI][cf + r] = x;
+  }
+}
+
+// A chunk also takes the exact phase 3 when some row decays by more than this
+// in one step: dg of such a row is of the order of e^-kExactStep times the
+// terms whose rounding the factored sums would leave in it.
+constexpr float kExactStep = 20.f;
 
 template <typename TIn, int BC, int D>
 __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
@@ -245,16 +365,19 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   for (int C = 0; C < NCB; ++C) dhraw[C] = *(const f16x4*)(dhsrc + state_tile<D>(C, wv));
 
   // ---- Gam: running sums per row group, then their prefix ----
+  bool steep = false;   // a single row decays by more than kExactStep
 #pragma unroll
   for (int hf = 0; hf < NHF; ++hf) {
     float run = 0.f;
 #pragma unroll
     for (int t = 0; t < RPT; ++t) {
+      steep |= gm[hf * RPT + t] < -kExactStep;
       run += gm[hf * RPT + t];
       gm[hf * RPT + t] = run;
     }
     s.part[rg][c0 + DH * hf] = run;
   }
+  if (tid == 0) s.bad = 0;
   __syncthreads();
 #pragma unroll
   for (int hf = 0; hf < NHF; ++hf) {
@@ -277,7 +400,10 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       }
       s.u.p.x.Kn[i][cc] = (_Float16)(-kk[n] * __expf(gm[n]));
     }
-    if (rg == 0) s.degc[cc] = __expf(tot);   // e^Gam_C until deGC is formed
+    if (rg == 0) {
+      s.degc[cc] = __expf(tot);   // e^Gam_C until deGC is formed
+      s.gcl[cc] = tot;
+    }
   }
   if (tid < BC) {
     s.orow[tid] = torow;
@@ -291,6 +417,15 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   }
   if (tid < BC * 2) *(f16x8*)&s.u.p.Td[tid / 2][(tid % 2) * 8] = tv;
   __syncthreads();
+  {  // decays past the factored range anywhere in the chunk: phase 3 takes exact pairs
+    bool bad = steep;
+#pragma unroll
+    for (int hf = 0; hf < NHF; ++hf)
+#pragma unroll
+      for (int t = 0; t < RPT; ++t)
+        bad |= s.gref[(r0 + t) >> 4][c0 + DH * hf] - gm[hf * RPT + t] > kExactDecay;
+    if (bad) s.bad = 1;
+  }
   // q (phase 3) through the input rows of the row table: addressed from LDS
   // after the barrier, these loads stay behind the prologue's, whose waits
   // then remain exact
@@ -511,10 +646,13 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   }
 
   // ---- phase 3: decay-weighted products and the combine, 64 channels per pass ----
+  const bool exact = s.bad != 0;   // block-uniform (set before two barriers)
 #pragma unroll
   for (int hf = 0; hf < NHF; ++hf) {
     __syncthreads();  // the previous phase's LDS readers are done
-    {  // staging: channel c0 of the pass, rows r0 .. r0 + RPT - 1
+    if (exact) {
+      phase3_exact_stage<BC, D>(s, hf, gm, qq, kk, Ph, Pl, Ah, Al, tI, tu);
+    } else {  // staging: channel c0 of the pass, rows r0 .. r0 + RPT - 1
       const int ch = DH * hf + c0;
       if constexpr (RPT == 8) {   // the thread's 8 rows are one 16-byte run of each [c][i] array
         bf16x8 rh8, rl8, qh8, ql8, kh8, kl8;
@@ -567,6 +705,14 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       }
     }
     __syncthreads();
+    if (exact) {
+#pragma unroll
+      for (int m = 0; m < NTW; ++m) {
+        const int C = tu + NG * m;
+        if (C < NCB && C / 4 == hf)
+          phase3_exact_tile<BC, D>(a, s, hf, C, tI, dQt[m], dKt[m], dKh[m], rep0, nrep, len, h);
+      }
+    } else {
 #pragma unroll
     for (int m = 0; m < NTW; ++m) {
       const int C = tu + NG * m;
@@ -640,14 +786,16 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
         }
       }
     }
+    }
     __syncthreads();
     // dg = reverse cumulative sum of dGam, the Gam_C terms entering at the last row
     const int ch = DH * hf + c0;
+    const float* dgr = exact ? &s.u.e.dgam[c0][0] : &s.u.d.gam[c0][0];
     float loc[RPT];
     float run = 0.f;
 #pragma unroll
     for (int t = RPT - 1; t >= 0; --t) {
-      run += s.u.d.gam[c0][r0 + t];
+      run += dgr[r0 + t];
       loc[t] = run;
     }
     s.part[rg][ch] = run;

@@ -16,7 +16,9 @@
 // kernels' sequential chain only copies an image and runs the state phase.
 // The state-dependent passes solve (I + diag(beta) A) delta = diag(beta) Z
 // (and its transpose) block by block with Td; the full inverse is never
-// formed.  Two blocks share a compute unit (63 KB of LDS, 128 registers).
+// formed.  Two blocks share a compute unit (70 KB of LDS, 128 registers).
+// Chunks with rows whose decay leaves the factored range (any g <= 0 is
+// accepted) recompute those rows' A and P pair by pair (chunk.h).
 #include "chunk.h"
 #include "timing.h"
 
@@ -31,6 +33,11 @@ struct PrepSmem {
       _Float16 A[BC][G::PB];
       _Float16 P[BC][G::PB];
     } o;
+    struct {                  // the exact path stages channels behind the outputs
+      _Float16 A[BC][G::PB];
+      _Float16 P[BC][G::PB];
+      float stage[3 * BC * 33];
+    } x;
   } u;
   ChunkTables<BC, D> tb;
   int irow[BC];   // input row of each chunk row (-1 past the chunk)
@@ -150,6 +157,12 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
     F->beta[tid] = s.tb.beta[tid];
     F->orow[tid] = s.tb.orow[tid];
   }
+  // rows past the factored decay range take exact pairs (their registers are
+  // free here: the element values have been stored)
+  if (s.tb.first_bad < BC)
+    chunk_AP_exact<TIn, BC, D>((const TIn*)a.q, (const TIn*)a.k, a.g, H, h, s.irow,
+                               s.tb.first_bad, s.u.x.stage, &s.u.o.A[0][0], G::PB,
+                               &s.u.o.P[0][0], G::PB);
   // A and P in 8-byte pieces, into their swizzled places
   for (int e = tid; e < BC * BC / 4; e += NT) {
     const int i = e / (BC / 4), j0 = (e % (BC / 4)) * 4;

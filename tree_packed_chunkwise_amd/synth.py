@@ -196,8 +196,13 @@ def make_kda_inputs(rng: np.random.Generator, n_rows: int, H: int, dk: int, dv: 
     beta-pre, g-pre, h0.
 
     Test-only variants: gate="weak" draws g = -softplus(N(-4,1)) (slow decay,
-    so boundary states stay visible), gate="zero" sets g = 0; beta_mode
-    "zero"/"one" pin beta; h0_mode="randn" draws h0 ~ N(0,1)/sqrt(dk)."""
+    so boundary states stay visible), gate="zero" sets g = 0, gate="strong"
+    draws g = -softplus(N(8,1)) (about 120 of decay over 15 rows), gate=
+    "extreme" g = -softplus(N(40,5)) (every row decays past fp32 range of
+    e^(15 g)), gate="mixed" draws each row (all heads and channels) from the
+    strong law with probability 1/8 and from the workload law otherwise;
+    beta_mode "zero"/"one" pin beta; h0_mode="randn" draws h0 ~
+    N(0,1)/sqrt(dk)."""
     f32 = np.float32
     q = _l2n(rng.standard_normal((n_rows, H, dk), dtype=f32))
     k = _l2n(rng.standard_normal((n_rows, H, dk), dtype=f32))
@@ -208,6 +213,14 @@ def make_kda_inputs(rng: np.random.Generator, n_rows: int, H: int, dk: int, dv: 
         g = -softplus(gpre - np.float32(4.0))
     elif gate == "zero":
         g = np.zeros_like(gpre)
+    elif gate == "strong":
+        g = -softplus(gpre + np.float32(8.0))
+    elif gate == "extreme":
+        g = -softplus(np.float32(5.0) * gpre + np.float32(40.0))
+    elif gate == "mixed":
+        strong = rng.random(n_rows) < 0.125
+        g = -softplus(gpre + np.where(strong, np.float32(8.0), np.float32(gate_mean))[:, None, None]
+                      .astype(np.float32))
     else:
         g = -softplus(gpre + np.float32(gate_mean))
     beta = 1.0 / (1.0 + np.exp(-bpre))
