@@ -367,6 +367,27 @@ int moe_router_stats(const void* logits, int32_t dtype, int64_t n_rows, int32_t 
                      size_t ws_bytes, void* stream);
 
 /*
+ * moe_router_stats_noalloc -- moe_router_stats without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and errors as moe_router_stats, bitwise the same
+ * results; the block partials go to a scratch array built into the library
+ * (8,404,992 bytes per device, the most any call needs: at most 2048 blocks
+ * of n_experts + 1 partials), held by each device the library runs on until
+ * the process ends; its device address is looked up on the first call on
+ * each device.  The call allocates nothing.  Every call on one device uses
+ * the same scratch (each call writes every partial before it reads it), so
+ * calls that overlap on one device -- on different streams, or from
+ * different threads without ordering -- race and must not be made.  Errors:
+ * as moe_router_stats; KDA_ERR_WORKSPACE if a call would need more scratch
+ * than the array holds, KDA_ERR_HIP if the scratch lookup fails.
+ */
+int moe_router_stats_noalloc(const void* logits, int32_t dtype, int64_t n_rows,
+                             int32_t n_experts, int32_t top_k, const int32_t* row_mult,
+                             int32_t* topk_idx, float* topk_prob, int64_t* load, float* psum,
+                             float* zsum, int64_t* n_tok, void* stream);
+
+/*
  * moe_router_stats_bwd -- gradient of L = <g_psum, psum> + g_z * zsum with
  * respect to the logits (top-k membership carries none):
  *   dlogits[r, :] = q_r * p_r * (g_psum - <p_r, g_psum> + 2 g_z lse_r),

@@ -42,7 +42,7 @@ EXPORTS = [
     "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
     "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "kda_state_copy",
     "kda_state_sum", "kda_set_overlap", "moe_router_workspace_bytes", "moe_router_stats",
-    "moe_router_stats_bwd", "kda_l1_plan",
+    "moe_router_stats_bwd", "kda_l1_plan", "moe_router_stats_noalloc",
 ]
 
 
@@ -99,6 +99,8 @@ def load_library(path: Path | str | None = None):
     L.moe_router_workspace_bytes.restype = sz
     L.moe_router_stats.argtypes = [vp, i32, i64, i32, i32] + [vp] * 8 + [sz, vp]
     L.moe_router_stats.restype = ctypes.c_int
+    L.moe_router_stats_noalloc.argtypes = [vp, i32, i64, i32, i32] + [vp] * 8
+    L.moe_router_stats_noalloc.restype = ctypes.c_int
     L.moe_router_stats_bwd.argtypes = [vp, i32, i64, i32, vp, vp, f32, vp, vp]
     L.moe_router_stats_bwd.restype = ctypes.c_int
     L.gather_logprobs.argtypes = [vp, i32, i64, i32, vp, vp, i64, vp, vp, vp]
@@ -537,6 +539,31 @@ def moe_router_stats(logits, row_mult, top_k: int, with_topk: bool = True):
                               _p(tp) if tp is not None else None, _p(out["load"]),
                               _p(out["psum"]), _p(out["zsum"]), _p(out["n_tok"]), _p(ws),
                               ws.numel(), _stream(logits)))
+    return out
+
+
+def moe_router_stats_noalloc(logits, row_mult, top_k: int, out: dict, with_topk: bool = True):
+    """moe_router_stats through the library's allocation-free entry point:
+    every output buffer is the caller's (out: load, psum, zsum, n_tok[,
+    topk_idx, topk_prob]); the scratch is the library's own."""
+    import torch
+    if logits is None or logits.dim() != 2:
+        raise KDAError("logits must be [rows, n_experts]")
+    n_rows, E = logits.shape
+    _expect("logits", logits, (n_rows, E), (torch.bfloat16, torch.float32))
+    _expect("row_mult", row_mult, (n_rows,), (torch.int32,))
+    _expect("load", out["load"], (E,), (torch.int64,))
+    _expect("psum", out["psum"], (E,), (torch.float32,))
+    _expect("zsum", out["zsum"], (1,), (torch.float32,))
+    _expect("n_tok", out["n_tok"], (1,), (torch.int64,))
+    ti = out.get("topk_idx") if with_topk else None
+    tp = out.get("topk_prob") if with_topk else None
+    _expect("topk_idx", ti, (n_rows, top_k), (torch.int32,), optional=True)
+    _expect("topk_prob", tp, (n_rows, top_k), (torch.float32,), optional=True)
+    _need_cuda(logits, row_mult, ti, tp, *[out[x] for x in ("load", "psum", "zsum", "n_tok")])
+    _check(load_library().moe_router_stats_noalloc(
+        _p(logits), _dtype_code(logits), n_rows, E, top_k, _p(row_mult), _p(ti), _p(tp),
+        _p(out["load"]), _p(out["psum"]), _p(out["zsum"]), _p(out["n_tok"]), _stream(logits)))
     return out
 
 

@@ -35,6 +35,7 @@ hipError_t launch_router_stats(const void* x, bool bf16, int64_t n_rows, int E, 
                                float* zsum, int64_t* n_tok, void* ws, hipStream_t st);
 hipError_t launch_router_bwd(const void* x, bool bf16, int64_t n_rows, int E, const int* q,
                              const float* g, float gz, float* dx, hipStream_t st);
+hipError_t router_scratch(void** ptr, size_t* bytes);
 int l1_plan(int32_t n, const int32_t* parent, const int32_t* seg_len, int64_t budget,
             std::vector<int32_t>& leaf_mb, std::vector<int64_t>& mb_unique,
             std::vector<int64_t>& mb_expanded, std::string& err);
@@ -467,6 +468,32 @@ int moe_router_stats(const void* logits, int32_t dtype, int64_t n_rows, int32_t 
                                           row_mult, topk_idx, topk_prob, load, psum, zsum, n_tok,
                                           ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "moe_router_stats launch");
+  return KDA_OK;
+}
+
+int moe_router_stats_noalloc(const void* logits, int32_t dtype, int64_t n_rows,
+                             int32_t n_experts, int32_t top_k, const int32_t* row_mult,
+                             int32_t* topk_idx, float* topk_prob, int64_t* load, float* psum,
+                             float* zsum, int64_t* n_tok, void* stream) {
+  if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_FP32) return fail(KDA_ERR_SHAPE, "dtype");
+  if (!router_shape_ok(n_experts)) return fail(KDA_ERR_SHAPE, "n_experts must be 64, 128, 256 or 512");
+  if (top_k < 1 || top_k > 32 || top_k > n_experts) return fail(KDA_ERR_SHAPE, "top_k");
+  if (n_rows < 0 || n_rows >= (int64_t)INT32_MAX) return fail(KDA_ERR_ARG, "bad n_rows");
+  if ((n_rows > 0 && (!logits || !row_mult)) || !load || !psum || !zsum || !n_tok)
+    return fail(KDA_ERR_ARG, "null argument");
+  void* ws = nullptr;
+  size_t cap = 0;
+  hipError_t e = kda::router_scratch(&ws, &cap);
+  if (e != hipSuccess) return hip_fail(e, "moe_router_stats_noalloc scratch lookup");
+  const size_t need = kda::router_ws_bytes(n_rows, n_experts);
+  if (need > cap)
+    return fail(KDA_ERR_WORKSPACE, "moe_router_stats_noalloc: " + std::to_string(need) +
+                                       " bytes of scratch needed, the built-in scratch holds " +
+                                       std::to_string(cap));
+  e = kda::launch_router_stats(logits, dtype == KDA_DTYPE_BF16, n_rows, n_experts, top_k, row_mult,
+                               topk_idx, topk_prob, load, psum, zsum, n_tok, ws,
+                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_router_stats_noalloc launch");
   return KDA_OK;
 }
 

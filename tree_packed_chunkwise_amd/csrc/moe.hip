@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "timing.h"
 
 namespace kda {
@@ -274,6 +276,34 @@ __global__ __launch_bounds__(MT) void k_router_bwd(const T* x, const int* q, int
 
 size_t router_ws_bytes(int64_t n_rows, int E) {
   return (size_t)router_blocks(n_rows) * (E + 1) * 8;
+}
+
+// Scratch of moe_router_stats_noalloc: the block partials of the largest
+// launch (2048 blocks, 512 experts), in a device array of the library, so
+// that the call allocates nothing.  Each device holds its own copy for the
+// life of the process; its address is looked up once per device (the name
+// itself is only a host-side handle).  Calls on one device share it.
+constexpr size_t kRouterScratchBytes = (size_t)2048 * (512 + 1) * 8;
+static __device__ __align__(256) unsigned char scratch[kRouterScratchBytes];
+
+hipError_t router_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {   // first call on this device, with it current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kRouterScratchBytes;
+  return hipSuccess;
 }
 
 hipError_t launch_router_stats(const void* x, bool bf16, int64_t n_rows, int E, int k,
