@@ -69,33 +69,47 @@ class _GatherRef(torch.autograd.Function):
         return torch.from_numpy(og.gather_bwd(ctx.z, ctx.pos_row, ctx.pos_tgt, _np(dlogp))), None, None
 
 
+def _round(x):
+    return torch.from_numpy(synth.round_bf16(x.detach().numpy().astype(np.float32))
+                            .astype(np.float64))
+
+
 def _bf16(x):
     """round to bf16 (RNE from the float32 value) without leaving autograd:
     the rounding is treated as identity in the backward, as on the GPU side."""
-    r = torch.from_numpy(synth.round_bf16(x.detach().numpy().astype(np.float32)).astype(np.float64))
-    return x + (r - x).detach()
+    return x + (_round(x) - x).detach()
 
 
-def reference_forward(params: dict, tree: Tree, tokens, pos_row, pos_tgt, H, D):
-    """params: float64 CPU leaf tensors named as HybridGroup's parameters."""
+
+def reference_forward(params: dict, tree: Tree, tokens, pos_row, pos_tgt, H, D,
+                      bf16_stream=False):
+    """params: float64 CPU leaf tensors named as HybridGroup's parameters.
+
+    bf16_stream=True rounds to bf16 wherever HybridGroup with dtype bf16
+    stores a bf16 tensor (every projection output, q and k after the L2
+    norm, the tree steps' outputs before their projection, the residual
+    stream after each add, the logits), the rounding being the identity in
+    the backward.  Otherwise only the tree attention inputs are rounded, as
+    in the fp32 group."""
     N = tokens.shape[0]
+    R = _bf16 if bf16_stream else (lambda t: t)
     x = params["embed"][tokens]
     scale = 1.0 / math.sqrt(D)
     i = 0
     while f"kda.{i}.wq" in params:
         P = lambda n: params[f"kda.{i}.{n}"]
-        q = torch.nn.functional.normalize((x @ P("wq")).view(N, H, D), dim=-1)
-        k = torch.nn.functional.normalize((x @ P("wk")).view(N, H, D), dim=-1)
-        v = (x @ P("wv")).view(N, H, D)
-        beta = torch.sigmoid(x @ P("wb"))
-        g = -torch.nn.functional.softplus((x @ P("wg")).view(N, H, D) + 2.0)
+        q = R(torch.nn.functional.normalize(R(x @ P("wq")).view(N, H, D), dim=-1))
+        k = R(torch.nn.functional.normalize(R(x @ P("wk")).view(N, H, D), dim=-1))
+        v = R(x @ P("wv")).view(N, H, D)
+        beta = torch.sigmoid(R(x @ P("wb")))
+        g = -torch.nn.functional.softplus(R(x @ P("wg")).view(N, H, D) + 2.0)
         o = _KDARef.apply(q, k, v, g, beta, tree, scale)
-        x = x + o.reshape(N, H * D) @ P("wo")
+        x = R(x + R(R(o).reshape(N, H * D) @ P("wo")))
         i += 1
-    q = _bf16((x @ params["attn.wq"]).view(N, H, D))
-    k = _bf16((x @ params["attn.wk"]).view(N, H, D))
-    v = _bf16((x @ params["attn.wv"]).view(N, H, D))
+    q = _bf16(R(x @ params["attn.wq"]).view(N, H, D))
+    k = _bf16(R(x @ params["attn.wk"]).view(N, H, D))
+    v = _bf16(R(x @ params["attn.wv"]).view(N, H, D))
     o = _AttnRef.apply(q, k, v, tree, scale)
-    x = x + o.reshape(N, H * D) @ params["attn.wo"]
-    logits = x @ params["lm"]
+    x = R(x + R(R(o).reshape(N, H * D) @ params["attn.wo"]))
+    logits = R(x @ params["lm"])
     return _GatherRef.apply(logits, pos_row, pos_tgt)

@@ -1,22 +1,21 @@
 """The hybrid layer group (3 KDA layers, one tree-attention layer, per-position
 log-prob gather) on the GPU against its float64 CPU reference composed from the
-oracle (tests/hybrid_ref.py), at a reduced size: per-position log-probs and
-the gradient of every parameter of sum(dlogp * logp).  The GPU side runs its
-stream and projections in fp32 here; tree attention takes bf16 q, k, v on
-both sides.
+oracle (tests/hybrid_ref.py), at a reduced size on whole small trees:
+per-position log-probs and the gradient of every parameter of
+sum(dlogp * logp).  The GPU side runs its stream and projections in fp32
+here; tree attention takes bf16 q, k, v on both sides.  (The hybrid
+workload's own shape and bf16 precision: tests/test_gpu_config4.py.)
 
-Bar: relative L2 <= 5e-3 per tensor (GROUP_TOL).  Each tree step is held to
-2e-3 against the oracle on identical inputs by its own tests; here four
-layers compose, each contributing about 1e-3 (the fp16 state products of the
-KDA layers), and the attention inputs are rounded to bf16 at a point that
-depends on that upstream error: a relative difference of 1e-3 in x moves a
-sizable share of q, k, v across bf16 rounding boundaries (one ulp is 2^-8
-relative), which adds about 1e-3 to the attention gradients.  Summed in
-quadrature the composed bound is about 3e-3; the bar leaves margin above it."""
+Bar: 2e-3 per tensor, except the gradients of the three attention input
+projections: q, k, v are rounded to bf16 where the GPU and reference streams
+differ by the KDA layers' error d (<= 4.5e-4 per call), so a share d / 2^-8
+of them round to the other bf16 neighbour: about sqrt(d 2^-8) = 1.3e-3 on
+q, k, v, passed on with a gain of about 2 -> 2e-3 + 2.6e-3, bar 5e-3
+(derivation and measurements at full size in test_gpu_config4.py)."""
 import numpy as np
 import pytest
 
-from gpu_cases import rel_l2
+from gpu_cases import TOL, rel_l2
 from hybrid_ref import reference_forward
 from oracle.tree import Tree
 from tree_packed_chunkwise_amd import binding as B
@@ -24,7 +23,7 @@ from tree_packed_chunkwise_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-GROUP_TOL = 5e-3
+ATTN_IN_TOL = 5e-3
 
 
 @pytest.mark.parametrize("kind", ["fig1", "random"])
@@ -54,5 +53,6 @@ def test_hybrid_group_parity(kind):
     for n, p in model.named_parameters():
         errs[n] = rel_l2(p.grad.cpu().numpy(), params[n].grad.numpy())
     print("  rel L2:", {n: f"{e:.1e}" for n, e in errs.items()}, flush=True)
-    bad = {n: e for n, e in errs.items() if not e <= GROUP_TOL}
+    tol = lambda n: ATTN_IN_TOL if n in ("attn.wq", "attn.wk", "attn.wv") else TOL
+    bad = {n: e for n, e in errs.items() if not e <= tol(n)}
     assert not bad, bad

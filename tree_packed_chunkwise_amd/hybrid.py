@@ -16,6 +16,10 @@ N(0, 1/fan_in).  Dense projections are torch matmuls (rocBLAS / hipBLASLt);
 the tree steps are autograd functions over the C-ABI calls.  `dtype` is the
 compute dtype of the stream and projections (bf16 for the benchmark, fp32 for
 parity runs); tree attention always takes bf16 q, k, v.
+
+`trace` (optional, a callable) receives every tree step's library inputs and
+outputs as they pass: trace(kind, layer, phase, tensors) with kind in
+{"kda", "attn", "gather"} and phase in {"fwd", "bwd"}.
 """
 from __future__ import annotations
 
@@ -28,49 +32,64 @@ from . import binding as B
 
 class _KDA(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, plan, scale):
+    def forward(ctx, q, k, v, g, beta, plan, scale, trace, layer):
         f = B.kda_tree_fwd(plan, q, k, v, g, beta, None, scale)
-        ctx.plan, ctx.scale = plan, scale
+        ctx.plan, ctx.scale, ctx.trace, ctx.layer = plan, scale, trace, layer
         ctx.save_for_backward(q, k, v, g, beta, f["saved"])
+        if trace:
+            trace("kda", layer, "fwd", dict(q=q, k=k, v=v, g=g, beta=beta, o=f["o"]))
         return f["o"]
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, g, beta, saved = ctx.saved_tensors
-        r = B.kda_tree_bwd(ctx.plan, q, k, v, g, beta, saved, do.to(q.dtype).contiguous(), None,
-                           None, ctx.scale)
+        dO = do.to(q.dtype).contiguous()
+        r = B.kda_tree_bwd(ctx.plan, q, k, v, g, beta, saved, dO, None, None, ctx.scale)
+        if ctx.trace:
+            ctx.trace("kda", ctx.layer, "bwd", dict(dO=dO, **{n: r[n] for n in (
+                "dq", "dk", "dv", "dg", "dbeta")}))
         return (r["dq"].to(q.dtype), r["dk"].to(k.dtype), r["dv"].to(v.dtype), r["dg"],
-                r["dbeta"], None, None)
+                r["dbeta"], None, None, None, None)
 
 
 class _Attn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, plan, scale):
+    def forward(ctx, q, k, v, plan, scale, trace):
         o, lse = B.tree_attn_fwd(plan, q, k, v, scale)
-        ctx.plan, ctx.scale = plan, scale
+        ctx.plan, ctx.scale, ctx.trace = plan, scale, trace
         ctx.save_for_backward(q, k, v, o, lse)
+        if trace:
+            trace("attn", 0, "fwd", dict(q=q, k=k, v=v, o=o, lse=lse))
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = B.tree_attn_bwd(ctx.plan, q, k, v, o, lse,
-                                     do.to(torch.bfloat16).contiguous(), ctx.scale)
-        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
+        dO = do.to(torch.bfloat16).contiguous()
+        dq, dk, dv = B.tree_attn_bwd(ctx.plan, q, k, v, o, lse, dO, ctx.scale)
+        if ctx.trace:
+            ctx.trace("attn", 0, "bwd", dict(dO=dO, dq=dq, dk=dk, dv=dv))
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None
 
 
 class _Gather(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, logits, pos_row, pos_tgt, row_pos_ptr, row_pos_idx):
+    def forward(ctx, logits, pos_row, pos_tgt, row_pos_ptr, row_pos_idx, trace):
         logp, lse = B.gather_logprobs(logits, pos_row, pos_tgt)
+        ctx.trace = trace
         ctx.save_for_backward(logits, lse, row_pos_ptr, row_pos_idx, pos_tgt)
+        if trace:
+            trace("gather", 0, "fwd", dict(logits=logits, logp=logp, lse=lse))
         return logp
 
     @staticmethod
     def backward(ctx, dlogp):
         logits, lse, rp_ptr, rp_idx, tgt = ctx.saved_tensors
-        dz = B.gather_logprobs_bwd(logits, lse, rp_ptr, rp_idx, tgt, dlogp.float().contiguous())
-        return dz, None, None, None, None
+        dl = dlogp.float().contiguous()
+        dz = B.gather_logprobs_bwd(logits, lse, rp_ptr, rp_idx, tgt, dl)
+        if ctx.trace:
+            ctx.trace("gather", 0, "bwd", dict(dlogp=dl, dlogits=dz))
+        return dz, None, None, None, None, None
 
 
 def _init(rng: torch.Generator, fan_in, shape, dtype, device):
@@ -103,31 +122,31 @@ class HybridGroup(torch.nn.Module):
             "wo": _init(g, hd, (hd, hidden), dtype, device)})
         self.lm = _init(g, hidden, (hidden, vocab), dtype, device)
 
-    def forward(self, plan, tokens, maps):
+    def forward(self, plan, tokens, maps, trace=None):
         """tokens [rows] int64 (compact rows); maps: device int32 tensors
         pos_row, pos_tgt, row_pos_ptr, row_pos_idx.  Returns logp [n_pos]."""
         N, H, D = tokens.shape[0], self.H, self.D
         x = self.embed[tokens]
         scale = 1.0 / math.sqrt(D)
-        for L in self.kda:
+        for li, L in enumerate(self.kda):
             q = torch.nn.functional.normalize((x @ L["wq"]).float().view(N, H, D), dim=-1)
             k = torch.nn.functional.normalize((x @ L["wk"]).float().view(N, H, D), dim=-1)
             v = (x @ L["wv"]).view(N, H, D)
             beta = torch.sigmoid((x @ L["wb"]).float()).contiguous()
             gate = -torch.nn.functional.softplus((x @ L["wg"]).float().view(N, H, D) + 2.0)
             o = _KDA.apply(q.to(self.dtype).contiguous(), k.to(self.dtype).contiguous(),
-                           v.contiguous(), gate.contiguous(), beta, plan, scale)
+                           v.contiguous(), gate.contiguous(), beta, plan, scale, trace, li)
             x = x + o.to(self.dtype).reshape(N, H * D) @ L["wo"]
         A = self.attn
         bf = torch.bfloat16
         q = (x @ A["wq"]).view(N, H, D).to(bf).contiguous()
         k = (x @ A["wk"]).view(N, H, D).to(bf).contiguous()
         v = (x @ A["wv"]).view(N, H, D).to(bf).contiguous()
-        o = _Attn.apply(q, k, v, plan, scale)
+        o = _Attn.apply(q, k, v, plan, scale, trace)
         x = x + o.to(self.dtype).reshape(N, H * D) @ A["wo"]
         logits = (x @ self.lm).contiguous()
         return _Gather.apply(logits, maps["pos_row"], maps["pos_tgt"], maps["row_pos_ptr"],
-                             maps["row_pos_idx"])
+                             maps["row_pos_idx"], trace)
 
 
 def gather_maps(plan: B.KDAPlan, tokens, device):
