@@ -254,11 +254,12 @@ def make_upstream(rng: np.random.Generator, n_out_rows: int, n_leaf: int, H: int
 
 
 def make_kda_inputs_device(seed: int, n_rows: int, H: int, dk: int, dv: int, device,
-                           bf16: bool = True):
+                           bf16: bool = True, gate: str = "default"):
     """The make_kda_inputs distributions drawn on a device with a seeded torch
     generator (for full-size workloads, whose host draws would take minutes):
     q,k ~ N(0,1) L2-normalised per head, v ~ N(0,1) (bf16 when bf16=True),
-    beta = sigmoid(N(0,1)), g = -softplus(N(2,1)) fp32.  Returns a dict of
+    beta = sigmoid(N(0,1)), g = -softplus(N(2,1)) fp32 (gate="weak":
+    -softplus(N(-4,1)); gate="strong": -softplus(N(8,1))).  Returns a dict of
     device tensors; draw order q, k, v, beta-pre, g-pre."""
     import torch
     gen = torch.Generator(device=device)
@@ -272,7 +273,8 @@ def make_kda_inputs_device(seed: int, n_rows: int, H: int, dk: int, dv: int, dev
     k = torch.nn.functional.normalize(randn(n_rows, H, dk), dim=-1).to(dt)
     v = randn(n_rows, H, dv).to(dt)
     beta = torch.sigmoid(randn(n_rows, H))
-    g = -torch.nn.functional.softplus(randn(n_rows, H, dk) + 2.0)
+    shift = {"default": 2.0, "weak": -4.0, "strong": 8.0}[gate]
+    g = -torch.nn.functional.softplus(randn(n_rows, H, dk) + shift)
     return dict(q=q, k=k, v=v, beta=beta, g=g, scale=1.0 / float(np.sqrt(dk)))
 
 
