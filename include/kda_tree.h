@@ -249,6 +249,12 @@ size_t kda_bwd_workspace_bytes(const kda_plan* plan, int32_t H, int32_t dk, int3
  *   h_leaf          [n_leaf,H,dk,dv] fp32 final state per leaf (leaves ascending)
  *   saved, saved_bytes  at least kda_saved_bytes(...) bytes, kept for kda_tree_bwd
  *   ws, ws_bytes    scratch of kda_fwd_workspace_bytes(...) bytes
+ * Precision: the state products run on fp16 matrix-core operands with fp32
+ * accumulation (the state itself stays fp32); the chunk start states kept in
+ * `saved` are fp16.  Values v and start states h0 of magnitude 2^-12 .. 2^12
+ * times unit scale keep the 2e-3 accuracy (the states then stay far inside
+ * fp16 range); far larger values overflow fp16 and far smaller ones lose
+ * precision.
  * Gates: any finite g <= 0.  The chunk math factors per-pair decays through
  * the first row of each 16-row block; rows whose decay from that row exceeds
  * 64 (from the first such row of a chunk on) take exact per-pair
@@ -293,6 +299,13 @@ int kda_set_overlap(int32_t enable);
  *   dh0        [n_root,H,dk,dv] fp32 gradient of each root state
  *   dh_boundary [n_buf,H,dk,dv] fp32 total gradient of each handoff state, or NULL
  *   ws, ws_bytes scratch of kda_bwd_workspace_bytes(...) bytes
+ * Range: the state gradients, the per-chunk dO and dy are fp16 matrix-core
+ * operands; the call first finds the largest |dO| * scale and |dh_leaf| and
+ * runs in units of a power of two that brings it to [8, 16), dividing every
+ * gradient by that power of two on output (exact).  Upstream gradients of
+ * any magnitude (a loss averaged over many positions, a scaled loss) give
+ * the same relative accuracy, and a call with dO and dh_leaf times 2^e
+ * returns exactly 2^e times the gradients.
  * Errors: as kda_tree_fwd.
  */
 int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t dk, int32_t dv,

@@ -218,3 +218,45 @@ def test_tree_equals_expanded_bitwise_strong_gates(gate):
     assert np.isfinite(tree["o"]).all()
     assert np.array_equal(exp["o"], tree["o"][row_index])
     assert np.array_equal(exp["h_leaf"], tree["h_leaf"])
+
+
+@pytest.mark.parametrize("e", [-24, -16, 12, 16, 24])
+@pytest.mark.parametrize("gate,leaf_grad", [("default", "randn"), ("weak", "zero")])
+def test_upstream_gradient_scale(e, gate, leaf_grad):
+    """The reverse pass runs in power-of-two units chosen from the largest
+    upstream gradient, so its fp16 intermediates keep their precision whether
+    the loss is averaged over many positions (tiny dO) or scaled up: with dO
+    and dh_leaf times 2^e every gradient is exactly 2^e times the unit-scale
+    run (bitwise), and within 2e-3 of the oracle."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    spec = synth.tree_random(rng, 9, 50, 400, n_roots=1)
+    t, inp, plan, dO, dhl = make_case(spec, 2, 128, True, 6, gate=gate, h0_mode="randn",
+                                      dh_leaf=leaf_grad, chunk=64)
+    s = float(2.0 ** e)
+    print(f"case gradient scale 2^{e} gate={gate} dh_leaf={leaf_grad}", flush=True)
+    base = gpu_run(plan, inp, dO, dhl)
+    got = gpu_run(plan, inp, synth.round_bf16((dO * s).astype(np.float32)), dhl * np.float32(s))
+    ref = oracle_tree(t, inp, dO, dhl, plan)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0", "dh_boundary"):
+        if got.get(n) is not None:
+            assert np.array_equal(got[n], base[n] * np.float32(s)), n
+    refs = {n: (v * s if n not in ("o", "h_leaf") else v) for n, v in ref.items()}
+    errs, bad = compare(got, refs, ALL)
+    print("  rel L2:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("e", [-12, 12])
+def test_value_range_of_the_forward(e):
+    """The forward keeps the state and the delta-rule writes in fp16 matrix-core
+    operands (fp32 accumulation): values v and start states h0 of magnitude
+    2^-12 .. 2^12 times unit scale stay within 2e-3 (the range the header
+    states)."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    spec = synth.tree_random(rng, 9, 50, 400, n_roots=1)
+    t, inp, plan, dO, dhl = make_case(spec, 2, 128, True, 6, gate="weak", h0_mode="randn",
+                                      chunk=64)
+    s = np.float32(2.0 ** e)
+    inp = synth.KDAInputs(q=inp.q, k=inp.k, v=synth.round_bf16(inp.v * s), g=inp.g,
+                          beta=inp.beta, h0=inp.h0 * s, scale=inp.scale, bf16=True)
+    _check(t, inp, plan, dO, dhl)

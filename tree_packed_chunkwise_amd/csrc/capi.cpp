@@ -133,10 +133,11 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
 
 // bwd workspace = [dO tiles per chunk-head (sized for fp32) | dy tiles | chunk
 //                  end-state gradients (fp16) | sequence start gradients |
-//                  replay-row gradients]
+//                  replay-row gradients | the largest |dO| and |dh_leaf|]
 struct BwdWS {
   float *dOp, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
   _Float16 *dy, *dhc;
+  unsigned* gmax;
 };
 BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) {
   Carver c(base);
@@ -152,6 +153,7 @@ BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) 
   w.rep_dg = c.take(nrep * H * D);
   w.rep_dv = c.take(nrep * H * D);
   w.rep_db = c.take(nrep * H);
+  w.gmax = (unsigned*)c.take(2);
   if (total) *total = c.off;
   return w;
 }
@@ -433,6 +435,7 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.slot = w.slot;
   a.rep_dq = w.rep_dq; a.rep_dk = w.rep_dk; a.rep_dg = w.rep_dg; a.rep_dv = w.rep_dv;
   a.rep_db = w.rep_db;
+  a.gmax = w.gmax;
   hipError_t e = kda::run_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_bwd launch");
   return KDA_OK;

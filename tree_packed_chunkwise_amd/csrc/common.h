@@ -113,7 +113,26 @@ struct BwdArgs {
   float* rep_dg;
   float* rep_dv;
   float* rep_db;          // [n_replay,H]
+  unsigned* gmax;         // [2] largest |dO| and |dh_leaf| (fp32 bits), see bwd_scale
 };
+
+// The reverse pass runs in units scaled by a power of two s, chosen from the
+// largest upstream gradient m = max(max|dO| * scale, max|dh_leaf|) so that
+// s m lies in [8, 16): the fp16 operands of the state-gradient products keep
+// their precision whatever the loss's scale (a loss averaged over many
+// positions has gradients far below fp16's normal range; a scaled one far
+// above it).  dO and dh_leaf enter multiplied by s, every gradient leaves
+// multiplied by 1 / s -- exact, s being a power of two.  s = 1 when every
+// upstream gradient is zero (or m is not finite).
+inline __device__ float bwd_scale(const unsigned* gmax, float scale) {
+  const float m = fmaxf(__uint_as_float(gmax[0]) * scale, __uint_as_float(gmax[1]));
+  if (!(m > 0.f) || !(m < INFINITY)) return 1.f;
+  int e = 0;
+  (void)frexpf(m, &e);    // m = f 2^e, f in [0.5, 1)
+  int k = 4 - e;
+  k = k < -120 ? -120 : (k > 120 ? 120 : k);
+  return ldexpf(1.f, k);
+}
 
 // Tree-ancestor attention (attn.hip): plan tables (see plan.h) and tensors.
 struct AttnArgs {

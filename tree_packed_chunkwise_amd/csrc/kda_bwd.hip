@@ -22,7 +22,7 @@
 // registers (MFMA accumulators reused as B operands, see chunk.h).  The
 // previous chunk's image is copied asynchronously into a second LDS buffer
 // (and its dO rows into registers) while the current chunk's state phase
-// runs.
+// runs.  Everything runs in the power-of-two units of bwd_scale (common.h).
 #include "chunk.h"
 #include "timing.h"
 
@@ -51,6 +51,11 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   const int cend = a.plan.seq_chunk_ptr[seq + 1];
   auto image = [&](int cc) { return a.fimg + ((size_t)cc * H + h) * fwd_image_bytes(BC, D); };
 
+  // gradients in units scaled by sg (bwd_scale): dO and dh_leaf enter
+  // scaled, the handoff-state gradients leave unscaled; the start-state
+  // slots, dy and the chunk-end dh stay scaled for the kernels after this one
+  const float sg = bwd_scale(a.gmax, a.scale), inv = 1.f / sg;
+  const float dscale = a.scale * sg;
   f32x4 dh[G::NCB];
   {
     const int leaf = a.plan.seq_leaf[seq];   // -1: the sequence ends at an inner segment
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
     for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        dh[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
+        dh[C][r] = (src && sw) ? sg * src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
   // dO of the chunk in flight, raw: this lane's accumulator piece of the
   // 16-row halves of every 32-deep k step, from the chunk's dO tiles (zero on
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
     for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) dof[ks][hf] = a.scale * in4_to_f32(dor[ks][hf]);
+      for (int hf = 0; hf < 2; ++hf) dof[ks][hf] = dscale * in4_to_f32(dor[ks][hf]);
     if (c > cbeg) {
       lds_copy_async(&buf[(cend - c) & 1], image(c - 1), NVEC);
       load_do(c - 1);
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
           for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = dh[C][r];
+            for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = inv * dh[C][r];
         }
       }
       {

@@ -208,7 +208,8 @@ __device__ inline void phase3_exact_stage(GradSmem<BC, D>& s, int hf, const floa
 template <int BC, int D>
 __device__ inline void phase3_exact_tile(const BwdArgs& a, GradSmem<BC, D>& s, int hf, int C,
                                          int tI, const f32x4& dQt, const f32x4& dKt,
-                                         const f32x4& dKh, int rep0, int nrep, int len, int h) {
+                                         const f32x4& dKh, int rep0, int nrep, int len, int h,
+                                         float inv) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int cb = 16 * (C % 4), cf = 64 * hf + cb + 4 * g;
   const int i = 16 * tI + l16;
@@ -245,8 +246,10 @@ __device__ inline void phase3_exact_tile(const BwdArgs& a, GradSmem<BC, D>& s, i
   }
   if (i < len) {
     const int orow = s.orow[i];
-    *(float4*)(grad_dst(a, a.dq, a.rep_dq, rep0, orow, i, nrep, h, D) + cf) = vq;
-    *(float4*)(grad_dst(a, a.dk, a.rep_dk, rep0, orow, i, nrep, h, D) + cf) = vk;
+    *(float4*)(grad_dst(a, a.dq, a.rep_dq, rep0, orow, i, nrep, h, D) + cf) =
+        make_float4(inv * vq.x, inv * vq.y, inv * vq.z, inv * vq.w);
+    *(float4*)(grad_dst(a, a.dk, a.rep_dk, rep0, orow, i, nrep, h, D) + cf) =
+        make_float4(inv * vk.x, inv * vk.y, inv * vk.z, inv * vk.w);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -285,7 +288,10 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   const TIn* dOp = (const TIn*)a.dOp;
   const FwdImage<BC, D, TIn>* F =
       (const FwdImage<BC, D, TIn>*)(a.fimg + blk * fwd_image_bytes(BC, D));
-  const float sc = a.scale;
+  // gradients in the power-of-two units of bwd_scale: dO enters scaled (dy and
+  // the end-state gradients come scaled), every gradient leaves times inv
+  const float sg = bwd_scale(a.gmax, a.scale), inv = 1.f / sg;
+  const float sc = a.scale * sg;
 
   // ---- global loads, issued in the order of their first use: loads return
   // in issue order, so each phase waits only for what it reads while the
@@ -519,7 +525,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
         const int i = 16 * I + 4 * g + r;
         const float dy = dyv[I][r], b = s.beta[i];
         ye[I][r] = dy * e[r];
-        if (i < len) grad_dst(a, a.dv, a.rep_dv, rep0, s.orow[i], i, nrep, h, D)[col] = b * dy;
+        if (i < len) grad_dst(a, a.dv, a.rep_dv, rep0, s.orow[i], i, nrep, h, D)[col] = inv * (b * dy);
         s.u.p.nZ[i][col] = (_Float16)(-b * dy);
         s.u.p.dl[i][col] = (_Float16)d[I][r];
       }
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   if (tid < BC && tid < len) {
     float acc = 0.f;
     for (int w = 0; w < NCB; ++w) acc += s.redb[w][tid];
-    *grad_dst(a, a.dbeta, a.rep_db, rep0, s.orow[tid], tid, nrep, h, 1) = acc;
+    *grad_dst(a, a.dbeta, a.rep_db, rep0, s.orow[tid], tid, nrep, h, 1) = inv * acc;
   }
   if (tid < D) {
     for (int I = 0; I < NB; ++I)
@@ -710,7 +716,8 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       for (int m = 0; m < NTW; ++m) {
         const int C = tu + NG * m;
         if (C < NCB && C / 4 == hf)
-          phase3_exact_tile<BC, D>(a, s, hf, C, tI, dQt[m], dKt[m], dKh[m], rep0, nrep, len, h);
+          phase3_exact_tile<BC, D>(a, s, hf, C, tI, dQt[m], dKt[m], dKh[m], rep0, nrep, len, h,
+                                   inv);
       }
     } else {
 #pragma unroll
@@ -776,8 +783,10 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
         }
         if (i < len) {
           const int orow = s.orow[i];
-          *(float4*)(grad_dst(a, a.dq, a.rep_dq, rep0, orow, i, nrep, h, D) + cf) = vq;
-          *(float4*)(grad_dst(a, a.dk, a.rep_dk, rep0, orow, i, nrep, h, D) + cf) = vk;
+          *(float4*)(grad_dst(a, a.dq, a.rep_dq, rep0, orow, i, nrep, h, D) + cf) =
+              make_float4(inv * vq.x, inv * vq.y, inv * vq.z, inv * vq.w);
+          *(float4*)(grad_dst(a, a.dk, a.rep_dk, rep0, orow, i, nrep, h, D) + cf) =
+              make_float4(inv * vk.x, inv * vk.y, inv * vk.z, inv * vk.w);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -808,7 +817,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
 #pragma unroll
     for (int t = 0; t < RPT; ++t) {
       const int i = r0 + t;
-      if (i < len) grad_dst(a, a.dg, a.rep_dg, rep0, s.orow[i], i, nrep, h, D)[ch] = loc[t] + tail;
+      if (i < len) grad_dst(a, a.dg, a.rep_dg, rep0, s.orow[i], i, nrep, h, D)[ch] = inv * (loc[t] + tail);
     }
   }
 }
