@@ -34,6 +34,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 
 
+def _progress(msg):
+    """A progress line on stderr (the result is the one JSON line on stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -46,6 +51,8 @@ def parse():
     ap.add_argument("--hybrid-steps", type=int, default=1,
                     help="timed steps of the hybrid layer group (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", dest="extra_configs", action="store_false",
+                    help="skip the forward-only and step-wise workloads and the gather")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel launch events in the timed region")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -202,11 +209,32 @@ def measure_window(w, dev, steps, ms_single):
             "vs_single_call": round(ms_single / ms, 3)}
 
 
+def method_bytes(name, info, H, D, in_bytes=2):
+    """Algorithmic bytes of all launches of a kernel class in one step, from
+    the method's own inputs and outputs per row (path_bytes_per_token): the
+    chunk-local gradient pass carries the reverse pass's input and output
+    traffic (q, k, v, g, beta re-read, dO read, dq, dk, dv, dg, dbeta
+    written) for every packed row (unique rows plus replayed rows); the
+    chunk pass carries the forward's input reads (q, k, v, g, beta) and the
+    forward rounds its output writes (o) plus the handoff and leaf states."""
+    P, Nrow = info["n_packed"], info["n_rows"]
+    fwd_b, bwd_b = path_bytes_per_token(H, D, in_bytes)
+    st = D * D * 4 * H
+    if name == "kda_bwd_chunk_grad":
+        return P * bwd_b
+    if name == "kda_chunk_decay":
+        return P * H * (3 * D * in_bytes + D * 4 + 4)
+    if name == "kda_fwd_round":
+        return Nrow * H * D * 4 + (info["n_buf"] + info["n_leaf"]) * st
+    return None
+
+
 def kernel_bytes(name, info, H, D, in_bytes=2):
-    """Algorithmic bytes of all launches of one kernel class in one step: the
-    tensors its role requires it to read and write once (documented per
-    kernel in the design doc).  P = packed rows (unique rows + replayed rows),
-    C = chunks, per head; states are D x D fp32."""
+    """Bytes of all launches of one kernel class in one step under this
+    design: what its role reads and writes once, including the design's own
+    intermediates (chunk images, fp16 per-chunk states, dy, dO tiles;
+    documented per kernel in the design doc).  P = packed rows (unique rows +
+    replayed rows), C = chunks, per head; states are D x D fp32."""
     P = info["n_packed"]
     Nrow = info["n_rows"]
     C = info["n_chunks"]
@@ -291,7 +319,17 @@ def cpu_baseline(spec, inp, dO, dhl_full, H, leaves):
     with ctx.Pool(cores) as pool:
         pool.map(_oracle_head, tasks)
     wall = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": n_sub / wall, "unit": "unique tokens/s", "cores": cores, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": model,
             "sample": (f"float64 numpy oracle forward+backward of all {H} heads (one process "
                        f"per head, {cores} workers) on a {n_sub}-row subtree of the workload "
                        f"tree (root, its first child and first grandchild, and that "
@@ -507,6 +545,230 @@ def measure_hybrid(steps):
         return {"error": repr(exc)}
 
 
+def expanded_batched(w, dev, steps, n_exp_rows, need_bytes, scale):
+    """Trajectory-expanded execution in batches of whole trajectories that
+    fit in device memory, times summed: each batch is the forest of its
+    trajectories' root paths run in EXPANDED mode (every trajectory its own
+    full-prefix sequence), on fresh inputs of the same distributions (the
+    timing does not depend on the values).  Returns (ms per step, batches)."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    H, D = w.H, w.dk
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    par = np.asarray(w.tree.parent)
+    lens = np.asarray(w.tree.seg_len, np.int64)
+    has_child = np.zeros(len(par), bool)
+    has_child[par[par >= 0]] = True
+    paths = []
+    for leaf in np.nonzero(~has_child)[0]:
+        p, x = [], int(leaf)
+        while x >= 0:
+            p.append(x)
+            x = int(par[x])
+        paths.append(p[::-1])
+    free, _ = torch.cuda.mem_get_info(dev)
+    cap = max(1, int(0.7 * free / (need_bytes / n_exp_rows)))   # expanded rows per batch
+    batches, cur, rows = [], [], 0
+    for p in paths:
+        t = int(lens[p].sum())
+        if cur and rows + t > cap:
+            batches.append(cur)
+            cur, rows = [], 0
+        cur.append(p)
+        rows += t
+    batches.append(cur)
+    total = 0.0
+    for bi, bp in enumerate(batches):
+        segs = sorted({x for p in bp for x in p})
+        idx = {x: j for j, x in enumerate(segs)}
+        sp = np.array([idx[int(par[x])] if par[x] >= 0 else -1 for x in segs], np.int32)
+        sl = lens[segs].astype(np.int32)
+        bplan = B.KDAPlan(sp, sl, None, w.chunk, B.EXPANDED)
+        bi_ = bplan.info
+        bin_ = synth.make_kda_inputs_device(7700 + bi, int(sl.sum()), H, D, D, dev, w.bf16)
+        mg = torch.Generator(device=dev)
+        mg.manual_seed(7800 + bi)
+        dOb = torch.randn((bi_["n_out_rows"], H, D), device=dev, generator=mg).to(dt)
+        dhb = torch.randn((bi_["n_leaf"], H, D, D), device=dev, generator=mg)
+        bfo = B.alloc_fwd(bplan, H, D, dev)
+        bbo = B.alloc_bwd(bplan, H, D, dev)
+
+        def bstep():
+            B.kda_tree_fwd(bplan, bin_["q"], bin_["k"], bin_["v"], bin_["g"], bin_["beta"],
+                           None, scale, out=bfo)
+            B.kda_tree_bwd(bplan, bin_["q"], bin_["k"], bin_["v"], bin_["g"], bin_["beta"],
+                           bfo["saved"], dOb, dhb, None, scale, out=bbo)
+        bstep()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            bstep()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1) / steps
+        del bfo, bbo, dOb, dhb, bin_
+        torch.cuda.empty_cache()
+    return total, len(batches)
+
+
+def expanded_need_bytes(w):
+    """Device bytes of one EXPANDED call of the whole tree (outputs, saved
+    state, workspaces, and the expanded copies of the inputs)."""
+    from tree_packed_chunkwise_amd import binding as B
+    H, D = w.H, w.dk
+    ep = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk, B.EXPANDED)
+    ei = ep.info
+    need = (ep.saved_bytes(H, D) + ep.fwd_ws_bytes(H, D) + ep.bwd_ws_bytes(H, D)
+            + ei["n_out_rows"] * H * D * (5 * 4 + 2) + ei["n_packed"] * H * D * 14)
+    return need, ei
+
+
+def _timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_config_forward(dev, steps, warmup):
+    """The forward-only workload on its own tree (complete 4-ary tree of depth
+    3 drawn with seed 1, U{256..2048} segments), one KDA layer forward, 16
+    heads, d = 128, bf16 q/k/v: unique tokens/s and the forward's roofline
+    (28,736 B per unique token at 16 heads plus the handoff and leaf
+    states)."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    try:
+        w = synth.workload(1)
+        H, D = w.H, w.dk
+        plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk)
+        info = plan.info
+        N = info["n_rows"]
+        inp = synth.make_kda_inputs_device(7300, N, H, D, D, dev, w.bf16)
+        fo = B.alloc_fwd(plan, H, D, dev)
+        fwd = lambda: B.kda_tree_fwd(plan, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                     None, inp["scale"], out=fo)
+        ms = _timed(fwd, steps, warmup)
+        fwd_b, _ = path_bytes_per_token(H, D, 2)
+        byts = N * fwd_b + (info["n_buf"] + info["n_leaf"]) * H * D * D * 4
+        ach = byts / (ms * 1e-3) / 1e9
+        return {"workload": w.name, "unique_rows": N, "expanded_rows": int(info["n_expanded"]),
+                "rounds": int(info["n_rounds"]), "replay_rows": int(info["R"]),
+                "ms_per_step": round(ms, 4), "unique_tokens_per_s": round(N / (ms * 1e-3), 1),
+                "path_roofline": {"bound": "hbm", "bytes_per_step": int(byts),
+                                  "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(ach / HBM_PEAK_GBS, 5)},
+                "finite": bool(torch.isfinite(fo["o"]).all())}
+    except Exception as exc:  # reported, never fatal to the headline line
+        return {"error": repr(exc)}
+
+
+def measure_config_stepwise(dev, steps, warmup, expanded_steps):
+    """The step-wise workload: 32,768-token trunk with 256 branches of 1-6
+    segments (U{128..1024} tokens), one KDA layer forward + backward, 16
+    heads, d = 128, bf16: unique tokens/s, the path roofline (86,208 B per
+    unique token plus states), and the speedup over trajectory-expanded
+    execution of the same tree (batched to fit device memory)."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    try:
+        w = synth.workload(3)
+        H, D = w.H, w.dk
+        plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk)
+        info = plan.info
+        N = info["n_rows"]
+        inp = synth.make_kda_inputs_device(7400, N, H, D, D, dev, w.bf16)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7401)
+        dO = torch.randn(N, H, D, generator=gen, device=dev).to(torch.bfloat16)
+        dhl = torch.randn(info["n_leaf"], H, D, D, generator=gen, device=dev)
+        fo = B.alloc_fwd(plan, H, D, dev)
+        bo = B.alloc_bwd(plan, H, D, dev)
+
+        def step():
+            B.kda_tree_fwd(plan, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], None,
+                           inp["scale"], out=fo)
+            B.kda_tree_bwd(plan, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], fo["saved"],
+                           dO, dhl, None, inp["scale"], out=bo)
+        ms = _timed(step, steps, warmup)
+        ok = bool(torch.isfinite(fo["o"]).all() and torch.isfinite(bo["dq"]).all())
+        fwd_b, bwd_b = path_bytes_per_token(H, D, 2)
+        st = H * D * D * 4
+        byts = N * (fwd_b + bwd_b) + (info["n_buf"] + info["n_leaf"]) * 2 * st
+        ach = byts / (ms * 1e-3) / 1e9
+        res = {"workload": w.name, "unique_rows": N, "expanded_rows": int(info["n_expanded"]),
+               "rounds": int(info["n_rounds"]), "replay_rows": int(info["R"]),
+               "sequences": int(info["n_seq"]),
+               "ms_per_step": round(ms, 4), "unique_tokens_per_s": round(N / (ms * 1e-3), 1),
+               "path_roofline": {"bound": "hbm", "bytes_per_step": int(byts),
+                                 "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(ach / HBM_PEAK_GBS, 5)},
+               "finite": ok}
+        del fo, bo, dO, dhl, inp
+        torch.cuda.empty_cache()
+        if expanded_steps > 0:
+            need, ei = expanded_need_bytes(w)
+            ems, nb = expanded_batched(w, dev, expanded_steps, int(ei["n_packed"]), need,
+                                       1.0 / float(np.sqrt(D)))
+            res["expanded"] = {"ms_per_step": round(ems, 3), "speedup": round(ems / ms, 3),
+                               "expanded_rows": int(ei["n_packed"]), "batches": nb,
+                               "note": "trajectory batches that fit device memory, times summed"}
+        return res
+    except Exception as exc:  # reported, never fatal to the headline line
+        return {"error": repr(exc)}
+
+
+def measure_gather(steps):
+    """gather_logprobs and its backward at vocabulary 32000 over the compact
+    rows of the hybrid workload's tree (bf16 logits, every trajectory
+    position): HBM-bound, the forward reads every logit once (plus the
+    position tables and outputs), the backward reads the logits and writes
+    their gradients once."""
+    import torch
+    from tree_packed_chunkwise_amd import binding as B
+    from tree_packed_chunkwise_amd import synth
+    try:
+        w = synth.workload(4)
+        plan = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, 64)
+        N, V, P = plan.info["n_rows"], 32000, plan.info["n_pos"]
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(14)
+        z = (3 * torch.randn(N, V, generator=gen, device="cuda")).to(torch.bfloat16)
+        tokens = torch.randint(0, V, (N,), generator=gen, device="cuda")
+        pos_row = plan.device_table("POS_ROW")
+        tgt = tokens[plan.device_table("POS_NEXT_ROW").long()].to(torch.int32).contiguous()
+        rp_ptr, rp_idx = plan.device_table("ROW_POS_PTR"), plan.device_table("ROW_POS_IDX")
+        dlogp = torch.randn(P, generator=gen, device="cuda")
+        logp, lse = B.gather_logprobs(z, pos_row, tgt)
+        dz = B.gather_logprobs_bwd(z, lse, rp_ptr, rp_idx, tgt, dlogp)
+        fms = _timed(lambda: B.gather_logprobs(z, pos_row, tgt, out=(logp, lse)), steps, 1)
+        bms = _timed(lambda: B.gather_logprobs_bwd(z, lse, rp_ptr, rp_idx, tgt, dlogp, out=dz),
+                     steps, 1)
+        fb = N * V * 2 + P * 12 + N * 4          # logits; pos_row, target, logp; lse
+        bb = 2 * N * V * 2 + N * 8 + P * 12      # logits in, gradients out; lse, CSR; dlogp, ...
+        fa, ba = fb / (fms * 1e-3) / 1e9, bb / (bms * 1e-3) / 1e9
+        roof = lambda a_, b_: {"bound": "hbm", "achieved": round(a_, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(a_ / HBM_PEAK_GBS, 4),
+                               "bytes_per_launch": int(b_)}
+        return {"workload": f"{w.tree.name} tree, {N} rows, {P} positions, vocab {V}, bf16 logits",
+                "fwd_ms": round(fms, 4), "bwd_ms": round(bms, 4),
+                "fwd_roofline": roof(fa, fb), "bwd_roofline": roof(ba, bb),
+                "expanded_logit_bytes_avoided": int((P - N) * V * 2)}
+    except Exception as exc:  # reported, never fatal to the headline line
+        return {"error": repr(exc)}
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -535,6 +797,7 @@ def main():
     # the CPU baseline runs first, in forked workers, before anything touches the GPU
     cpu = None
     if not a.no_cpu_baseline:
+        _progress("cpu baseline (oracle)")
         cpu = cpu_baseline(w.tree, inp, dO_np, dhl_np, H, list(plan.export("LEAF_SEG")))
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.bf16 else torch.float32
@@ -555,6 +818,7 @@ def main():
         B.kda_tree_fwd(plan, q, k, v, g, beta, None, inp.scale, out=fo)
         B.kda_tree_bwd(plan, q, k, v, g, beta, fo["saved"], dO, dhl, None, inp.scale, out=bo)
 
+    _progress(f"headline: {a.warmup} warmup + {a.steps} timed steps")
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -623,7 +887,8 @@ def main():
             kernels[name] = {"launches_per_step": per_step, "ms_per_step": tot / a.steps,
                              "avg_launch_ms": tot / max(cnt, 1)}
         dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
-        kb = kernel_bytes(dom, info, H, D, 2 if w.bf16 else 4)
+        kb = method_bytes(dom, info, H, D, 2 if w.bf16 else 4)
+        kd = kernel_bytes(dom, info, H, D, 2 if w.bf16 else 4)
         if kb is not None:
             lps = kernels[dom]["launches_per_step"]
             per_launch = kb / lps
@@ -631,6 +896,7 @@ def main():
             roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                     "traffic": measured_traffic(dom, a.workload), "bytes_per_launch": int(per_launch),
+                    "design_bytes_per_launch": int(kd / lps) if kd is not None else None,
                     "avg_launch_ms": round(kernels[dom]["avg_launch_ms"], 4),
                     "launches_per_step": lps}
             if dom in kt_seq:
@@ -681,79 +947,18 @@ def main():
         free, _ = torch.cuda.mem_get_info(dev)
         return need < 0.9 * free, mi
 
-    def expanded_batched(steps, n_exp_rows, need_bytes):
-        """Trajectory-expanded execution in batches of whole trajectories that
-        fit in device memory, times summed: each batch is the forest of its
-        trajectories' root paths run in EXPANDED mode (every trajectory its own
-        full-prefix sequence), on fresh inputs of the same distributions (the
-        timing does not depend on the values)."""
-        par = np.asarray(w.tree.parent)
-        lens = np.asarray(w.tree.seg_len, np.int64)
-        has_child = np.zeros(len(par), bool)
-        has_child[par[par >= 0]] = True
-        paths = []
-        for leaf in np.nonzero(~has_child)[0]:
-            p, x = [], int(leaf)
-            while x >= 0:
-                p.append(x)
-                x = int(par[x])
-            paths.append(p[::-1])
-        free, _ = torch.cuda.mem_get_info(dev)
-        cap = max(1, int(0.7 * free / (need_bytes / n_exp_rows)))   # expanded rows per batch
-        batches, cur, rows = [], [], 0
-        for p in paths:
-            t = int(lens[p].sum())
-            if cur and rows + t > cap:
-                batches.append(cur)
-                cur, rows = [], 0
-            cur.append(p)
-            rows += t
-        batches.append(cur)
-        total = 0.0
-        for bi, bp in enumerate(batches):
-            segs = sorted({x for p in bp for x in p})
-            idx = {x: j for j, x in enumerate(segs)}
-            sp = np.array([idx[int(par[x])] if par[x] >= 0 else -1 for x in segs], np.int32)
-            sl = lens[segs].astype(np.int32)
-            bplan = B.KDAPlan(sp, sl, None, w.chunk, B.EXPANDED)
-            bi_ = bplan.info
-            bin_ = synth.make_kda_inputs_device(7700 + bi, int(sl.sum()), H, D, D, dev, w.bf16)
-            mg = torch.Generator(device=dev)
-            mg.manual_seed(7800 + bi)
-            dOb = torch.randn((bi_["n_out_rows"], H, D), device=dev, generator=mg).to(dt)
-            dhb = torch.randn((bi_["n_leaf"], H, D, D), device=dev, generator=mg)
-            bfo = B.alloc_fwd(bplan, H, D, dev)
-            bbo = B.alloc_bwd(bplan, H, D, dev)
-
-            def bstep():
-                B.kda_tree_fwd(bplan, bin_["q"], bin_["k"], bin_["v"], bin_["g"], bin_["beta"],
-                               None, inp.scale, out=bfo)
-                B.kda_tree_bwd(bplan, bin_["q"], bin_["k"], bin_["v"], bin_["g"], bin_["beta"],
-                               bfo["saved"], dOb, dhb, None, inp.scale, out=bbo)
-            bstep()
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(steps):
-                bstep()
-            e1.record()
-            torch.cuda.synchronize()
-            total += e0.elapsed_time(e1) / steps
-            del bfo, bbo, dOb, dhb, bin_
-            torch.cuda.empty_cache()
-        return total, len(batches)
-
     expanded, modes = None, None
     if a.expanded_steps > 0:
+        _progress("trajectory-expanded run and plan modes")
         ok_e, ei = fits(B.EXPANDED)
         if ok_e:
             ems, ei = time_mode(B.EXPANDED, a.expanded_steps, 7)
             expanded = {"ms_per_step": round(ems, 3), "speedup": round(ems / ms, 3),
                         "expanded_rows": int(ei["n_packed"])}
         else:
-            ep = B.KDAPlan(w.tree.parent, w.tree.seg_len, w.tree.seg_row, w.chunk, B.EXPANDED)
-            need = (ep.saved_bytes(H, D) + ep.fwd_ws_bytes(H, D) + ep.bwd_ws_bytes(H, D)
-                    + ep.info["n_out_rows"] * H * D * (5 * 4 + 2) + ei["n_packed"] * H * D * 14)
-            ems, nb = expanded_batched(a.expanded_steps, int(ei["n_packed"]), need)
+            need, ei = expanded_need_bytes(w)
+            ems, nb = expanded_batched(w, dev, a.expanded_steps, int(ei["n_packed"]), need,
+                                       inp.scale)
             expanded = {"ms_per_step": round(ems, 3), "speedup": round(ems / ms, 3),
                         "expanded_rows": int(ei["n_packed"]),
                         "batches": nb, "note": "trajectory batches that fit device memory, "
@@ -772,12 +977,23 @@ def main():
                            "replay_rows": int(mi["R"]),
                            "unique_tokens_per_s": round(N / (mms / 1e3), 1)}
 
+    _progress("replay ablation, sharing window, attention, router, L1, hybrid group")
     ablation = replay_ablation(dev) if a.expanded_steps > 0 else None
     window = measure_window(w, dev, a.expanded_steps, ms) if a.expanded_steps > 0 else None
     attention = measure_attention(a.attn_steps) if a.attn_steps > 0 else None
     router = measure_router(10) if a.attn_steps > 0 else None
     l1plan = measure_l1()
     hybrid = measure_hybrid(a.hybrid_steps) if a.hybrid_steps > 0 else None
+    del fo, bo
+    torch.cuda.empty_cache()
+    cfg_fwd = cfg_step = gather = None
+    if a.workload == 2 and a.extra_configs:
+        _progress("forward-only workload")
+        cfg_fwd = measure_config_forward(dev, a.steps, a.warmup)
+        _progress("step-wise workload")
+        cfg_step = measure_config_stepwise(dev, max(3, a.steps // 4), 1, a.expanded_steps)
+        _progress("gather at vocabulary 32000")
+        gather = measure_gather(5)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "unique tokens/s", "n_gpus": 1,
@@ -803,6 +1019,7 @@ def main():
                                   for n, (c, t) in sorted(kt_seq.items())},
         "finite": ok,
         "tree_attention": attention, "hybrid_group": hybrid, "moe_router": router, "l1_planner": l1plan,
+        "config_forward": cfg_fwd, "config_stepwise": cfg_step, "gather": gather,
     }
     print(json.dumps(out), flush=True)
 

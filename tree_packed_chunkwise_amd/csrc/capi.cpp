@@ -98,6 +98,7 @@ kda::DevPlan make_dev_plan(const kda::Plan& p, const void* dev) {
   v.chunk_save = b + d.chunk_save;
   v.chunk_nrep = b + d.chunk_nrep;
   v.chunk_rep0 = b + d.chunk_rep0;
+  v.chunk_round = b + d.chunk_round;
   v.row_index = b + d.row_index;
   v.out_row = b + d.out_row;
   v.buf_cons_ptr = b + d.buf_cons_ptr;
@@ -133,7 +134,7 @@ SavedView carve_saved(const kda::Plan& p, int H, int D, void* base, size_t* tota
 
 // bwd workspace = [dO tiles per chunk-head (sized for fp32) | dy tiles | chunk
 //                  end-state gradients (fp16) | sequence start gradients |
-//                  replay-row gradients | the largest |dO| and |dh_leaf|]
+//                  replay-row gradients | gradient-scale words (common.h)]
 struct BwdWS {
   float *dOp, *slot, *rep_dq, *rep_dk, *rep_dg, *rep_dv, *rep_db;
   _Float16 *dy, *dhc;
@@ -153,7 +154,7 @@ BwdWS carve_bwd_ws(const kda::Plan& p, int H, int D, void* base, size_t* total) 
   w.rep_dg = c.take(nrep * H * D);
   w.rep_dv = c.take(nrep * H * D);
   w.rep_db = c.take(nrep * H);
-  w.gmax = (unsigned*)c.take(2);
+  w.gmax = (unsigned*)c.take(kda::scale_words(p.n_rounds));
   if (total) *total = c.off;
   return w;
 }
@@ -436,6 +437,7 @@ int kda_tree_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t 
   a.rep_dq = w.rep_dq; a.rep_dk = w.rep_dk; a.rep_dg = w.rep_dg; a.rep_dv = w.rep_dv;
   a.rep_db = w.rep_db;
   a.gmax = w.gmax;
+  a.n_rounds = p.n_rounds;
   hipError_t e = kda::run_bwd(a, in_dtype == KDA_DTYPE_BF16, p.B, dk, p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kda_tree_bwd launch");
   return KDA_OK;

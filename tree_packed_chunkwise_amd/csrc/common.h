@@ -21,6 +21,7 @@ struct DevPlan {
   const int* chunk_save;
   const int* chunk_nrep;
   const int* chunk_rep0;
+  const int* chunk_round;
   const int* row_index;
   const int* out_row;
   const int* buf_cons_ptr;
@@ -113,25 +114,58 @@ struct BwdArgs {
   float* rep_dg;
   float* rep_dv;
   float* rep_db;          // [n_replay,H]
-  unsigned* gmax;         // [2] largest |dO| and |dh_leaf| (fp32 bits), see bwd_scale
+  int n_rounds;
+  unsigned* gmax;         // [scale_words(n_rounds)] gradient-scale words (fp32 bits), see below
 };
 
-// The reverse pass runs in units scaled by a power of two s, chosen from the
-// largest upstream gradient m = max(max|dO| * scale, max|dh_leaf|) so that
-// s m lies in [8, 16): the fp16 operands of the state-gradient products keep
-// their precision whatever the loss's scale (a loss averaged over many
-// positions has gradients far below fp16's normal range; a scaled one far
-// above it).  dO and dh_leaf enter multiplied by s, every gradient leaves
-// multiplied by 1 / s -- exact, s being a power of two.  s = 1 when every
-// upstream gradient is zero (or m is not finite).
-inline __device__ float bwd_scale(const unsigned* gmax, float scale) {
-  const float m = fmaxf(__uint_as_float(gmax[0]) * scale, __uint_as_float(gmax[1]));
+// The reverse pass runs each round in units scaled by a power of two s_r,
+// chosen so that the largest upstream gradient the round takes in lies in
+// [8, 16): the fp16 operands of the state-gradient products then keep their
+// precision whatever the loss's scale (a loss averaged over many positions
+// has gradients far below fp16's normal range, a scaled one far above it).
+// The gradients a round takes in: its chunks' dO (times scale), the leaf
+// states' gradients, and the start-state gradients of the sequences of later
+// rounds that started from its handoff states.  Those and every gradient
+// leave a round unscaled (fp32), so each round may have its own s_r.
+// Maxima are kept as fp32 bits (non-negative floats order like their bits,
+// so an integer atomic max gives the maximum in any order), each spread over
+// SPREAD words (a writer picks one by its block index, so that atomics to
+// one address do not queue up; a reader takes the maximum of all of them).
+// Words of gmax, R = n_rounds:
+//   [0, S)                       max |dh_leaf|
+//   [S + r S, S + (r + 1) S)     max |dO| over the chunks of round r  (the dO gather)
+//   [S + R S + r S, ...)         max |start-state gradient| written by round r
+//   [S + 2 R S + r]              max over the start-state words of rounds r' > r (round r)
+//   [S + 2 R S + R + r]          s_r                                  (round r)
+constexpr int SPREAD = 64;
+constexpr __host__ __device__ size_t scale_words(int R) { return (size_t)SPREAD * (1 + 2 * R) + 2 * R; }
+__device__ inline unsigned* leaf_words(unsigned* g) { return g; }
+__device__ inline unsigned* dO_words(unsigned* g, int r) { return g + SPREAD * (1 + r); }
+__device__ inline unsigned* slot_words(unsigned* g, int R, int r) { return g + SPREAD * (1 + R + r); }
+__device__ inline unsigned* suffix_word(unsigned* g, int R, int r) { return g + SPREAD * (1 + 2 * R) + r; }
+__device__ inline unsigned* scale_word(unsigned* g, int R, int r) { return g + SPREAD * (1 + 2 * R) + R + r; }
+// maximum of SPREAD words, by one whole wave (every lane returns it)
+__device__ inline float spread_max(const unsigned* w) {
+  float m = __uint_as_float(w[threadIdx.x & 63]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+inline __device__ float pow2_scale(float m) {
   if (!(m > 0.f) || !(m < INFINITY)) return 1.f;
   int e = 0;
   (void)frexpf(m, &e);    // m = f 2^e, f in [0.5, 1)
   int k = 4 - e;
   k = k < -120 ? -120 : (k > 120 ? 120 : k);
   return ldexpf(1.f, k);
+}
+// the scale of round r, by whole waves of the round's own kernel; `later`
+// receives the maximum over the later rounds' start-state gradients
+inline __device__ float round_scale(unsigned* gm, int R, int r, float attn_scale, float* later) {
+  float suf = 0.f;
+  if (r + 1 < R) suf = fmaxf(__uint_as_float(*suffix_word(gm, R, r + 1)), spread_max(slot_words(gm, R, r + 1)));
+  *later = suf;
+  return pow2_scale(fmaxf(fmaxf(spread_max(dO_words(gm, r)) * attn_scale, spread_max(leaf_words(gm))), suf));
 }
 
 // Tree-ancestor attention (attn.hip): plan tables (see plan.h) and tensors.

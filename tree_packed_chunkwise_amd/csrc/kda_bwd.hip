@@ -22,14 +22,17 @@
 // registers (MFMA accumulators reused as B operands, see chunk.h).  The
 // previous chunk's image is copied asynchronously into a second LDS buffer
 // (and its dO rows into registers) while the current chunk's state phase
-// runs.  Everything runs in the power-of-two units of bwd_scale (common.h).
+// runs.  Each round runs in the power-of-two units of round_scale (common.h).
 #include "chunk.h"
 #include "timing.h"
 
 namespace kda {
 
+__device__ inline float in_f32(float x) { return x; }
+__device__ inline float in_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
 template <typename TIn, int BC, int D, int NV>
-__global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
+__global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int round) {
   using G = Geom<BC, D>;
   using BI = FwdHead<BC, D>;
   static_assert(NV <= NW, "one column block per wave");
@@ -51,11 +54,6 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
   const int cend = a.plan.seq_chunk_ptr[seq + 1];
   auto image = [&](int cc) { return a.fimg + ((size_t)cc * H + h) * fwd_image_bytes(BC, D); };
 
-  // gradients in units scaled by sg (bwd_scale): dO and dh_leaf enter
-  // scaled, the handoff-state gradients leave unscaled; the start-state
-  // slots, dy and the chunk-end dh stay scaled for the kernels after this one
-  const float sg = bwd_scale(a.gmax, a.scale), inv = 1.f / sg;
-  const float dscale = a.scale * sg;
   f32x4 dh[G::NCB];
   {
     const int leaf = a.plan.seq_leaf[seq];   // -1: the sequence ends at an inner segment
@@ -64,7 +62,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
     for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        dh[C][r] = (src && sw) ? sg * src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
+        dh[C][r] = (src && sw) ? src[(size_t)(16 * C + 4 * g + r) * D + col] : 0.f;
   }
   // dO of the chunk in flight, raw: this lane's accumulator piece of the
   // 16-row halves of every 32-deep k step, from the chunk's dO tiles (zero on
@@ -85,6 +83,20 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
     lds_copy_async(&buf[0], image(cend - 1), NVEC);
     load_do(cend - 1);
   }
+  // the round's gradients in units scaled by sg (round_scale, common.h): dO,
+  // dh_leaf and later rounds' start-state gradients enter scaled, the
+  // handoff-state and start-state gradients leave unscaled; dy and the
+  // chunk-end dh stay scaled for the chunk-local pass (which reads sg back).
+  // Its words are read behind the first chunk's loads.
+  float later = 0.f;
+  const float sg = round_scale(a.gmax, a.n_rounds, round, a.scale, &later), inv = 1.f / sg;
+  const float dscale = a.scale * sg;
+  if (blockIdx.x == 0 && blockIdx.z == 0 && tid == 0) {
+    *suffix_word(a.gmax, a.n_rounds, round) = __float_as_uint(later);
+    *scale_word(a.gmax, a.n_rounds, round) = __float_as_uint(sg);
+  }
+#pragma unroll
+  for (int C = 0; C < G::NCB; ++C) dh[C] *= sg;
   for (int c = cend - 1; c >= cbeg; --c) {
     const int row0 = a.plan.chunk_row0[c];
     const int len = a.plan.chunk_len[c];
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 #pragma unroll
           for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dh[C][r] += src[(size_t)(16 * C + 4 * g + r) * D + col];
+            for (int r = 0; r < 4; ++r) dh[C][r] += sg * src[(size_t)(16 * C + 4 * g + r) * D + col];
         }
         if (a.dh_boundary) {
           float* dst = a.dh_boundary + ((size_t)save * H + h) * DD;
@@ -227,12 +239,22 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
       }
     }
   }
-  if (sw) {
+  if (sw) {   // the start-state gradient, unscaled, and its largest magnitude
     float* dst = a.slot + ((size_t)seq * H + h) * DD;
+    float mx = 0.f;
 #pragma unroll
     for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * C + 4 * g + r) * D + col] = dh[C][r];
+      for (int r = 0; r < 4; ++r) {
+        const float x = inv * dh[C][r];
+        dst[(size_t)(16 * C + 4 * g + r) * D + col] = x;
+        mx = fmaxf(mx, fabsf(x));
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0 && mx > 0.f)
+      atomicMax(slot_words(a.gmax, a.n_rounds, round) + (blockIdx.x * NW + wave) % SPREAD,
+                __float_as_uint(mx));
   }
 }
 
@@ -243,23 +265,36 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin) {
 // tiles are written in their own order (a wave per contiguous tile).
 template <typename TIn, int BC, int D>
 __global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, DevPlan plan, int H, TIn* dOp,
-                                                   int c_begin) {
+                                                   int c_begin, unsigned* gmax) {
   constexpr int PER = 16 / (int)sizeof(TIn);  // elements per 16-byte piece: 8 or 4
   constexpr int PPR = D / PER;                // pieces per row
   constexpr int PITCH = D + PER;              // LDS row pitch, padded by one piece
   using V = TIn __attribute__((ext_vector_type(PER)));
   using V4 = in4_t<TIn>;
   __shared__ __attribute__((aligned(16))) TIn rowsm[BC * PITCH];
+  __shared__ float wmax[4];
   const int c = c_begin + blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int row0 = plan.chunk_row0[c], len = plan.chunk_len[c];
+  float mx = 0.f;   // largest |dO| of the chunk-head, for its round's gradient scale
   for (int p = tid; p < BC * PPR; p += 256) {
     const int i = p / PPR, j = p % PPR;
     const int o = i < len ? plan.out_row[row0 + i] : -1;
     V x = (V)0;
     if (o >= 0) x = *(const V*)&dO[((size_t)o * H + h) * D + j * PER];
     *(V*)&rowsm[i * PITCH + j * PER] = x;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) mx = fmaxf(mx, fabsf(in_f32(x[e])));
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) wmax[tid >> 6] = mx;
   __syncthreads();
+  if (tid == 0) {
+    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (mx > 0.f)
+      atomicMax(dO_words(gmax, plan.chunk_round[c]) + (blockIdx.x + 7 * blockIdx.y) % SPREAD,
+                __float_as_uint(mx));
+  }
   TIn* dst = dOp + ((size_t)c * H + h) * (BC * D);
   for (int q = tid; q < BC * D / 4; q += 256) {   // lane l of tile t: its accumulator piece
     const int t = q >> 6, l = q & 63;
@@ -279,7 +314,7 @@ hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int c_be
 #define KDA_GDO(T, BCv, Dv)                                                                    \
   if (BC == BCv && D == Dv) {                                                                  \
     KDA_LAUNCH("kda_bwd_gather_dO", (k_gather_dO<T, BCv, Dv>), dim3(n_chunks, a.H), dim3(256), \
-               st, (const T*)a.dO, a.plan, a.H, (T*)a.dOp, c_begin);                           \
+               st, (const T*)a.dO, a.plan, a.H, (T*)a.dOp, c_begin, a.gmax);                   \
     return hipGetLastError();                                                                  \
   }
   if (bf16) {
@@ -295,9 +330,10 @@ hipError_t launch_gather_dO(const BwdArgs& a, bool bf16, int BC, int D, int c_be
 int round_slices(int nseq, int H, int D, int max_slices);
 
 template <typename TIn, int BC, int D, int NV>
-hipError_t launch_bround(const BwdArgs& a, int nseq, int seq0, int slices, hipStream_t st) {
+hipError_t launch_bround(const BwdArgs& a, int nseq, int seq0, int round, int slices,
+                         hipStream_t st) {
   KDA_LAUNCH("kda_bwd_round", (k_bwd_round<TIn, BC, D, NV>), dim3(nseq * a.H, 1, slices), dim3(NT),
-             st, a, seq0);
+             st, a, seq0, round);
   return hipGetLastError();
 }
 
@@ -311,10 +347,10 @@ hipError_t launch_brounds_t(const BwdArgs& a, const int* round_ptr_host, int r_b
     const int sl = round_slices(nseq, a.H, D, max_slices);
     const int nv = NCB / sl;
     hipError_t e = hipErrorInvalidValue;
-    if (nv == NCB) e = launch_bround<TIn, BC, D, NCB>(a, nseq, round_ptr_host[r], sl, st);
-    else if (nv == 4) e = launch_bround<TIn, BC, D, 4>(a, nseq, round_ptr_host[r], sl, st);
-    else if (nv == 2) e = launch_bround<TIn, BC, D, 2>(a, nseq, round_ptr_host[r], sl, st);
-    else if (nv == 1) e = launch_bround<TIn, BC, D, 1>(a, nseq, round_ptr_host[r], sl, st);
+    if (nv == NCB) e = launch_bround<TIn, BC, D, NCB>(a, nseq, round_ptr_host[r], r, sl, st);
+    else if (nv == 4) e = launch_bround<TIn, BC, D, 4>(a, nseq, round_ptr_host[r], r, sl, st);
+    else if (nv == 2) e = launch_bround<TIn, BC, D, 2>(a, nseq, round_ptr_host[r], r, sl, st);
+    else if (nv == 1) e = launch_bround<TIn, BC, D, 1>(a, nseq, round_ptr_host[r], r, sl, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -288,10 +288,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   const TIn* dOp = (const TIn*)a.dOp;
   const FwdImage<BC, D, TIn>* F =
       (const FwdImage<BC, D, TIn>*)(a.fimg + blk * fwd_image_bytes(BC, D));
-  // gradients in the power-of-two units of bwd_scale: dO enters scaled (dy and
-  // the end-state gradients come scaled), every gradient leaves times inv
-  const float sg = bwd_scale(a.gmax, a.scale), inv = 1.f / sg;
-  const float sc = a.scale * sg;
+  const int cround = a.plan.chunk_round[c];
 
   // ---- global loads, issued in the order of their first use: loads return
   // in issue order, so each phase waits only for what it reads while the
@@ -423,6 +420,13 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   }
   if (tid < BC * 2) *(f16x8*)&s.u.p.Td[tid / 2][(tid % 2) * 8] = tv;
   __syncthreads();
+  // gradients in the power-of-two units of the chunk's round (round_scale,
+  // stored by the round's reverse pass): dO enters scaled (dy and the
+  // end-state gradients come scaled), every gradient leaves times inv.  Read
+  // here, behind the prologue's loads and ahead of q's.
+  const float sg = __uint_as_float(*scale_word(a.gmax, a.n_rounds, cround));
+  const float inv = 1.f / sg;
+  const float sc = a.scale * sg;
   {  // decays past the factored range anywhere in the chunk: phase 3 takes exact pairs
     bool bad = steep;
 #pragma unroll

@@ -6,8 +6,8 @@
 //   - dh0 of every root: the sum of the start-state gradients of the
 //     sequences that start from it.
 // Both reductions add in a fixed order, so results do not depend on timing.
-// Also the pass before the rounds that finds the reverse call's power-of-two
-// scale (the largest upstream gradient, bwd_scale in common.h).
+// Also the pass before the rounds that clears the reverse call's
+// gradient-scale words and finds the largest leaf-state gradient (common.h).
 #include "common.h"
 #include "timing.h"
 
@@ -54,7 +54,6 @@ __global__ __launch_bounds__(BT) void k_reduce_dh0(BwdArgs a) {
   const int rh = blockIdx.y, H = a.H, rt = rh / H, h = rh % H;
   const int e4 = blockIdx.x * BT + threadIdx.x;   // grid.x * BT == DD4
   const int p0 = a.plan.root_seq_ptr[rt], p1 = a.plan.root_seq_ptr[rt + 1];
-  const float inv = 1.f / bwd_scale(a.gmax, a.scale);   // the slots are in scaled units
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int p = p0; p < p1; ++p) {
     const float4 x = ((const float4*)(a.slot + ((size_t)a.plan.root_seq[p] * H + h) * (4 * DD4)))[e4];
@@ -63,66 +62,54 @@ __global__ __launch_bounds__(BT) void k_reduce_dh0(BwdArgs a) {
     acc.z += x.z;
     acc.w += x.w;
   }
-  ((float4*)(a.dh0 + ((size_t)rt * H + h) * (4 * DD4)))[e4] =
-      make_float4(inv * acc.x, inv * acc.y, inv * acc.z, inv * acc.w);
+  ((float4*)(a.dh0 + ((size_t)rt * H + h) * (4 * DD4)))[e4] = acc;
 }
 
-// The largest |dO| and |dh_leaf| of a reverse call (bwd_scale, common.h):
-// 16-byte loads, a wave maximum, one integer atomic max per wave on the fp32
-// bits (non-negative floats order like their bits, and a maximum does not
-// depend on the order of the updates, so the result is deterministic).
-__global__ __launch_bounds__(64) void k_zero_gmax(unsigned* gmax) {
-  if (threadIdx.x < 2) gmax[threadIdx.x] = 0u;
+// The gradient-scale words of a reverse call (common.h): cleared, then the
+// largest |dh_leaf| (16-byte loads, four in flight per thread, a block
+// maximum, one integer atomic max per block on a spread word).
+__global__ __launch_bounds__(BT) void k_zero_words(unsigned* w, int n) {
+  for (int i = threadIdx.x; i < n; i += BT) w[i] = 0u;
 }
 
-__device__ inline float elem_f32(float x) { return x; }
-__device__ inline float elem_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-template <typename TIn>
-__global__ __launch_bounds__(BT) void k_absmax(const TIn* dO, size_t n_do, const float* dhl,
-                                               size_t n_dhl, unsigned* gmax) {
-  typedef __attribute__((__vector_size__(16))) unsigned u4;
-  constexpr int PER = 16 / (int)sizeof(TIn);
-  const size_t stride = (size_t)gridDim.x * BT, t0 = (size_t)blockIdx.x * BT + threadIdx.x;
-  float m0 = 0.f, m1 = 0.f;
-  for (size_t i = t0; i < n_do / PER; i += stride) {
-    const u4 v = ((const u4*)dO)[i];
-    const TIn* e = (const TIn*)&v;
+__global__ __launch_bounds__(BT) void k_leaf_absmax(const float* dhl, size_t n, unsigned* gmax) {
+  constexpr int U = 4;
+  __shared__ float red[BT / 64];
+  const size_t stride = (size_t)gridDim.x * BT * U;
+  const size_t t0 = (size_t)blockIdx.x * BT * U + threadIdx.x;
+  const float4* s4 = (const float4*)dhl;
+  const size_t n4 = n / 4;
+  float m = 0.f;
+  for (size_t i = t0; i < n4; i += stride) {
+    float4 v[U];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) m0 = fmaxf(m0, fabsf(elem_f32(e[j])));
-  }
-  if (dhl) {
-    for (size_t i = t0; i < n_dhl / 4; i += stride) {
-      const float4 v = ((const float4*)dhl)[i];
-      m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
+    for (int u = 0; u < U; ++u)
+      v[u] = i + (size_t)u * BT < n4 ? s4[i + (size_t)u * BT] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    m0 = fmaxf(m0, __shfl_xor(m0, o));
-    m1 = fmaxf(m1, __shfl_xor(m1, o));
-  }
-  if ((threadIdx.x & 63) == 0) {
-    atomicMax(&gmax[0], __float_as_uint(m0));
-    atomicMax(&gmax[1], __float_as_uint(m1));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < BT / 64; ++w) m = fmaxf(m, red[w]);
+    if (m > 0.f) atomicMax(leaf_words(gmax) + blockIdx.x % SPREAD, __float_as_uint(m));
   }
 }
 
-// n_do elements of dO (a multiple of 16 / sizeof(element)), n_dhl of dh_leaf
-// (a multiple of 4; dh_leaf may be null)
-hipError_t launch_absmax(const BwdArgs& a, bool bf16, size_t n_do, size_t n_dhl, hipStream_t st) {
-  KDA_LAUNCH("kda_bwd_grad_scale", k_zero_gmax, dim3(1), dim3(64), st, a.gmax);
+// n_dhl elements of dh_leaf (a multiple of 4; dh_leaf may be null)
+hipError_t launch_scale_words(const BwdArgs& a, size_t n_dhl, hipStream_t st) {
+  KDA_LAUNCH("kda_bwd_grad_scale", k_zero_words, dim3(1), dim3(BT), st, a.gmax,
+             (int)scale_words(a.n_rounds));
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t n = n_do > n_dhl ? n_do : n_dhl;
-  size_t nb = (n / 8 + BT - 1) / BT;
+  if (e != hipSuccess || !a.dh_leaf || n_dhl == 0) return e;
+  size_t nb = (n_dhl / 16 + BT - 1) / BT;
   nb = nb < 1 ? 1 : (nb > 2048 ? 2048 : nb);
-  if (bf16)
-    KDA_LAUNCH("kda_bwd_grad_scale", k_absmax<uint16_t>, dim3((unsigned)nb), dim3(BT), st,
-               (const uint16_t*)a.dO, n_do, a.dh_leaf, n_dhl, a.gmax);
-  else
-    KDA_LAUNCH("kda_bwd_grad_scale", k_absmax<float>, dim3((unsigned)nb), dim3(BT), st,
-               (const float*)a.dO, n_do, a.dh_leaf, n_dhl, a.gmax);
+  KDA_LAUNCH("kda_bwd_grad_scale", k_leaf_absmax, dim3((unsigned)nb), dim3(BT), st, a.dh_leaf,
+             n_dhl, a.gmax);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ constexpr int32_t ATT_KW_TARGET = 2048; // about this many work items in all
 // Offsets (in int32 elements) of each device table inside the uploaded block.
 struct DevLayout {
   int64_t round_seq_ptr, seq_chunk_ptr, seq_row_ptr, seq_init_kind, seq_init_idx, seq_leaf, seq_lpt;
-  int64_t chunk_seq, chunk_row0, chunk_len, chunk_save, chunk_nrep, chunk_rep0;
+  int64_t chunk_seq, chunk_row0, chunk_len, chunk_save, chunk_nrep, chunk_rep0, chunk_round;
   int64_t row_index, out_row;
   int64_t buf_cons_ptr, buf_cons, buf_chunk;
   int64_t rep_row, rep_ptr, rep_slot;
@@ -49,6 +49,7 @@ struct Plan {
   std::vector<int32_t> seq_row_ptr;  // packed rows fit int32 (checked)
   // per chunk
   std::vector<int32_t> chunk_seq, chunk_row0, chunk_len, chunk_save, chunk_nrep, chunk_rep0;
+  std::vector<int32_t> chunk_round;   // round of the chunk's sequence
   // per packed row
   std::vector<int32_t> row_index, out_row;
   // handoff buffers

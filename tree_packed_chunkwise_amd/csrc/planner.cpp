@@ -641,6 +641,9 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
     P.att_n_slots = slot;
   }
 
+  P.chunk_round.resize(P.chunk_seq.size());
+  for (size_t c = 0; c < P.chunk_seq.size(); ++c) P.chunk_round[c] = P.seq_round[P.chunk_seq[c]];
+
   // ---- device block: int32 tables, each 64-element (256 B) aligned ----
   {
     DevLayout& d = P.dev;
@@ -653,6 +656,7 @@ int build_plan(int32_t n_seg, const int32_t* parent, const int32_t* seg_len,
         {&d.chunk_seq, &P.chunk_seq},         {&d.chunk_row0, &P.chunk_row0},
         {&d.chunk_len, &P.chunk_len},         {&d.chunk_save, &P.chunk_save},
         {&d.chunk_nrep, &P.chunk_nrep},       {&d.chunk_rep0, &P.chunk_rep0},
+        {&d.chunk_round, &P.chunk_round},
         {&d.row_index, &P.row_index},         {&d.out_row, &P.out_row},
         {&d.buf_cons_ptr, &P.buf_cons_ptr},   {&d.buf_cons, &P.buf_cons},
         {&d.buf_chunk, &P.buf_chunk},         {&d.rep_row, &P.rep_row},

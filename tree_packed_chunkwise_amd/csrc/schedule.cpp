@@ -10,10 +10,10 @@
 //             pass of the later rounds' chunks, run round group by round
 //             group (a group: consecutive rounds of at least an eighth of
 //             all chunks); each round waits only for its own group's pass.
-//   reverse:  the call's gradient scale (largest |dO|, |dh_leaf|) on the
-//             second stream beside the gathering of the last round's dO
-//             tiles (the rest gathered there beside that round); rounds last
-//             to first; once
+//   reverse:  the gradient-scale words cleared (and the largest leaf-state
+//             gradient found); dO of the last round's chunks gathered (the
+//             rest on the second stream beside that round); rounds last to
+//             first; once
 //             the chunks whose rounds are done amount to a quarter of all
 //             chunks, their chunk-local gradients run on the second stream
 //             beside the remaining rounds; the rest after round 0; the
@@ -46,7 +46,7 @@ hipError_t launch_bwd_rounds(const BwdArgs& a, bool bf16, int BC, int D, const i
 hipError_t launch_grad(const BwdArgs& a, bool bf16, int BC, int D, int c_begin, int n_chunks,
                        hipStream_t st);
 hipError_t launch_reduce(const BwdArgs& a, int D, int n_rep_rows, int n_root, hipStream_t st);
-hipError_t launch_absmax(const BwdArgs& a, bool bf16, size_t n_do, size_t n_dhl, hipStream_t st);
+hipError_t launch_scale_words(const BwdArgs& a, size_t n_dhl, hipStream_t st);
 
 namespace {
 
@@ -166,26 +166,21 @@ hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
   if (R > 1 && nc > 0 && g_overlap.load()) KDA_TRY(side_of_current_device(&sd));
   std::unique_lock<std::mutex> lk;
   if (sd) lk = std::unique_lock<std::mutex>(sd->mu);
-  // the call's gradient scale (the largest upstream gradient) and the dO
-  // tiles: with a second stream the scale pass runs there beside the
-  // gathering of the last round's chunks, and the rest of dO is gathered
-  // there while that round runs
-  const size_t n_do = (size_t)p.n_out_rows * a.H * D;
+  // the gradient-scale words (cleared; the largest leaf-state gradient), then
+  // the dO tiles, whose gathering also records each round's largest |dO|:
+  // the last round's chunks first; with a second stream the rest are
+  // gathered there while that round runs
   const size_t n_dhl = a.dh_leaf ? (size_t)p.n_leaf * a.H * D * D : 0;
+  KDA_TRY(launch_scale_words(a, n_dhl, st));
   const int cl = R > 0 ? round_chunk_begin(p, R - 1) : nc;
-  hipEvent_t gathered = nullptr, scaled = nullptr;
+  hipEvent_t gathered = nullptr;
   if (sd && cl > 0) {
-    KDA_TRY(order_after(sd->fork, st, sd->s));
-    KDA_TRY(launch_absmax(a, bf16, n_do, n_dhl, sd->s));
-    KDA_TRY(group_event(sd, 1, &scaled));
-    KDA_TRY(hipEventRecord(scaled, sd->s));
     KDA_TRY(launch_gather_dO(a, bf16, BC, D, cl, nc - cl, st));
+    KDA_TRY(order_after(sd->fork, st, sd->s));
     KDA_TRY(launch_gather_dO(a, bf16, BC, D, 0, cl, sd->s));
     KDA_TRY(group_event(sd, 0, &gathered));
     KDA_TRY(hipEventRecord(gathered, sd->s));
-    KDA_TRY(hipStreamWaitEvent(st, scaled, 0));
   } else {
-    KDA_TRY(launch_absmax(a, bf16, n_do, n_dhl, st));
     KDA_TRY(launch_gather_dO(a, bf16, BC, D, 0, nc, st));
   }
   const int group = nc / 4 > 1 ? nc / 4 : 1;
