@@ -362,6 +362,36 @@ __device__ inline void lds_copy_async(void* dst, const unsigned char* src, int n
                                        16, 0, 0);
   }
 }
+// The same copy, issued so that the compiler does not see it: it places no
+// wait of its own for the copy before later LDS reads (for reads whose
+// memory operands it knows, e.g. the transposing reads, it would wait for
+// every copy in flight, however disjoint the addresses).  The caller's
+// s_waitcnt vmcnt(0) and barrier complete it.  The instruction writes LDS
+// only (no register results); M0 holds the LDS base of the wave's piece and
+// one wait state separates its write from the load.
+// Part `part` of NPART of it: each wave's pieces split into NPART runs, so
+// that the copy can be issued in steps between other work.
+template <int NPART = 1>
+__device__ inline void lds_copy_async_untracked(void* dst, const unsigned char* src, int nvec,
+                                                int part = 0) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)dst;
+  const int per_wave = ((nvec + 63) / 64 + NW - 1) / NW;
+  const int j0 = part * per_wave / NPART, j1 = (part + 1) * per_wave / NPART;
+  for (int j = j0; j < j1; ++j) {
+    const int p = wave + NW * j;
+    if (64 * p >= nvec) break;
+    const int e = 64 * p + lane;
+    if (e < nvec) {
+      const unsigned char* gp = src + 16 * (size_t)e;
+      const unsigned m = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)p);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(gp), "s"(m)
+                   : "memory", "m0");
+    }
+  }
+}
 
 // pair index p (0..NPAIR-1) -> block pair (I, J), J <= I, row-major over I
 __device__ inline void pair_of(int p, int& I, int& J) {

@@ -203,6 +203,16 @@ struct AttnArgs {
   float* part;        // [n_slots][H][2][64][D] partial dk, dv
 };
 
+// A plan value at a block-uniform index, read through the constant address
+// space so that it becomes a scalar load: the plan tables are never written
+// while a kernel runs.  A vector load of it would share the vector-memory
+// wait counter with the block's image prefetch and result stores, and the
+// wait for its value would wait for all of them.
+template <typename T>
+__device__ inline T ld_uni(const T* p, size_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 // One input element as fp32, loaded through the global address space (every
 // input lives in device memory; the compiler cannot always infer that, and a
 // flat load counts against both wait counters).

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int 
   constexpr int NVEC = (int)(sizeof(BI) / 16);
   __shared__ BI buf[2];   // this chunk's image and the next one's (chunks run backwards)
   // blocks in the round's launch order: sequence rank major, head minor
-  const int seq = a.plan.seq_lpt[seq_begin + (int)blockIdx.x / a.H];
+  const int seq = ld_uni(a.plan.seq_lpt, seq_begin + (int)blockIdx.x / a.H);
   const int h = (int)blockIdx.x % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;
@@ -50,13 +50,13 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int 
   const int H = a.H;
   const TIn* dOp = (const TIn*)a.dOp;
   const size_t DD = (size_t)D * D;
-  const int cbeg = a.plan.seq_chunk_ptr[seq];
-  const int cend = a.plan.seq_chunk_ptr[seq + 1];
+  const int cbeg = ld_uni(a.plan.seq_chunk_ptr, seq);
+  const int cend = ld_uni(a.plan.seq_chunk_ptr, seq + 1);
   auto image = [&](int cc) { return a.fimg + ((size_t)cc * H + h) * fwd_image_bytes(BC, D); };
 
   f32x4 dh[G::NCB];
   {
-    const int leaf = a.plan.seq_leaf[seq];   // -1: the sequence ends at an inner segment
+    const int leaf = ld_uni(a.plan.seq_leaf, seq);   // -1: the sequence ends at an inner segment
     const float* src = (a.dh_leaf && leaf >= 0) ? a.dh_leaf + ((size_t)leaf * H + h) * DD : nullptr;
 #pragma unroll
     for (int C = 0; C < G::NCB; ++C)
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int 
       }
   };
   if (cbeg < cend) {
-    lds_copy_async(&buf[0], image(cend - 1), NVEC);
+    lds_copy_async_untracked(&buf[0], image(cend - 1), NVEC);
     load_do(cend - 1);
   }
   // the round's gradients in units scaled by sg (round_scale, common.h): dO,
@@ -98,8 +98,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int 
 #pragma unroll
   for (int C = 0; C < G::NCB; ++C) dh[C] *= sg;
   for (int c = cend - 1; c >= cbeg; --c) {
-    const int row0 = a.plan.chunk_row0[c];
-    const int len = a.plan.chunk_len[c];
+    const int len = ld_uni(a.plan.chunk_len, c);
     const size_t blk = (size_t)c * H + h;
     __builtin_amdgcn_s_waitcnt(0);  // this chunk's image (and dO) have landed ...
     __syncthreads();                // ... for every wave; the other buffer is free
@@ -110,7 +109,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int 
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) dof[ks][hf] = dscale * in4_to_f32(dor[ks][hf]);
     if (c > cbeg) {
-      lds_copy_async(&buf[(cend - c) & 1], image(c - 1), NVEC);
+      lds_copy_async_untracked(&buf[(cend - c) & 1], image(c - 1), NVEC);
       load_do(c - 1);
     }
 
@@ -118,11 +117,11 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int 
       f16x8 dob[KB];
 #pragma unroll
       for (int ks = 0; ks < KB; ++ks) dob[ks] = acc_pair(dof[ks][0], dof[ks][1]);
-      const int save = a.plan.chunk_save[c];
+      const int save = ld_uni(a.plan.chunk_save, c);
       if (save >= 0) {
-        const int p0 = a.plan.buf_cons_ptr[save], p1 = a.plan.buf_cons_ptr[save + 1];
+        const int p0 = ld_uni(a.plan.buf_cons_ptr, save), p1 = ld_uni(a.plan.buf_cons_ptr, save + 1);
         for (int pi = p0; pi < p1; ++pi) {
-          const float* src = a.slot + ((size_t)a.plan.buf_cons[pi] * H + h) * DD;
+          const float* src = a.slot + ((size_t)ld_uni(a.plan.buf_cons, pi) * H + h) * DD;
 #pragma unroll
           for (int C = 0; C < G::NCB; ++C)
 #pragma unroll
@@ -274,7 +273,7 @@ __global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, DevPlan plan, 
   __shared__ __attribute__((aligned(16))) TIn rowsm[BC * PITCH];
   __shared__ float wmax[4];
   const int c = c_begin + blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int row0 = plan.chunk_row0[c], len = plan.chunk_len[c];
+  const int row0 = ld_uni(plan.chunk_row0, c), len = ld_uni(plan.chunk_len, c);
   float mx = 0.f;   // largest |dO| of the chunk-head, for its round's gradient scale
   for (int p = tid; p < BC * PPR; p += 256) {
     const int i = p / PPR, j = p % PPR;
@@ -292,7 +291,7 @@ __global__ __launch_bounds__(256) void k_gather_dO(const TIn* dO, DevPlan plan, 
   if (tid == 0) {
     mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     if (mx > 0.f)
-      atomicMax(dO_words(gmax, plan.chunk_round[c]) + (blockIdx.x + 7 * blockIdx.y) % SPREAD,
+      atomicMax(dO_words(gmax, ld_uni(plan.chunk_round, c)) + (blockIdx.x + 7 * blockIdx.y) % SPREAD,
                 __float_as_uint(mx));
   }
   TIn* dst = dOp + ((size_t)c * H + h) * (BC * D);

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
   constexpr int NVEC = (int)(sizeof(FH) / 16);
   __shared__ FH buf[2];                      // this chunk's image and the next one's
   // blocks in the round's launch order: sequence rank major, head minor
-  const int seq = a.plan.seq_lpt[seq_begin + (int)blockIdx.x / a.H];
+  const int seq = ld_uni(a.plan.seq_lpt, seq_begin + (int)blockIdx.x / a.H);
   const int h = (int)blockIdx.x % a.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const bool sw = wave < NV;                 // this wave carries a column block of the state
@@ -48,17 +48,17 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
   const int rq = quad_row();                 // its row within a 16-row block
   const int H = a.H;
   const size_t DD = (size_t)D * D;
-  const int cbeg = a.plan.seq_chunk_ptr[seq];
-  const int cend = a.plan.seq_chunk_ptr[seq + 1];
+  const int cbeg = ld_uni(a.plan.seq_chunk_ptr, seq);
+  const int cend = ld_uni(a.plan.seq_chunk_ptr, seq + 1);
   auto image = [&](int cc) { return a.fimg + ((size_t)cc * H + h) * fwd_image_bytes(BC, D); };
 
   f32x4 hs[G::NCB];
   {
     const float* src = nullptr;
-    if (a.plan.seq_init_kind[seq] == 0) {
-      if (a.h0) src = a.h0 + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
+    if (ld_uni(a.plan.seq_init_kind, seq) == 0) {
+      if (a.h0) src = a.h0 + ((size_t)ld_uni(a.plan.seq_init_idx, seq) * H + h) * DD;
     } else {
-      src = a.bufs + ((size_t)a.plan.seq_init_idx[seq] * H + h) * DD;
+      src = a.bufs + ((size_t)ld_uni(a.plan.seq_init_idx, seq) * H + h) * DD;
     }
 #pragma unroll
     for (int C = 0; C < G::NCB; ++C)
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       vr[J] = sw ? *(const in4_t<TIn>*)(&F->V[0][0] + state_tile<D>(J, col >> 4)) : (in4_t<TIn>)0;
   };
   if (cbeg < cend) {
-    lds_copy_async(&buf[0], image(cbeg), NVEC);
+    lds_copy_async_untracked(&buf[0], image(cbeg), NVEC);
     load_v(cbeg);
   }
   for (int c = cbeg; c < cend; ++c) {
@@ -87,10 +87,10 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
     f32x4 z[G::NB];
 #pragma unroll
     for (int J = 0; J < G::NB; ++J) z[J] = in4_to_f32(vr[J]);
-    if (c + 1 < cend) {
-      lds_copy_async(&buf[(c - cbeg + 1) & 1], image(c + 1), NVEC);
-      load_v(c + 1);
-    }
+    // the next chunk's image, in two parts: the second once this wave's
+    // first products are issued
+    if (c + 1 < cend) lds_copy_async_untracked<2>(&buf[(c - cbeg + 1) & 1], image(c + 1), NVEC, 0);
+    if (!sw && c + 1 < cend) lds_copy_async_untracked<2>(&buf[(c - cbeg + 1) & 1], image(c + 1), NVEC, 1);
 
     // ---- state phase: wave w < NV owns column block w of the slice ----
     if (sw) {
@@ -117,6 +117,10 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       for (int J = 0; J < G::NB; ++J)
 #pragma unroll
         for (int ks = 0; ks < KD; ++ks) z[J] = mfma16(fa[J][ks], hb[ks], z[J]);
+      // the next chunk's V, into the registers this chunk's V has left
+      // (loaded on every step, so that they stay the same registers)
+      load_v(c + 1 < cend ? c + 1 : c);
+      if (c + 1 < cend) lds_copy_async_untracked<2>(&buf[(c - cbeg + 1) & 1], image(c + 1), NVEC, 1);
       // (Q e^Gam) h: independent of the solve below, so it overlaps it
 #pragma unroll
       for (int I = 0; I < G::NB; ++I)
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
 #pragma unroll
         for (int ks = 0; ks < KB; ++ks) hs[C] = mfma16(fk[C][ks], db[ks], hs[C]);
       }
-      const int save = a.plan.chunk_save[c];
+      const int save = ld_uni(a.plan.chunk_save, c);
       if (save >= 0) {
         float* dst = a.bufs + ((size_t)save * H + h) * DD;
 #pragma unroll
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
       }
     }
   }
-  if (sw && a.plan.seq_leaf[seq] >= 0) {   // node-wise sequences may end at an inner segment
-    float* dst = a.h_leaf + ((size_t)a.plan.seq_leaf[seq] * H + h) * DD;
+  if (sw && ld_uni(a.plan.seq_leaf, seq) >= 0) {   // node-wise sequences may end at an inner segment
+    float* dst = a.h_leaf + ((size_t)ld_uni(a.plan.seq_leaf, seq) * H + h) * DD;
 #pragma unroll
     for (int C = 0; C < G::NCB; ++C)
 #pragma unroll

@@ -281,14 +281,14 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   const int H = a.H;
   const size_t blk = (size_t)c * H + h;
   const size_t DD = (size_t)D * D;
-  const int row0 = a.plan.chunk_row0[c], len = a.plan.chunk_len[c], nrep = a.plan.chunk_nrep[c];
-  const int rep0 = a.plan.chunk_rep0[c];
+  const int row0 = ld_uni(a.plan.chunk_row0, c), len = ld_uni(a.plan.chunk_len, c);
+  const int nrep = ld_uni(a.plan.chunk_nrep, c), rep0 = ld_uni(a.plan.chunk_rep0, c);
   const TIn* q = (const TIn*)a.q;
   const TIn* k = (const TIn*)a.k;
   const TIn* dOp = (const TIn*)a.dOp;
   const FwdImage<BC, D, TIn>* F =
       (const FwdImage<BC, D, TIn>*)(a.fimg + blk * fwd_image_bytes(BC, D));
-  const int cround = a.plan.chunk_round[c];
+  const int cround = ld_uni(a.plan.chunk_round, c);
 
   // ---- global loads, issued in the order of their first use: loads return
   // in issue order, so each phase waits only for what it reads while the

@@ -61,9 +61,9 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
   const int c = c_begin + blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int H = a.H;
   const size_t blk = (size_t)c * H + h;
-  const int row0 = a.plan.chunk_row0[c];
-  const int len = a.plan.chunk_len[c];
-  const int nrep = a.plan.chunk_nrep[c];
+  const int row0 = ld_uni(a.plan.chunk_row0, c);
+  const int len = ld_uni(a.plan.chunk_len, c);
+  const int nrep = ld_uni(a.plan.chunk_nrep, c);
   // the A/P phase's global loads are issued first (v follows that phase);
   // each thread reads the row indices of its own element rows from the plan
   // (no round trip through a shared table)
