@@ -45,7 +45,8 @@ struct DevPlan {
 //
 // Forward image (BC rows, head dim D):
 //   Qt  [BC][D]     q e^Gam                 Kn  [BC][D]    -k e^Gam
-//   KhT [D][BC]     (k e^(Gam_C - Gam))^T   L   [BC][BC]   A (strict lower)
+//   KhT [D][BC]     (k e^(Gam_C - Gam))^T   L   [BC][BC]   -A (strict lower; every reader
+//                                                           subtracts A times something)
 //   P   [BC][BC]    P (lower)               Td  [BC][24]   (I + diag(beta) A_II)^-1 per 16-row block
 //   gc  [D] fp32    e^Gam_C                 beta [BC] fp32     orow [BC] int (-1: no output)
 //   V   [BC][D]     v in the input dtype, in 16x16 accumulator-order tiles

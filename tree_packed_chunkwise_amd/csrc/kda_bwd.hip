@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NT) void k_bwd_round(BwdArgs a, int seq_begin, int 
           if (32 * ks + 31 >= 16 * J) fp[J][ks] = lds_a_perm_tr_sw<BC>(&s.P[0][0], 32 * ks, 16 * J, HALF);
         ft[J] = lds_tr4(&s.Td[0][0], 24, 16 * J, 0);
 #pragma unroll
-        for (int I = 0; I < J; ++I) fl[I][J] = -lds_tr4_sw<BC>(&s.L[0][0], 16 * J, 16 * I);  // block (I, J) of A^T
+        for (int I = 0; I < J; ++I) fl[I][J] = lds_tr4_sw<BC>(&s.L[0][0], 16 * J, 16 * I);  // block (I, J) of -A^T
 #pragma unroll
         for (int r = 0; r < 4; ++r) bz[J][r] = s.beta[16 * J + 4 * g + r];
       }

@@ -106,7 +106,7 @@ struct GradSmem {
   using G = GradGeom<BC, D>;
   union {
     struct {                       // phases 1-2
-      _Float16 A[BC][G::PB];       // A (strict lower)
+      _Float16 A[BC][G::PB];       // -A (strict lower), as the image holds it
       _Float16 Td[BC][24];         // diagonal-block inverses
       union {
         _Float16 Kn[BC][G::PD];    // -(K e^Gam)        [i][c], until Z is formed
@@ -498,9 +498,7 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       f32x4 rr = z[I];
 #pragma unroll
       for (int J = 0; J < I; ++J) {
-        f16x4 la = *(const f16x4*)&s.u.p.A[16 * I + l16][16 * J + 4 * g];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) la[e] = -la[e];
+        const f16x4 la = *(const f16x4*)&s.u.p.A[16 * I + l16][16 * J + 4 * g];   // -A
         rr = mfma16k16(la, acc4(d[J]), rr);
       }
 #pragma unroll
@@ -519,20 +517,25 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
 #pragma unroll
       for (int ks = 0; ks < KB; ++ks)
         if (32 * ks <= 16 * I + 15) {
-          f16x8 aa = lds_a_perm(&s.u.p.A[0][0], G::PB, 16 * I + l16, 32 * ks, g, HALF);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) aa[x] = -aa[x];
+          const f16x8 aa = lds_a_perm(&s.u.p.A[0][0], G::PB, 16 * I + l16, 32 * ks, g, HALF);   // -A
           e = mfma16(aa, db[ks], e);
         }
+      float dvv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
         const float dy = dyv[I][r], b = s.beta[i];
         ye[I][r] = dy * e[r];
-        if (i < len) grad_dst(a, a.dv, a.rep_dv, rep0, s.orow[i], i, nrep, h, D)[col] = inv * (b * dy);
+        dvv[r] = inv * (b * dy);
         s.u.p.nZ[i][col] = (_Float16)(-b * dy);
         s.u.p.dl[i][col] = (_Float16)d[I][r];
       }
+      // dv as one 16-byte piece of a row per lane
+      quad_transpose(dvv);
+      const int i = 16 * I + quad_row();
+      if (i < len)
+        *(float4*)(grad_dst(a, a.dv, a.rep_dv, rep0, s.orow[i], i, nrep, h, D) + col - l16 + quad_col()) =
+            make_float4(dvv[0], dvv[1], dvv[2], dvv[3]);
     }
     // dbeta partial over this wave's 16 columns: row 16 I + 4 g + r
     if constexpr (NB == 4) {

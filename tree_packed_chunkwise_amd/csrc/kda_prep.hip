@@ -163,10 +163,10 @@ __global__ __launch_bounds__(NT) void k_chunk_prep(FwdArgs a, int c_begin) {
     chunk_AP_exact<TIn, BC, D>((const TIn*)a.q, (const TIn*)a.k, a.g, H, h, s.irow,
                                s.tb.first_bad, s.u.x.stage, &s.u.o.A[0][0], G::PB,
                                &s.u.o.P[0][0], G::PB);
-  // A and P in 8-byte pieces, into their swizzled places
+  // -A and P in 8-byte pieces, into their swizzled places
   for (int e = tid; e < BC * BC / 4; e += NT) {
     const int i = e / (BC / 4), j0 = (e % (BC / 4)) * 4;
-    *(f16x4*)&F->L[i][swz<BC>(i, j0)] = *(const f16x4*)&s.u.o.A[i][j0];
+    *(f16x4*)&F->L[i][swz<BC>(i, j0)] = -*(const f16x4*)&s.u.o.A[i][j0];
     *(f16x4*)&F->P[i][swz<BC>(i, j0)] = *(const f16x4*)&s.u.o.P[i][j0];
   }
   __syncthreads();  // beta of every row
