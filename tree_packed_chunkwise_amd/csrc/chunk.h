@@ -367,8 +367,11 @@ __device__ inline void lds_copy_async(void* dst, const unsigned char* src, int n
 // memory operands it knows, e.g. the transposing reads, it would wait for
 // every copy in flight, however disjoint the addresses).  The caller's
 // s_waitcnt vmcnt(0) and barrier complete it.  The instruction writes LDS
-// only (no register results); M0 holds the LDS base of the wave's piece and
-// one wait state separates its write from the load.
+// only (no register results).  M0 holds the LDS base of the wave's piece,
+// written in the same statement, one wait state before the load that reads
+// it; M0 is a reserved register, which a clobber list cannot protect, so the
+// kernels that issue this copy keep nothing else in it (they use no LDS-DMA
+// builtin and no indirectly indexed registers, the compiler's uses of M0).
 // Part `part` of NPART of it: each wave's pieces split into NPART runs, so
 // that the copy can be issued in steps between other work.
 template <int NPART = 1>
@@ -388,7 +391,7 @@ __device__ inline void lds_copy_async_untracked(void* dst, const unsigned char* 
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                    :
                    : "v"(gp), "s"(m)
-                   : "memory", "m0");
+                   : "memory");
     }
   }
 }
