@@ -428,8 +428,11 @@ int moe_router_stats_bwd(const void* logits, int32_t dtype, int64_t n_rows, int3
  *   ws of tree_attn_workspace_bytes(plan, H, d) bytes (row deltas and partial
  *   sums of key tiles whose queries are split over several blocks; summed in
  *   a fixed order, so results are deterministic).
- * Errors: KDA_ERR_SHAPE for other head dims, KDA_ERR_ARG for null pointers,
- * KDA_ERR_WORKSPACE for a small workspace, KDA_ERR_HIP for launch failures.
+ * scale must be positive and finite (the kernels take each query's running
+ * maximum over unscaled scores).
+ * Errors: KDA_ERR_SHAPE for other head dims, KDA_ERR_ARG for null pointers or
+ * a scale that is not positive and finite, KDA_ERR_WORKSPACE for a small
+ * workspace, KDA_ERR_HIP for launch failures.
  */
 size_t tree_attn_workspace_bytes(const kda_plan* plan, int32_t H, int32_t d);
 int tree_attn_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t d, float scale,

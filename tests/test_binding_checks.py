@@ -120,3 +120,12 @@ def test_gather_attention_router_state_checks(plan):
                         False)
     with pytest.raises(B.KDAError, match="device tensors"):
         B.kda_state_copy(st, None, st, None, 3)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_attention_scale_must_be_positive(plan, scale):
+    # the C-ABI refuses the scale before it looks at the device plan or tensors
+    L = B.load_library()
+    assert L.tree_attn_fwd(plan.handle, None, 2, 64, scale, None, None, None, None, None, None) == -4
+    assert L.tree_attn_bwd(plan.handle, None, 2, 64, scale, *([None] * 10), 0, None) == -4
+    assert b"scale" in L.kda_last_error()

@@ -63,7 +63,7 @@ __device__ inline f32x4 mfma_hl(const bf16x8& a, const bf16x8& bh, const bf16x8&
   c = mfmab(a, bh, c);
   return mfmab(a, bl, c);
 }
-__device__ inline float xmax(float a, float b) { return a > b ? a : b; }
+__device__ inline float xmax(float a, float b) { return __builtin_fmaxf(a, b); }
 
 // ---- swizzled tiles ----
 // A 64-row tile of a bf16 [N][H][D] tensor in LDS, rows unpadded (2 D bytes);
@@ -95,12 +95,27 @@ __device__ inline void tile_dma(unsigned char* dst, const uint16_t* src, int r0,
   constexpr int LPR = (2 * D) / 16;   // lanes per tile row
   constexpr int RPP = 64 / LPR;       // tile rows per 1 KB piece
   constexpr int NP = AT / RPP;
+  // a wave's pieces are NWV RPP rows apart, a multiple of the swizzle's
+  // period (16 rows for d = 128, 8 for d = 64): every piece of the wave
+  // takes the same swizzled chunk per lane
+  static_assert((NWV * RPP) % (D == 128 ? 16 : 8) == 0, "swizzle period");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rl = lane / LPR, pos = lane % LPR;
+  const int rb = wave * RPP + rl;
+  const int c = pos ^ SwTile<D>::swz(rb);
+  if (n == AT) {   // a whole tile: one address, advanced by a fixed row stride
+    const uint16_t* s0 = src + ((size_t)(r0 + rb) * H + h) * D + 8 * c;
+    const size_t step = (size_t)NWV * RPP * H * D;
+#pragma unroll
+    for (int j = 0; wave + NWV * j < NP; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(s0 + j * step),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * (wave + NWV * j)),
+                                       16, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int p = wave; p < NP; p += NWV) {
     const int r = p * RPP + rl;
-    const int c = pos ^ SwTile<D>::swz(r);
     const int gr = r0 + (r < n ? r : n - 1);
     __builtin_amdgcn_global_load_lds((const void*)(src + ((size_t)gr * H + h) * D + 8 * c),
                                      (__attribute__((address_space(3))) void*)(dst + 1024 * p),
@@ -227,16 +242,14 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) vf[db] = tile_a_tr<D>(Vt, 32 * kh, 16 * db);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      // the tile's maximum over raw scores (the scale is positive), masked
+      // keys at -inf
       float mt = -INFINITY;
       if (full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float x = sc[kb][qb][r] * sl2;
-            sc[kb][qb][r] = x;
-            mt = xmax(mt, x);
-          }
+          for (int r = 0; r < 4; ++r) mt = xmax(mt, sc[kb][qb][r]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -244,12 +257,12 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
           for (int r = 0; r < 4; ++r) {
             const int j = 32 * kh + 16 * kb + 4 * g + r;
             const bool vis = j < klen && (!own || k0 + j <= qpos[qb]);
-            const float x = vis ? sc[kb][qb][r] * sl2 : -INFINITY;
+            const float x = vis ? sc[kb][qb][r] : -INFINITY;
             sc[kb][qb][r] = x;
             mt = xmax(mt, x);
           }
       }
-      mt = max_rows4(mt);
+      mt = max_rows4(mt) * sl2;
       const float mn = mt > m[qb] + ATT_MAX_SLACK ? mt : m[qb];
       if (__builtin_amdgcn_ballot_w64(mn != m[qb])) {   // some query's reference moved
         const float alpha = m[qb] == -INFINITY ? 0.f : exp2_(m[qb] - mn);
@@ -258,12 +271,15 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
         for (int db = 0; db < NDB; ++db) ot[db][qb] *= alpha;
         m[qb] = mn;
       }
+      // a query with no visible key yet keeps mn = -inf: its scores are all
+      // -inf and any finite reference gives p = 0
+      const float mb = mn == -INFINITY ? 0.f : mn;
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = mn == -INFINITY ? 0.f : exp2_(sc[kb][qb][r] - mn);
+          const float p = exp2_(__builtin_fmaf(sc[kb][qb][r], sl2, -mb));
           sc[kb][qb][r] = p;
           ps += p;
         }
@@ -442,9 +458,11 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dq(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = 32 * kh + 16 * kb + 4 * g + r;
-          const bool vis = full || (j < klen && (!own || k0 + j <= qpos[qb]));
-          const float p = vis ? exp2_(sc[kb][qb][r] * sl2 - lq[qb]) : 0.f;
+          float p = exp2_(__builtin_fmaf(sc[kb][qb][r], sl2, -lq[qb]));
+          if (!full) {
+            const int j = 32 * kh + 16 * kb + 4 * g + r;
+            p = j < klen && (!own || k0 + j <= qpos[qb]) ? p : 0.f;
+          }
           sc[kb][qb][r] = p * (dp[kb][qb][r] - dl[qb]);   // dS^T
         }
       pair_hl(sc[0][qb], sc[1][qb], bh[qb], bl[qb]);
@@ -508,7 +526,7 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dkv(AttnArgs a) {
   using T = SwTile<D>;
   constexpr int KD = D / 32, NDB = D / 16;
   __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][T::BYTES];  // [stage][Q, dO]
-  __shared__ float sld[2][2][AT];                                            // [stage][lse log2e, delta]
+  __shared__ __attribute__((aligned(16))) float sld[2][2][AT];              // [stage][lse log2e, delta]
   const int item = blockIdx.x, h = blockIdx.y, H = a.H;
   const int t = a.kw_tile[item], q0 = a.kw_q0[item], nq = a.kw_nq[item], slot = a.kw_slot[item];
   const int seg = a.tile_seg[t], koff = a.tile_off[t];
@@ -582,15 +600,19 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dkv(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < 4; ++qb) {
+      // lse and delta of this lane's four queries 16 qb + 4 g .. +3 (rows of S)
+      const float4 lv = *(const float4*)&sld[st][0][16 * qb + 4 * g];
+      const float4 dv = *(const float4*)&sld[st][1][16 * qb + 4 * g];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int qq = 16 * qb + 4 * g + r;   // query of this element (row of S)
-        const bool vis = full || (qq < qlen && kj < klen && (!own || koff + kj <= qoff + qq));
-        const float p = vis ? exp2_(sp[qb][r] * sl2 - sld[st][0][qq]) : 0.f;
+        const int qq = 16 * qb + 4 * g + r;
+        float p = exp2_(__builtin_fmaf(sp[qb][r], sl2, -(&lv.x)[r]));
+        if (!full) p = qq < qlen && kj < klen && (!own || koff + kj <= qoff + qq) ? p : 0.f;
         sp[qb][r] = p;
-        dp[qb][r] = p * (dp[qb][r] - sld[st][1][qq]);
+        dp[qb][r] = p * (dp[qb][r] - (&dv.x)[r]);
       }
+    }
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {   // 32-deep k steps over the query tile's rows
       bf16x8 ph, pl, dh, dlo;

@@ -8,6 +8,7 @@
 #include <initializer_list>
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <string>
 
@@ -591,6 +592,8 @@ size_t tree_attn_workspace_bytes(const kda_plan* plan, int32_t H, int32_t d) {
 
 int tree_attn_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t d, float scale,
                   const void* q, const void* k, const void* v, float* o, float* lse, void* stream) {
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(KDA_ERR_ARG, "attention scale must be a positive finite number");
   int rc = check_dev_plan(plan, dev_plan);
   if (rc) return rc;
   if (!attn_shape_ok(H, d)) return fail(KDA_ERR_SHAPE, "supported: head dim 64 or 128, H > 0");
@@ -611,6 +614,8 @@ int tree_attn_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t
                   const void* q, const void* k, const void* v, const float* o, const float* lse,
                   const void* dO, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
                   void* stream) {
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(KDA_ERR_ARG, "attention scale must be a positive finite number");
   int rc = check_dev_plan(plan, dev_plan);
   if (rc) return rc;
   if (!attn_shape_ok(H, d)) return fail(KDA_ERR_SHAPE, "supported: head dim 64 or 128, H > 0");
