@@ -167,29 +167,33 @@ __device__ inline float sum_rows4(float x) {
 // 2^8 and most tiles skip the rescale of the accumulators.
 constexpr float ATT_MAX_SLACK = 8.f;
 
-// Forward, one block (4 waves) per (query tile, head).  Wave w owns queries
-// 32 (w & 1) .. +31 of the tile and keys 32 (w >> 1) .. +31 of every key tile:
-// each wave runs its own online softmax over its half of the keys, and the two
-// halves are merged at the end (running maxima, sums and outputs, through
-// LDS).  Key tiles (every ancestor segment, then the own segment up to the
-// tile's end) are double-buffered by asynchronous copies.
+// Forward, one block (4 waves) per (pair of consecutive query tiles of a
+// segment, head): 128 query rows share every key tile the block copies (the
+// block launched for a pair's second tile returns at once).  Wave w owns
+// queries 32 w .. +31 of the pair and all 64 keys of every key tile, with its
+// own online softmax.  Key tiles (every ancestor segment, then the own
+// segment up to the pair's end) are double-buffered by asynchronous copies; a
+// wave skips own-segment key tiles wholly past its queries, and a wave with no
+// queries (a segment's odd last tile) only helps copy.
 template <int D>
 __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
   using T = SwTile<D>;
   constexpr int KD = D / 32, NDB = D / 16;
+  constexpr int AQ = 2 * AT;   // query rows of a block
   __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][T::BYTES];  // [stage][K, V]
   const int t = a.qorder[blockIdx.x], h = blockIdx.y, H = a.H;
   const int seg = a.tile_seg[t], qoff = a.tile_off[t];
+  if (qoff % AQ != 0) return;    // the second tile of a pair
   const int slen = a.seg_len[seg], srow = a.seg_row[seg];
-  const int qlen = min(AT, slen - qoff);
+  const int qlen = min(AQ, slen - qoff);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int qh = wave & 1, kh = wave >> 1;
+  const bool qany = 32 * wave < qlen;   // the wave has queries
   const float sl2 = a.scale * 1.4426950408889634f;   // scores in log2 units
   bf16x8 qf[2][KD];
   int qpos[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qi = 32 * qh + 16 * qb + l16;
+    const int qi = 32 * wave + 16 * qb + l16;
     const int qrow = srow + qoff + min(qi, qlen - 1);
     qpos[qb] = qoff + qi;
 #pragma unroll
@@ -220,123 +224,105 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0);  // this tile has landed ...
     __syncthreads();                // ... for every wave; the other stage is free
     if (more) stage(st ^ 1, nri, nk0);
-    const unsigned char* Kt = sm[st][0];
-    const unsigned char* Vt = sm[st][1];
-    bf16x8 kf[2][KD];
+    if (qany && !(own && k0 > qoff + 32 * wave + 31)) {
+      const unsigned char* Kt = sm[st][0];
+      const unsigned char* Vt = sm[st][1];
+      f32x4 sc[4][2];   // S^T tiles [key block][query block], raw scores
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < KD; ++ks) kf[kb][ks] = tile_row8<D>(Kt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 sc[2][2];   // S^T tiles [key block][query block]
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        sc[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KD; ++ks) sc[kb][qb] = mfmab(kf[kb][ks], qf[qb][ks], sc[kb][qb]);
-      }
-    bf16x8 vf[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) vf[db] = tile_a_tr<D>(Vt, 32 * kh, 16 * db);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // the tile's maximum over raw scores (the scale is positive), masked
-      // keys at -inf
-      float mt = -INFINITY;
-      if (full) {
+      for (int k2 = 0; k2 < 4; k2 += 2) {
+        bf16x8 kf[2][KD];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mt = xmax(mt, sc[kb][qb][r]);
-      } else {
+          for (int ks = 0; ks < KD; ++ks) kf[kb][ks] = tile_row8<D>(Kt, 16 * (k2 + kb) + l16, 32 * ks + 8 * g);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 32 * kh + 16 * kb + 4 * g + r;
-            const bool vis = j < klen && (!own || k0 + j <= qpos[qb]);
-            const float x = vis ? sc[kb][qb][r] : -INFINITY;
-            sc[kb][qb][r] = x;
-            mt = xmax(mt, x);
+          for (int qb = 0; qb < 2; ++qb) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KD; ++ks) x = mfmab(kf[kb][ks], qf[qb][ks], x);
+            sc[k2 + kb][qb] = x;
           }
       }
-      mt = max_rows4(mt) * sl2;
-      const float mn = mt > m[qb] + ATT_MAX_SLACK ? mt : m[qb];
-      if (__builtin_amdgcn_ballot_w64(mn != m[qb])) {   // some query's reference moved
-        const float alpha = m[qb] == -INFINITY ? 0.f : exp2_(m[qb] - mn);
-        l[qb] *= alpha;
+      bf16x8 ph[2][2], pl[2][2];   // [32-key step][query block]
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) ot[db][qb] *= alpha;
-        m[qb] = mn;
-      }
-      // a query with no visible key yet keeps mn = -inf: its scores are all
-      // -inf and any finite reference gives p = 0
-      const float mb = mn == -INFINITY ? 0.f : mn;
-      float ps = 0.f;
+      for (int qb = 0; qb < 2; ++qb) {
+        // the tile's maximum over raw scores (the scale is positive), masked
+        // keys at -inf
+        float mt = -INFINITY;
+        if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2_(__builtin_fmaf(sc[kb][qb][r], sl2, -mb));
-          sc[kb][qb][r] = p;
-          ps += p;
+            for (int r = 0; r < 4; ++r) mt = xmax(mt, sc[kb][qb][r]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = 16 * kb + 4 * g + r;
+              const bool vis = j < klen && (!own || k0 + j <= qpos[qb]);
+              const float x = vis ? sc[kb][qb][r] : -INFINITY;
+              sc[kb][qb][r] = x;
+              mt = xmax(mt, x);
+            }
         }
-      l[qb] += ps;   // this lane's keys; the 4 lanes of a query are summed at the end
-      bf16x8 ph, pl;
-      pair_hl(sc[0][qb], sc[1][qb], ph, pl);
+        mt = max_rows4(mt) * sl2;
+        const float mn = mt > m[qb] + ATT_MAX_SLACK ? mt : m[qb];
+        if (__builtin_amdgcn_ballot_w64(mn != m[qb])) {   // some query's reference moved
+          const float alpha = m[qb] == -INFINITY ? 0.f : exp2_(m[qb] - mn);
+          l[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) ot[db][qb] = mfma_hl(vf[db], ph, pl, ot[db][qb]);
+          for (int db = 0; db < NDB; ++db) ot[db][qb] *= alpha;
+          m[qb] = mn;
+        }
+        // a query with no visible key yet keeps mn = -inf: its scores are all
+        // -inf and any finite reference gives p = 0
+        const float mb = mn == -INFINITY ? 0.f : mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = exp2_(__builtin_fmaf(sc[kb][qb][r], sl2, -mb));
+            sc[kb][qb][r] = p;
+            ps += p;
+          }
+        l[qb] += ps;   // this lane's keys; the 4 lanes of a query are summed at the end
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) pair_hl(sc[2 * k2][qb], sc[2 * k2 + 1][qb], ph[k2][qb], pl[k2][qb]);
+      }
+      // O^T += V^T P^T, 32 keys per step
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 vf[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vf[db] = tile_a_tr<D>(Vt, 32 * k2, 16 * db);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) ot[db][qb] = mfma_hl(vf[db], ph[k2][qb], pl[k2][qb], ot[db][qb]);
+      }
     }
     if (!more) break;
     ri = nri; k0 = nk0; st ^= 1;
   }
-  // merge the two key halves: waves 2, 3 hand their state to waves 0, 1
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) l[qb] = sum_rows4(l[qb]);
-  __syncthreads();   // every wave is done with the tiles: reuse them
-  float* xo = (float*)&sm[0][0][0];               // [qh][NDB * 2 * 4][64]
-  float* xm = xo + 2 * NDB * 2 * 4 * 64;           // [qh][2][64]
-  float* xl = xm + 2 * 2 * 64;
-  if (kh == 1) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = sum_rows4(l[qb]);
+    const int qi = 32 * wave + 16 * qb + l16;
+    if (qi < qlen) {
+      const int qrow = srow + qoff + qi;
+      const float inv = 1.f / lt;
+      float* dst = a.o + ((size_t)qrow * H + h) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane] = ot[db][qb][r];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      xm[(qh * 2 + qb) * 64 + lane] = m[qb];
-      xl[(qh * 2 + qb) * 64 + lane] = l[qb];
-    }
-  }
-  __syncthreads();
-  if (kh == 0) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qi = 32 * qh + 16 * qb + l16;
-      const float m2 = xm[(qh * 2 + qb) * 64 + lane], l2 = xl[(qh * 2 + qb) * 64 + lane];
-      const float mm = xmax(m[qb], m2);
-      const float w1 = m[qb] == -INFINITY ? 0.f : exp2_(m[qb] - mm);
-      const float w2 = m2 == -INFINITY ? 0.f : exp2_(m2 - mm);
-      const float lt = l[qb] * w1 + l2 * w2;
-      if (qi < qlen) {
-        const int qrow = srow + qoff + qi;
-        const float inv = 1.f / lt;
-        float* dst = a.o + ((size_t)qrow * H + h) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          float4 v;
-          float* vp = &v.x;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            vp[r] = (ot[db][qb][r] * w1 + xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane] * w2) * inv;
-          *(float4*)(dst + 16 * db + 4 * g) = v;
-        }
-        if (g == 0) a.lse[(size_t)qrow * H + h] = (mm + __log2f(lt)) * 0.6931471805599453f;
-      }
+      for (int db = 0; db < NDB; ++db)
+        *(float4*)(dst + 16 * db + 4 * g) =
+            make_float4(ot[db][qb][0] * inv, ot[db][qb][1] * inv, ot[db][qb][2] * inv, ot[db][qb][3] * inv);
+      if (g == 0) a.lse[(size_t)qrow * H + h] = (m[qb] + __log2f(lt)) * 0.6931471805599453f;
     }
   }
 }
@@ -358,31 +344,34 @@ __global__ __launch_bounds__(ANT) void k_attn_delta(AttnArgs a, int64_t n_rh) {
   if (rh < n_rh && part == 0) a.delta[rh] = x;
 }
 
-// dq, one block (4 waves) per (query tile, head), over the same key tiles as
-// the forward.  Wave w owns queries 32 (w & 1) .. +31 and keys 32 (w >> 1) ..
-// +31 of every key tile:
+// dq, one block (4 waves) per (pair of consecutive query tiles of a segment,
+// head), over the same key tiles as the forward (the block of a pair's second
+// tile returns at once).  Wave w owns queries 32 w .. +31 of the pair and
+// takes each key tile in two 32-key halves:
 //   S^T = K Q^T, dP^T = V dO^T (bf16 matrix cores, exact inputs),
 //   P^T = 2^(S^T scale log2e - lse log2e), dS^T = P^T (dP^T - delta),
 //   dQ^T += K^T dS^T (K^T from the tile by transposing reads, dS^T hi/lo),
-// and the two key halves' partial dq are summed at the end.
+// skipping, as the forward, own-segment key tiles wholly past its queries.
 template <int D>
 __global__ __launch_bounds__(ANT, 2) void k_attn_dq(AttnArgs a) {
   using T = SwTile<D>;
   constexpr int KD = D / 32, NDB = D / 16;
+  constexpr int AQ = 2 * AT;   // query rows of a block
   __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][T::BYTES];  // [stage][K, V]
   const int t = a.qorder[blockIdx.x], h = blockIdx.y, H = a.H;
   const int seg = a.tile_seg[t], qoff = a.tile_off[t];
+  if (qoff % AQ != 0) return;    // the second tile of a pair
   const int slen = a.seg_len[seg], srow = a.seg_row[seg];
-  const int qlen = min(AT, slen - qoff);
+  const int qlen = min(AQ, slen - qoff);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int qh = wave & 1, kh = wave >> 1;
+  const bool qany = 32 * wave < qlen;
   const float sl2 = a.scale * 1.4426950408889634f;
   bf16x8 qf[2][KD], df[2][KD];
   int qpos[2];
   float lq[2], dl[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qi = 32 * qh + 16 * qb + l16;
+    const int qi = 32 * wave + 16 * qb + l16;
     const int qrow = srow + qoff + min(qi, qlen - 1);
     qpos[qb] = qoff + qi;
 #pragma unroll
@@ -416,99 +405,85 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dq(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (more) stage(st ^ 1, nri, nk0);
-    const unsigned char* Kt = sm[st][0];
-    const unsigned char* Vt = sm[st][1];
-    f32x4 sc[2][2], dp[2][2];
-    {
-      bf16x8 kf[2][KD];
+    if (qany && !(own && k0 > qoff + 32 * wave + 31)) {
+      const unsigned char* Kt = sm[st][0];
+      const unsigned char* Vt = sm[st][1];
+#pragma unroll 1
+      for (int kh = 0; kh < 2; ++kh) {   // keys 32 kh .. +31 of the tile
+        f32x4 sc[2][2], dp[2][2];
+        {
+          bf16x8 kf[2][KD];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) kf[kb][ks] = tile_row8<D>(Kt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
-      __builtin_amdgcn_sched_barrier(0);
+            for (int ks = 0; ks < KD; ++ks) kf[kb][ks] = tile_row8<D>(Kt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              sc[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int ks = 0; ks < KD; ++ks) sc[kb][qb] = mfmab(kf[kb][ks], qf[qb][ks], sc[kb][qb]);
+            }
+        }
+        {
+          bf16x8 vf[2][KD];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KD; ++ks) vf[kb][ks] = tile_row8<D>(Vt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              dp[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int ks = 0; ks < KD; ++ks) dp[kb][qb] = mfmab(vf[kb][ks], df[qb][ks], dp[kb][qb]);
+            }
+        }
+        bf16x8 bh[2], bl[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          sc[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KD; ++ks) sc[kb][qb] = mfmab(kf[kb][ks], qf[qb][ks], sc[kb][qb]);
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float p = exp2_(__builtin_fmaf(sc[kb][qb][r], sl2, -lq[qb]));
+              if (!full) {
+                const int j = 32 * kh + 16 * kb + 4 * g + r;
+                p = j < klen && (!own || k0 + j <= qpos[qb]) ? p : 0.f;
+              }
+              sc[kb][qb][r] = p * (dp[kb][qb][r] - dl[qb]);   // dS^T
+            }
+          pair_hl(sc[0][qb], sc[1][qb], bh[qb], bl[qb]);
         }
-    }
-    {
-      bf16x8 vf[2][KD];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int d0 = 0; d0 < NDB; d0 += 4) {
+          bf16x8 kt[4];
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) vf[kb][ks] = tile_row8<D>(Vt, 32 * kh + 16 * kb + l16, 32 * ks + 8 * g);
-      __builtin_amdgcn_sched_barrier(0);
+          for (int db = 0; db < 4; ++db) kt[db] = tile_a_tr<D>(Kt, 32 * kh, 16 * (d0 + db));
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          dp[kb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KD; ++ks) dp[kb][qb] = mfmab(vf[kb][ks], df[qb][ks], dp[kb][qb]);
+            for (int qb = 0; qb < 2; ++qb) acc[d0 + db][qb] = mfma_hl(kt[db], bh[qb], bl[qb], acc[d0 + db][qb]);
         }
-    }
-    bf16x8 bh[2], bl[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float p = exp2_(__builtin_fmaf(sc[kb][qb][r], sl2, -lq[qb]));
-          if (!full) {
-            const int j = 32 * kh + 16 * kb + 4 * g + r;
-            p = j < klen && (!own || k0 + j <= qpos[qb]) ? p : 0.f;
-          }
-          sc[kb][qb][r] = p * (dp[kb][qb][r] - dl[qb]);   // dS^T
-        }
-      pair_hl(sc[0][qb], sc[1][qb], bh[qb], bl[qb]);
-    }
-#pragma unroll
-    for (int d0 = 0; d0 < NDB; d0 += 4) {
-      bf16x8 kt[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) kt[db] = tile_a_tr<D>(Kt, 32 * kh, 16 * (d0 + db));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) acc[d0 + db][qb] = mfma_hl(kt[db], bh[qb], bl[qb], acc[d0 + db][qb]);
+      }
     }
     if (!more) break;
     ri = nri; k0 = nk0; st ^= 1;
   }
-  // sum the two key halves: waves 2, 3 hand their partial dq to waves 0, 1
-  __syncthreads();
-  float* xo = (float*)&sm[0][0][0];   // [qh][NDB * 2 * 4][64]
-  if (kh == 1) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = 32 * wave + 16 * qb + l16;
+    if (qi < qlen) {
+      float* dst = a.dq + ((size_t)(srow + qoff + qi) * H + h) * D;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane] = acc[db][qb][r];
-  }
-  __syncthreads();
-  if (kh == 0) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qi = 32 * qh + 16 * qb + l16;
-      if (qi < qlen) {
-        float* dst = a.dq + ((size_t)(srow + qoff + qi) * H + h) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          float4 v;
-          float* vp = &v.x;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            vp[r] = a.scale * (acc[db][qb][r] + xo[((qh * NDB + db) * 8 + qb * 4 + r) * 64 + lane]);
-          *(float4*)(dst + 16 * db + 4 * g) = v;
-        }
-      }
+      for (int db = 0; db < NDB; ++db)
+        *(float4*)(dst + 16 * db + 4 * g) = make_float4(a.scale * acc[db][qb][0], a.scale * acc[db][qb][1],
+                                                        a.scale * acc[db][qb][2], a.scale * acc[db][qb][3]);
     }
   }
 }
