@@ -38,14 +38,8 @@ __device__ inline float bf2f(uint16_t x) { return __uint_as_float(((uint32_t)x) 
 // two accumulator tiles (rows 0-15, 16-31 of a 32-deep k step) as hi/lo bf16
 // B fragments in register k order (chunk.h)
 __device__ inline void pair_hl(const f32x4& t0, const f32x4& t1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    __bf16 x, y;
-    split_bf16(t0[r], x, y);
-    hi[r] = x; lo[r] = y;
-    split_bf16(t1[r], x, y);
-    hi[4 + r] = x; lo[4 + r] = y;
-  }
+  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  split8(x, hi, lo);
 }
 // A fragment in register k order from a bf16 [*][pitch] LDS array
 __device__ inline bf16x8 lds_a_perm_bf(const uint16_t* base, int pitch, int row, int kb, int g) {

@@ -55,6 +55,31 @@ __device__ inline void split_bf16(float x, __bf16& hi, __bf16& lo) {
   hi = (__bf16)x;
   lo = (__bf16)(x - (float)hi);
 }
+// The same split of two values at once, in the packed form the conversions
+// produce (element 0 in the low half): one packed conversion for the high
+// parts, whose values come back by shift and mask, the exact remainders, one
+// packed conversion for the low parts.  Identical results to split_bf16.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ inline void split_bf16x2(float x0, float x1, bf16x2& hi, bf16x2& lo) {
+  hi = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+  const unsigned hb = __builtin_bit_cast(unsigned, hi);
+  const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xffff0000u);
+  lo = __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, bf16x2);
+}
+// eight values of hi/lo splits, from four pairs
+__device__ inline bf16x8 join8(const bf16x2& a, const bf16x2& b, const bf16x2& c, const bf16x2& d) {
+  return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3),
+                                 __builtin_shufflevector(c, d, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// hi/lo splits of eight values
+__device__ inline void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  bf16x2 h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) split_bf16x2(x[2 * p], x[2 * p + 1], h[p], l[p]);
+  hi = join8(h[0], h[1], h[2], h[3]);
+  lo = join8(l[0], l[1], l[2], l[3]);
+}
 
 __device__ inline f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

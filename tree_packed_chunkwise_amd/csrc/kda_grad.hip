@@ -53,13 +53,11 @@ __device__ inline short bf16_bits(__bf16 x) { return __builtin_bit_cast(short, x
 __device__ inline float bf16_val(__bf16 x) { return (float)x; }
 // accumulator tile -> hi/lo bf16 B fragment of the 16x16x16 op
 __device__ inline void split_tile(const f32x4& t, s16x4& hi, s16x4& lo) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    __bf16 h, l;
-    split_bf16(t[r], h, l);
-    hi[r] = bf16_bits(h);
-    lo[r] = bf16_bits(l);
-  }
+  bf16x2 h0, l0, h1, l1;
+  split_bf16x2(t[0], t[1], h0, l0);
+  split_bf16x2(t[2], t[3], h1, l1);
+  hi = __builtin_bit_cast(s16x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3));
+  lo = __builtin_bit_cast(s16x4, __builtin_shufflevector(l0, l1, 0, 1, 2, 3));
 }
 // the hi/lo product  ah bh + ah bl + al bh
 __device__ inline f32x4 mma3(const s16x4& ah, const s16x4& al, const s16x4& bh, const s16x4& bl) {
@@ -669,20 +667,20 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
       const int ch = DH * hf + c0;
       if constexpr (RPT == 8) {   // the thread's 8 rows are one 16-byte run of each [c][i] array
         bf16x8 rh8, rl8, qh8, ql8, kh8, kl8;
+        float rv[8], qv[8], kv[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int n = hf * RPT + t, i = r0 + t;
           const float ref = s.gref[i >> 4][ch];
           const float f = __expf(gm[n] - ref), fi = __expf(ref - gm[n]);
-          __bf16 x, y;
-          split_bf16(kk[n] * fi, x, y);
-          rh8[t] = x; rl8[t] = y;
-          split_bf16(qq[n] * f, x, y);
-          qh8[t] = x; ql8[t] = y;
-          split_bf16(kk[n] * f, x, y);
-          kh8[t] = x; kl8[t] = y;
+          rv[t] = kk[n] * fi;
+          qv[t] = qq[n] * f;
+          kv[t] = kk[n] * f;
           s.u.d.gam[c0][i] = gm[n];
         }
+        split8(rv, rh8, rl8);
+        split8(qv, qh8, ql8);
+        split8(kv, kh8, kl8);
         put8(&s.u.d.rh[c0][r0], rh8); put8(&s.u.d.rl[c0][r0], rl8);
         put8(&s.u.d.qh[c0][r0], qh8); put8(&s.u.d.ql[c0][r0], ql8);
         put8(&s.u.d.kh[c0][r0], kh8); put8(&s.u.d.kl[c0][r0], kl8);
