@@ -451,8 +451,12 @@ int tree_attn_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t
  * and returns, for kernel class idx, its name, the number of timed launches
  * and their summed duration in milliseconds; it returns the number of kernel
  * classes (call with idx < 0 to get the count only), or KDA_ERR_ARG.
+ * kda_timing_filter(name) limits the recording to launches of that kernel
+ * class (NULL or "" : every class), so that a timed region carries only the
+ * events it needs; it applies from the next launch on.
  */
 int kda_timing_enable(int32_t on);
+int kda_timing_filter(const char* name);
 int kda_timing_read(int32_t idx, char* name, int32_t name_len, int64_t* launches,
                     double* total_ms);
 

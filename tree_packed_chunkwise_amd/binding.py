@@ -39,7 +39,7 @@ EXPORTS = [
     "kda_tree_plan", "kda_plan_destroy", "kda_plan_info", "kda_plan_export", "kda_plan_upload",
     "kda_plan_device_offset", "kda_saved_bytes", "kda_fwd_workspace_bytes",
     "kda_bwd_workspace_bytes", "kda_tree_fwd", "kda_tree_bwd", "gather_logprobs",
-    "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_read", "kda_last_error",
+    "gather_logprobs_bwd", "kda_timing_enable", "kda_timing_filter", "kda_timing_read", "kda_last_error",
     "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "kda_state_copy",
     "kda_state_sum", "kda_set_overlap", "moe_router_workspace_bytes", "moe_router_stats",
     "moe_router_stats_bwd", "kda_l1_plan", "moe_router_stats_noalloc",
@@ -119,6 +119,8 @@ def load_library(path: Path | str | None = None):
     L.kda_state_sum.restype = ctypes.c_int
     L.kda_timing_enable.argtypes = [i32]
     L.kda_timing_enable.restype = ctypes.c_int
+    L.kda_timing_filter.argtypes = [ctypes.c_char_p]
+    L.kda_timing_filter.restype = ctypes.c_int
     L.kda_set_overlap.argtypes = [i32]
     L.kda_set_overlap.restype = ctypes.c_int
     L.kda_timing_read.argtypes = [i32, ctypes.c_char_p, i32, ctypes.POINTER(i64),
@@ -655,9 +657,12 @@ def set_overlap(on: bool = True):
     _check(load_library().kda_set_overlap(1 if on else 0))
 
 
-def timing_enable(on: bool = True):
-    """Start (clearing the counters) or stop per-kernel launch timing."""
-    _check(load_library().kda_timing_enable(1 if on else 0))
+def timing_enable(on: bool = True, only: str | None = None):
+    """Start (clearing the counters) or stop per-kernel launch timing; `only`
+    limits it to one kernel class (None: every class)."""
+    L = load_library()
+    _check(L.kda_timing_filter(only.encode() if only else None))
+    _check(L.kda_timing_enable(1 if on else 0))
 
 
 def timing_read() -> dict:

@@ -24,6 +24,8 @@ std::vector<Rec> g_recs;          // launches since the last reset
 std::vector<hipEvent_t> g_pool;   // reusable events
 std::string g_pending;
 hipEvent_t g_pending_ev = nullptr;
+std::string g_only;               // time only launches of this kernel class ("" = all)
+bool g_skip = false;              // the launch in progress is not timed
 // totals after kda_timing_read folds the records: name -> (launches, ms)
 std::map<std::string, std::pair<int64_t, double>> g_tot;
 std::vector<std::string> g_names;
@@ -60,6 +62,8 @@ bool timing_on() { return g_on.load(std::memory_order_relaxed); }
 
 void timing_begin(const char* name, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);
+  g_skip = !g_only.empty() && g_only != name;
+  if (g_skip) return;
   g_pending = name;
   g_pending_ev = take_event();
   if (g_pending_ev) (void)hipEventRecord(g_pending_ev, st);
@@ -67,6 +71,10 @@ void timing_begin(const char* name, hipStream_t st) {
 
 void timing_end(hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);
+  if (g_skip) {
+    g_skip = false;
+    return;
+  }
   hipEvent_t b = take_event();
   if (b) (void)hipEventRecord(b, st);
   g_recs.push_back({g_pending, g_pending_ev, b});
@@ -82,6 +90,12 @@ int kda_timing_enable(int32_t on) {
   kda::fold();
   kda::g_tot.clear();
   kda::g_on.store(on != 0);
+  return KDA_OK;
+}
+
+int kda_timing_filter(const char* name) {
+  std::lock_guard<std::mutex> lk(kda::g_mu);
+  kda::g_only = name ? name : "";
   return KDA_OK;
 }
 
