@@ -129,3 +129,21 @@ def test_attention_scale_must_be_positive(plan, scale):
     assert L.tree_attn_fwd(plan.handle, None, 2, 64, scale, None, None, None, None, None, None) == -4
     assert L.tree_attn_bwd(plan.handle, None, 2, 64, scale, *([None] * 10), 0, None) == -4
     assert b"scale" in L.kda_last_error()
+
+
+@pytest.mark.parametrize("bad", range(10))
+def test_attention_pointers_must_be_aligned(plan, bad):
+    # the C-ABI refuses a misaligned tensor before anything is launched: the
+    # pointers below are never dereferenced (each call fails on the one offset
+    # by 8 bytes, or by 2 for lse)
+    L = B.load_library()
+    dev_plan = 0x10000
+    ptrs = [0x100000 * (i + 1) for i in range(10)]   # q k v o lse dO dq dk dv ws
+    ptrs[bad] += 2 if bad == 4 else 8
+    q, k, v, o, lse, dO, dq, dk, dv, ws = ptrs
+    if bad <= 4:
+        assert L.tree_attn_fwd(plan.handle, dev_plan, 2, 64, 0.125, q, k, v, o, lse, None) == -4
+        assert b"aligned" in L.kda_last_error()
+    assert L.tree_attn_bwd(plan.handle, dev_plan, 2, 64, 0.125, q, k, v, o, lse, dO, dq, dk, dv,
+                           ws, 1 << 40, None) == -4
+    assert b"aligned" in L.kda_last_error()

@@ -62,15 +62,17 @@ __device__ inline float xmax(float a, float b) { return __builtin_fmaxf(a, b); }
 // ---- swizzled tiles ----
 // A 64-row tile of a bf16 [N][H][D] tensor in LDS, rows unpadded (2 D bytes);
 // the 16-byte chunk c of row r sits at chunk position c ^ swz(r).  The swizzle
-// keeps both fragment reads free of bank conflicts: a 16-byte row read by 16
-// lanes of distinct rows (swz is a bijection on r mod 16), and the transposing
-// 8-byte read, whose 16 lanes address four consecutive rows x two adjacent
-// chunks (swz differs between those rows above bit 0).
+// keeps both fragment reads free of bank conflicts whether the LDS serves 128
+// or 256 bytes a cycle.  A 16-byte row read, one row per lane of a 16-lane
+// group: for d = 128 swz is a bijection on r mod 16 and on each aligned 8 rows
+// also a bijection mod 8 (bit 0 is bit 2 ^ bit 3 of r, bits 1-3 are r mod 8).
+// The transposing 8-byte read, whose 16 lanes address four consecutive rows x
+// two adjacent chunks: swz >> 1 differs between any aligned 4 (and 8) rows.
 template <int D>
 struct SwTile {
   static constexpr int BYTES = AT * D * 2;
   __device__ static int swz(int r) {
-    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
+    return D == 128 ? (((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1)) : (((r & 3) << 1) | ((r >> 2) & 1));
   }
   // byte offset of element (r, d)
   __device__ static int off(int r, int d) {
@@ -632,13 +634,23 @@ __global__ __launch_bounds__(ANT) void k_attn_dkv_reduce(AttnArgs a) {
   const int t = a.ks_tile[i], slot0 = a.ks_slot0[i], ns = a.ks_n[i];
   const int seg = a.tile_seg[t], koff = a.tile_off[t];
   const int klen = min(AT, a.seg_len[seg] - koff), krow0 = a.seg_row[seg] + koff;
-  for (int e = threadIdx.x; e < 2 * AT * D; e += ANT) {
-    const int which = e / (AT * D), j = (e / D) % AT, d = e % D;
+  constexpr int N4 = 2 * AT * D / 4, D4 = D / 4;                // float4s of a slot, of a row
+  const float4* src = (const float4*)(a.part + ((size_t)slot0 * H + h) * 2 * AT * D);
+  const size_t stride = (size_t)H * N4;                          // float4s from slot to slot
+  for (int e = threadIdx.x; e < N4; e += ANT) {
+    const int which = e / (AT * D4), j = (e / D4) % AT, d = 4 * (e % D4);
     if (j >= klen) continue;
-    float acc = 0.f;
-    for (int sl = 0; sl < ns; ++sl) acc += a.part[((size_t)(slot0 + sl) * H + h) * 2 * AT * D + e];
+    float4 acc = src[e];
+#pragma unroll 4
+    for (int sl = 1; sl < ns; ++sl) {
+      const float4 x = src[sl * stride + e];
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
     float* dst = which == 0 ? a.dk : a.dv;
-    dst[((size_t)(krow0 + j) * H + h) * D + d] = acc;
+    *(float4*)(dst + ((size_t)(krow0 + j) * H + h) * D + d) = acc;
   }
 }
 

@@ -598,6 +598,8 @@ int tree_attn_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t
   if (rc) return rc;
   if (!attn_shape_ok(H, d)) return fail(KDA_ERR_SHAPE, "supported: head dim 64 or 128, H > 0");
   if (!q || !k || !v || !o || !lse) return fail(KDA_ERR_ARG, "null tensor argument");
+  if (!aligned16({q, k, v, o}) || ((uintptr_t)lse) % 4)
+    return fail(KDA_ERR_ARG, "q, k, v, o must be 16-byte aligned, lse 4-byte aligned");
   const kda::Plan& p = plan->p;
   kda::AttnArgs a = make_attn_args(p, dev_plan, H, scale);
   a.q = (const uint16_t*)q;
@@ -621,6 +623,8 @@ int tree_attn_bwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t
   if (!attn_shape_ok(H, d)) return fail(KDA_ERR_SHAPE, "supported: head dim 64 or 128, H > 0");
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !ws)
     return fail(KDA_ERR_ARG, "null tensor argument");
+  if (!aligned16({q, k, v, o, dO, dq, dk, dv, ws}) || ((uintptr_t)lse) % 4)
+    return fail(KDA_ERR_ARG, "tensors and ws must be 16-byte aligned, lse 4-byte aligned");
   const kda::Plan& p = plan->p;
   if (ws_bytes < attn_ws_carve(p, H, d, nullptr, nullptr, nullptr))
     return fail(KDA_ERR_WORKSPACE, "attention workspace too small");
