@@ -1,12 +1,13 @@
-"""Invariants of the compiled round kernels that their sources rely on.
+"""Invariants of the compiled kernels that their sources rely on.
 
-The image prefetch of the forward and reverse round kernels is issued in
-inline assembly that writes M0 (csrc/chunk.h, lds_copy_async_untracked).  M0
-is a reserved register: a clobber list cannot protect it, so these kernels
-must keep nothing else in it.  This test compiles the two kernel sources for
-gfx950 and checks, in their AMD assembly, that every access to M0 is one of
-those copies (a write immediately followed by the wait state and the load),
-and that no indirect register indexing (which reads M0) appears.
+The image prefetch of the forward and reverse round kernels and the tile
+copies of tree attention are issued in inline assembly that writes M0
+(csrc/chunk.h, lds_load16_untracked).  M0 is a reserved register: a clobber
+list cannot protect it, so these kernels must keep nothing else in it.  This
+test compiles the kernel sources for gfx950 and checks, in their AMD
+assembly, that every access to M0 is one of those copies (a write
+immediately followed by the wait state and the load), and that no indirect
+register indexing (which reads M0) appears.
 CPU only: it needs hipcc, not a GPU.
 """
 import os
@@ -32,7 +33,7 @@ def _asm(src, tmp_path):
 
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not available")
-@pytest.mark.parametrize("name", ["kda_fwd.hip", "kda_bwd.hip"])
+@pytest.mark.parametrize("name", ["kda_fwd.hip", "kda_bwd.hip", "attn.hip"])
 def test_m0_only_in_the_image_copies(name, tmp_path):
     lines = [l.strip() for l in _asm(os.path.join(CSRC, name), tmp_path)]
     code = [l for l in lines if l and not l.startswith((";", ".")) and not l.endswith(":")]

@@ -84,8 +84,11 @@ struct SwTile {
 // into a swizzled tile (global_load_lds_dwordx4: straight to LDS).  Each 1 KB
 // piece of the tile is one wave instruction: lane l fills chunk position l of
 // the piece and so loads the chunk that the swizzle places there; rows past n
-// repeat row n-1 (their scores are masked).  Completion: s_waitcnt vmcnt(0)
-// and a barrier, by the caller.
+// repeat row n-1 (their scores are masked).  The loads are issued outside the
+// compiler's wait tracking (chunk.h, lds_load16_untracked): tracked, the
+// compiler waited for the next tile's copy before the current tile's first
+// transposing LDS read.  Completion: s_waitcnt vmcnt(0) and a barrier, by the
+// caller.
 template <int D, int NWV>
 __device__ inline void tile_dma(unsigned char* dst, const uint16_t* src, int r0, int n, int H, int h) {
   constexpr int LPR = (2 * D) / 16;   // lanes per tile row
@@ -99,23 +102,19 @@ __device__ inline void tile_dma(unsigned char* dst, const uint16_t* src, int r0,
   const int rl = lane / LPR, pos = lane % LPR;
   const int rb = wave * RPP + rl;
   const int c = pos ^ SwTile<D>::swz(rb);
+  const unsigned base = __builtin_amdgcn_readfirstlane(lds_addr(dst) + 1024u * (unsigned)wave);
   if (n == AT) {   // a whole tile: one address, advanced by a fixed row stride
     const uint16_t* s0 = src + ((size_t)(r0 + rb) * H + h) * D + 8 * c;
     const size_t step = (size_t)NWV * RPP * H * D;
 #pragma unroll
-    for (int j = 0; wave + NWV * j < NP; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(s0 + j * step),
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * (wave + NWV * j)),
-                                       16, 0, 0);
+    for (int j = 0; wave + NWV * j < NP; ++j) lds_load16_untracked(s0 + j * step, base + 1024u * NWV * j);
     return;
   }
 #pragma unroll
-  for (int p = wave; p < NP; p += NWV) {
-    const int r = p * RPP + rl;
+  for (int j = 0; wave + NWV * j < NP; ++j) {
+    const int r = (wave + NWV * j) * RPP + rl;
     const int gr = r0 + (r < n ? r : n - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + ((size_t)gr * H + h) * D + 8 * c),
-                                     (__attribute__((address_space(3))) void*)(dst + 1024 * p),
-                                     16, 0, 0);
+    lds_load16_untracked(src + ((size_t)gr * H + h) * D + 8 * c, base + 1024u * NWV * j);
   }
 }
 
@@ -158,6 +157,24 @@ __device__ inline float sum_rows4(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// The key tiles a query-tile pair visits: every ancestor segment's tiles, root
+// first, then its own segment's up to the pair's end.  Plan values are
+// block-uniform and read by scalar loads (a vector load would share the
+// in-order vector counter with the tile copies in flight); the loops look up
+// the next tile's place before they wait for the current tile's copy.
+struct KeyWalk {
+  const int* anc;
+  const int* seg_row;
+  const int* seg_len;
+  int a0, na, seg, own_len;   // own_len: the own segment's rows up to the pair's end
+  // first row and length of segment ri of the walk (ri == na: the own segment)
+  __device__ void place(int ri, int& row, int& len) const {
+    const int sg = ri == na ? seg : ld_uni(anc, a0 + ri);
+    row = ld_uni(seg_row, sg);
+    len = ri == na ? own_len : ld_uni(seg_len, sg);
+  }
+};
+
 // Running maximum of the online softmax (log2 units): it moves only when a
 // tile's maximum exceeds it by more than this, so probabilities stay below
 // 2^8 and most tiles skip the rescale of the accumulators.
@@ -200,26 +217,30 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) ot[db][0] = ot[db][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  const int a0 = a.anc_ptr[seg], na = a.anc_ptr[seg + 1] - a0;
-  auto seg_of = [&](int ri) { return ri == na ? seg : a.anc[a0 + ri]; };
-  auto len_of = [&](int ri) { return ri == na ? qoff + qlen : a.seg_len[seg_of(ri)]; };
-  auto stage = [&](int st, int ri, int k0) {
-    const int r0 = a.seg_row[seg_of(ri)] + k0, n = min(AT, len_of(ri) - k0);
+  const int a0 = ld_uni(a.anc_ptr, seg);
+  const KeyWalk walk{a.anc, a.seg_row, a.seg_len, a0, ld_uni(a.anc_ptr, seg + 1) - a0, seg, qoff + qlen};
+  const int na = walk.na;
+  auto stage = [&](int st, int r0, int n) {
     tile_dma<D, ANT / 64>(sm[st][0], a.k, r0, n, H, h);
     tile_dma<D, ANT / 64>(sm[st][1], a.v, r0, n, H, h);
   };
-  int ri = 0, k0 = 0, st = 0;
-  stage(0, 0, 0);
+  int ri = 0, k0 = 0, st = 0, rrow, rlen;   // the tile in LDS stage st: segment ri of the walk, rows k0..
+  walk.place(0, rrow, rlen);
+  stage(0, rrow, min(AT, rlen));
   for (;;) {
     const bool own = ri == na;
-    const int rlen = len_of(ri), klen = min(AT, rlen - k0);
+    const int klen = min(AT, rlen - k0);
     const bool full = !own && klen == AT;   // no masking needed
-    int nri = ri, nk0 = k0 + AT;
-    if (nk0 >= rlen) { nri = ri + 1; nk0 = 0; }
+    int nri = ri, nk0 = k0 + AT, nrow = rrow, nlen = rlen;
+    if (nk0 >= rlen) {
+      nri = ri + 1;
+      nk0 = 0;
+      if (nri <= na) walk.place(nri, nrow, nlen);
+    }
     const bool more = nri <= na;
     __builtin_amdgcn_s_waitcnt(0);  // this tile has landed ...
     __syncthreads();                // ... for every wave; the other stage is free
-    if (more) stage(st ^ 1, nri, nk0);
+    if (more) stage(st ^ 1, nrow + nk0, min(AT, nlen - nk0));
     if (qany && !(own && k0 > qoff + 32 * wave + 31)) {
       const unsigned char* Kt = sm[st][0];
       const unsigned char* Vt = sm[st][1];
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_fwd(AttnArgs a) {
       }
     }
     if (!more) break;
-    ri = nri; k0 = nk0; st ^= 1;
+    ri = nri; k0 = nk0; rrow = nrow; rlen = nlen; st ^= 1;
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -381,26 +402,30 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dq(AttnArgs a) {
   f32x4 acc[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int a0 = a.anc_ptr[seg], na = a.anc_ptr[seg + 1] - a0;
-  auto seg_of = [&](int ri) { return ri == na ? seg : a.anc[a0 + ri]; };
-  auto len_of = [&](int ri) { return ri == na ? qoff + qlen : a.seg_len[seg_of(ri)]; };
-  auto stage = [&](int st, int ri, int k0) {
-    const int r0 = a.seg_row[seg_of(ri)] + k0, n = min(AT, len_of(ri) - k0);
+  const int a0 = ld_uni(a.anc_ptr, seg);
+  const KeyWalk walk{a.anc, a.seg_row, a.seg_len, a0, ld_uni(a.anc_ptr, seg + 1) - a0, seg, qoff + qlen};
+  const int na = walk.na;
+  auto stage = [&](int st, int r0, int n) {
     tile_dma<D, ANT / 64>(sm[st][0], a.k, r0, n, H, h);
     tile_dma<D, ANT / 64>(sm[st][1], a.v, r0, n, H, h);
   };
-  int ri = 0, k0 = 0, st = 0;
-  stage(0, 0, 0);
+  int ri = 0, k0 = 0, st = 0, rrow, rlen;   // the tile in LDS stage st: segment ri of the walk, rows k0..
+  walk.place(0, rrow, rlen);
+  stage(0, rrow, min(AT, rlen));
   for (;;) {
     const bool own = ri == na;
-    const int rlen = len_of(ri), klen = min(AT, rlen - k0);
+    const int klen = min(AT, rlen - k0);
     const bool full = !own && klen == AT;
-    int nri = ri, nk0 = k0 + AT;
-    if (nk0 >= rlen) { nri = ri + 1; nk0 = 0; }
+    int nri = ri, nk0 = k0 + AT, nrow = rrow, nlen = rlen;
+    if (nk0 >= rlen) {
+      nri = ri + 1;
+      nk0 = 0;
+      if (nri <= na) walk.place(nri, nrow, nlen);
+    }
     const bool more = nri <= na;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (more) stage(st ^ 1, nri, nk0);
+    if (more) stage(st ^ 1, nrow + nk0, min(AT, nlen - nk0));
     if (qany && !(own && k0 > qoff + 32 * wave + 31)) {
       const unsigned char* Kt = sm[st][0];
       const unsigned char* Vt = sm[st][1];
@@ -469,7 +494,7 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dq(AttnArgs a) {
       }
     }
     if (!more) break;
-    ri = nri; k0 = nk0; st ^= 1;
+    ri = nri; k0 = nk0; rrow = nrow; rlen = nlen; st ^= 1;
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -499,9 +524,10 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dkv(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sm[2][2][T::BYTES];  // [stage][Q, dO]
   __shared__ __attribute__((aligned(16))) float sld[2][2][AT];              // [stage][lse log2e, delta]
   const int item = blockIdx.x, h = blockIdx.y, H = a.H;
-  const int t = a.kw_tile[item], q0 = a.kw_q0[item], nq = a.kw_nq[item], slot = a.kw_slot[item];
-  const int seg = a.tile_seg[t], koff = a.tile_off[t];
-  const int klen = min(AT, a.seg_len[seg] - koff), krow0 = a.seg_row[seg] + koff;
+  const int t = ld_uni(a.kw_tile, item), q0 = ld_uni(a.kw_q0, item), nq = ld_uni(a.kw_nq, item);
+  const int slot = ld_uni(a.kw_slot, item);
+  const int seg = ld_uni(a.tile_seg, t), koff = ld_uni(a.tile_off, t);
+  const int klen = min(AT, ld_uni(a.seg_len, seg) - koff), krow0 = ld_uni(a.seg_row, seg) + koff;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int kj = 16 * wave + l16;              // this lane's key (column of S)
   const int krow = krow0 + min(kj, klen - 1);
@@ -515,35 +541,46 @@ __global__ __launch_bounds__(ANT, 2) void k_attn_dkv(AttnArgs a) {
   f32x4 dkt[NDB], dvt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dkt[db] = dvt[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int e0 = a.kq_ptr[t] + q0;
-  float rl = 0.f, rd = 0.f;   // lse / delta of row tid of the query tile in flight (tid < 64)
-  auto stage = [&](int st, int i) {
-    const int u = a.kq[e0 + i];
-    const int qseg = a.tile_seg[u], qoff = a.tile_off[u];
-    const int qlen = min(AT, a.seg_len[qseg] - qoff), qrow0 = a.seg_row[qseg] + qoff;
-    tile_dma<D, ANT / 64>(sm[st][0], a.q, qrow0, qlen, H, h);
-    tile_dma<D, ANT / 64>(sm[st][1], a.dO, qrow0, qlen, H, h);
-    if (tid < AT) {
-      const bool ok = tid < qlen;
-      const size_t o = (size_t)(qrow0 + (ok ? tid : 0)) * H + h;
-      rl = ok ? a.lsec[o] * 1.4426950408889634f : 0.f;
-      rd = ok ? a.delta[o] : 0.f;
-    }
+  const int e0 = ld_uni(a.kq_ptr, t) + q0;
+  // query tile i of the item: its segment's offset, its length, whether it is
+  // in the key tile's own segment, its first row (plan values: scalar loads)
+  struct QTile { int qoff, qlen, qrow0; bool own; };
+  auto qtile = [&](int i) {
+    const int u = ld_uni(a.kq, e0 + i);
+    const int qseg = ld_uni(a.tile_seg, u), qoff = ld_uni(a.tile_off, u);
+    return QTile{qoff, min(AT, ld_uni(a.seg_len, qseg) - qoff), ld_uni(a.seg_row, qseg) + qoff, qseg == seg};
   };
-  if (nq > 0) stage(0, 0);
+  float rl = 0.f, rd = 0.f;   // raw lse / delta of row tid of the query tile in flight (tid < 64)
+  auto stage = [&](int st, const QTile& q) {
+    // lse and delta before the tiles: a wait for them is no wait for the tiles
+    // (rows past the tile repeat its last row; their scores are masked)
+    if (tid < AT) {
+      const size_t o = (size_t)(q.qrow0 + min(tid, q.qlen - 1)) * H + h;
+      rl = a.lsec[o];
+      rd = a.delta[o];
+    }
+    tile_dma<D, ANT / 64>(sm[st][0], a.q, q.qrow0, q.qlen, H, h);
+    tile_dma<D, ANT / 64>(sm[st][1], a.dO, q.qrow0, q.qlen, H, h);
+  };
+  QTile cur{0, 0, 0, false};
+  if (nq > 0) {
+    cur = qtile(0);
+    stage(0, cur);
+  }
   for (int i = 0, st = 0; i < nq; ++i, st ^= 1) {
-    const int u = a.kq[e0 + i];
-    const int qseg = a.tile_seg[u], qoff = a.tile_off[u];
-    const int qlen = min(AT, a.seg_len[qseg] - qoff);
-    const bool own = qseg == seg;
+    const int qoff = cur.qoff, qlen = cur.qlen;
+    const bool own = cur.own;
     const bool full = !own && qlen == AT && klen == AT;
+    QTile nxt{0, 0, 0, false};
+    if (i + 1 < nq) nxt = qtile(i + 1);   // in flight across the wait below
     __builtin_amdgcn_s_waitcnt(0);   // this query tile has landed (tiles and rl / rd)
     if (tid < AT) {
-      sld[st][0][tid] = rl;
+      sld[st][0][tid] = rl * 1.4426950408889634f;
       sld[st][1][tid] = rd;
     }
     __syncthreads();
-    if (i + 1 < nq) stage(st ^ 1, i + 1);
+    if (i + 1 < nq) stage(st ^ 1, nxt);
+    cur = nxt;
     const unsigned char* Qt = sm[st][0];
     const unsigned char* Ot = sm[st][1];
     f32x4 sp[4], dp[4];   // S and dP tiles [query block], then P and dS

@@ -399,25 +399,31 @@ __device__ inline void lds_copy_async(void* dst, const unsigned char* src, int n
 // builtin and no indirectly indexed registers, the compiler's uses of M0).
 // Part `part` of NPART of it: each wave's pieces split into NPART runs, so
 // that the copy can be issued in steps between other work.
+// One such load: lane l's 16 bytes at gp go to LDS bytes m + 16 l (m
+// wave-uniform, an LDS byte address).
+__device__ inline void lds_load16_untracked(const void* gp, unsigned m) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gp), "s"(m)
+               : "memory");
+}
+// LDS byte address of a shared-memory pointer
+__device__ inline unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
 template <int NPART = 1>
 __device__ inline void lds_copy_async_untracked(void* dst, const unsigned char* src, int nvec,
                                                 int part = 0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const unsigned base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)dst;
+  const unsigned base = lds_addr(dst);
   const int per_wave = ((nvec + 63) / 64 + NW - 1) / NW;
   const int j0 = part * per_wave / NPART, j1 = (part + 1) * per_wave / NPART;
   for (int j = j0; j < j1; ++j) {
     const int p = wave + NW * j;
     if (64 * p >= nvec) break;
     const int e = 64 * p + lane;
-    if (e < nvec) {
-      const unsigned char* gp = src + 16 * (size_t)e;
-      const unsigned m = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)p);
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(gp), "s"(m)
-                   : "memory");
-    }
+    if (e < nvec)
+      lds_load16_untracked(src + 16 * (size_t)e, __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)p));
   }
 }
 
