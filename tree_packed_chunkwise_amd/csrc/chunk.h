@@ -372,35 +372,17 @@ static_assert(sizeof(FwdImage<64, 128, float>) == fwd_image_bytes(64, 128), "ima
 static_assert(sizeof(FwdImage<16, 64, uint16_t>) == fwd_image_used(16, 64, 2), "image layout");
 static_assert(sizeof(FwdHead<64, 128>) == fwd_image_head_bytes(64, 128), "image layout");
 
-// Asynchronous copy of `nvec` 16-byte vectors from global memory into LDS
-// (global_load_lds_dwordx4: the data goes straight to LDS, no registers).
-// Wave w moves the 1 KB pieces w, w + 8, ...; lane l of a piece moves its
-// 16 bytes to piece base + 16 l.  Completion is the caller's: s_waitcnt
-// vmcnt(0), then a barrier, before any wave reads the copy.
-__device__ inline void lds_copy_async(void* dst, const unsigned char* src, int nvec) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int p = wave; 64 * p < nvec; p += NW) {
-    const int e = 64 * p + lane;
-    if (e < nvec)
-      __builtin_amdgcn_global_load_lds((const void*)(src + 16 * (size_t)e),
-                                       (__attribute__((address_space(3))) void*)((char*)dst + 1024 * p),
-                                       16, 0, 0);
-  }
-}
-// The same copy, issued so that the compiler does not see it: it places no
-// wait of its own for the copy before later LDS reads (for reads whose
-// memory operands it knows, e.g. the transposing reads, it would wait for
-// every copy in flight, however disjoint the addresses).  The caller's
-// s_waitcnt vmcnt(0) and barrier complete it.  The instruction writes LDS
-// only (no register results).  M0 holds the LDS base of the wave's piece,
+// One global_load_lds_dwordx4 (the data goes straight to LDS, no registers):
+// lane l's 16 bytes at gp go to LDS bytes m + 16 l (m wave-uniform, an LDS
+// byte address).  It is issued from inline assembly so that the compiler does
+// not see it and places no wait of its own for it before later LDS reads (for
+// reads whose memory operands it knows, e.g. the transposing reads, it would
+// wait for every copy in flight, however disjoint the addresses); the
+// caller's s_waitcnt vmcnt(0) and barrier complete it.  M0 holds the LDS base,
 // written in the same statement, one wait state before the load that reads
 // it; M0 is a reserved register, which a clobber list cannot protect, so the
-// kernels that issue this copy keep nothing else in it (they use no LDS-DMA
+// kernels that issue these loads keep nothing else in it (they use no LDS-DMA
 // builtin and no indirectly indexed registers, the compiler's uses of M0).
-// Part `part` of NPART of it: each wave's pieces split into NPART runs, so
-// that the copy can be issued in steps between other work.
-// One such load: lane l's 16 bytes at gp go to LDS bytes m + 16 l (m
-// wave-uniform, an LDS byte address).
 __device__ inline void lds_load16_untracked(const void* gp, unsigned m) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
@@ -411,6 +393,11 @@ __device__ inline void lds_load16_untracked(const void* gp, unsigned m) {
 __device__ inline unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) const char*)p;
 }
+// Asynchronous copy of `nvec` 16-byte vectors from global memory into LDS by
+// such loads: wave w moves the 1 KB pieces w, w + NW, ...; lane l of a piece
+// moves its 16 bytes to piece base + 16 l.  Part `part` of NPART of it: each
+// wave's pieces split into NPART runs, so that the copy can be issued in
+// steps between other work.
 template <int NPART = 1>
 __device__ inline void lds_copy_async_untracked(void* dst, const unsigned char* src, int nvec,
                                                 int part = 0) {

@@ -293,9 +293,12 @@ __global__ __launch_bounds__(NT) void k_bwd_grad(BwdArgs a, int c_begin) {
   // later ones are still in flight.  LDS writes and register layouts come
   // where they are needed. ----
   const int c0 = tid % DH, rg = tid / DH, r0 = rg * RPT;  // element mapping: channel c0 + 64 hf, rows r0 ..
+  // the row indices are wave-uniform (a wave's lanes share rows r0 ..): scalar
+  // loads, so that the input loads they address wait for no vector load
+  const int r0w = __builtin_amdgcn_readfirstlane(r0);
   int rows[RPT];
 #pragma unroll
-  for (int t = 0; t < RPT; ++t) rows[t] = r0 + t < len ? a.plan.row_index[row0 + r0 + t] : -1;
+  for (int t = 0; t < RPT; ++t) rows[t] = r0w + t < len ? ld_uni(a.plan.row_index, row0 + r0w + t) : -1;
   int trow = -1, torow = -1;  // row table entries (tid < BC)
   if (tid < BC && tid < len) {
     trow = a.plan.row_index[row0 + tid];
