@@ -99,8 +99,8 @@ DOMINANT = "kda_bwd_chunk_grad"
 
 MEASURED_TRAFFIC = {
     "kda_bwd_chunk_grad": {"sources": ("kda_grad.hip", "chunk.h", "common.h"),
-                           "sha256_16": "00a41afb3cef0722", "workload": 2,
-                           "bytes_per_launch": 2194198383},
+                           "sha256_16": "13478cf6bd36288a", "workload": 2,
+                           "bytes_per_launch": 2197249232},
 }
 
 
