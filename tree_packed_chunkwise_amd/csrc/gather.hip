@@ -5,13 +5,14 @@
 // distinct targets; Figure C.1(d): no expanded vocabulary-sized logits.
 //
 //   k_row_lse   one block per compact row: online max / sum-of-exp over the
-//               vocabulary in one pass (16-byte loads), fixed-order tree
-//               reduction -> lse[row]
+//               vocabulary in one pass (16-byte loads, one rescale per load),
+//               fixed-order tree reduction -> lse[row]
 //   k_pos_logp  one thread per position: logits[row, tgt] - lse[row]
 //   k_row_grad  one block per compact row: w = sum of the row's dlogp (CSR
-//               order); every element -softmax * w, then the row's target
+//               order); every element -softmax * w (16-byte loads and
+//               stores), then the row's target
 //               columns get their exact value (-softmax*w + sum of dlogp of the
-//               positions targeting that column), written by one thread.
+//               positions targeting that column), one position per thread.
 // HBM-bound: each logit is read once per pass and each gradient written once.
 //
 // Masked entries: a logit of -inf has probability zero (it adds nothing to
@@ -57,6 +58,24 @@ __device__ inline void online_merge(float& m, float& s, float m2, float s2) {
   }
 }
 
+// a run of n logits into (m, s) at once: one rescale for the run's maximum,
+// then its exponentials (-inf logits add nothing; an all -inf run changes nothing)
+template <int N>
+__device__ inline void online_add_run(float& m, float& s, const float (&x)[N]) {
+  float mx = x[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) mx = __builtin_fmaxf(mx, x[j]);
+  if (mx == -INFINITY) return;
+  if (mx > m) {
+    s *= __expf(m - mx);   // 0 while m = -inf
+    m = mx;
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < N; ++j) t += __expf(x[j] - m);
+  s += t;
+}
+
 template <typename T>
 __device__ inline void row_stats(const T* z, int vocab, float& m, float& s, float* sm, float* ss) {
   m = -INFINITY;
@@ -67,11 +86,14 @@ __device__ inline void row_stats(const T* z, int vocab, float& m, float& s, floa
   if ((((uintptr_t)z) % 16) == 0) {
     typedef __attribute__((__vector_size__(16))) int v4i;
     const v4i* zv = (const v4i*)z;
+#pragma unroll 2
     for (int i = tid; i < nvec; i += GT) {
       v4i pk = zv[i];
       const T* e = (const T*)&pk;
+      float x[VEC];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) online_add(m, s, ld_logit(e, j));
+      for (int j = 0; j < VEC; ++j) x[j] = ld_logit(e, j);
+      online_add_run(m, s, x);
     }
     for (int i = nvec * VEC + tid; i < vocab; i += GT) online_add(m, s, ld_logit(z, i));
   } else {
@@ -126,17 +148,34 @@ __global__ __launch_bounds__(GT) void k_row_grad(const T* logits, int vocab, con
   const bool dead = l == -INFINITY;   // every entry masked: softmax taken as 0
   const T* z = logits + row * vocab;
   T* dz = dlogits + row * vocab;
-  for (int i = tid; i < vocab; i += GT)
+  int done = 0;   // elements the 16-byte loop covers
+  if (((((uintptr_t)z) | ((uintptr_t)dz)) % 16) == 0) {
+    typedef __attribute__((__vector_size__(16))) int v4i;
+    constexpr int VEC = 16 / sizeof(T);
+    const int nvec = vocab / VEC;
+#pragma unroll 2
+    for (int i = tid; i < nvec; i += GT) {
+      const v4i pk = ((const v4i*)z)[i];
+      v4i out;
+      const T* e = (const T*)&pk;
+      T* o = (T*)&out;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) st_logit(o, j, dead ? 0.f : -__expf(ld_logit(e, j) - l) * w);
+      ((v4i*)dz)[i] = out;
+    }
+    done = nvec * VEC;
+  }
+  for (int i = done + tid; i < vocab; i += GT)
     st_logit(dz, i, dead ? 0.f : -__expf(ld_logit(z, i) - l) * w);
   __syncthreads();
-  if (tid == 0) {
-    for (int p = p0; p < p1; ++p) {
-      const int t = pos_tgt[row_pos_idx[p]];
-      float acc = dead ? 0.f : -__expf(ld_logit(z, t) - l) * w;
-      for (int p2 = p0; p2 < p1; ++p2)
-        if (pos_tgt[row_pos_idx[p2]] == t) acc += dlogp[row_pos_idx[p2]];
-      st_logit(dz, t, acc);
-    }
+  // target columns, one position per thread: positions sharing a target sum
+  // the same terms in the same (CSR) order and write the same value
+  for (int q = p0 + tid; q < p1; q += GT) {
+    const int t = pos_tgt[row_pos_idx[q]];
+    float acc = dead ? 0.f : -__expf(ld_logit(z, t) - l) * w;
+    for (int p2 = p0; p2 < p1; ++p2)
+      if (pos_tgt[row_pos_idx[p2]] == t) acc += dlogp[row_pos_idx[p2]];
+    st_logit(dz, t, acc);
   }
 }
 
