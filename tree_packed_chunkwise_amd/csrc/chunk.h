@@ -389,6 +389,18 @@ __device__ inline void lds_load16_untracked(const void* gp, unsigned m) {
                : "v"(gp), "s"(m)
                : "memory");
 }
+// The same load with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset (address = sbase + voff): a copy whose lanes keep one
+// offset for all its pieces holds no per-piece 64-bit addresses in registers.
+// (Held across a copy, such addresses were spilled to scratch, and the wait
+// for a reload waited for the pieces already issued: vector loads complete in
+// order.)
+__device__ inline void lds_load16_untracked(const void* sbase, unsigned voff, unsigned m) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m)
+               : "memory");
+}
 // LDS byte address of a shared-memory pointer
 __device__ inline unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) const char*)p;
@@ -401,16 +413,15 @@ __device__ inline unsigned lds_addr(const void* p) {
 template <int NPART = 1>
 __device__ inline void lds_copy_async_untracked(void* dst, const unsigned char* src, int nvec,
                                                 int part = 0) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const unsigned base = lds_addr(dst);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const unsigned base = lds_addr(dst), voff = 16u * (unsigned)lane;
   const int per_wave = ((nvec + 63) / 64 + NW - 1) / NW;
   const int j0 = part * per_wave / NPART, j1 = (part + 1) * per_wave / NPART;
   for (int j = j0; j < j1; ++j) {
     const int p = wave + NW * j;
     if (64 * p >= nvec) break;
-    const int e = 64 * p + lane;
-    if (e < nvec)
-      lds_load16_untracked(src + 16 * (size_t)e, __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)p));
+    if (64 * p + lane < nvec)
+      lds_load16_untracked(src + 1024 * (size_t)p, voff, base + 1024u * (unsigned)p);
   }
 }
 
