@@ -272,37 +272,49 @@ __device__ inline f16x8 lds_a_perm_tr(const _Float16* X, int pitch, int r0, int 
 
 // The chunk image's fp16 arrays are stored without padding; within a row of
 // W halves, the 8-byte piece q (halves 4q .. 4q + 3) of row r sits at piece
-// q ^ s(r), where s(r) takes the low four row bits with their two halves
-// swapped (masked to the row's piece count when a row has fewer than 16
-// pieces).  LDS serves 16 lanes of 8 bytes per cycle over 32 banks: the row
-// fragment reads (16 rows, one piece each) and the transposing reads (4 rows
-// x 4 consecutive pieces) then touch 16 distinct 8-byte bank pairs.
+// q ^ s(r).  Measured on gfx950 (SQ_LDS_BANK_CONFLICT of probe kernels): an
+// 8-byte row read is served 16 lanes at a time over 32 four-byte banks, a
+// transposing read 32 lanes at a time over 64 banks.  The row fragment reads
+// (16 rows, one piece each) need s distinct modulo 16 over each aligned 16
+// rows; the transposing reads (two groups of 4 rows x 4 consecutive pieces)
+// need, for rows of 32 pieces, bits 2-4 of s distinct over each aligned 8
+// rows and, for rows of 16 pieces (a row pair spans the 64 banks), bits 2-3
+// distinct over the 4 rows of one parity among each aligned 8.  s depends on
+// the row modulo 16.
 template <int W>
-__device__ inline int swz_mask() {
-  return W / 4 < 16 ? W / 4 - 1 : 15;
+__device__ inline int swz_term(int r) {
+  if constexpr (W / 4 >= 32)        // 32 pieces: the low four bits with their halves swapped, plus bit 2 as bit 4
+    return ((r & 3) << 2) | ((r >> 2) & 3) | (((r >> 2) & 1) << 4);
+  else if constexpr (W / 4 == 16)   // 16 pieces: bits 1-2 as bits 2-3, bit 3 as bit 1, bit 0
+    return (((r >> 1) & 3) << 2) | (((r >> 3) & 1) << 1) | (r & 1);
+  else                              // fewer: the halves-swapped low bits, masked to the row
+    return (((r & 3) << 2) | ((r >> 2) & 3)) & (W / 4 - 1);
 }
-__device__ inline int swz_rot(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 template <int W>
 __device__ inline int swz(int r, int c) {
-  return (((c >> 2) ^ (swz_rot(r) & swz_mask<W>())) << 2) | (c & 3);
+  return (((c >> 2) ^ swz_term<W>(r)) << 2) | (c & 3);
 }
-// piece q0 (a compile-time multiple of 4 in the callers) XORed with the
-// lane's term t < 16: the high bits stay an immediate offset, only the low
-// four bits combine with t
-__device__ inline int swz_piece(int q0, int t) { return (q0 & ~15) | ((q0 & 15) ^ t); }
+// piece q0 (compile-time in the callers) XORed with the lane's term t (below
+// the row's piece count, at most 32): the bits above the term's stay an
+// immediate offset
+template <int W>
+__device__ inline int swz_piece(int q0, int t) {
+  constexpr int M = W / 4 >= 32 ? 31 : 15;
+  return (q0 & ~M) | ((q0 & M) ^ t);
+}
 // lds_a_perm on a swizzled [*][W] array; row = 16 J + l16 (J compile-time)
 template <int W>
 __device__ inline f16x8 lds_a_perm_sw(const _Float16* base, int row, int kb, int g,
                                       bool half_only = false) {
-  const int t = (g ^ swz_rot(row)) & swz_mask<W>();   // kb / 4 is a multiple of 4: g fills bits 0-1
+  const int t = g ^ swz_term<W>(row);   // kb / 4 is a multiple of 4: g fills bits 0-1
   const _Float16* rp = base + row * W;
-  const f16x4 lo = *(const f16x4*)(rp + 4 * swz_piece(kb >> 2, t));
+  const f16x4 lo = *(const f16x4*)(rp + 4 * swz_piece<W>(kb >> 2, t));
   f16x8 r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   if (half_only) {
     r[4] = r[5] = r[6] = r[7] = (_Float16)0.f;
   } else {
-    const f16x4 hi = *(const f16x4*)(rp + 4 * swz_piece((kb + 16) >> 2, t));
+    const f16x4 hi = *(const f16x4*)(rp + 4 * swz_piece<W>((kb + 16) >> 2, t));
     r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   }
   return r;
@@ -314,8 +326,8 @@ __device__ inline f16x4 lds_tr4_sw(const _Float16* X, int r0, int c0) {
   typedef short s16x4_t __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
   const int rl = 4 * g + (s >> 2);                          // row within the 16-row block
-  const int t = ((s & 3) ^ swz_rot(rl)) & swz_mask<W>();
-  const _Float16* p = X + (r0 + rl) * W + 4 * swz_piece(c0 >> 2, t);
+  const int t = (s & 3) ^ swz_term<W>(rl);
+  const _Float16* p = X + (r0 + rl) * W + 4 * swz_piece<W>(c0 >> 2, t);
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
   return __builtin_bit_cast(f16x4, v);
 }

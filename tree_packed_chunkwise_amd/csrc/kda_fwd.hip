@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NT) void k_fwd_round(FwdArgs a, int seq_begin) {
         ft[I] = *(const f16x4*)&s.Td[16 * I + l16][4 * g];
 #pragma unroll
         for (int J = 0; J < I; ++J)   // columns 16 J + 4 g .. of the swizzled row
-          fl[I][J] = *(const f16x4*)&s.L[16 * I + l16][4 * swz_piece(4 * J, (g ^ swz_rot(l16)) & swz_mask<BC>())];
+          fl[I][J] = *(const f16x4*)&s.L[16 * I + l16][4 * swz_piece<BC>(4 * J, g ^ swz_term<BC>(l16))];
       }
       f32x4 bz[G::NB];
 #pragma unroll
