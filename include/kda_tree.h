@@ -430,9 +430,11 @@ int moe_router_stats_bwd(const void* logits, int32_t dtype, int64_t n_rows, int3
  *   a fixed order, so results are deterministic).
  * scale must be positive and finite (the kernels take each query's running
  * maximum over unscaled scores).
- * Errors: KDA_ERR_SHAPE for other head dims, KDA_ERR_ARG for null pointers or
- * a scale that is not positive and finite, KDA_ERR_WORKSPACE for a small
- * workspace, KDA_ERR_HIP for launch failures.
+ * Tensors, o and ws are 16-byte aligned, lse 4-byte aligned (rows move in
+ * 16-byte vectors).
+ * Errors: KDA_ERR_SHAPE for other head dims, KDA_ERR_ARG for null or
+ * misaligned pointers or a scale that is not positive and finite,
+ * KDA_ERR_WORKSPACE for a small workspace, KDA_ERR_HIP for launch failures.
  */
 size_t tree_attn_workspace_bytes(const kda_plan* plan, int32_t H, int32_t d);
 int tree_attn_fwd(const kda_plan* plan, const void* dev_plan, int32_t H, int32_t d, float scale,
