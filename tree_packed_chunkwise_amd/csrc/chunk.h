@@ -432,8 +432,15 @@ __device__ inline void lds_copy_async_untracked(void* dst, const unsigned char* 
   for (int j = j0; j < j1; ++j) {
     const int p = wave + NW * j;
     if (64 * p >= nvec) break;
-    if (64 * p + lane < nvec)
-      lds_load16_untracked(src + 1024 * (size_t)p, voff, base + 1024u * (unsigned)p);
+    if (64 * p + lane < nvec) {
+      // the scalar operands made wave-uniform explicitly (at low optimisation
+      // levels the compiler does not prove it)
+      const size_t sb = (size_t)(src + 1024 * (size_t)p);
+      const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)sb);
+      const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(sb >> 32));
+      lds_load16_untracked((const void*)(((size_t)hi << 32) | lo), voff,
+                           __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)p));
+    }
   }
 }
 
