@@ -99,8 +99,8 @@ DOMINANT = "kda_bwd_chunk_grad"
 
 MEASURED_TRAFFIC = {
     "kda_bwd_chunk_grad": {"sources": ("kda_grad.hip", "chunk.h", "common.h"),
-                           "sha256_16": "6df63653aa2bb3a9", "workload": 2,
-                           "bytes_per_launch": 2197082704},
+                           "sha256_16": "d71ffa3564731483", "workload": 2,
+                           "bytes_per_launch": 2196944092},
 }
 
 
