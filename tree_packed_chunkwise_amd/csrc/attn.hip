@@ -12,8 +12,11 @@
 //             ds_rj = p_rj (dp_rj - delta_r),  dq_r = scale sum_j ds_rj k_j,
 //             dk_j = scale sum_r ds_rj q_r,  dv_j = sum_r p_rj do_r
 //
-// Tiles of 64 rows; 4 waves per block, each wave owning 16 query rows (forward,
-// dq) or 16 key rows (dk / dv).  Scores are formed transposed on bf16 matrix
+// Tiles of 64 rows; 4 waves per block.  Forward and dq blocks take two
+// consecutive query tiles of a segment (128 rows), each wave 32 of them
+// against whole key tiles; a dk / dv block takes one key tile, each wave 16
+// of its keys against whole query tiles.  Key or query tiles are copied into
+// LDS asynchronously, double-buffered.  Scores are formed transposed on bf16 matrix
 // cores from the exact bf16 inputs, S^T = K Q^T, so that the accumulator tile
 // of probabilities (keys down, queries across) is, split into hi/lo bf16, the
 // B operand of O^T = V^T P^T without leaving registers (the k order of the
