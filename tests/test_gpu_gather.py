@@ -29,13 +29,32 @@ def _dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
 
 
+def _star(n_children):
+    """A root segment of 20 rows with `n_children` leaf segments of 3 rows: the
+    root's last row predicts the first token of every child, so that one
+    logit row carries n_children positions."""
+    parent = np.array([-1] + [0] * n_children, dtype=np.int32)
+    seg_len = np.array([20] + [3] * n_children, dtype=np.int32)
+    seg_row = np.concatenate([[0], 20 + 3 * np.arange(n_children)]).astype(np.int64)
+    return synth.TreeSpec(parent, seg_len, seg_row, f"star{n_children}")
+
+
 @pytest.mark.parametrize("spec_name,vocab,bf16", [
     ("fig1", 1000, False), ("fig1", 1000, True), ("fig1", 1001, True),
-    ("random", 4096, True), ("random", 777, False)])
+    ("random", 4096, True), ("random", 777, False),
+    # a row with more positions than a block has threads (its target columns
+    # are written in several passes, some targets shared), a vocabulary
+    # shorter than one 16-byte load, fp32 logits on the 16-byte path
+    ("star300", 1000, True), ("fig1", 5, True), ("fig1", 4096, False)])
 def test_gather_small(spec_name, vocab, bf16):
     import torch
     rng = np.random.Generator(np.random.PCG64(11 + vocab))
-    spec = synth.tree_fig1() if spec_name == "fig1" else synth.tree_random(rng, 12, 1, 40, 2)
+    if spec_name == "fig1":
+        spec = synth.tree_fig1()
+    elif spec_name == "star300":
+        spec = _star(300)
+    else:
+        spec = synth.tree_random(rng, 12, 1, 40, 2)
     plan = B.KDAPlan(spec.parent, spec.seg_len, spec.seg_row, 16)
     N = plan.info["n_rows"]
     pos_row, pos_next, rp_ptr, rp_idx = _maps(plan)
