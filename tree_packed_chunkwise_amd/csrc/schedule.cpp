@@ -14,7 +14,7 @@
 //             gradient found); dO of the last round's chunks gathered (the
 //             rest on the second stream beside that round); rounds last to
 //             first; once
-//             the chunks whose rounds are done amount to half of all
+//             the chunks whose rounds are done amount to a quarter of all
 //             chunks, their chunk-local gradients run on the second stream
 //             beside the remaining rounds; the rest after round 0; the
 //             second stream is joined before the fixed-order reductions.
@@ -183,7 +183,7 @@ hipError_t run_bwd(const BwdArgs& a, bool bf16, int BC, int D, const Plan& p, hi
   } else {
     KDA_TRY(launch_gather_dO(a, bf16, BC, D, 0, nc, st));
   }
-  const int group = nc / 2 > 1 ? nc / 2 : 1;
+  const int group = nc / 4 > 1 ? nc / 4 : 1;
   int ready_end = nc;   // chunks [ready_end, nc) have their gradients launched
   bool forked = false;
   for (int r = R - 1; r >= 0; --r) {
